@@ -1,0 +1,232 @@
+"""Benchmark of the LoRA hot path on one MI355X.
+
+One step = one single-adapter forward + backward pass over a batch:
+lora_fwd (Y += s*(X*A)*B), lora_bwd_dx_da (dX, dA), lora_bwd_db (dB), on the
+bf16-in / fp32-out workload M = 8192 tokens (4 x 2048), K = L = 4096, rank 16,
+s = 2.0 (synthetic seeded data, see synth/). Inputs are resident in HBM before
+the timed region; several copies of the streamed tensors rotate so that
+successive steps do not read the previous step's data from the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line with the throughput (tokens/s over the whole step), the
+step's algorithmic HBM bandwidth, a roofline entry for the dominant kernel
+(the fused forward: algorithmic bytes / its average duration measured with
+HIP events on its stream), and the CPU oracle's throughput on the same
+workload as a baseline.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "LoRA fwd+bwd tokens/s and achieved HBM GB/s (% of roofline), 1×MI355X"
+
+WORKLOADS = {
+    # name: (M, K, L, r, scale, seed)
+    "single-bf16-M8192-K4096-L4096-r16": (8192, 4096, 4096, 16, 2.0, 2),
+    "single-bf16-M16384-K4096-L14336-r64": (16384, 4096, 14336, 64, 0.5, 3),
+}
+DEFAULT_WORKLOAD = "single-bf16-M8192-K4096-L4096-r16"
+
+
+def algorithmic_bytes(M, K, L, r, es=2):
+    """Bytes each call must move at least once (streamed tensors once, weights
+    once, fp32 outputs; on-chip intermediates not counted)."""
+    fwd = M * (es * K + 8 * L) + es * r * (K + L)
+    dxda = M * (es * L + 4 * K + es * K) + es * r * (K + L) + 4 * K * r
+    db = M * (es * K + es * L) + es * r * K + 4 * r * L
+    return {"fwd": fwd, "dx_da": dxda, "db": db}
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = ["lora_rank_adapter_amd/csrc/lora_single.hip", "lora_rank_adapter_amd/csrc/lora_device.hpp"]
+
+
+def traffic_from_profile(workload):
+    """HBM traffic of the forward kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_fwd_" + workload + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(KERNEL_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, min_seconds=10.0, max_runs=20):
+    """The fp64 CPU oracle on the same batch, repeated for >= min_seconds."""
+    import threadpoolctl
+
+    import oracle
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
+        t0 = time.perf_counter()
+        oracle.lora_fwd(case.X, case.A, case.B, case.Y0, case.scale)
+        oracle.lora_bwd_dx_da(case.X.T, case.dY, case.B.T, case.A.T, case.scale)
+        oracle.lora_bwd_db(case.A.T, case.X.T, case.dY, case.scale)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    return {
+        "value": case.M / med,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"whole batch ({case.M} tokens), fwd+bwd_dx_da+bwd_db in float64 numpy, "
+                  f"median of {len(times)} runs ({sum(times):.1f} s total)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the single-adapter and multi-adapter paths run on one MI355X and are not sharded here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lora_rank_adapter_amd as L
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.load_library()
+    dev = torch.device("cuda:0")
+    M, K, Lc, r, scale, seed = WORKLOADS[args.workload]
+    case = synth.single_adapter(M, K, Lc, r, seed=seed, dtype="bf16", scale=scale, name=args.workload)
+
+    def bf16(a):
+        return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    A_w = bf16(np.ascontiguousarray(case.A.T))   # lora_A weight, r x K
+    B_w = bf16(np.ascontiguousarray(case.B.T))   # lora_B weight, L x r
+    X0 = bf16(case.X)
+    dY0 = bf16(case.dY)
+    set_bytes = M * (2 * K + 2 * Lc + 4 * Lc + 4 * K)
+    n_sets = max(2, min(6, int(np.ceil(1.0e9 / set_bytes))))
+    sets = []
+    for i in range(n_sets):
+        sets.append({
+            "X": X0.clone(), "dY": dY0.clone(),
+            "Y": torch.zeros((M, Lc), dtype=torch.float32, device=dev),
+            "dX": torch.empty((M, K), dtype=torch.float32, device=dev),
+        })
+    del X0, dY0
+    dA = torch.empty((K, r), dtype=torch.float32, device=dev)
+    dB = torch.empty((r, Lc), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(L.lora_workspace_bytes(L.LORA_OP_BWD_DX_DA, M, K, Lc, r, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+    ws2 = torch.empty(L.lora_workspace_bytes(L.LORA_OP_BWD_DB, M, K, Lc, r, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+
+    def step(i, ev=None):
+        s = sets[i % n_sets]
+        if ev is not None:
+            ev[0].record()
+        L.lora_fwd(s["X"], A_w.t(), B_w.t(), s["Y"], scale)
+        if ev is not None:
+            ev[1].record()
+        L.lora_bwd_dx_da(s["X"].t(), s["dY"], B_w, A_w, scale, dx=s["dX"], dA=dA, workspace=ws1)
+        if ev is not None:
+            ev[2].record()
+        L.lora_bwd_db(A_w, s["X"].t(), s["dY"], scale, dB=dB, workspace=ws2)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    dxda_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    db_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+
+    ab = algorithmic_bytes(M, K, Lc, r)
+    step_bytes = ab["fwd"] + ab["dx_da"] + ab["db"]
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    fwd_gbs = ab["fwd"] / (fwd_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": M / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": M, "in_features": K, "out_features": Lc, "rank": r,
+                   "scale": scale, "outputs": "fp32", "rotating_input_sets": n_sets},
+        "hbm_gbs": step_gbs,
+        "hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "per_call_ms": {"lora_fwd": fwd_ms, "lora_bwd_dx_da": dxda_ms, "lora_bwd_db": db_ms},
+        "per_call_algorithmic_gbs": {
+            "lora_fwd": fwd_gbs,
+            "lora_bwd_dx_da": ab["dx_da"] / (dxda_ms * 1e-3) / 1e9,
+            "lora_bwd_db": ab["db"] / (db_ms * 1e-3) / 1e9,
+        },
+        "roofline": {
+            "kernel": "fused_kernel (lora_fwd)",
+            "bound": "hbm",
+            "achieved": fwd_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": fwd_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(case),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

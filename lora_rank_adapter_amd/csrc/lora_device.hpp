@@ -1,0 +1,152 @@
+// Device-side building blocks of the gfx950 LoRA kernels: element tags,
+// 128-bit loads, the MFMA steps used by every kernel, and the bf16 hi/lo
+// split that keeps float32 intermediates exact enough for a bf16 MFMA.
+//
+// MFMA conventions (CDNA 16x16 shapes, wave64): for D = A * B + C with
+// A 16 x k and B k x 16, lane l supplies row (l % 16) of A and column (l % 16)
+// of B, each with the contraction values of lane group g = l / 16; lane l
+// holds D[4*g + i][l % 16] for i = 0..3. The kernels only rely on A and B
+// using the same contraction order, which they choose freely.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bfloat16 inputs: 8 elements per 128-bit vector; one 16x16x32 MFMA per vector.
+struct BF16 {
+  using elem = uint16_t;
+  static constexpr int VEC = 8;
+};
+// float32 inputs: 4 elements per 128-bit vector; four 16x16x4 MFMAs per vector.
+struct F32 {
+  using elem = float;
+  static constexpr int VEC = 4;
+};
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ f32x4_t ld16f(const float* p) {
+  return __builtin_bit_cast(f32x4_t, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ void st16f(float* p, f32x4_t v) {
+  *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  __bf16 h = static_cast<__bf16>(v);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// ---------------------------------------------------------------------------
+// contraction step over one 128-bit vector per lane:  acc += A * B
+// (a: A operand vector of this lane, b: B operand vector; same contraction
+// order in both). bf16: 8 values per lane -> one 16x16x32 MFMA. f32: 4 values
+// per lane -> four 16x16x4 MFMAs, the e-th taking value e of every lane.
+// ---------------------------------------------------------------------------
+template <class Tag>
+__device__ __forceinline__ void mma_vec(f32x4_t& acc, uint4 a, uint4 b);
+
+template <>
+__device__ __forceinline__ void mma_vec<BF16>(f32x4_t& acc, uint4 a, uint4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_vec<F32>(f32x4_t& acc, uint4 a, uint4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Operand of a float32 intermediate (h = s*X*A, dYB, XA) against a weight.
+// A lane holds 4 float32 values v[i] of consecutive rank indices.
+//  bf16 path: v = hi + lo with hi = bf16(v), lo = bf16(v - hi) (both exact
+//  roundings, residual <= 2^-17 |v|); the B operand vector is
+//  {hi0..hi3, lo0..lo3} and the matching weight vector is {w0..w3, w0..w3},
+//  so one 16x16x32 MFMA contracts 16 rank indices at float32-like accuracy.
+//  f32 path: the 4 values themselves.
+// ---------------------------------------------------------------------------
+template <class Tag>
+__device__ __forceinline__ uint4 split_frag(f32x4_t v);
+
+template <>
+__device__ __forceinline__ uint4 split_frag<BF16>(f32x4_t v) {
+  uint32_t h0 = bf16_bits(v[0]), h1 = bf16_bits(v[1]), h2 = bf16_bits(v[2]), h3 = bf16_bits(v[3]);
+  uint32_t l0 = bf16_bits(v[0] - bf16_value(h0));
+  uint32_t l1 = bf16_bits(v[1] - bf16_value(h1));
+  uint32_t l2 = bf16_bits(v[2] - bf16_value(h2));
+  uint32_t l3 = bf16_bits(v[3] - bf16_value(h3));
+  return make_uint4(h0 | (h1 << 16), h2 | (h3 << 16), l0 | (l1 << 16), l2 | (l3 << 16));
+}
+
+template <>
+__device__ __forceinline__ uint4 split_frag<F32>(f32x4_t v) {
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Weight vector of 4 consecutive rank columns j0..j0+3 of one weight row, with
+// columns >= r read as zero (so padding, possibly NaN, is never used).
+// bf16: 8-byte aligned row segment, duplicated to {w0..w3, w0..w3}.
+// f32: 16-byte aligned row segment.
+template <class Tag>
+__device__ __forceinline__ uint4 load_wvec4(const typename Tag::elem* row, int j0, int r);
+
+template <>
+__device__ __forceinline__ uint4 load_wvec4<BF16>(const uint16_t* row, int j0, int r) {
+  uint32_t lo, hi;
+  if (j0 + 4 <= r) {
+    uint2 w = *reinterpret_cast<const uint2*>(row + j0);
+    lo = w.x;
+    hi = w.y;
+  } else if (j0 < r) {
+    uint32_t e0 = row[j0];
+    uint32_t e1 = (j0 + 1 < r) ? row[j0 + 1] : 0u;
+    uint32_t e2 = (j0 + 2 < r) ? row[j0 + 2] : 0u;
+    lo = e0 | (e1 << 16);
+    hi = e2;
+  } else {
+    lo = 0u;
+    hi = 0u;
+  }
+  return make_uint4(lo, hi, lo, hi);
+}
+
+template <>
+__device__ __forceinline__ uint4 load_wvec4<F32>(const float* row, int j0, int r) {
+  if (j0 + 4 <= r) return ld16(row + j0);
+  uint4 w = zero4();
+  if (j0 < r) w.x = __float_as_uint(row[j0]);
+  if (j0 + 1 < r) w.y = __float_as_uint(row[j0 + 1]);
+  if (j0 + 2 < r) w.z = __float_as_uint(row[j0 + 2]);
+  return w;
+}
+
+// acc += W(4 rank columns) * frag over 16 rank indices of one rank block.
+template <class Tag>
+__device__ __forceinline__ void mma_rank16(f32x4_t& acc, uint4 wvec, uint4 frag);
+
+template <>
+__device__ __forceinline__ void mma_rank16<BF16>(f32x4_t& acc, uint4 wvec, uint4 frag) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wvec), __builtin_bit_cast(bf16x8_t, frag),
+                                                acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_rank16<F32>(f32x4_t& acc, uint4 wvec, uint4 frag) {
+  mma_vec<F32>(acc, wvec, frag);
+}
+
+}  // namespace lora

@@ -1,0 +1,79 @@
+// Host-side helpers shared by the entry points: argument checks (all done
+// before any launch), sizes, workspace carving and launch-error mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/lora.h"
+
+namespace lora {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+inline size_t elem_size(int32_t dtype) {
+  return dtype == LORA_BF16 ? 2 : (dtype == LORA_F32 ? 4 : 0);
+}
+inline int vec_elems(int32_t dtype) { return dtype == LORA_BF16 ? 8 : 4; }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Rank rounded up to the kernels' rank-block count (1, 2, 4 or 8 blocks of 16).
+inline int rank_blocks(int r) {
+  int rb = static_cast<int>(ceil_div(r, 16));
+  return rb <= 1 ? 1 : rb <= 2 ? 2 : rb <= 4 ? 4 : 8;
+}
+inline int padded_rank(int r) { return 16 * rank_blocks(r); }
+
+// A matrix operand that is streamed row by row with 128-bit loads/stores:
+// unit column stride, 16-byte aligned base and row pitch.
+inline int check_rowmajor_stream(const lora_mat* m) {
+  if (m->stride_col != 1) return LORA_ERR_STRIDE;
+  size_t es = elem_size(m->dtype);
+  if (m->rows > 1 && (m->stride_row < m->cols || (m->stride_row * (int64_t)es) % 16 != 0)) return LORA_ERR_STRIDE;
+  if (!aligned(m->ptr, 16)) return LORA_ERR_STRIDE;
+  return LORA_OK;
+}
+
+// The transposed view of a row-major stream (rows = features, cols = tokens).
+inline int check_colmajor_stream(const lora_mat* m) {
+  if (m->stride_row != 1) return LORA_ERR_STRIDE;
+  size_t es = elem_size(m->dtype);
+  if (m->cols > 1 && (m->stride_col < m->rows || (m->stride_col * (int64_t)es) % 16 != 0)) return LORA_ERR_STRIDE;
+  if (!aligned(m->ptr, 16)) return LORA_ERR_STRIDE;
+  return LORA_OK;
+}
+
+inline bool float_dtype_ok(int32_t d) { return d == LORA_BF16 || d == LORA_F32; }
+
+inline bool valid_dims(const lora_mat* m) {
+  return m->rows >= 0 && m->cols >= 0;
+}
+
+// Carves 256-byte aligned sub-buffers out of a caller workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += static_cast<size_t>(round_up(static_cast<int64_t>(bytes), 256));
+    return p;
+  }
+};
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH;
+}
+
+// Optional tile overrides for tuning sweeps (unset in normal use).
+inline int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+}  // namespace lora

@@ -1,0 +1,650 @@
+// Slot-addressed multi-adapter LoRA ops on gfx950 (API page
+// "mstar.engine.resources.lora.ops", class LoraOpsBackend):
+//   shrink:        h[t] = x[t] @ a[slot(t)]^T          (per output slice)
+//   expand_fused:  y[t, slice i] += sc[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T
+//   gather_shrink: h[t] = a[slot(t)][:, ids[t]]        (the one-hot shrink)
+// plus the token-to-slot grouping that every op reads. The page requires the
+// ops to run with no host sync and no data-dependent shape: grids are sized
+// from host-known bounds (T, S, slice widths) and each workgroup finds its
+// work on the device, exiting early when there is none.
+//
+// Work decomposition: the active tokens of a slot, in grouped order, are cut
+// into tiles of TB tokens; tile k of the batch is found from counts[] with a
+// wave-level scan. Every tile touches one slot's adapter only, so its rows are
+// shared by all tokens of the tile.
+
+#include "lora_device.hpp"
+#include "lora_host.hpp"
+
+namespace lora {
+
+constexpr int kMaxSlots = 1024;
+constexpr int kMaxSlices = 16;
+
+__device__ __forceinline__ int clamp_rank(int v, int r_max) { return v < 0 ? 0 : (v > r_max ? r_max : v); }
+
+// ---------------------------------------------------------------------------
+// grouping: stable counting sort of the active tokens by slot (one workgroup)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ token_slot, int T, int S,
+                                                     const int32_t* __restrict__ ranks, int r_max,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_tokens) {
+  __shared__ int rho[kMaxSlots];
+  __shared__ int cnt[kMaxSlots + 1];
+  __shared__ int base[kMaxSlots + 1];
+  __shared__ int wcnt[16][kMaxSlots + 1];  // per-wave count of each key in the current chunk
+  __shared__ int wsum[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (tid < S) rho[tid] = clamp_rank(ranks[tid], r_max);
+  for (int i = tid; i <= S; i += 1024) {
+    cnt[i] = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) wcnt[w][i] = 0;
+  }
+  __syncthreads();
+
+  // histogram (integer LDS atomics: the counts do not depend on their order)
+  for (int t = tid; t < T; t += 1024) {
+    const int s = token_slot[t];
+    if (s >= 0 && s < S && rho[s] > 0) atomicAdd(&cnt[s], 1);
+  }
+  __syncthreads();
+
+  // exclusive scan of the counts (S <= 1024: one value per thread)
+  const int c = (tid < S) ? cnt[tid] : 0;
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int excl = before + incl - c;
+  if (tid < S) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    base[tid] = excl;
+  }
+  if (tid == S - 1) offsets[S] = excl + c;
+  if (S == 0 && tid == 0) offsets[0] = 0;
+  __syncthreads();
+
+  // stable scatter in chunks of 1024 tokens, token order preserved within a slot
+  int nbits = 0;
+  while ((1 << nbits) <= S) ++nbits;  // keys 0..S (S = inactive)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int t0 = 0; t0 < T; t0 += 1024) {
+    const int t = t0 + tid;
+    int key = S;
+    if (t < T) {
+      const int s = token_slot[t];
+      if (s >= 0 && s < S && rho[s] > 0) key = s;
+    }
+    uint64_t peers = ~0ull;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (key >> bit) & 1;
+      const uint64_t bal = __ballot(on);
+      peers &= on ? bal : ~bal;
+    }
+    const int rank_in_wave = __popcll(peers & lt_mask);
+    const bool leader = (peers & lt_mask) == 0;
+    if (leader) wcnt[wave][key] = __popcll(peers);
+    __syncthreads();
+    if (key < S) {
+      int pos = base[key] + rank_in_wave;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][key];
+      sorted_tokens[pos] = t;
+    }
+    __syncthreads();
+    if (tid < S) {
+      int add = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) add += wcnt[w][tid];
+      base[tid] += add;
+    }
+    __syncthreads();
+    if (leader) wcnt[wave][key] = 0;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tile lookup: tile `ti` of the batch -> (slot, first grouped index, length)
+// ---------------------------------------------------------------------------
+
+struct Tile {
+  int slot;  // -1: no such tile
+  int start;
+  int len;
+};
+
+// Called by one full wave; every lane returns the same tile.
+__device__ Tile find_tile(int ti, int tb, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                          int S) {
+  const int lane = threadIdx.x & 63;
+  int running = 0;
+  Tile out{-1, 0, 0};
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    const int c = (s < S) ? counts[s] : 0;
+    const int nt = (c + tb - 1) / tb;
+    int incl = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const int excl = running + incl - nt;
+    const bool mine = ti >= excl && ti < excl + nt;
+    const uint64_t who = __ballot(mine);
+    if (who) {
+      const int src = __ffsll(static_cast<long long>(who)) - 1;
+      const int k = ti - __shfl(excl, src, 64);
+      const int cs = __shfl(c, src, 64);
+      out.slot = s0 + src;
+      out.start = __shfl(s < S ? offsets[s] : 0, src, 64) + k * tb;
+      out.len = (cs - k * tb) < tb ? (cs - k * tb) : tb;
+      return out;
+    }
+    running += __shfl(incl, 63, 64);
+    if (running > ti) break;
+  }
+  return out;
+}
+
+// ---------------------------------------------------------------------------
+// shrink: h[t, i, j] = sum_k x[t, k] * a[s, i*r_max + j, k], j < rank(s)
+// ---------------------------------------------------------------------------
+
+struct ShrinkArgs {
+  const void* x;
+  int64_t ldx;
+  const void* a;
+  int64_t as0, as1;  // slot and row strides (elements); k is contiguous
+  float* h;
+  int64_t hs0, hs1;  // token and slice strides; j contiguous
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted;
+  const int32_t* ranks;
+  int64_t K;
+  int S, r_max, n_slices, row_chunks;
+};
+
+template <class Tag, int BMB, int RB>
+__global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
+  using E = typename Tag::elem;
+  constexpr int VEC = Tag::VEC;
+  constexpr int CH = 4 * VEC;
+  constexpr int TB = 16 * BMB;
+  constexpr int U = (8 / (BMB + RB)) > 0 ? (8 / (BMB + RB)) : 1;
+  __shared__ f32x4_t red[4][BMB * RB][64];
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int per_tile = p.n_slices * p.row_chunks;
+  const int ti = blockIdx.x / per_tile;
+  const int rem = blockIdx.x - ti * per_tile;
+  const int slice = rem / p.row_chunks;
+  const int j0 = (rem - slice * p.row_chunks) * 16 * RB;
+
+  if (wave == 0) {
+    const Tile tl = find_tile(ti, TB, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  if (j0 >= rho) return;
+  if (threadIdx.x < TB) sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
+  __syncthreads();
+
+  f32x4_t acc[BMB][RB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b)
+#pragma unroll
+    for (int q = 0; q < RB; ++q) acc[b][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const E* xrow[BMB];
+  bool xok[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) {
+    xok[b] = 16 * b + col < tl.len;
+    xrow[b] = static_cast<const E*>(p.x) + (int64_t)sh_tok[16 * b + col] * p.ldx + grp * VEC;
+  }
+  const E* arow[RB];
+  bool aok[RB];
+  const E* a_slot = static_cast<const E*>(p.a) + (int64_t)tl.slot * p.as0;
+#pragma unroll
+  for (int q = 0; q < RB; ++q) {
+    const int j = j0 + 16 * q + col;
+    aok[q] = j < rho;
+    arow[q] = a_slot + (int64_t)(slice * p.r_max + (aok[q] ? j : 0)) * p.as1 + grp * VEC;
+  }
+  bool bany[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) bany[b] = 16 * b < tl.len;
+
+  const int64_t nch = (p.K + CH - 1) / CH;
+  for (int64_t c = wave; c < nch; c += 4 * U) {
+    uint4 xf[U][BMB];
+    uint4 af[U][RB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cc = c + 4 * u;
+      const bool kok = cc < nch && cc * CH + grp * VEC < p.K;
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) xf[u][b] = (kok && xok[b]) ? ld16(xrow[b] + cc * CH) : zero4();
+#pragma unroll
+      for (int q = 0; q < RB; ++q) af[u][q] = (kok && aok[q]) ? ld16(arow[q] + cc * CH) : zero4();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < BMB; ++b)
+        if (bany[b]) {
+#pragma unroll
+          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], af[u][q], xf[u][b]);
+        }
+  }
+
+#pragma unroll
+  for (int b = 0; b < BMB; ++b)
+#pragma unroll
+    for (int q = 0; q < RB; ++q) red[wave][b * RB + q][lane] = acc[b][q];
+  __syncthreads();
+  // wave w stores token blocks w, w+4, ...
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) {
+    if ((b & 3) != wave) continue;
+    if (16 * b + col >= tl.len) continue;
+    float* hrow = p.h + (int64_t)sh_tok[16 * b + col] * p.hs0 + (int64_t)slice * p.hs1;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int i = b * RB + q;
+      f32x4_t s = red[0][i][lane];
+      s += red[1][i][lane];
+      s += red[2][i][lane];
+      s += red[3][i][lane];
+      const int j = j0 + 16 * q + 4 * grp;
+      if (j + 4 <= rho) {
+        st16f(hrow + j, s);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < rho) hrow[j + e] = s[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// expand_fused: y[t, off_i + c] += sc[s] * sum_{j < rank} h[t, i, j] * b[s, off_i + c, j]
+// ---------------------------------------------------------------------------
+
+struct ExpandArgs {
+  const float* h;
+  int64_t hs0, hs1;
+  const void* b;
+  int64_t bs0, bs1;  // slot and row strides; j contiguous
+  float* y;
+  int64_t ldy;
+  const float* scalings;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted;
+  const int32_t* ranks;
+  int S, r_max, n_slices, total_chunks;
+  int64_t slice_off[kMaxSlices];
+  int64_t slice_w[kMaxSlices];
+  int chunk_begin[kMaxSlices + 1];
+};
+
+constexpr int kExpandNBU = 4;                  // 16-column blocks per wave
+constexpr int kExpandCols = 64 * kExpandNBU;   // columns per workgroup
+
+template <class Tag, int BMB, int RBM>
+__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
+  using E = typename Tag::elem;
+  constexpr int TB = 16 * BMB;
+  constexpr int NBU = kExpandNBU;
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int ti = blockIdx.x / p.total_chunks;
+  const int ch = blockIdx.x - ti * p.total_chunks;
+  int slice = 0;
+  while (slice + 1 < p.n_slices && ch >= p.chunk_begin[slice + 1]) ++slice;
+  const int64_t c0 = (int64_t)(ch - p.chunk_begin[slice]) * kExpandCols;
+  const int64_t width = p.slice_w[slice];
+  const int64_t off = p.slice_off[slice];
+
+  if (wave == 0) {
+    const Tile tl = find_tile(ti, TB, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  if (threadIdx.x < TB) sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
+  __syncthreads();
+  const float sc = p.scalings[tl.slot];
+  const int nq = (rho + 15) / 16;
+
+  // (sc * h)^T operand fragments of the tile's tokens; columns >= rank read as 0
+  uint4 hf[BMB][RBM];
+  bool tok_ok[BMB];
+  const float* hrow[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) {
+    tok_ok[b] = 16 * b + col < tl.len;
+    hrow[b] = p.h + (int64_t)sh_tok[16 * b + col] * p.hs0 + (int64_t)slice * p.hs1;
+#pragma unroll
+    for (int q = 0; q < RBM; ++q) {
+      f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int j = 16 * q + 4 * grp;
+      if (tok_ok[b] && q < nq) {
+        if (j + 4 <= rho) {
+          v = ld16f(hrow[b] + j);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < rho) v[e] = hrow[b][j + e];
+        }
+      }
+      v *= sc;
+      hf[b][q] = split_frag<Tag>(v);
+    }
+  }
+
+  const E* b_slot = static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0;
+  // wave w: 16-column blocks w*NBU .. w*NBU+NBU-1 of this chunk
+  uint4 wv[NBU][RBM];
+  f32x4_t cv[NBU][BMB];
+#pragma unroll
+  for (int u = 0; u < NBU; ++u) {
+    const int64_t cb = c0 + (int64_t)(wave * NBU + u) * 16;
+    const int64_t nrow = cb + col;
+    const bool nok = nrow < width;
+    const E* wr = b_slot + (off + (nok ? nrow : 0)) * p.bs1;
+#pragma unroll
+    for (int q = 0; q < RBM; ++q) wv[u][q] = (nok && q < nq) ? load_wvec4<Tag>(wr, 16 * q + 4 * grp, rho) : zero4();
+    const int64_t ncol = cb + 4 * grp;
+#pragma unroll
+    for (int b = 0; b < BMB; ++b) {
+      const bool ok = tok_ok[b] && ncol < width;
+      cv[u][b] = ok ? ld16f(p.y + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NBU; ++u) {
+    const int64_t cb = c0 + (int64_t)(wave * NBU + u) * 16;
+    const int64_t ncol = cb + 4 * grp;
+#pragma unroll
+    for (int b = 0; b < BMB; ++b) {
+      if (16 * b >= tl.len) continue;
+#pragma unroll
+      for (int q = 0; q < RBM; ++q)
+        if (q < nq) mma_rank16<Tag>(cv[u][b], wv[u][q], hf[b][q]);
+      if (tok_ok[b] && ncol < width) st16f(p.y + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol, cv[u][b]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gather_shrink: h[t, 0, j] = a[s, j, ids[t]] (exact), +0.0 for ids outside [0, V)
+// ---------------------------------------------------------------------------
+
+template <class E>
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ ids, const E* __restrict__ a,
+                                                     int64_t as0, int64_t as1, int64_t as2, int64_t V,
+                                                     const int32_t* __restrict__ token_slot,
+                                                     const int32_t* __restrict__ ranks, int T, int S, int r_max,
+                                                     float* __restrict__ h, int64_t hs0) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int s = token_slot[t];
+  if (s < 0 || s >= S) return;
+  const int rho = clamp_rank(ranks[s], r_max);
+  if (rho == 0) return;
+  const int64_t id = ids[t];
+  const bool valid = id >= 0 && id < V;
+  const E* src = a + (int64_t)s * as0 + (valid ? id : 0) * as2;
+  float* dst = h + (int64_t)t * hs0;
+  for (int j = lane; j < rho; j += 64) {
+    float v = 0.0f;
+    if (valid) {
+      if constexpr (sizeof(E) == 2)
+        v = __uint_as_float(static_cast<uint32_t>(src[j * as1]) << 16);
+      else
+        v = src[j * as1];
+    }
+    dst[j] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+static int check_addressing(const lora_addressing* addr, const int32_t* ranks) {
+  if (!addr) return LORA_ERR_NULL;
+  if (addr->T < 0 || addr->S < 0) return LORA_ERR_SHAPE;
+  if (addr->S > kMaxSlots) return LORA_ERR_LIMIT;
+  if (addr->T > 0 && (!addr->token_slot || !addr->sorted_tokens)) return LORA_ERR_NULL;
+  if (!addr->counts && addr->S > 0) return LORA_ERR_NULL;
+  if (!addr->offsets) return LORA_ERR_NULL;
+  if (addr->S > 0 && !ranks) return LORA_ERR_NULL;
+  return LORA_OK;
+}
+
+static int tile_bmb(int T) { return T >= 1024 ? 4 : 1; }
+
+template <class Tag>
+static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
+  if (bmb == 4) {
+    if (rb == 4)
+      hipLaunchKernelGGL((shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((shrink_kernel<Tag, 4, 1>), grid, dim3(256), 0, st, a);
+  } else {
+    if (rb == 4)
+      hipLaunchKernelGGL((shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
+  }
+}
+
+template <class Tag, int BMB>
+static void launch_expand_b(const ExpandArgs& a, int rbm, dim3 grid, hipStream_t st) {
+  switch (rbm) {
+    case 1: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
+  }
+}
+
+template <class Tag>
+static void launch_expand(const ExpandArgs& a, int bmb, int rbm, int64_t tiles, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(tiles * a.total_chunks));
+  if (bmb == 4)
+    launch_expand_b<Tag, 4>(a, rbm, grid, st);
+  else
+    launch_expand_b<Tag, 1>(a, rbm, grid, st);
+}
+
+}  // namespace lora
+
+using namespace lora;
+
+extern "C" int lora_addressing_build(const lora_addressing* addr, const int32_t* ranks, int32_t r_max, void* stream) {
+  const int rc = check_addressing(addr, ranks);
+  if (rc != LORA_OK) return rc;
+  if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
+  if (addr->S > 0 && !addr->counts) return LORA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, st, addr->token_slot, addr->T, addr->S, ranks, r_max,
+                     addr->counts, addr->offsets, addr->sorted_tokens);
+  return launch_status();
+}
+
+extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
+                           int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream) {
+  if (!x || !a || !h) return LORA_ERR_NULL;
+  int rc = check_addressing(addr, ranks);
+  if (rc != LORA_OK) return rc;
+  if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
+  if (num_slices < 1 || num_slices > kMaxSlices) return LORA_ERR_SHAPE;
+  const int64_t T = addr->T, S = addr->S, K = x->cols;
+  if (x->rows != T || x->cols < 0) return LORA_ERR_SHAPE;
+  if (a->d0 != S || a->d1 != (int64_t)num_slices * r_max || a->d2 != K) return LORA_ERR_SHAPE;
+  if (h->d0 != T || h->d1 != num_slices || h->d2 != r_max) return LORA_ERR_SHAPE;
+  if (!float_dtype_ok(x->dtype) || a->dtype != x->dtype || h->dtype != LORA_F32) return LORA_ERR_DTYPE;
+  if ((T * K > 0 && !x->ptr) || (S * K > 0 && !a->ptr) || (T > 0 && !h->ptr)) return LORA_ERR_NULL;
+  const size_t es = elem_size(x->dtype);
+  if (K % vec_elems(x->dtype) != 0) return LORA_ERR_SHAPE;
+  if (T * K > 0 && check_rowmajor_stream(x) != LORA_OK) return LORA_ERR_STRIDE;
+  if (a->s2 != 1 || (a->s1 * (int64_t)es) % 16 != 0 || (a->s0 * (int64_t)es) % 16 != 0 || !aligned(a->ptr, 16))
+    return LORA_ERR_STRIDE;
+  if (h->s2 != 1 || h->s1 % 4 != 0 || h->s0 % 4 != 0 || !aligned(h->ptr, 16)) return LORA_ERR_STRIDE;
+  if (T == 0 || S == 0) return LORA_OK;
+  const int bmb = tile_bmb(static_cast<int>(T));
+  const int rb = (T >= 1024) ? 4 : 1;
+  const int64_t tiles = ceil_div(T, 16 * bmb) + S;
+  ShrinkArgs p{};
+  p.x = x->ptr;
+  p.ldx = x->stride_row;
+  p.a = a->ptr;
+  p.as0 = a->s0;
+  p.as1 = a->s1;
+  p.h = static_cast<float*>(h->ptr);
+  p.hs0 = h->s0;
+  p.hs1 = h->s1;
+  p.counts = addr->counts;
+  p.offsets = addr->offsets;
+  p.sorted = addr->sorted_tokens;
+  p.ranks = ranks;
+  p.K = K;
+  p.S = static_cast<int>(S);
+  p.r_max = r_max;
+  p.n_slices = num_slices;
+  p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (x->dtype == LORA_BF16)
+    launch_shrink<BF16>(p, bmb, rb, tiles, st);
+  else
+    launch_shrink<F32>(p, bmb, rb, tiles, st);
+  return launch_status();
+}
+
+extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing* addr,
+                                 const int32_t* ranks, const float* scalings, const lora_mat* y,
+                                 const int64_t* out_slices, int32_t num_slices, int32_t r_max, void* stream) {
+  if (!h || !b || !y || !out_slices) return LORA_ERR_NULL;
+  int rc = check_addressing(addr, ranks);
+  if (rc != LORA_OK) return rc;
+  if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
+  if (num_slices < 1 || num_slices > kMaxSlices) return LORA_ERR_SHAPE;
+  const int64_t T = addr->T, S = addr->S;
+  int64_t O = 0;
+  for (int i = 0; i < num_slices; ++i) {
+    if (out_slices[i] < 0 || out_slices[i] % 4 != 0) return LORA_ERR_SHAPE;
+    O += out_slices[i];
+  }
+  if (h->d0 != T || h->d1 != num_slices || h->d2 != r_max) return LORA_ERR_SHAPE;
+  if (b->d0 != S || b->d1 != O || b->d2 != r_max) return LORA_ERR_SHAPE;
+  if (y->rows != T || y->cols != O) return LORA_ERR_SHAPE;
+  if (h->dtype != LORA_F32 || !float_dtype_ok(b->dtype) || y->dtype != LORA_F32) return LORA_ERR_DTYPE;
+  if ((T > 0 && !h->ptr) || (S * O > 0 && !b->ptr) || (T * O > 0 && !y->ptr) || (S > 0 && !scalings))
+    return LORA_ERR_NULL;
+  const size_t es = elem_size(b->dtype);
+  if (h->s2 != 1 || h->s1 % 4 != 0 || h->s0 % 4 != 0 || !aligned(h->ptr, 16)) return LORA_ERR_STRIDE;
+  if (b->s2 != 1 || b->s1 % 4 != 0 || b->s0 % 4 != 0 || !aligned(b->ptr, 4 * es)) return LORA_ERR_STRIDE;
+  if (T * O > 0 && check_rowmajor_stream(y) != LORA_OK) return LORA_ERR_STRIDE;
+  if (T == 0 || S == 0 || O == 0) return LORA_OK;
+  ExpandArgs p{};
+  p.h = static_cast<const float*>(h->ptr);
+  p.hs0 = h->s0;
+  p.hs1 = h->s1;
+  p.b = b->ptr;
+  p.bs0 = b->s0;
+  p.bs1 = b->s1;
+  p.y = static_cast<float*>(y->ptr);
+  p.ldy = y->stride_row;
+  p.scalings = scalings;
+  p.counts = addr->counts;
+  p.offsets = addr->offsets;
+  p.sorted = addr->sorted_tokens;
+  p.ranks = ranks;
+  p.S = static_cast<int>(S);
+  p.r_max = r_max;
+  p.n_slices = num_slices;
+  int64_t off = 0;
+  int chunks = 0;
+  for (int i = 0; i < num_slices; ++i) {
+    p.slice_off[i] = off;
+    p.slice_w[i] = out_slices[i];
+    p.chunk_begin[i] = chunks;
+    chunks += static_cast<int>(ceil_div(out_slices[i], kExpandCols));
+    off += out_slices[i];
+  }
+  p.chunk_begin[num_slices] = chunks;
+  p.total_chunks = chunks;
+  if (chunks == 0) return LORA_OK;
+  const int bmb = tile_bmb(static_cast<int>(T));
+  const int rbm = rank_blocks(r_max);
+  const int64_t tiles = ceil_div(T, 16 * bmb) + S;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (b->dtype == LORA_BF16)
+    launch_expand<BF16>(p, bmb, rbm, tiles, st);
+  else
+    launch_expand<F32>(p, bmb, rbm, tiles, st);
+  return launch_status();
+}
+
+extern "C" int lora_gather_shrink(const int32_t* ids, const lora_t3* a, const lora_addressing* addr,
+                                  const int32_t* ranks, int32_t r_max, const lora_t3* h, void* stream) {
+  if (!a || !h) return LORA_ERR_NULL;
+  int rc = check_addressing(addr, ranks);
+  if (rc != LORA_OK) return rc;
+  if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
+  const int64_t T = addr->T, S = addr->S, V = a->d2;
+  if (a->d0 != S || a->d1 != r_max || V < 0) return LORA_ERR_SHAPE;
+  if (h->d0 != T || h->d1 != 1 || h->d2 != r_max) return LORA_ERR_SHAPE;
+  if (!float_dtype_ok(a->dtype) || h->dtype != LORA_F32) return LORA_ERR_DTYPE;
+  if ((T > 0 && (!ids || !h->ptr)) || (S * V > 0 && !a->ptr)) return LORA_ERR_NULL;
+  if (h->s2 != 1) return LORA_ERR_STRIDE;
+  if (T == 0) return LORA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4)));
+  if (a->dtype == LORA_BF16)
+    hipLaunchKernelGGL(gather_kernel<uint16_t>, grid, dim3(256), 0, st, ids, static_cast<const uint16_t*>(a->ptr),
+                       a->s0, a->s1, a->s2, V, addr->token_slot, ranks, static_cast<int>(T), static_cast<int>(S),
+                       r_max, static_cast<float*>(h->ptr), h->s0);
+  else
+    hipLaunchKernelGGL(gather_kernel<float>, grid, dim3(256), 0, st, ids, static_cast<const float*>(a->ptr), a->s0,
+                       a->s1, a->s2, V, addr->token_slot, ranks, static_cast<int>(T), static_cast<int>(S), r_max,
+                       static_cast<float*>(h->ptr), h->s0);
+  return launch_status();
+}

@@ -1,0 +1,44 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import synth
+
+DEV = torch.device("cuda:0")
+TOL_BF16 = 2e-3   # relative Frobenius error, bf16 inputs / fp32 accumulate and outputs
+TOL_F32 = 1e-5    # relative Frobenius error, fp32 inputs and outputs
+
+
+def tol(dtype: str) -> float:
+    return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+def note(msg: str) -> None:
+    """Print and flush what names the case before a GPU step."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32 numpy values (exact in ``dtype``) -> device tensor of that dtype."""
+    if dtype == "bf16":
+        return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def same_bits(a: np.ndarray, b: np.ndarray) -> bool:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -1,0 +1,251 @@
+"""GPU parity of the slot-addressed multi-adapter ops against the CPU oracle.
+
+Grouping and gather_shrink are compared bit for bit; shrink and expand_fused
+within a relative Frobenius error of 2e-3 (bf16 inputs) or 1e-5 (fp32),
+on the entries the page specifies (active tokens, rank columns below the
+slot's rank). Rows of inactive tokens must stay bitwise untouched and NaN
+padding must never reach an output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lora_rank_adapter_amd as L
+import oracle
+import synth
+from tests.gpu_util import DEV, dev, f32, host, note, same_bits, tol
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 12345.0
+
+# name, T, K, out_slices, S, r_max, rank choices, zero-adapter probability, dtype
+CASES = [
+    ("decode-small", 40, 256, (128, 64, 64), 6, 32, (0, 8, 16, 32), 0.1, "bf16"),
+    ("ragged-ranks", 203, 520, (100, 28), 9, 40, (0, 3, 17, 40), 0.1, "bf16"),
+    ("prefill-like", 1500, 1024, (512, 128, 128), 12, 128, (8, 16, 32, 64, 128), 0.0, "bf16"),
+    ("fp32", 77, 64, (32, 16), 5, 16, (0, 4, 16), 0.2, "f32"),
+    ("one-token", 1, 8, (4,), 1, 1, (1,), 0.0, "bf16"),
+]
+
+
+def _case(name, T, K, out_slices, S, r_max, choices, zero_p, dtype, seed=0, int_exact=False, wild_slots=True):
+    rng = np.random.default_rng(1000 + seed + T)
+    if name == "prefill-like":
+        ts, ranks, _ = synth.prefill_routing(12, S, choices, rng, median=120.0, sigma=0.6, cap=400)
+        T = ts.shape[0]
+    else:
+        ts, ranks = synth.decode_routing(T, S, r_max, choices, zero_p, rng) if S > 1 else (
+            np.zeros(T, np.int32), np.asarray([choices[0]], np.int32))
+        if wild_slots and T >= 8:
+            ts[3] = -1          # slot ids outside [0, S): inactive
+            ts[5] = S
+            ts[7] = 999
+    # bf16-rounded values are exact in fp32 too, so the fp32 cases reuse the same draws
+    return synth.multi_lora(ts, ranks, K, out_slices, r_max, rng=rng, int_exact=int_exact, name=name)
+
+
+def _addr(m):
+    ts = torch.from_numpy(m.token_slot).to(DEV)
+    ranks = torch.from_numpy(m.ranks).to(DEV)
+    addr = L.lora_addressing_build(L.Addressing(ts, m.S), ranks, m.r_max)
+    return addr, ranks
+
+
+def _spec_mask(m):
+    """Entries of h the page specifies: active tokens, j < rank."""
+    act = oracle.active_mask(m.token_slot, m.ranks, m.r_max)
+    spec = np.zeros((m.T, m.num_slices, m.r_max), bool)
+    for t in np.nonzero(act)[0]:
+        rho = min(int(m.ranks[m.token_slot[t]]), m.r_max)
+        spec[t, :, :rho] = True
+    return act, spec
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_grouping_bitwise(case):
+    m = _case(*case)
+    note(f"grouping {case[0]} T={m.T} S={m.S}")
+    addr, _ = _addr(m)
+    torch.cuda.synchronize()
+    counts, offsets, sorted_tokens, n = oracle.group_tokens(m.token_slot, m.ranks, m.r_max)
+    assert np.array_equal(host(addr.counts)[:m.S], counts)
+    assert np.array_equal(host(addr.offsets), offsets)
+    assert np.array_equal(host(addr.sorted_tokens)[:n], sorted_tokens)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_shrink(case):
+    m = _case(*case)
+    dtype = case[-1]
+    note(f"shrink {case[0]} T={m.T}")
+    addr, ranks = _addr(m)
+    h = torch.full((m.T, m.num_slices, m.r_max), SENTINEL, dtype=torch.float32, device=DEV)
+    L.lora_shrink(dev(m.x, dtype), dev(m.a, dtype), addr, ranks, m.num_slices, m.r_max, h=h)
+    torch.cuda.synchronize()
+    want = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max)
+    got = host(h)
+    act, spec = _spec_mask(m)
+    assert np.all(got[~spec] == SENTINEL), "unspecified entries of h were written"
+    assert np.isfinite(got[spec]).all()
+    assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_expand_fused(case):
+    m = _case(*case)
+    dtype = case[-1]
+    note(f"expand {case[0]} T={m.T}")
+    addr, ranks = _addr(m)
+    rng = np.random.default_rng(7)
+    act, spec = _spec_mask(m)
+    hin = rng.standard_normal((m.T, m.num_slices, m.r_max)).astype(np.float32)
+    hin[~spec] = np.nan                      # the expand must not read unspecified entries
+    y = f32(m.y0)
+    L.lora_expand_fused(f32(hin), dev(m.b, dtype), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    got = host(y)
+    want = oracle.expand_fused(hin, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max)
+    assert same_bits(got[~act], m.y0[~act]), "rows of inactive tokens were written"
+    assert np.isfinite(got).all(), "NaN padding reached y"
+    assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_shrink_then_expand(case):
+    m = _case(*case)
+    dtype = case[-1]
+    note(f"apply {case[0]}")
+    addr, ranks = _addr(m)
+    h = L.lora_shrink(dev(m.x, dtype), dev(m.a, dtype), addr, ranks, m.num_slices, m.r_max)
+    y = f32(m.y0)
+    L.lora_expand_fused(h, dev(m.b, dtype), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    want = oracle.apply_linear(m.x, m.y0, m.a, m.b, m.token_slot, m.ranks, m.scalings, m.out_slices, m.r_max)
+    act, _ = _spec_mask(m)
+    got = host(y)
+    assert same_bits(got[~act], m.y0[~act])
+    assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_integer_exact_bitwise(dtype):
+    note(f"multi integer-exact {dtype}")
+    m = _case("ragged-ranks", 203, 200, (100, 28), 9, 40, (0, 3, 17, 40), 0.1, dtype, int_exact=True)
+    addr, ranks = _addr(m)
+    h = L.lora_shrink(dev(m.x, dtype), dev(m.a, dtype), addr, ranks, m.num_slices, m.r_max)
+    y = f32(m.y0)
+    L.lora_expand_fused(h, dev(m.b, dtype), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    act, spec = _spec_mask(m)
+    hw = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max)
+    assert same_bits(host(h)[spec], hw[spec].astype(np.float32))
+    want = oracle.expand_fused(hw, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max)
+    assert same_bits(host(y), want.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["rank-contiguous", "vocab-contiguous"])
+def test_gather_shrink_bitwise(dtype, layout):
+    note(f"gather {dtype} {layout}")
+    rng = np.random.default_rng(77)
+    T, S, r_max, V = 300, 7, 48, 1000
+    ts, ranks = synth.decode_routing(T, S, r_max, (0, 5, 16, 48), 0.1, rng)
+    ts[4] = -3
+    ts[6] = S
+    ids = synth.gather_ids(T, V, rng)
+    ids[:4] = [V, V + 7, np.iinfo(np.int32).min, -1]
+    table = rng.standard_normal((S, r_max, V)).astype(np.float32)
+    for s in range(S):
+        table[s, ranks[s]:, :] = np.nan
+    table = synth.round_bf16(table)
+    if layout == "rank-contiguous":
+        a_dev = dev(np.ascontiguousarray(table.transpose(0, 2, 1)), dtype).permute(0, 2, 1)   # S x r_max x V view
+    else:
+        a_dev = dev(table, dtype)
+    ranks_d = torch.from_numpy(ranks).to(DEV)
+    addr = L.lora_addressing_build(L.Addressing(torch.from_numpy(ts).to(DEV), S), ranks_d, r_max)
+    h = torch.full((T, 1, r_max), SENTINEL, dtype=torch.float32, device=DEV)
+    L.lora_gather_shrink(torch.from_numpy(ids).to(DEV), a_dev, addr, ranks_d, r_max, h=h)
+    torch.cuda.synchronize()
+    want = oracle.gather_shrink(ids, table, ts, ranks, r_max)
+    got = host(h)
+    act = oracle.active_mask(ts, ranks, r_max)
+    spec = np.zeros((T, 1, r_max), bool)
+    for t in np.nonzero(act)[0]:
+        spec[t, 0, :ranks[ts[t]]] = True
+    assert same_bits(got[spec], want[spec].astype(np.float32))
+    assert np.all(got[~spec] == SENTINEL)
+    invalid = act & ((ids < 0) | (ids >= V))
+    assert invalid.any()
+    assert not np.signbit(got[invalid][spec[invalid]]).any(), "an out-of-range id must give +0.0"
+
+
+def test_bad_arguments():
+    note("multi bad args")
+    ts = torch.zeros(4, dtype=torch.int32, device=DEV)
+    ranks = torch.ones(1100, dtype=torch.int32, device=DEV)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_addressing_build(L.Addressing(ts, 1100), ranks, 16)
+    assert e.value.status == -8
+    addr = L.lora_addressing_build(L.Addressing(ts, 2), ranks[:2], 16)
+    h = torch.zeros((4, 2, 16), device=DEV)
+    b = torch.zeros((2, 12, 16), device=DEV, dtype=torch.bfloat16)
+    y = torch.zeros((4, 12), device=DEV)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_expand_fused(h, b, addr, ranks[:2], torch.ones(2, device=DEV), y, (8, 8), 16)
+    assert e.value.status == -2
+    with pytest.raises(L.LoraError) as e:
+        L.lora_expand_fused(h, b, addr, ranks[:2], torch.ones(2, device=DEV), y, (6, 6), 16)
+    assert e.value.status == -2
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["config4", "config5"])
+def test_full_size_shrink_expand(cfg):
+    m = getattr(synth, cfg)()
+    note(f"full size {m.name} T={m.T}")
+    addr, ranks = _addr(m)
+    counts, offsets, sorted_tokens, n = oracle.group_tokens(m.token_slot, m.ranks, m.r_max)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(addr.sorted_tokens)[:n], sorted_tokens)
+    h = L.lora_shrink(dev(m.x, "bf16"), dev(m.a, "bf16"), addr, ranks, m.num_slices, m.r_max)
+    y = f32(m.y0)
+    L.lora_expand_fused(h, dev(m.b, "bf16"), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([[0, m.T - 1], rng.integers(0, m.T, 200)]))
+    act, spec = _spec_mask(m)
+    hw = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max, tokens=toks)
+    hg = host(h)
+    assert oracle.rel_frobenius(hg[toks][spec[toks]], hw[toks][spec[toks]]) <= 2e-3
+    want = oracle.expand_fused(hw, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max, tokens=toks)
+    got = host(y)[toks]
+    a_t = act[toks]
+    assert same_bits(got[~a_t], m.y0[toks][~a_t])
+    assert oracle.rel_frobenius(got[a_t] - m.y0[toks][a_t], want[a_t] - m.y0[toks][a_t]) <= 2e-3
+
+
+@pytest.mark.slow
+def test_full_size_gather_shrink():
+    """Vocabulary 128256, 128 slots of rank <= 128: a 4.2 GB table (64-bit offsets)."""
+    ts, ranks, _lengths, rng = synth.config5_routing()
+    T, S, r_max, V = ts.shape[0], 128, 128, 128256
+    note(f"full size gather T={T} V={V}")
+    ids = synth.gather_ids(T, V, rng)
+    ids[:3] = [V, V + 7, np.iinfo(np.int32).min]
+    bits = synth.gather_table_bits(S, r_max, V, ranks, seed=55)       # S x V x r_max, rank index contiguous
+    a_dev = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16).permute(0, 2, 1)
+    ts_d = torch.from_numpy(ts).to(DEV)
+    ranks_d = torch.from_numpy(ranks).to(DEV)
+    addr = L.lora_addressing_build(L.Addressing(ts_d, S), ranks_d, r_max)
+    h = torch.full((T, 1, r_max), SENTINEL, dtype=torch.float32, device=DEV)
+    L.lora_gather_shrink(torch.from_numpy(ids).to(DEV), a_dev, addr, ranks_d, r_max, h=h)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, 1, 2, T - 1], rng.integers(0, T, 300)]))
+    want = oracle.gather_shrink(ids, bits.transpose(0, 2, 1), ts, ranks, r_max, tokens=toks, a_is_bf16_bits=True)
+    got = host(h)
+    for t in toks:
+        rho = int(ranks[ts[t]])
+        assert same_bits(got[t, 0, :rho], want[t, 0, :rho].astype(np.float32)), t
+        assert np.all(got[t, 0, rho:] == SENTINEL)

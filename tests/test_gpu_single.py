@@ -1,0 +1,217 @@
+"""GPU parity of the single-adapter forward and backward against the CPU oracle.
+
+Every case goes through the C ABI (ctypes binding). Tolerances: relative
+Frobenius error <= 2e-3 for bf16 inputs, <= 1e-5 for fp32 inputs, measured on
+the added delta for the in-place forward; bitwise equality for integer-valued
+inputs whose every partial sum is exact in fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lora_rank_adapter_amd as L
+import oracle
+import synth
+from tests.gpu_util import dev, f32, host, note, same_bits, tol
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, L, r, dtype, scale): ragged against every tile size (16-token blocks,
+# 32/16-wide contraction steps, 4-wave feature split, 16-column output blocks,
+# 256-column gradient slices, 32-token gradient stages).
+CASES = [
+    (200, 264, 1000, 16, "bf16", 2.0),
+    (77, 128, 64, 1, "bf16", 0.5),
+    (300, 512, 256, 5, "bf16", 1.0),
+    (129, 1032, 520, 33, "bf16", 2.0),
+    (64, 4096, 128, 64, "bf16", 0.5),
+    (40, 256, 96, 128, "bf16", 2.0),
+    (1, 8, 4, 7, "bf16", 1.5),
+    (517, 2048, 1536, 100, "bf16", 0.25),
+    (256, 512, 512, 8, "f32", 2.0),
+    (70, 132, 300, 19, "f32", 0.5),
+    (33, 4, 8, 128, "f32", 1.0),
+]
+
+
+def _ids(c):
+    return "M{}-K{}-L{}-r{}-{}".format(*c[:5])
+
+
+def _upload(c, dtype):
+    X = dev(c.X, dtype)
+    A_w = dev(np.ascontiguousarray(c.A.T), dtype)   # lora_A weight, r x K
+    B_w = dev(np.ascontiguousarray(c.B.T), dtype)   # lora_B weight, L x r
+    dY = dev(c.dY, dtype)
+    return X, A_w, B_w, dY
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_fwd(case):
+    M, K, L_, r, dtype, s = case
+    note(f"fwd {case}")
+    c = synth.single_adapter(M, K, L_, r, seed=100 + M, dtype=dtype, scale=s, y0="normal")
+    X, A_w, B_w, _ = _upload(c, dtype)
+    y = f32(c.Y0)
+    L.lora_fwd(X, A_w.t(), B_w.t(), y, s)
+    torch.cuda.synchronize()
+    want = oracle.lora_fwd(c.X, c.A, c.B, c.Y0, s)
+    err = oracle.rel_frobenius(host(y) - c.Y0, want - c.Y0)
+    assert err <= tol(dtype), err
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_bwd(case):
+    M, K, L_, r, dtype, s = case
+    note(f"bwd {case}")
+    c = synth.single_adapter(M, K, L_, r, seed=200 + M, dtype=dtype, scale=s)
+    X, A_w, B_w, dY = _upload(c, dtype)
+    dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s)
+    dB = L.lora_bwd_db(A_w, X.t(), dY, s)
+    torch.cuda.synchronize()
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    odB = oracle.lora_bwd_db(c.A.T, c.X.T, c.dY, s)
+    for name, g, w in (("dX", dx, odx), ("dA", dA, odA), ("dB", dB, odB)):
+        err = oracle.rel_frobenius(host(g), w)
+        assert err <= tol(dtype), (name, err)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("s", [2.0, 0.5])
+def test_integer_exact_bitwise(dtype, s):
+    """Integer inputs in [-2, 2]: every fp32 partial sum (and the hi+lo split)
+    is exact, so any summation order gives the oracle's value bit for bit."""
+    note(f"integer-exact {dtype} s={s}")
+    M, K, L_, r = 96, 256, 200, 16
+    c = synth.single_adapter(M, K, L_, r, seed=31, dtype=dtype, scale=s, y0="normal", int_exact=True)
+    X, A_w, B_w, dY = _upload(c, dtype)
+    y = f32(c.Y0)
+    L.lora_fwd(X, A_w.t(), B_w.t(), y, s)
+    dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s)
+    dB = L.lora_bwd_db(A_w, X.t(), dY, s)
+    torch.cuda.synchronize()
+    assert same_bits(host(y), oracle.lora_fwd(c.X, c.A, c.B, c.Y0, s).astype(np.float32))
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    assert same_bits(host(dx), odx.astype(np.float32))
+    assert same_bits(host(dA), odA.astype(np.float32))
+    assert same_bits(host(dB), oracle.lora_bwd_db(c.A.T, c.X.T, c.dY, s).astype(np.float32))
+
+
+def test_weight_layouts_and_output_strides():
+    """Weights given in the other orientation (packed by the library) and
+    strided gradient outputs give the same results as the natural layouts."""
+    note("layouts")
+    M, K, L_, r, s = 150, 384, 272, 24, 2.0
+    c = synth.single_adapter(M, K, L_, r, seed=41, dtype="bf16", scale=s, y0="normal")
+    X, A_w, B_w, dY = _upload(c, "bf16")
+    A_kr = dev(c.A, "bf16")          # K x r contiguous
+    B_rl = dev(c.B, "bf16")          # r x L contiguous
+    y1 = f32(c.Y0)
+    y2 = f32(c.Y0)
+    L.lora_fwd(X, A_w.t(), B_w.t(), y1, s)
+    L.lora_fwd(X, A_kr, B_rl, y2, s)
+    dx1, dA1 = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s)
+    dA_rk = torch.empty((r, K), dtype=torch.float32, device=X.device)   # dA stored r x K (lora_A layout)
+    dx2, _ = L.lora_bwd_dx_da(X.t(), dY, B_rl.t(), A_kr.t(), s, dA=dA_rk.t())
+    dB1 = L.lora_bwd_db(A_w, X.t(), dY, s)
+    dB_lr = torch.empty((L_, r), dtype=torch.float32, device=X.device)  # dB stored L x r (lora_B layout)
+    L.lora_bwd_db(A_kr.t(), X.t(), dY, s, dB=dB_lr.t())
+    torch.cuda.synchronize()
+    assert same_bits(host(y1), host(y2))
+    assert same_bits(host(dx1), host(dx2))
+    assert same_bits(host(dA1), host(dA_rk.t()))
+    assert same_bits(host(dB1), host(dB_lr.t()))
+    want = oracle.lora_fwd(c.X, c.A, c.B, c.Y0, s)
+    assert oracle.rel_frobenius(host(y1) - c.Y0, want - c.Y0) <= 2e-3
+
+
+def test_deterministic_reruns():
+    note("determinism")
+    c = synth.single_adapter(333, 1024, 640, 48, seed=51, dtype="bf16", scale=0.5)
+    X, A_w, B_w, dY = _upload(c, "bf16")
+    outs = []
+    for _ in range(2):
+        y = torch.zeros((333, 640), dtype=torch.float32, device=X.device)
+        L.lora_fwd(X, A_w.t(), B_w.t(), y, 0.5)
+        dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, 0.5)
+        dB = L.lora_bwd_db(A_w, X.t(), dY, 0.5)
+        torch.cuda.synchronize()
+        outs.append([host(t) for t in (y, dx, dA, dB)])
+    for a, b in zip(*outs):
+        assert same_bits(a, b)
+
+
+def test_empty_and_degenerate():
+    note("empty")
+    dv = torch.device("cuda:0")
+    bf = torch.bfloat16
+    # M = 0: forward is a no-op, gradients of the weights are zero
+    x = torch.empty((0, 64), dtype=bf, device=dv)
+    a_w = torch.randn((8, 64), device=dv).to(bf)
+    b_w = torch.randn((32, 8), device=dv).to(bf)
+    y = torch.empty((0, 32), dtype=torch.float32, device=dv)
+    L.lora_fwd(x, a_w.t(), b_w.t(), y, 1.0)
+    dy = torch.empty((0, 32), dtype=bf, device=dv)
+    dx, dA = L.lora_bwd_dx_da(x.t(), dy, b_w, a_w, 1.0, dA=torch.full((64, 8), 7.0, device=dv))
+    dB = L.lora_bwd_db(a_w, x.t(), dy, 1.0, dB=torch.full((8, 32), 7.0, device=dv))
+    torch.cuda.synchronize()
+    assert not dA.any() and not dB.any()
+    # A = 0: the output is untouched bit for bit
+    x = torch.randn((50, 64), device=dv).to(bf)
+    y0 = torch.randn((50, 32), device=dv)
+    y = y0.clone()
+    L.lora_fwd(x, torch.zeros((8, 64), dtype=bf, device=dv).t(), b_w.t(), y, 3.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+
+
+def test_bad_arguments_raise_before_launch():
+    note("bad args")
+    dv = torch.device("cuda:0")
+    bf = torch.bfloat16
+    x = torch.randn((16, 64), device=dv).to(bf)
+    a_w = torch.randn((8, 64), device=dv).to(bf)
+    b_w = torch.randn((32, 8), device=dv).to(bf)
+    y = torch.zeros((16, 32), device=dv)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_fwd(x, a_w.t(), b_w.t(), torch.zeros((16, 33), device=dv), 1.0)
+    assert e.value.status == -2
+    with pytest.raises(L.LoraError) as e:
+        L.lora_fwd(x.float(), a_w.t(), b_w.t(), y, 1.0)
+    assert e.value.status == -3
+    with pytest.raises(L.LoraError) as e:
+        L.lora_fwd(x.t().contiguous().t(), a_w.t(), b_w.t(), y, 1.0)   # column-major x
+    assert e.value.status == -4
+    big = torch.randn((129, 64), device=dv).to(bf)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_fwd(x, big.t(), torch.randn((32, 129), device=dv).to(bf).t(), y, 1.0)
+    assert e.value.status == -5
+    assert torch.equal(y, torch.zeros_like(y))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["config1", "config2", "config3"])
+def test_full_size_configs(cfg):
+    """The workloads at full size: sampled rows of Y and dX, all of dA and dB."""
+    c = getattr(synth, cfg)()
+    note(f"full size {c.name}")
+    dtype = c.dtype
+    X, A_w, B_w, dY = _upload(c, dtype)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, c.M - 1], rng.integers(0, c.M, 254)]))
+    y = torch.zeros((c.M, c.L), dtype=torch.float32, device=X.device)
+    L.lora_fwd(X, A_w.t(), B_w.t(), y, c.scale)
+    torch.cuda.synchronize()
+    want = oracle.lora_fwd(c.X[rows], c.A, c.B, c.Y0[rows], c.scale)
+    assert oracle.rel_frobenius(host(y[torch.from_numpy(rows).to(X.device)]), want) <= tol(dtype)
+    del y
+    dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, c.scale)
+    dB = L.lora_bwd_db(A_w, X.t(), dY, c.scale)
+    torch.cuda.synchronize()
+    odx_rows, _ = oracle.lora_bwd_dx_da(c.X[rows].T, c.dY[rows], c.B.T, c.A.T, c.scale)
+    assert oracle.rel_frobenius(host(dx[torch.from_numpy(rows).to(X.device)]), odx_rows) <= tol(dtype)
+    # dA and dB contract over every token
+    _, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, c.scale)
+    assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
+    odB = oracle.lora_bwd_db(c.A.T, c.X.T, c.dY, c.scale)
+    assert oracle.rel_frobenius(host(dB), odB) <= tol(dtype)
