@@ -141,10 +141,15 @@ size_t lora_workspace_bytes(int op, int64_t M, int64_t K, int64_t L, int32_t r, 
  *   res     M x L   float32, accumulated in place (the page's `res`; pass a
  *                   zeroed buffer when there is none). stride_col 1, row
  *                   16-byte aligned, L a multiple of 4.
- *   1 <= r <= 128. The rank-r intermediate stays in registers and LDS; it is
- *   never written to memory.
- *   workspace: lora_workspace_bytes(LORA_OP_FWD, ...) bytes; may be NULL with
- *   size 0 when both weights are read in place.
+ *   1 <= r <= 128.
+ *   The library picks one of two schedules from the shapes: fused (one
+ *   workgroup per token tile computes the rank-r intermediate and expands it,
+ *   the intermediate never leaves registers and LDS) or split (a shrink kernel
+ *   writes the intermediate to the workspace as MFMA operand fragments, 1 KB
+ *   per 16 tokens and 16 ranks, and several workgroups per token tile expand
+ *   disjoint column ranges). Both give the same results up to float32
+ *   summation order.
+ *   workspace: lora_workspace_bytes(LORA_OP_FWD, ...) bytes, required.
  */
 int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_mat* lora_B, const lora_mat* res,
              float scale, void* workspace, size_t workspace_bytes, void* stream);

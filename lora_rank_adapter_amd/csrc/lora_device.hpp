@@ -30,6 +30,35 @@ struct F32 {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// ---------------------------------------------------------------------------
+// Buffer-resource (V#) memory access. A raw buffer descriptor carries a base
+// address and a byte size; the hardware returns 0 for loads and drops stores
+// whose byte offset falls outside [0, size). Masked lanes therefore use the
+// offset kOOB instead of a branch, which keeps every loop free of divergent
+// control flow around memory operations (the compiler can then wait for
+// exactly the loads a step consumes).
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;          // any offset >= every descriptor size
+constexpr int64_t kMaxBufferBytes = 0x7FFFFFFF;  // descriptor sizes are clamped to this
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > kMaxBufferBytes ? kMaxBufferBytes : bytes);
+  // 0x00020000: gfx9-family descriptor word 3 (32-bit data format, no swizzle).
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
@@ -99,15 +128,16 @@ __device__ __forceinline__ uint4 split_frag<F32>(f32x4_t v) {
 
 // Weight vector of 4 consecutive rank columns j0..j0+3 of one weight row, with
 // columns >= r read as zero (so padding, possibly NaN, is never used).
-// bf16: 8-byte aligned row segment, duplicated to {w0..w3, w0..w3}.
-// f32: 16-byte aligned row segment.
+// bf16: one 8-byte load (duplicated to {w0..w3, w0..w3}); f32: one 16-byte
+// load; element loads when vec_ok is false (row not aligned for that) or the
+// segment crosses r.
 template <class Tag>
-__device__ __forceinline__ uint4 load_wvec4(const typename Tag::elem* row, int j0, int r);
+__device__ __forceinline__ uint4 load_wvec4(const typename Tag::elem* row, int j0, int r, bool vec_ok);
 
 template <>
-__device__ __forceinline__ uint4 load_wvec4<BF16>(const uint16_t* row, int j0, int r) {
+__device__ __forceinline__ uint4 load_wvec4<BF16>(const uint16_t* row, int j0, int r, bool vec_ok) {
   uint32_t lo, hi;
-  if (j0 + 4 <= r) {
+  if (vec_ok && j0 + 4 <= r) {
     uint2 w = *reinterpret_cast<const uint2*>(row + j0);
     lo = w.x;
     hi = w.y;
@@ -115,8 +145,9 @@ __device__ __forceinline__ uint4 load_wvec4<BF16>(const uint16_t* row, int j0, i
     uint32_t e0 = row[j0];
     uint32_t e1 = (j0 + 1 < r) ? row[j0 + 1] : 0u;
     uint32_t e2 = (j0 + 2 < r) ? row[j0 + 2] : 0u;
+    uint32_t e3 = (j0 + 3 < r) ? row[j0 + 3] : 0u;
     lo = e0 | (e1 << 16);
-    hi = e2;
+    hi = e2 | (e3 << 16);
   } else {
     lo = 0u;
     hi = 0u;
@@ -125,14 +156,61 @@ __device__ __forceinline__ uint4 load_wvec4<BF16>(const uint16_t* row, int j0, i
 }
 
 template <>
-__device__ __forceinline__ uint4 load_wvec4<F32>(const float* row, int j0, int r) {
-  if (j0 + 4 <= r) return ld16(row + j0);
+__device__ __forceinline__ uint4 load_wvec4<F32>(const float* row, int j0, int r, bool vec_ok) {
+  if (vec_ok && j0 + 4 <= r) return ld16(row + j0);
   uint4 w = zero4();
   if (j0 < r) w.x = __float_as_uint(row[j0]);
   if (j0 + 1 < r) w.y = __float_as_uint(row[j0 + 1]);
   if (j0 + 2 < r) w.z = __float_as_uint(row[j0 + 2]);
+  if (j0 + 3 < r) w.w = __float_as_uint(row[j0 + 3]);
   return w;
 }
+
+// Compact register form of a 4-column weight vector: bf16 keeps 8 bytes and is
+// duplicated to the MFMA operand at use; f32 keeps the 16-byte vector.
+template <class Tag>
+struct WFrag;
+//
+// masked(row, jl, j0, r, ok): unconditional load of the 4 columns starting at
+// jl (an in-bounds, 4-aligned column of the row), then columns j0+e >= r, or
+// every column when !ok, replaced by zero. Callers pass jl = j0 unless j0 lies
+// past the readable part of the row, in which case every column is masked.
+template <>
+struct WFrag<BF16> {
+  using type = uint2;
+  static __device__ __forceinline__ type pack(uint4 w) { return make_uint2(w.x, w.y); }
+  static __device__ __forceinline__ uint4 operand(type w) { return make_uint4(w.x, w.y, w.x, w.y); }
+  static __device__ __forceinline__ type zero() { return make_uint2(0u, 0u); }
+  static __device__ __forceinline__ type masked(const uint16_t* row, int jl, int j0, int r, bool ok) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + jl);
+    const uint32_t m0 = (ok && j0 < r ? 0xFFFFu : 0u) | (ok && j0 + 1 < r ? 0xFFFF0000u : 0u);
+    const uint32_t m1 = (ok && j0 + 2 < r ? 0xFFFFu : 0u) | (ok && j0 + 3 < r ? 0xFFFF0000u : 0u);
+    return make_uint2(w.x & m0, w.y & m1);
+  }
+  // Buffer form: off = byte offset of column j0 of the row, or kOOB.
+  static __device__ __forceinline__ type bload(rsrc_t rs, uint32_t off, int j0, int r) {
+    const uint2 w = bload8(rs, off);
+    const uint32_t m0 = (j0 < r ? 0xFFFFu : 0u) | (j0 + 1 < r ? 0xFFFF0000u : 0u);
+    const uint32_t m1 = (j0 + 2 < r ? 0xFFFFu : 0u) | (j0 + 3 < r ? 0xFFFF0000u : 0u);
+    return make_uint2(w.x & m0, w.y & m1);
+  }
+};
+template <>
+struct WFrag<F32> {
+  using type = uint4;
+  static __device__ __forceinline__ type pack(uint4 w) { return w; }
+  static __device__ __forceinline__ uint4 operand(type w) { return w; }
+  static __device__ __forceinline__ type zero() { return zero4(); }
+  static __device__ __forceinline__ type masked(const float* row, int jl, int j0, int r, bool ok) {
+    const uint4 w = ld16(row + jl);
+    return make_uint4((ok && j0 < r) ? w.x : 0u, (ok && j0 + 1 < r) ? w.y : 0u, (ok && j0 + 2 < r) ? w.z : 0u,
+                      (ok && j0 + 3 < r) ? w.w : 0u);
+  }
+  static __device__ __forceinline__ type bload(rsrc_t rs, uint32_t off, int j0, int r) {
+    const uint4 w = bload16(rs, off);
+    return make_uint4(j0 < r ? w.x : 0u, j0 + 1 < r ? w.y : 0u, j0 + 2 < r ? w.z : 0u, j0 + 3 < r ? w.w : 0u);
+  }
+};
 
 // acc += W(4 rank columns) * frag over 16 rank indices of one rank block.
 template <class Tag>

@@ -177,6 +177,7 @@ struct ShrinkArgs {
   const int32_t* ranks;
   int64_t K;
   int S, r_max, n_slices, row_chunks;
+  bool h_vec;  // h rows 16-byte aligned (strides multiples of 4)
 };
 
 template <class Tag, int BMB, int RB>
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
       s += red[2][i][lane];
       s += red[3][i][lane];
       const int j = j0 + 16 * q + 4 * grp;
-      if (j + 4 <= rho) {
+      if (p.h_vec && j + 4 <= rho) {
         st16f(hrow + j, s);
       } else {
 #pragma unroll
@@ -308,6 +309,8 @@ struct ExpandArgs {
   const int32_t* sorted;
   const int32_t* ranks;
   int S, r_max, n_slices, total_chunks;
+  bool h_vec;  // h rows 16-byte aligned
+  bool b_vec;  // b rows aligned for 4-element loads
   int64_t slice_off[kMaxSlices];
   int64_t slice_w[kMaxSlices];
   int chunk_begin[kMaxSlices + 1];
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
       f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int j = 16 * q + 4 * grp;
       if (tok_ok[b] && q < nq) {
-        if (j + 4 <= rho) {
+        if (p.h_vec && j + 4 <= rho) {
           v = ld16f(hrow[b] + j);
         } else {
 #pragma unroll
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
     const bool nok = nrow < width;
     const E* wr = b_slot + (off + (nok ? nrow : 0)) * p.bs1;
 #pragma unroll
-    for (int q = 0; q < RBM; ++q) wv[u][q] = (nok && q < nq) ? load_wvec4<Tag>(wr, 16 * q + 4 * grp, rho) : zero4();
+    for (int q = 0; q < RBM; ++q) wv[u][q] = (nok && q < nq) ? load_wvec4<Tag>(wr, 16 * q + 4 * grp, rho, p.b_vec) : zero4();
     const int64_t ncol = cb + 4 * grp;
 #pragma unroll
     for (int b = 0; b < BMB; ++b) {
@@ -527,7 +530,7 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   if (T * K > 0 && check_rowmajor_stream(x) != LORA_OK) return LORA_ERR_STRIDE;
   if (a->s2 != 1 || (a->s1 * (int64_t)es) % 16 != 0 || (a->s0 * (int64_t)es) % 16 != 0 || !aligned(a->ptr, 16))
     return LORA_ERR_STRIDE;
-  if (h->s2 != 1 || h->s1 % 4 != 0 || h->s0 % 4 != 0 || !aligned(h->ptr, 16)) return LORA_ERR_STRIDE;
+  if (h->s2 != 1) return LORA_ERR_STRIDE;
   if (T == 0 || S == 0) return LORA_OK;
   const int bmb = tile_bmb(static_cast<int>(T));
   const int rb = (T >= 1024) ? 4 : 1;
@@ -550,6 +553,7 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   p.r_max = r_max;
   p.n_slices = num_slices;
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
+  p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (x->dtype == LORA_BF16)
     launch_shrink<BF16>(p, bmb, rb, tiles, st);
@@ -579,8 +583,7 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   if ((T > 0 && !h->ptr) || (S * O > 0 && !b->ptr) || (T * O > 0 && !y->ptr) || (S > 0 && !scalings))
     return LORA_ERR_NULL;
   const size_t es = elem_size(b->dtype);
-  if (h->s2 != 1 || h->s1 % 4 != 0 || h->s0 % 4 != 0 || !aligned(h->ptr, 16)) return LORA_ERR_STRIDE;
-  if (b->s2 != 1 || b->s1 % 4 != 0 || b->s0 % 4 != 0 || !aligned(b->ptr, 4 * es)) return LORA_ERR_STRIDE;
+  if (h->s2 != 1 || b->s2 != 1) return LORA_ERR_STRIDE;
   if (T * O > 0 && check_rowmajor_stream(y) != LORA_OK) return LORA_ERR_STRIDE;
   if (T == 0 || S == 0 || O == 0) return LORA_OK;
   ExpandArgs p{};
@@ -593,6 +596,8 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   p.y = static_cast<float*>(y->ptr);
   p.ldy = y->stride_row;
   p.scalings = scalings;
+  p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
+  p.b_vec = b->s1 % 4 == 0 && b->s0 % 4 == 0 && aligned(b->ptr, 4 * es);
   p.counts = addr->counts;
   p.offsets = addr->offsets;
   p.sorted = addr->sorted_tokens;

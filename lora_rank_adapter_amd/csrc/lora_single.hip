@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ out,
 }
 
 // out(n, j) = sum over p = 0..P-1 (in that order) of part[p][n][j], j < r.
+// Loads are issued 8 partials at a time; the adds keep the p order.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int P, int64_t N, int rp, int r,
                                                      float* __restrict__ out, int64_t os_n, int64_t os_j) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -64,8 +65,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
   const int j = static_cast<int>(idx - n * r);
   const float* src = part + n * rp + j;
   const int64_t step = N * rp;
-  float s = src[0];
-  for (int pp = 1; pp < P; ++pp) s += src[pp * step];
+  float s = 0.0f;
+  int pp = 0;
+  for (; pp + 8 <= P; pp += 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = src[(pp + e) * step];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = (pp + e == 0) ? v[e] : s + v[e];
+  }
+  for (; pp < P; ++pp) s = (pp == 0) ? src[0] : s + src[pp * step];
   out[n * os_n + j * os_j] = s;
 }
 
@@ -74,166 +83,412 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 // ---------------------------------------------------------------------------
 
 struct FusedArgs {
-  const void* z;   // M x Kin stream (row-major, 16-byte rows)
+  // shrink: stream Z (M x Kin) against W1 (r rows of Kin values)
+  const void* z;
   int64_t ldz;
-  const void* w1;  // rows j < r of Kin contiguous values
+  const void* w1;
   int64_t ldw1;
-  const void* w2;  // rows n < Nout of r contiguous values
+  // expand: W2 (Nout rows of r values) into the fp32 output (M x Nout)
+  const void* w2;
   int64_t ldw2;
-  float* out;      // M x Nout float32
+  float* out;
   int64_t ldo;
-  void* g;         // emitted s*H transposed: rp rows of ldg tokens
+  // s*H written for other kernels: transposed hi/lo planes for the gradient
+  // kernels (rp rows of ldg tokens) and MFMA operand fragments for the
+  // column-split expand (16-token block b, rank block q, lane l at
+  // frag[(b * RB + q) * 64 + l])
+  void* g;
   int64_t ldg;
+  uint4* frag;
   int64_t M, Kin, Nout;
   int r, rp;
   float scale;
+  // expand work split: nsplit workgroups per token tile, nbs 16-column blocks
+  // each; tiles = token tiles present; rot = column-walk rotation per tile
+  int nsplit;
+  int64_t nbs;
+  int64_t tiles;
+  int rot;
 };
 
-template <class Tag, int RB, int BMB, int NBU, bool EXPAND, bool ACCUM, bool EMIT>
-__global__ __launch_bounds__(256) void fused_kernel(FusedArgs p) {
+// ---- shrink of one token tile --------------------------------------------
+// H^T (rank x tokens) = W1 * Z^T over the whole feature axis for the tile's
+// 16*BMB tokens. Wave w takes contraction chunks w, w+NW, ...; U chunks per
+// pipeline stage, two stages in flight; the NW partial sums are reduced
+// through LDS in a fixed order. On return every wave holds s*H (acc) and its
+// MFMA operand form (hf). Rows past M (Z) or past r (W1) lie outside their
+// buffer descriptors and read as zero.
+template <class Tag, int NW, int RB, int BMB, int U>
+__device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x4_t (*red)[BMB * RB][64],
+                                            f32x4_t (&acc)[BMB][RB], uint4 (&hf)[BMB][RB]) {
   using E = typename Tag::elem;
   constexpr int VEC = Tag::VEC;
+  constexpr int ES = sizeof(E);
   constexpr int CH = 4 * VEC;  // contraction values per MFMA step (4 lane groups)
-  constexpr int U = (8 / (BMB + RB)) > 0 ? (8 / (BMB + RB)) : 1;
-  __shared__ f32x4_t red[4][BMB * RB][64];
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * (16 * BMB);
 
-  // ---- phase 1: H^T (rank x tokens) = W1 * Z^T, waves split the feature axis
-  f32x4_t acc[BMB][RB];
+  const rsrc_t rz = make_rsrc(static_cast<const E*>(p.z) + m0 * p.ldz, (p.M - m0) * p.ldz * ES);
+  const rsrc_t rw1 = make_rsrc(p.w1, (int64_t)p.r * p.ldw1 * ES);
+  uint32_t zoff[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) zoff[b] = static_cast<uint32_t>(((16 * b + col) * p.ldz + grp * VEC) * ES);
+  uint32_t woff[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) woff[q] = static_cast<uint32_t>(((int64_t)(16 * q + col) * p.ldw1 + grp * VEC) * ES);
+
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
 #pragma unroll
     for (int q = 0; q < RB; ++q) acc[b][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const E* zrow[BMB];
-  bool zok[BMB];
-#pragma unroll
-  for (int b = 0; b < BMB; ++b) {
-    const int64_t m = m0 + 16 * b + col;
-    zok[b] = m < p.M;
-    zrow[b] = static_cast<const E*>(p.z) + (zok[b] ? m : 0) * p.ldz + grp * VEC;
-  }
-  const E* wrow[RB];
-  bool wok[RB];
-#pragma unroll
-  for (int q = 0; q < RB; ++q) {
-    const int j = 16 * q + col;
-    wok[q] = j < p.r;
-    wrow[q] = static_cast<const E*>(p.w1) + (int64_t)(wok[q] ? j : 0) * p.ldw1 + grp * VEC;
-  }
-
   const int64_t nch = (p.Kin + CH - 1) / CH;
-  for (int64_t c = wave; c < nch; c += 4 * U) {
-    uint4 zf[U][BMB];
-    uint4 wf[U][RB];
+  const int64_t cstep = (int64_t)NW * U;
+  auto load1 = [&](uint4 (&zf)[U][BMB], uint4 (&wf)[U][RB], int64_t c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t cc = c + 4 * u;
+      const int64_t cc = c + (int64_t)NW * u;
       const bool kok = cc < nch && cc * CH + grp * VEC < p.Kin;
+      const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
 #pragma unroll
-      for (int b = 0; b < BMB; ++b) zf[u][b] = (kok && zok[b]) ? ld16(zrow[b] + cc * CH) : zero4();
+      for (int b = 0; b < BMB; ++b) zf[u][b] = bload16(rz, kok ? zoff[b] + kb : kOOB);
 #pragma unroll
-      for (int q = 0; q < RB; ++q) wf[u][q] = (kok && wok[q]) ? ld16(wrow[q] + cc * CH) : zero4();
+      for (int q = 0; q < RB; ++q) wf[u][q] = bload16(rw1, kok ? woff[q] + kb : kOOB);
     }
+  };
+  auto mma1 = [&](const uint4 (&zf)[U][BMB], const uint4 (&wf)[U][RB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int b = 0; b < BMB; ++b)
 #pragma unroll
         for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], wf[u][q], zf[u][b]);
+  };
+  {
+    uint4 zA[U][BMB], wA[U][RB], zB[U][BMB], wB[U][RB];
+    int64_t c = wave;
+    if (c < nch) {
+      load1(zA, wA, c);
+      for (;;) {
+        load1(zB, wB, c + cstep);  // reads 0 past the end
+        mma1(zA, wA);
+        c += cstep;
+        if (c >= nch) break;
+        load1(zA, wA, c + cstep);
+        mma1(zB, wB);
+        c += cstep;
+        if (c >= nch) break;
+      }
+    }
   }
 
-  // fixed-order reduction of the four waves' partial sums
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
 #pragma unroll
     for (int q = 0; q < RB; ++q) red[wave][b * RB + q][lane] = acc[b][q];
   __syncthreads();
-  uint4 hf[BMB][RB];
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
       const int i = b * RB + q;
-      f32x4_t s = red[0][i][lane];
-      s += red[1][i][lane];
-      s += red[2][i][lane];
-      s += red[3][i][lane];
-      s *= p.scale;
-      acc[b][q] = s;
-      hf[b][q] = split_frag<Tag>(s);
+      f32x4_t sum = red[0][i][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[w][i][lane];
+      sum *= p.scale;
+      acc[b][q] = sum;
+      hf[b][q] = split_frag<Tag>(sum);
     }
+}
 
-  // ---- optional: write s*H transposed (rank-major, token-contiguous)
-  if constexpr (EMIT) {
-    if (wave == 0) {
+// s*H of the tile as transposed planes (rank-major, token-contiguous; bf16:
+// hi plane then lo plane; f32: one plane) for every token row below ldg (rows
+// past M hold zeros). Called by one wave.
+template <class Tag, int RB, int BMB>
+__device__ __forceinline__ void emit_planes(const FusedArgs& p, int64_t m0, const f32x4_t (&acc)[BMB][RB],
+                                            const uint4 (&hf)[BMB][RB]) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
 #pragma unroll
-      for (int b = 0; b < BMB; ++b) {
-        const int64_t m = m0 + 16 * b + col;
-        if (m < p.M) {
+  for (int b = 0; b < BMB; ++b) {
+    const int64_t m = m0 + 16 * b + col;
+    if (m < p.ldg) {
 #pragma unroll
-          for (int q = 0; q < RB; ++q)
+      for (int q = 0; q < RB; ++q)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int64_t j = 16 * q + 4 * grp + i;
-              if constexpr (sizeof(E) == 2) {
-                uint16_t* gh = static_cast<uint16_t*>(p.g);
-                const uint32_t hw = (i < 2 ? hf[b][q].x : hf[b][q].y) >> (16 * (i & 1));
-                const uint32_t lw = (i < 2 ? hf[b][q].z : hf[b][q].w) >> (16 * (i & 1));
-                gh[j * p.ldg + m] = static_cast<uint16_t>(hw & 0xFFFFu);
-                gh[((int64_t)p.rp + j) * p.ldg + m] = static_cast<uint16_t>(lw & 0xFFFFu);
-              } else {
-                static_cast<float*>(p.g)[j * p.ldg + m] = acc[b][q][i];
-              }
-            }
+        for (int i = 0; i < 4; ++i) {
+          const int64_t j = 16 * q + 4 * grp + i;
+          if constexpr (sizeof(typename Tag::elem) == 2) {
+            uint16_t* gh = static_cast<uint16_t*>(p.g);
+            const uint32_t hw = (i < 2 ? hf[b][q].x : hf[b][q].y) >> (16 * (i & 1));
+            const uint32_t lw = (i < 2 ? hf[b][q].z : hf[b][q].w) >> (16 * (i & 1));
+            gh[j * p.ldg + m] = static_cast<uint16_t>(hw & 0xFFFFu);
+            gh[((int64_t)p.rp + j) * p.ldg + m] = static_cast<uint16_t>(lw & 0xFFFFu);
+          } else {
+            static_cast<float*>(p.g)[j * p.ldg + m] = acc[b][q][i];
+          }
         }
-      }
     }
   }
+}
 
-  // ---- phase 2: out^T tile (16 columns x 16 tokens) (+)= W2 * (s*H)^T
-  if constexpr (EXPAND) {
-    const E* w2 = static_cast<const E*>(p.w2);
-    const int64_t nnb = (p.Nout + 15) / 16;
-    for (int64_t nb0 = (int64_t)wave * NBU; nb0 < nnb; nb0 += 4 * NBU) {
-      uint4 wv[NBU][RB];
-      f32x4_t cv[NBU][BMB];
+// ---- expand of one token tile over a column range -----------------------
+// out^T tile (16 columns x 16 tokens) (+)= W2 * (s*H)^T for the 16-column
+// blocks [nb_begin, nb_end). Wave w takes NBU consecutive blocks per stage
+// (the NW waves cover NW*NBU adjacent blocks together); two stages in flight.
+// The stage order is rotated by `rot` so that tiles in flight at the same
+// time do not walk the same column offsets in lockstep. Output rows past M lie
+// outside the output descriptor (loads read 0, stores are dropped); columns
+// past the range use kOOB.
+template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
+__device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int64_t nb_begin, int64_t nb_end,
+                                            int64_t rot, const uint4 (&hf)[BMB][RB]) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
+  const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
+  const int64_t gstep = (int64_t)NW * NBU;
+  const int64_t nst = (nb_end - nb_begin + gstep - 1) / gstep;
+  const int64_t r0 = nst > 0 ? rot % nst : 0;
+  uint32_t orow[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) orow[b] = static_cast<uint32_t>((16 * b + col) * p.ldo * 4);
+  // first column block of this wave in stage k (nb_end when k is past the end)
+  auto stage_nb = [&](int64_t k) -> int64_t {
+    if (k >= nst) return nb_end;
+    const int64_t st = (k + r0 < nst) ? k + r0 : k + r0 - nst;
+    return nb_begin + st * gstep + (int64_t)wave * NBU;
+  };
+  auto ooff = [&](int b, int64_t nb) -> uint32_t {
+    const int64_t ncol = nb * 16 + 4 * grp;
+    return (nb < nb_end && ncol < p.Nout) ? orow[b] + static_cast<uint32_t>(ncol * 4) : kOOB;
+  };
+  auto load2 = [&](wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NBU][BMB], int64_t nb0) {
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+      const int64_t nb = nb0 + u;
+      const int64_t nrow = (nb < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int j0 = 16 * q + 4 * grp;
+        wv[u][q] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+      }
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) {
+        if constexpr (ACCUM)
+          cv[u][b] = __builtin_bit_cast(f32x4_t, bload16(ro, ooff(b, nb)));
+        else
+          cv[u][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto comp2 = [&](const wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NBU][BMB], int64_t nb0) {
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) {
+#pragma unroll
+        for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
+        bstore16(ro, ooff(b, nb0 + u), __builtin_bit_cast(uint4, cv[u][b]));
+      }
+    }
+  };
+  wf_t wvA[NBU][RB], wvB[NBU][RB];
+  f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
+  if (nst > 0) {
+    int64_t k = 0;
+    load2(wvA, cvA, stage_nb(0));
+    for (;;) {
+      load2(wvB, cvB, stage_nb(k + 1));  // reads 0 past the end
+      comp2(wvA, cvA, stage_nb(k));
+      if (++k >= nst) break;
+      load2(wvA, cvA, stage_nb(k + 1));
+      comp2(wvB, cvB, stage_nb(k));
+      if (++k >= nst) break;
+    }
+  }
+}
+
+// Fused shrink -> expand: one workgroup per token tile, the rank intermediate
+// never leaves registers and LDS (optionally also written as planes for the
+// gradient kernels).
+template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G>
+__global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
+  __shared__ f32x4_t red[NW][BMB * RB][64];
+  const int64_t tile = blockIdx.x;
+  const int64_t m0 = tile * (16 * BMB);
+  f32x4_t acc[BMB][RB];
+  uint4 hf[BMB][RB];
+  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf);
+  if constexpr (EMIT_G) {
+    if ((threadIdx.x >> 6) == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
+  }
+  expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, 0, (p.Nout + 15) / 16, tile * p.rot, hf);
+}
+
+// Shrink only: s*H of each token tile, written as gradient-kernel planes
+// (EMIT_G) and/or expand fragments (EMIT_F).
+template <class Tag, int NW, int RB, int BMB, int U, bool EMIT_G, bool EMIT_F>
+__global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
+  __shared__ f32x4_t red[NW][BMB * RB][64];
+  const int64_t m0 = (int64_t)blockIdx.x * (16 * BMB);
+  f32x4_t acc[BMB][RB];
+  uint4 hf[BMB][RB];
+  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf);
+  const int wave = threadIdx.x >> 6;
+  if constexpr (EMIT_G) {
+    if (wave == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
+  }
+  if constexpr (EMIT_F) {
+    if (wave == NW - 1) {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int b = 0; b < BMB; ++b)
+#pragma unroll
+        for (int q = 0; q < RB; ++q) p.frag[((m0 / 16 + b) * RB + q) * 64 + lane] = hf[b][q];
+    }
+  }
+}
+
+// Column-split expand from fragments: nsplit workgroups per token tile, each
+// over nbs column blocks. Workgroups are dispatched round-robin over the 8
+// XCDs (id mod 8); ids are mapped so that the splits of one tile run on the
+// same XCD in consecutive slots, which keeps the tile's fragments in that
+// XCD's L2 and the rows being updated at any time few and adjacent.
+template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
+__global__ __launch_bounds__(64 * NW) void expand_kernel(FusedArgs p) {
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid & 7;
+  const int64_t kk = bid >> 3;
+  const int64_t tile = (kk / p.nsplit) * 8 + xcd;
+  const int64_t split = kk % p.nsplit;
+  if (tile >= p.tiles) return;
+  const int64_t m0 = tile * (16 * BMB);
+  const int lane = threadIdx.x & 63;
+  uint4 hf[BMB][RB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b)
+#pragma unroll
+    for (int q = 0; q < RB; ++q) hf[b][q] = p.frag[((m0 / 16 + b) * RB + q) * 64 + lane];
+  const int64_t nnb = (p.Nout + 15) / 16;
+  const int64_t nb_begin = split * p.nbs;
+  const int64_t nb_end = (nb_begin + p.nbs < nnb) ? nb_begin + p.nbs : nnb;
+  expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, nb_begin, nb_end, 0, hf);
+}
+
+// Column-owner expand. Workgroup (c, g) owns the 16-column blocks
+// [c*nbs, (c+1)*nbs) and walks the token tiles g, g+G, g+2G, ...; its slice of
+// W2 is staged once in LDS in MFMA operand order, so the loop holds only the
+// output tiles in registers and can keep many loads in flight. Workgroups with
+// the same g start on the same tile: at any time the chip updates the full
+// rows of a few adjacent tiles. Output tiles of the next token tile are
+// prefetched while the current one is computed. nbs = NW * NBU.
+template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
+__global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  constexpr int NBS = NW * NBU;             // column blocks of this workgroup
+  __shared__ wf_t w2s[NBS * RB * 64];       // [block][rank block][lane]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t nnb = (p.Nout + 15) / 16;
+  const int64_t nb_base = (int64_t)blockIdx.x * NBS;
+
+  // stage the W2 slice (rows past Nout and columns past r become zero)
+  {
+    const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
+    for (int i = threadIdx.x; i < NBS * RB * 64; i += 64 * NW) {
+      const int l = i & 63;
+      const int q = (i >> 6) % RB;
+      const int nbl = (i >> 6) / RB;
+      const int64_t nb = nb_base + nbl;
+      const int64_t n = nb * 16 + (l & 15);
+      const int j0 = 16 * q + 4 * (l >> 4);
+      const int64_t nrow = (nb < nnb && n < p.Nout) ? n : p.Nout;  // p.Nout: outside rw2
+      w2s[i] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+    }
+  }
+  __syncthreads();
+
+  const int64_t gstride = gridDim.y;
+  auto tile_m0 = [&](int64_t t) -> int64_t { return t * (16 * BMB); };
+  // per-tile loads: fragments of s*H and (ACCUM) the output tiles
+  auto load_tile = [&](uint4 (&hf)[BMB][RB], f32x4_t (&cv)[NBU][BMB], int64_t t) {
+    const bool tok = t < p.tiles;
+    const int64_t m0 = tok ? tile_m0(t) : 0;
+#pragma unroll
+    for (int b = 0; b < BMB; ++b)
+#pragma unroll
+      for (int q = 0; q < RB; ++q) hf[b][q] = tok ? p.frag[((m0 / 16 + b) * RB + q) * 64 + lane] : zero4();
+    if constexpr (ACCUM) {
+      const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, tok ? (p.M - m0) * p.ldo * 4 : 0);
 #pragma unroll
       for (int u = 0; u < NBU; ++u) {
-        const int64_t nb = nb0 + u;
-        const int64_t nrow = nb * 16 + col;
-        const bool nok = nb < nnb && nrow < p.Nout;
-        const E* wr = w2 + (nok ? nrow : 0) * p.ldw2;
-#pragma unroll
-        for (int q = 0; q < RB; ++q) wv[u][q] = nok ? load_wvec4<Tag>(wr, 16 * q + 4 * grp, p.r) : zero4();
+        const int64_t nb = nb_base + wave * NBU + u;
         const int64_t ncol = nb * 16 + 4 * grp;
 #pragma unroll
         for (int b = 0; b < BMB; ++b) {
-          const int64_t m = m0 + 16 * b + col;
-          const bool ok = nb < nnb && ncol < p.Nout && m < p.M;
-          if (ACCUM && ok)
-            cv[u][b] = ld16f(p.out + m * p.ldo + ncol);
-          else
-            cv[u][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const uint32_t off = (nb < nnb && ncol < p.Nout)
+                                   ? static_cast<uint32_t>(((16 * b + col) * p.ldo + ncol) * 4)
+                                   : kOOB;
+          cv[u][b] = __builtin_bit_cast(f32x4_t, bload16(ro, off));
         }
       }
+    } else {
 #pragma unroll
-      for (int u = 0; u < NBU; ++u) {
-        const int64_t nb = nb0 + u;
-        const int64_t ncol = nb * 16 + 4 * grp;
+      for (int u = 0; u < NBU; ++u)
 #pragma unroll
-        for (int b = 0; b < BMB; ++b) {
+        for (int b = 0; b < BMB; ++b) cv[u][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto comp_tile = [&](const uint4 (&hf)[BMB][RB], f32x4_t (&cv)[NBU][BMB], int64_t t) {
+    const int64_t m0 = tile_m0(t);
+    const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
 #pragma unroll
-          for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], wv[u][q], hf[b][q]);
-          const int64_t m = m0 + 16 * b + col;
-          if (nb < nnb && ncol < p.Nout && m < p.M) st16f(p.out + m * p.ldo + ncol, cv[u][b]);
-        }
+    for (int u = 0; u < NBU; ++u) {
+      const int nbl = wave * NBU + u;
+      const int64_t nb = nb_base + nbl;
+      const int64_t ncol = nb * 16 + 4 * grp;
+      wf_t w[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) w[q] = w2s[(nbl * RB + q) * 64 + lane];
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) {
+#pragma unroll
+        for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(w[q]), hf[b][q]);
+        const uint32_t off =
+            (nb < nnb && ncol < p.Nout) ? static_cast<uint32_t>(((16 * b + col) * p.ldo + ncol) * 4) : kOOB;
+        bstore16(ro, off, __builtin_bit_cast(uint4, cv[u][b]));
       }
+    }
+  };
+  uint4 hfA[BMB][RB], hfB[BMB][RB];
+  f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
+  int64_t t = blockIdx.y;
+  if (t < p.tiles) {
+    load_tile(hfA, cvA, t);
+    for (;;) {
+      load_tile(hfB, cvB, t + gstride);  // reads 0 past the last tile
+      comp_tile(hfA, cvA, t);
+      t += gstride;
+      if (t >= p.tiles) break;
+      load_tile(hfA, cvA, t + gstride);
+      comp_tile(hfB, cvB, t);
+      t += gstride;
+      if (t >= p.tiles) break;
     }
   }
 }
@@ -297,38 +552,25 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   uint4 zr[ZV];
   uint4 gr[GV];
 
+  // Z rows past the chunk end and G columns past M read 0 (the G buffer holds
+  // zeros for tokens in [M, ldg)); Z columns past N use kOOB.
+  const rsrc_t rz = make_rsrc(z + m_begin * p.ldz, (m_end - m_begin) * p.ldz * ES);
+  const rsrc_t rg = make_rsrc(g, (int64_t)GPL * p.rp * p.ldg * ES);
   auto load_stage = [&](int64_t m0) {
 #pragma unroll
     for (int i = 0; i < ZV; ++i) {
       const int v = tid + 256 * i;
       const int row = v / VPR;
       const int vc = v - row * VPR;
-      const int64_t m = m0 + row;
       const int64_t n = n_base + (int64_t)vc * VEC;
-      zr[i] = (m < m_end && n < p.N) ? ld16(z + m * p.ldz + n) : zero4();
+      zr[i] = bload16(rz, n < p.N ? static_cast<uint32_t>(((m0 - m_begin + row) * p.ldz + n) * ES) : kOOB);
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
       const int v = tid + 256 * i;
-      uint4 val = zero4();
-      if (v < GTOT) {
-        const int grow = v / GVR;  // plane * 16*RB + j
-        const int vc = v - grow * GVR;
-        const int64_t m = m0 + (int64_t)vc * VEC;
-        const E* src = g + (int64_t)grow * p.ldg + m;
-        if (m + VEC <= m_end) {
-          val = ld16(src);
-        } else if (m < m_end) {
-          union {
-            E e[VEC];
-            uint4 v;
-          } tmp;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) tmp.e[e] = (m + e < m_end) ? src[e] : E(0);
-          val = tmp.v;
-        }
-      }
-      gr[i] = val;
+      const int grow = v / GVR;  // plane * 16*RB + j
+      const int vc = v - grow * GVR;
+      gr[i] = bload16(rg, v < GTOT ? static_cast<uint32_t>(((int64_t)grow * p.ldg + m0 + vc * VEC) * ES) : kOOB);
     }
   };
 
@@ -422,17 +664,70 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
 
 constexpr int kTnCols = 256;  // columns per tn_kernel workgroup
 
-// Fused-kernel token tile: the largest of 4/2/1 token blocks that still gives
-// >= 512 workgroups (two per CU), with at most 16 (block x rank-block) tiles.
-static int pick_bmb(int64_t M, int rb) {
-  int bmb = env_int("LORA_FUSED_BMB", 0);
-  if (bmb == 1 || bmb == 2 || bmb == 4) {
-    if (bmb * rb <= 16) return bmb;
-  }
+// ---------------------------------------------------------------------------
+// tile and strategy choices (host). Every (rank blocks, token blocks) pair a
+// chooser returns has a kernel instance in the dispatch switches below. The
+// LORA_* environment variables override the defaults for tuning sweeps only.
+// ---------------------------------------------------------------------------
+
+// Stage sizes: U contraction chunks (shrink) and NBU column blocks (expand)
+// per pipeline stage. A bf16 expand stage holds RB weight fragments
+// (2 VGPRs) and BMB output tiles (4 VGPRs) per column block; keep a stage
+// near 48 VGPRs. A shrink stage holds U*(BMB+RB) 16-byte vectors.
+constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+template <int RB, int BMB>
+struct FusedShape {
+  static constexpr int U = (8 / (BMB + RB)) > 0 ? (8 / (BMB + RB)) : 1;
+  static constexpr int NBU = pow2_floor(48 / (2 * RB + 4 * BMB));
+};
+
+// Token blocks per fused/expand tile (rb * bmb <= 8).
+static int pick_bmb_expand(const char* env, int64_t M, int rb, int64_t wgs_per_tile) {
+  int bmb = env_int(env, 0);
+  if ((bmb == 1 || bmb == 2 || bmb == 4) && bmb * rb <= 8) return bmb;
   for (int c : {4, 2}) {
-    if (c * rb <= 16 && ceil_div(M, 16 * c) >= 512) return c;
+    if (c * rb <= 8 && ceil_div(M, 16 * c) * wgs_per_tile >= 512) return c;
   }
   return 1;
+}
+
+// Token blocks per shrink tile (rb * bmb <= 16): large tiles share each weight
+// chunk among more tokens, while keeping >= 256 workgroups.
+static int pick_bmb_shrink(int64_t M, int rb) {
+  int bmb = env_int("LORA_SHRINK_BMB", 0);
+  if ((bmb == 1 || bmb == 2 || bmb == 4) && bmb * rb <= 16) return bmb;
+  for (int c : {4, 2}) {
+    if (c * rb <= 16 && ceil_div(M, 16 * c) >= 256) return c;
+  }
+  return 1;
+}
+
+// Waves per workgroup: 8 while the partial-sum buffer stays <= 32 KB, else 4.
+static int pick_nw(const char* env, int rb, int bmb) {
+  const int over = env_int(env, 0);
+  if ((over == 4 && rb * bmb <= 16) || (over == 8 && rb * bmb <= 4)) return over;
+  return (8 * rb * bmb <= 32) ? 8 : 4;
+}
+
+// Column splits of each token tile for the split expand: about `cols` output
+// columns per workgroup.
+static int pick_split(int64_t nout) {
+  const int64_t cols = env_int("LORA_SPLIT_COLS", 512);
+  int64_t s = ceil_div(nout, cols > 16 ? cols : 16);
+  const int64_t nnb = ceil_div(nout, 16);
+  if (s > nnb) s = nnb;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
+
+// Forward / dX strategy: fused (rank intermediate only in registers and LDS)
+// or split (shrink kernel writes it as MFMA fragments, column-split expand).
+// The split form lets several workgroups update the rows of one token tile
+// together; it wins when the output rows are long.
+static bool use_split(int64_t nout) {
+  const int over = env_int("LORA_EXPAND_MODE", 0);  // 1 fused, 2 split
+  if (over == 1) return false;
+  if (over == 2) return true;
+  return nout > 8192;
 }
 
 static int64_t tn_chunks_max(int64_t M, int64_t N) {
@@ -450,29 +745,166 @@ static int64_t tn_chunk_tokens(int64_t M, int64_t N) {
   return round_up(ceil_div(M, P), 32);
 }
 
-template <class Tag, int RB, int BMB, bool EXPAND, bool ACCUM, bool EMIT>
-static void launch_fused_t(const FusedArgs& a, hipStream_t st) {
-  constexpr int NBU0 = 8 / BMB;
-  constexpr int NBU1 = 16 / RB;
-  constexpr int NBU = (NBU0 < NBU1 ? NBU0 : NBU1) > 0 ? (NBU0 < NBU1 ? NBU0 : NBU1) : 1;
-  const dim3 grid(static_cast<unsigned>(ceil_div(a.M, 16 * BMB)));
-  hipLaunchKernelGGL((fused_kernel<Tag, RB, BMB, NBU, EXPAND, ACCUM, EMIT>), grid, dim3(256), 0, st, a);
+// ---------------------------------------------------------------------------
+// kernel dispatch
+// ---------------------------------------------------------------------------
+
+template <class Tag, int NW, int RB, int BMB, bool ACCUM, bool EMIT_G>
+struct FusedLaunch {
+  static void run(FusedArgs a, hipStream_t st) {
+    using S = FusedShape<RB, BMB>;
+    // kernels that write planes cover every token row below ldg (zeros past M)
+    const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
+    a.tiles = ceil_div(rows, 16 * BMB);
+    hipLaunchKernelGGL((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G>), dim3((unsigned)a.tiles),
+                       dim3(64 * NW), 0, st, a);
+  }
+};
+
+template <class Tag, int NW, int RB, int BMB, bool EMIT_G, bool EMIT_F>
+struct ShrinkLaunch {
+  static void run(FusedArgs a, hipStream_t st) {
+    using S = FusedShape<RB, BMB>;
+    const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
+    a.tiles = ceil_div(rows, 16 * BMB);
+    hipLaunchKernelGGL((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F>), dim3((unsigned)a.tiles),
+                       dim3(64 * NW), 0, st, a);
+  }
+};
+
+template <class Tag, int NW, int RB, int BMB, bool ACCUM>
+struct ExpandLaunch {
+  static void run(FusedArgs a, hipStream_t st) {
+    using S = FusedShape<RB, BMB>;
+    a.tiles = ceil_div(a.M, 16 * BMB);
+    const int64_t nnb = ceil_div(a.Nout, 16);
+    a.nbs = round_up(ceil_div(nnb, a.nsplit), (int64_t)NW * S::NBU);  // whole workgroup stages
+    a.nsplit = static_cast<int>(ceil_div(nnb, a.nbs));
+    const dim3 grid(static_cast<unsigned>(round_up(a.tiles, 8) * a.nsplit));
+    hipLaunchKernelGGL((expand_kernel<Tag, NW, RB, BMB, S::NBU, ACCUM>), grid, dim3(64 * NW), 0, st, a);
+  }
+};
+
+template <class Tag, int NW, int RB, int BMB, bool ACCUM>
+struct ExpandColsLaunch {
+  // column blocks per workgroup: NW * NBU with the W2 slice <= 64 KB of LDS
+  static constexpr int WBYTES = (sizeof(typename Tag::elem) == 2) ? 8 : 16;
+  static constexpr int NBU0 = 65536 / (NW * RB * 64 * WBYTES);
+  static constexpr int NBU = NBU0 >= 8 ? 8 : (NBU0 >= 4 ? 4 : (NBU0 >= 2 ? 2 : 1));
+  static void run(FusedArgs a, hipStream_t st) {
+    a.tiles = ceil_div(a.M, 16 * BMB);
+    const int64_t cols = ceil_div(ceil_div(a.Nout, 16), (int64_t)NW * NBU);
+    // token groups: enough workgroups to fill the chip twice, at most one per tile
+    int64_t groups = env_int("LORA_COLS_GROUPS", 0);
+    if (groups <= 0) groups = ceil_div(512, cols);
+    if (groups > a.tiles) groups = a.tiles;
+    if (groups < 1) groups = 1;
+    hipLaunchKernelGGL((expand_cols_kernel<Tag, NW, RB, BMB, NBU, ACCUM>),
+                       dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st, a);
+  }
+};
+
+// (rank blocks, token blocks) with rb * bmb <= 8
+template <template <int, int> class L, class... A>
+static void dispatch8(int rb, int bmb, A&&... args) {
+  switch (rb * 10 + bmb) {
+    case 11: L<1, 1>::run(args...); break;
+    case 12: L<1, 2>::run(args...); break;
+    case 14: L<1, 4>::run(args...); break;
+    case 21: L<2, 1>::run(args...); break;
+    case 22: L<2, 2>::run(args...); break;
+    case 24: L<2, 4>::run(args...); break;
+    case 41: L<4, 1>::run(args...); break;
+    case 42: L<4, 2>::run(args...); break;
+    default: L<8, 1>::run(args...); break;  // rb 8 (bmb 1 only)
+  }
+}
+// (rank blocks, token blocks) with rb * bmb <= 16
+template <template <int, int> class L, class... A>
+static void dispatch16(int rb, int bmb, A&&... args) {
+  switch (rb * 10 + bmb) {
+    case 11: L<1, 1>::run(args...); break;
+    case 12: L<1, 2>::run(args...); break;
+    case 14: L<1, 4>::run(args...); break;
+    case 21: L<2, 1>::run(args...); break;
+    case 22: L<2, 2>::run(args...); break;
+    case 24: L<2, 4>::run(args...); break;
+    case 41: L<4, 1>::run(args...); break;
+    case 42: L<4, 2>::run(args...); break;
+    case 44: L<4, 4>::run(args...); break;
+    case 81: L<8, 1>::run(args...); break;
+    default: L<8, 2>::run(args...); break;  // rb 8, bmb 2
+  }
 }
 
-template <class Tag, bool EXPAND, bool ACCUM, bool EMIT>
+template <class Tag, int NW, bool ACCUM, bool EMIT_G>
+struct FusedNW {
+  template <int RB, int BMB>
+  using L = FusedLaunch<Tag, NW, RB, BMB, ACCUM, EMIT_G>;
+};
+template <class Tag, int NW, bool EMIT_G, bool EMIT_F>
+struct ShrinkNW {
+  template <int RB, int BMB>
+  using L = ShrinkLaunch<Tag, NW, RB, BMB, EMIT_G, EMIT_F>;
+};
+template <class Tag, int NW, bool ACCUM>
+struct ExpandColsNW {
+  template <int RB, int BMB>
+  using L = ExpandColsLaunch<Tag, NW, RB, BMB, ACCUM>;
+};
+template <class Tag, int NW, bool ACCUM>
+struct ExpandNW {
+  template <int RB, int BMB>
+  using L = ExpandLaunch<Tag, NW, RB, BMB, ACCUM>;
+};
+
+template <class Tag, bool ACCUM, bool EMIT_G>
 static void launch_fused(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  switch (rb * 10 + bmb) {
-    case 11: launch_fused_t<Tag, 1, 1, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 12: launch_fused_t<Tag, 1, 2, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 14: launch_fused_t<Tag, 1, 4, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 21: launch_fused_t<Tag, 2, 1, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 22: launch_fused_t<Tag, 2, 2, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 24: launch_fused_t<Tag, 2, 4, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 41: launch_fused_t<Tag, 4, 1, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 42: launch_fused_t<Tag, 4, 2, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 44: launch_fused_t<Tag, 4, 4, EXPAND, ACCUM, EMIT>(a, st); break;
-    case 81: launch_fused_t<Tag, 8, 1, EXPAND, ACCUM, EMIT>(a, st); break;
-    default: launch_fused_t<Tag, 8, 2, EXPAND, ACCUM, EMIT>(a, st); break;
+  if (pick_nw("LORA_FUSED_NW", rb, bmb) == 8)
+    dispatch8<FusedNW<Tag, 8, ACCUM, EMIT_G>::template L>(rb, bmb, a, st);
+  else
+    dispatch8<FusedNW<Tag, 4, ACCUM, EMIT_G>::template L>(rb, bmb, a, st);
+}
+template <class Tag, bool EMIT_G, bool EMIT_F>
+static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
+  if (pick_nw("LORA_SHRINK_NW", rb, bmb) == 8)
+    dispatch16<ShrinkNW<Tag, 8, EMIT_G, EMIT_F>::template L>(rb, bmb, a, st);
+  else
+    dispatch16<ShrinkNW<Tag, 4, EMIT_G, EMIT_F>::template L>(rb, bmb, a, st);
+}
+template <class Tag, bool ACCUM>
+static void launch_expand(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
+  if (pick_nw("LORA_EXPAND_NW", rb, bmb) == 8)
+    dispatch8<ExpandNW<Tag, 8, ACCUM>::template L>(rb, bmb, a, st);
+  else
+    dispatch8<ExpandNW<Tag, 4, ACCUM>::template L>(rb, bmb, a, st);
+}
+
+template <class Tag, bool ACCUM>
+static void launch_expand_cols(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
+  if (env_int("LORA_EXPAND_NW", 4) == 8 && rb * bmb <= 4)
+    dispatch8<ExpandColsNW<Tag, 8, ACCUM>::template L>(rb, bmb, a, st);
+  else
+    dispatch8<ExpandColsNW<Tag, 4, ACCUM>::template L>(rb, bmb, a, st);
+}
+
+// Shrink Z against W1 and expand into the output, fused or split (see
+// use_split); with EMIT_G also writes the planes for the gradient kernels.
+template <class Tag, bool ACCUM, bool EMIT_G>
+static void run_shrink_expand(FusedArgs a, int rb, hipStream_t st) {
+  if (env_int("LORA_EXPAND_MODE", 0) == 3) {
+    launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
+    launch_expand_cols<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, 8), st);
+    return;
+  }
+  if (use_split(a.Nout)) {
+    launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
+    a.nsplit = pick_split(a.Nout);
+    launch_expand<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, a.nsplit), st);
+  } else {
+    a.nsplit = 1;
+    a.rot = env_int("LORA_FUSED_ROT", 1);
+    launch_fused<Tag, ACCUM, EMIT_G>(a, rb, pick_bmb_expand("LORA_FUSED_BMB", a.M, rb, 1), st);
   }
 }
 
@@ -520,12 +952,24 @@ static void launch_reduce(const float* part, int P, int64_t N, int rp, int r, fl
                      rp, r, out, os_n, os_j);
 }
 
+// Buffer descriptors address with 32-bit byte offsets: every range one
+// descriptor spans must stay below 2^31 bytes.
+static bool fits32(int64_t bytes) { return bytes >= 0 && bytes <= kMaxBufferBytes; }
+
+// Offsets the shrink/expand kernels form: one 64-token tile of the stream
+// and of the output, and the whole of each weight.
+static bool fused_fits(int64_t ldz, size_t es, int64_t r, int64_t ldw1, int64_t nout, int64_t ldw2, int64_t ldo) {
+  return fits32(64 * ldz * (int64_t)es) && fits32(r * ldw1 * (int64_t)es) && fits32(nout * ldw2 * (int64_t)es) &&
+         fits32(64 * ldo * 4);
+}
+
 // Workspace pieces of each operation (the same function sizes and carves).
 struct SingleLayout {
-  size_t w1 = 0, w2 = 0, g = 0, part = 0;
-  int64_t ldg = 0, chunk = 0, P = 0;
+  size_t w1 = 0, w2 = 0, g = 0, part = 0, frag = 0;
+  int64_t ldg = 0, P = 0;
   size_t total() const {
-    return static_cast<size_t>(round_up(w1, 256) + round_up(w2, 256) + round_up(g, 256) + round_up(part, 256));
+    return static_cast<size_t>(round_up(w1, 256) + round_up(w2, 256) + round_up(g, 256) + round_up(part, 256) +
+                               round_up(frag, 256));
   }
 };
 
@@ -533,9 +977,13 @@ static SingleLayout layout_for(int op, int64_t M, int64_t K, int64_t L, int r, i
   SingleLayout s;
   const size_t es = elem_size(dtype);
   const int64_t rp = padded_rank(r);
+  // MFMA fragments of s*H: one 1 KB record per 16-token block and rank block,
+  // for token rows rounded up to a 64-token tile
+  const size_t frag = static_cast<size_t>(round_up(M > 0 ? M : 1, 64) / 16 * (rp / 16)) * 1024;
   if (op == LORA_OP_FWD) {
     s.w1 = static_cast<size_t>(rp * K) * es;  // A as r x K
     s.w2 = static_cast<size_t>(L * rp) * es;  // B as L x r
+    s.frag = frag;
   } else if (op == LORA_OP_BWD_DX_DA) {
     s.w1 = static_cast<size_t>(rp * L) * es;  // B as r x L
     s.w2 = static_cast<size_t>(K * rp) * es;  // A as K x r
@@ -543,6 +991,7 @@ static SingleLayout layout_for(int op, int64_t M, int64_t K, int64_t L, int r, i
     s.g = static_cast<size_t>(4 * rp * s.ldg);
     s.P = tn_chunks_max(M, K);
     s.part = static_cast<size_t>(s.P * K * rp) * 4;
+    s.frag = frag;
   } else {
     s.w1 = static_cast<size_t>(rp * K) * es;  // A as r x K
     s.ldg = round_up(M > 0 ? M : 1, 32);
@@ -604,17 +1053,21 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   // A is read in place when it is a view of an r x K row-major weight.
   const bool a_direct = lora_A->stride_row == 1 && lora_A->stride_col >= K &&
                         (lora_A->stride_col * (int64_t)es) % 16 == 0 && aligned(lora_A->ptr, 16);
-  // B is read in place when it is a view of an L x r weight with r contiguous.
-  const bool b_direct = lora_B->stride_row == 1 && lora_B->stride_col % 4 == 0 && aligned(lora_B->ptr, 4 * es);
+  // B is read in place when it is a view of an L x r weight with r contiguous,
+  // r a multiple of 4 and 4-element aligned rows (the kernel reads rank columns
+  // in groups of 4).
+  const bool b_direct = lora_B->stride_row == 1 && r % 4 == 0 && lora_B->stride_col >= r &&
+                        lora_B->stride_col % 4 == 0 && aligned(lora_B->ptr, 4 * es);
   const SingleLayout lay = layout_for(LORA_OP_FWD, M, K, L, static_cast<int>(r), x->dtype);
+  if (!workspace || !aligned(workspace, 256)) return LORA_ERR_WORKSPACE;
+  if (workspace_bytes < lay.total()) return LORA_ERR_WORKSPACE;
   Carver cv(workspace);
   void* w1p = cv.take(lay.w1);
   void* w2p = cv.take(lay.w2);
-  if (!a_direct || !b_direct) {
-    if (!workspace) return LORA_ERR_WORKSPACE;
-    if (workspace_bytes < cv.used) return LORA_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return LORA_ERR_WORKSPACE;
-  }
+  uint4* frag = static_cast<uint4*>(cv.take(lay.frag));
+  if (!fused_fits(x->stride_row, es, r, a_direct ? lora_A->stride_col : K, L, b_direct ? lora_B->stride_col : rp,
+                  res->stride_row))
+    return LORA_ERR_LIMIT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   FusedArgs a{};
   a.z = x->ptr;
@@ -643,11 +1096,11 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   a.r = static_cast<int>(r);
   a.rp = static_cast<int>(rp);
   a.scale = scale;
-  const int bmb = pick_bmb(M, rb);
+  a.frag = frag;
   if (x->dtype == LORA_BF16)
-    launch_fused<BF16, true, true, false>(a, rb, bmb, st);
+    run_shrink_expand<BF16, true, false>(a, rb, st);
   else
-    launch_fused<F32, true, true, false>(a, rb, bmb, st);
+    run_shrink_expand<F32, true, false>(a, rb, st);
   return launch_status();
 }
 
@@ -689,9 +1142,15 @@ extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora
   void* w2p = cv.take(lay.w2);
   void* gbuf = cv.take(lay.g);
   float* part = static_cast<float*>(cv.take(lay.part));
+  uint4* frag = static_cast<uint4*>(cv.take(lay.frag));
 
   const int rb = rank_blocks(static_cast<int>(r));
   const int64_t rp = 16 * rb;
+  const size_t es = elem_size(xt->dtype);
+  const int64_t chunk = tn_chunk_tokens(M, K);
+  if (!fused_fits(dy->stride_row, es, r, L, K, rp, dx->stride_row) || !fits32(chunk * xt->stride_col * (int64_t)es) ||
+      !fits32((int64_t)lay.g))
+    return LORA_ERR_LIMIT;
   // W1 = B^T (r x L, L contiguous); W2 = A^T (K x r, r contiguous).
   launch_pack(xt->dtype, lora_B->ptr, lora_B->stride_col, lora_B->stride_row, r, L, w1p, rp, L, L, st);
   launch_pack(xt->dtype, lora_A->ptr, lora_A->stride_col, lora_A->stride_row, K, r, w2p, K, rp, rp, st);
@@ -713,7 +1172,7 @@ extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora
   a.r = static_cast<int>(r);
   a.rp = static_cast<int>(rp);
   a.scale = scale;
-  const int bmb = pick_bmb(M, rb);
+  a.frag = frag;
   TnArgs t{};
   t.z = xt->ptr;
   t.ldz = xt->stride_col;
@@ -723,13 +1182,13 @@ extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora
   t.M = M;
   t.N = K;
   t.rp = static_cast<int>(rp);
-  t.chunk = tn_chunk_tokens(M, K);
+  t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
   if (xt->dtype == LORA_BF16) {
-    launch_fused<BF16, true, false, true>(a, rb, bmb, st);
+    run_shrink_expand<BF16, false, true>(a, rb, st);
     launch_tn<BF16>(t, rb, st);
   } else {
-    launch_fused<F32, true, false, true>(a, rb, bmb, st);
+    run_shrink_expand<F32, false, true>(a, rb, st);
     launch_tn<F32>(t, rb, st);
   }
   launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dA->ptr), dA->stride_row,
@@ -774,6 +1233,10 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   FusedArgs a{};
   const bool a_direct = lora_A->stride_col == 1 && lora_A->stride_row >= K &&
                         (lora_A->stride_row * (int64_t)es) % 16 == 0 && aligned(lora_A->ptr, 16);
+  const int64_t chunk = tn_chunk_tokens(M, L);
+  if (!fused_fits(xt->stride_col, es, r, a_direct ? lora_A->stride_row : K, 0, 0, 0) ||
+      !fits32(chunk * dy->stride_row * (int64_t)es) || !fits32((int64_t)lay.g))
+    return LORA_ERR_LIMIT;
   if (a_direct) {
     a.w1 = lora_A->ptr;
     a.ldw1 = lora_A->stride_row;
@@ -792,7 +1255,8 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   a.r = static_cast<int>(r);
   a.rp = static_cast<int>(rp);
   a.scale = scale;
-  const int bmb = pick_bmb(M, rb);
+  a.nsplit = 1;
+  const int bmb = pick_bmb_shrink(M, rb);
   TnArgs t{};
   t.z = dy->ptr;
   t.ldz = dy->stride_row;
@@ -802,13 +1266,13 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   t.M = M;
   t.N = L;
   t.rp = static_cast<int>(rp);
-  t.chunk = tn_chunk_tokens(M, L);
+  t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
   if (xt->dtype == LORA_BF16) {
-    launch_fused<BF16, false, false, true>(a, rb, bmb, st);
+    launch_shrink<BF16, true, false>(a, rb, bmb, st);
     launch_tn<BF16>(t, rb, st);
   } else {
-    launch_fused<F32, false, false, true>(a, rb, bmb, st);
+    launch_shrink<F32, true, false>(a, rb, bmb, st);
     launch_tn<F32>(t, rb, st);
   }
   // dB is r x L: partial row n = l, column j.

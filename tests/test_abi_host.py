@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import lora_rank_adapter_amd as L
 from lora_rank_adapter_amd import _lib
@@ -15,6 +16,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lora.h")
 
 FAKE = 0x10000  # a 64 KiB-aligned non-NULL address; never dereferenced by these calls
+
+# These checks hand the library fake device pointers and expect every call to be
+# rejected (or to be an empty no-op) before any launch; they run only where no
+# GPU is visible, so a check that wrongly reached a launch could never touch one.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only checks (fake device pointers)")
 
 
 def declared_functions():
@@ -84,9 +90,11 @@ def test_fwd_validation(lib):
     assert fwd(lib, m(M, K, sr=K + 2), A, B, res) == -4                    # row pitch not 16-byte aligned
     assert fwd(lib, m(M, 132), m(132, r, sr=1, sc=132), B, res) == -2      # K not a multiple of 8 (bf16)
     assert fwd(lib, x, A, m(r, 98, sr=1, sc=r), m(M, 98, dtype=0)) == -2   # L not a multiple of 4
-    # weights in the other orientation need a workspace for packing
+    # the forward needs its workspace (weight packing, split schedule)
+    assert fwd(lib, x, A, B, res) == -6
     assert fwd(lib, x, m(K, r), B, res) == -6
     assert fwd(lib, x, m(K, r), B, res, ctypes.c_void_p(FAKE), 16) == -6
+    assert fwd(lib, x, A, B, res, ctypes.c_void_p(FAKE + 128), 1 << 20) == -6   # not 256-byte aligned
     # empty problems launch nothing and succeed
     assert fwd(lib, m(0, K), A, B, m(0, L_, dtype=0)) == 0
     assert fwd(lib, m(M, 0), m(0, r, sr=1, sc=1), B, res) == 0
@@ -159,7 +167,7 @@ def test_multi_validation(lib):
     assert expand(slices=(ctypes.c_int64 * 2)(30, 18)) == -2      # widths must be multiples of 4
     assert expand(slices=(ctypes.c_int64 * 2)(32, 20)) == -2      # must sum to y's width
     assert expand(y_=m(T, 48, dtype=1)) == -3
-    assert expand(h_=LoraT3(FAKE, 0, 0, T, 2, r_max, 2 * r_max + 2, r_max, 1)) == -4
+    assert expand(h_=LoraT3(FAKE, 0, 0, T, 2, r_max, 2 * r_max, 1, 2)) == -4      # rank index not contiguous
 
     ah = LoraT3(FAKE, 1, 0, S, r_max, 1000, r_max * 1000, 1000, 1)
     h1 = LoraT3(FAKE, 0, 0, T, 1, r_max, r_max, r_max, 1)

@@ -26,7 +26,7 @@ CASES = [
     (129, 1032, 520, 33, "bf16", 2.0),
     (64, 4096, 128, 64, "bf16", 0.5),
     (40, 256, 96, 128, "bf16", 2.0),
-    (1, 8, 4, 7, "bf16", 1.5),
+    (1, 8, 8, 7, "bf16", 1.5),
     (517, 2048, 1536, 100, "bf16", 0.25),
     (256, 512, 512, 8, "f32", 2.0),
     (70, 132, 300, 19, "f32", 0.5),
