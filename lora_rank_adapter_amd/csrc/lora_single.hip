@@ -30,6 +30,8 @@
 
 namespace lora {
 
+__device__ __forceinline__ int64_t round_up_dev(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
 // ---------------------------------------------------------------------------
 // small utility kernels
 // ---------------------------------------------------------------------------
@@ -494,6 +496,203 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Token-split shrink: wave w of the workgroup owns the 16-token block
+// tile*NW + w and contracts it over the whole feature axis, so no cross-wave
+// reduction is needed. The first weight is staged in LDS one panel of KP
+// features at a time (MFMA operand order, double-buffered) and shared by all
+// waves; each wave streams its own stream rows one panel ahead of use.
+// ---------------------------------------------------------------------------
+template <class Tag, int NW, int RB, int KP, bool EMIT_G, bool EMIT_F>
+__global__ __launch_bounds__(64 * NW) void shrink_tok_kernel(FusedArgs p) {
+  using E = typename Tag::elem;
+  constexpr int VEC = Tag::VEC;
+  constexpr int ES = sizeof(E);
+  constexpr int CH = 4 * VEC;             // features per MFMA step
+  constexpr int NSTEP = KP / CH;          // steps per panel
+  constexpr int PVEC = RB * 16 * KP / VEC;  // 16-byte weight vectors per panel
+  constexpr int PV = (PVEC + 64 * NW - 1) / (64 * NW);
+  __shared__ uint4 wpan[2][NSTEP * RB * 64];  // [buffer][step][rank block][lane]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t m0 = ((int64_t)blockIdx.x * NW + wave) * 16;  // this wave's token block
+  const rsrc_t rz = make_rsrc(static_cast<const E*>(p.z) + m0 * p.ldz, (p.M - m0) * p.ldz * ES);
+  const rsrc_t rw1 = make_rsrc(p.w1, (int64_t)p.r * p.ldw1 * ES);
+  const uint32_t zrow = static_cast<uint32_t>((col * p.ldz + grp * VEC) * ES);
+  const int64_t npan = (p.Kin + KP - 1) / KP;
+
+  // weight panel: thread vector i -> rank row j, features kk..kk+VEC-1 of the panel
+  uint4 wreg[PV];
+  auto load_panel = [&](int64_t pan) {
+#pragma unroll
+    for (int v = 0; v < PV; ++v) {
+      const int i = threadIdx.x + v * 64 * NW;
+      const int j = i / (KP / VEC);
+      const int kk = (i - j * (KP / VEC)) * VEC;
+      const int64_t k = pan * KP + kk;
+      const bool ok = i < PVEC && pan < npan && k < p.Kin;
+      wreg[v] = bload16(rw1, ok ? static_cast<uint32_t>(((int64_t)j * p.ldw1 + k) * ES) : kOOB);
+    }
+  };
+  auto store_panel = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < PV; ++v) {
+      const int i = threadIdx.x + v * 64 * NW;
+      if (i < PVEC) {
+        const int j = i / (KP / VEC);
+        const int kk = (i - j * (KP / VEC)) * VEC;
+        const int c = kk / CH;
+        const int g = (kk - c * CH) / VEC;
+        wpan[buf][(c * RB + (j >> 4)) * 64 + g * 16 + (j & 15)] = wreg[v];
+      }
+    }
+  };
+  uint4 zA[NSTEP], zB[NSTEP];
+  auto load_z = [&](uint4 (&zf)[NSTEP], int64_t pan) {
+#pragma unroll
+    for (int c = 0; c < NSTEP; ++c) {
+      const int64_t k = pan * KP + c * CH + grp * VEC;
+      zf[c] = bload16(rz, (pan < npan && k < p.Kin) ? zrow + static_cast<uint32_t>((pan * KP + c * CH) * ES) : kOOB);
+    }
+  };
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto comp = [&](const uint4 (&zf)[NSTEP], int buf) {
+#pragma unroll
+    for (int c = 0; c < NSTEP; ++c)
+#pragma unroll
+      for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[q], wpan[buf][(c * RB + q) * 64 + lane], zf[c]);
+  };
+
+  // prologue: panel 0 into LDS, stream rows of panel 0 in flight
+  load_panel(0);
+  load_z(zA, 0);
+  store_panel(0);
+  __syncthreads();
+  for (int64_t pan = 0; pan < npan; pan += 2) {
+    // panel pan (buffer 0, rows zA) is ready; fetch panel pan+1
+    load_panel(pan + 1);
+    load_z(zB, pan + 1);
+    comp(zA, 0);
+    store_panel(1);
+    __syncthreads();
+    if (pan + 1 >= npan) break;
+    load_panel(pan + 2);
+    load_z(zA, pan + 2);
+    comp(zB, 1);
+    store_panel(0);
+    __syncthreads();
+  }
+
+  uint4 hf[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) {
+    acc[q] *= p.scale;
+    hf[q] = split_frag<Tag>(acc[q]);
+  }
+  if constexpr (EMIT_G) {
+    const f32x4_t (&a1)[1][RB] = reinterpret_cast<const f32x4_t (&)[1][RB]>(acc);
+    const uint4 (&h1)[1][RB] = reinterpret_cast<const uint4 (&)[1][RB]>(hf);
+    emit_planes<Tag, RB, 1>(p, m0, a1, h1);
+  }
+  if constexpr (EMIT_F) {
+    if (m0 < round_up_dev(p.M, 64)) {
+#pragma unroll
+      for (int q = 0; q < RB; ++q) p.frag[((m0 / 16) * RB + q) * 64 + lane] = hf[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token-split column-owner expand: workgroup (c, g) owns the 16-column blocks
+// [c*NBS, (c+1)*NBS) with its W2 slice in LDS (MFMA operand order); wave w
+// updates token block tile*NW + w of the tiles g, g+G, ...; the output tiles
+// of the next token tile are loaded while the current one is computed.
+// ---------------------------------------------------------------------------
+template <class Tag, int NW, int RB, int NBS, bool ACCUM>
+__global__ __launch_bounds__(64 * NW) void expand_tok_kernel(FusedArgs p) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  __shared__ wf_t w2s[NBS * RB * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t nnb = (p.Nout + 15) / 16;
+  const int64_t nb_base = (int64_t)blockIdx.x * NBS;
+  {
+    const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
+    for (int i = threadIdx.x; i < NBS * RB * 64; i += 64 * NW) {
+      const int l = i & 63;
+      const int q = (i >> 6) % RB;
+      const int nbl = (i >> 6) / RB;
+      const int64_t nb = nb_base + nbl;
+      const int64_t n = nb * 16 + (l & 15);
+      const int j0 = 16 * q + 4 * (l >> 4);
+      const int64_t nrow = (nb < nnb && n < p.Nout) ? n : p.Nout;  // p.Nout: outside rw2
+      w2s[i] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+    }
+  }
+  __syncthreads();
+  const int64_t nblk = (p.M + 15) / 16;     // 16-token blocks present
+  const int64_t ntile = (nblk + NW - 1) / NW;
+  const int64_t gstride = gridDim.y;
+  uint32_t coff[NBS];
+#pragma unroll
+  for (int u = 0; u < NBS; ++u) {
+    const int64_t nb = nb_base + u;
+    const int64_t ncol = nb * 16 + 4 * grp;
+    coff[u] = (nb < nnb && ncol < p.Nout) ? static_cast<uint32_t>((col * p.ldo + ncol) * 4) : kOOB;
+  }
+  auto block_of = [&](int64_t t) -> int64_t { return t * NW + wave; };
+  auto load_tile = [&](uint4 (&hf)[RB], f32x4_t (&cv)[NBS], int64_t t) {
+    const int64_t blk = block_of(t);
+    const bool ok = t < ntile && blk < nblk;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) hf[q] = ok ? p.frag[(blk * RB + q) * 64 + lane] : zero4();
+    if constexpr (ACCUM) {
+      const rsrc_t ro = make_rsrc(p.out + blk * 16 * p.ldo, ok ? (p.M - blk * 16) * p.ldo * 4 : 0);
+#pragma unroll
+      for (int u = 0; u < NBS; ++u) cv[u] = __builtin_bit_cast(f32x4_t, bload16(ro, coff[u]));
+    } else {
+#pragma unroll
+      for (int u = 0; u < NBS; ++u) cv[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto comp_tile = [&](const uint4 (&hf)[RB], f32x4_t (&cv)[NBS], int64_t t) {
+    const int64_t blk = block_of(t);
+    const rsrc_t ro = make_rsrc(p.out + blk * 16 * p.ldo, blk < nblk ? (p.M - blk * 16) * p.ldo * 4 : 0);
+#pragma unroll
+    for (int u = 0; u < NBS; ++u) {
+#pragma unroll
+      for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u], WF::operand(w2s[(u * RB + q) * 64 + lane]), hf[q]);
+      bstore16(ro, coff[u], __builtin_bit_cast(uint4, cv[u]));
+    }
+  };
+  uint4 hfA[RB], hfB[RB];
+  f32x4_t cvA[NBS], cvB[NBS];
+  int64_t t = blockIdx.y;
+  if (t < ntile) {
+    load_tile(hfA, cvA, t);
+    for (;;) {
+      load_tile(hfB, cvB, t + gstride);  // reads 0 past the last tile
+      comp_tile(hfA, cvA, t);
+      t += gstride;
+      if (t >= ntile) break;
+      load_tile(hfA, cvA, t + gstride);
+      comp_tile(hfB, cvB, t);
+      t += gstride;
+      if (t >= ntile) break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // weight-gradient partial sums over token chunks
 // ---------------------------------------------------------------------------
 
@@ -804,6 +1003,62 @@ struct ExpandColsLaunch {
   }
 };
 
+// Token-split shrink: NW = 8 waves (128 tokens per workgroup); KP features
+// per weight panel, panel <= 32 KB of LDS per buffer.
+template <class Tag, bool EMIT_G, bool EMIT_F>
+static void launch_shrink_tok(FusedArgs a, int rb, hipStream_t st) {
+  constexpr int NW = 8;
+  constexpr int CHB = 4 * Tag::VEC;  // features per MFMA step
+  const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
+  const dim3 grid(static_cast<unsigned>(ceil_div(ceil_div(rows, 16), NW)));
+  const dim3 block(64 * NW);
+  // two panel buffers of KP features x 16*RB ranks: <= 64 KB of LDS (bf16)
+  switch (rb) {
+    case 1: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 1, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 2, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 4, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 8, 4 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+  }
+}
+
+// Token-split expand: NW = 8 waves, NBS column blocks per workgroup with the
+// W2 slice <= 16 KB of LDS; token groups fill the chip about twice.
+template <class Tag, bool ACCUM>
+static void launch_expand_tok(FusedArgs a, int rb, hipStream_t st) {
+  constexpr int NW = 8;
+  constexpr int WB = (sizeof(typename Tag::elem) == 2) ? 8 : 16;  // bytes per weight fragment lane
+  const int64_t nblk = ceil_div(a.M, 16);
+  const int64_t ntile = ceil_div(nblk, NW);
+  auto go = [&](auto kern, int nbs) {
+    const int64_t cols = ceil_div(ceil_div(a.Nout, 16), nbs);
+    int64_t groups = env_int("LORA_TOK_GROUPS", 0);
+    if (groups <= 0) groups = ceil_div(512, cols);
+    if (groups > ntile) groups = ntile;
+    if (groups < 1) groups = 1;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st,
+                       a);
+  };
+  const int nbs_env = env_int("LORA_TOK_NBS", 0);
+  switch (rb) {
+    case 1:
+      if (nbs_env == 4) go(expand_tok_kernel<Tag, NW, 1, 4, ACCUM>, 4);
+      else go(expand_tok_kernel<Tag, NW, 1, 8, ACCUM>, 8);
+      break;
+    case 2:
+      if (nbs_env == 4) go(expand_tok_kernel<Tag, NW, 2, 4, ACCUM>, 4);
+      else go(expand_tok_kernel<Tag, NW, 2, 8, ACCUM>, 8);
+      break;
+    case 4:
+      if (nbs_env == 4) go(expand_tok_kernel<Tag, NW, 4, 4, ACCUM>, 4);
+      else go(expand_tok_kernel<Tag, NW, 4, 8, ACCUM>, 8);
+      break;
+    default:
+      go(expand_tok_kernel<Tag, NW, 8, 4, ACCUM>, 4);
+      break;
+  }
+  (void)WB;
+}
+
 // (rank blocks, token blocks) with rb * bmb <= 8
 template <template <int, int> class L, class... A>
 static void dispatch8(int rb, int bmb, A&&... args) {
@@ -892,6 +1147,11 @@ static void launch_expand_cols(const FusedArgs& a, int rb, int bmb, hipStream_t 
 // use_split); with EMIT_G also writes the planes for the gradient kernels.
 template <class Tag, bool ACCUM, bool EMIT_G>
 static void run_shrink_expand(FusedArgs a, int rb, hipStream_t st) {
+  if (env_int("LORA_EXPAND_MODE", 0) == 4) {
+    launch_shrink_tok<Tag, EMIT_G, true>(a, rb, st);
+    launch_expand_tok<Tag, ACCUM>(a, rb, st);
+    return;
+  }
   if (env_int("LORA_EXPAND_MODE", 0) == 3) {
     launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
     launch_expand_cols<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, 8), st);
@@ -959,7 +1219,8 @@ static bool fits32(int64_t bytes) { return bytes >= 0 && bytes <= kMaxBufferByte
 // Offsets the shrink/expand kernels form: one 64-token tile of the stream
 // and of the output, and the whole of each weight.
 static bool fused_fits(int64_t ldz, size_t es, int64_t r, int64_t ldw1, int64_t nout, int64_t ldw2, int64_t ldo) {
-  return fits32(64 * ldz * (int64_t)es) && fits32(r * ldw1 * (int64_t)es) && fits32(nout * ldw2 * (int64_t)es) &&
+  const int64_t rp = padded_rank(static_cast<int>(r));
+  return fits32(64 * ldz * (int64_t)es) && fits32(rp * ldw1 * (int64_t)es) && fits32((nout + 16) * ldw2 * (int64_t)es) &&
          fits32(64 * ldo * 4);
 }
 
