@@ -15,13 +15,22 @@ HIP events on its stream), and the CPU oracle's throughput on the same
 workload as a baseline.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py ... --copy-probe      (adds 1 GiB plain copies after the
+                                             timed region, the calibration for
+                                             the byte counters)
+       python bench.py --traffic-summary FETCH_CSV WRITE_CSV [--workload NAME]
+           reads two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE,
+           then WRITE_SIZE) of a bench run with --copy-probe and writes the
+           roofline kernel's HBM bytes per launch to profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -38,6 +47,26 @@ WORKLOADS = {
     "single-bf16-M16384-K4096-L14336-r64": (16384, 4096, 14336, 64, 0.5, 3),
 }
 DEFAULT_WORKLOAD = "single-bf16-M8192-K4096-L4096-r16"
+
+# The kernels the roofline entry is about, per workload: what lora_fwd
+# launches at that shape (weights used in place, so no packing launch). At
+# M8192 K4096 L4096 r16 that is the one fused shrink+expand kernel; at the
+# 14336-wide output the call is a shrink launch followed by an expand launch.
+ROOFLINE_KERNEL = {
+    "single-bf16-M8192-K4096-L4096-r16": ["fused_kernel"],
+    "single-bf16-M16384-K4096-L14336-r64": ["shrink_kernel", "expand_kernel"],
+}
+# How those launches are told apart from the same templates' backward
+# instances in a profile: the forward ones accumulate into Y (ACCUM = true,
+# EMIT_G = false in fused_kernel / expand_kernel; EMIT_G = false, EMIT_F = true
+# in shrink_kernel).
+ROOFLINE_PATTERN = {
+    "fused_kernel": r"\bfused_kernel<.*, true, false>",
+    "shrink_kernel": r"\bshrink_kernel<.*, false, true>",
+    "expand_kernel": r"\bexpand_kernel<.*, true>",
+}
+COPY_PROBE_BYTES = 1 << 30
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def algorithmic_bytes(M, K, L, r, es=2):
@@ -60,10 +89,14 @@ def source_digest(paths):
 KERNEL_SOURCES = ["lora_rank_adapter_amd/csrc/lora_single.hip", "lora_rank_adapter_amd/csrc/lora_device.hpp"]
 
 
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{'+'.join(ROOFLINE_KERNEL[workload])}_{workload}.json")
+
+
 def traffic_from_profile(workload):
-    """HBM traffic of the forward kernel from the committed rocprofv3 counter
+    """HBM traffic of the roofline kernel from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_fwd_" + workload + ".json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -73,7 +106,71 @@ def traffic_from_profile(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, min_seconds=10.0, max_runs=20):
+def _counter_per_dispatch(path, counter, pattern):
+    """{dispatch id: counter value} (KiB for the byte counters) over the
+    dispatches whose kernel name matches the regex `pattern`."""
+    per = {}
+    rx = re.compile(pattern)
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and rx.search(row["Kernel_Name"]):
+                d = int(row["Dispatch_Id"])
+                per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+    return per
+
+
+def _kernel_mean(path, counter, pattern):
+    per = _counter_per_dispatch(path, counter, pattern)
+    if not per:
+        raise SystemExit(f"no dispatch of {pattern!r} with {counter} in {path}")
+    return statistics.mean(per.values()), len(per)
+
+
+def _copy_probe_kib(path, counter):
+    """The counter for the 1 GiB copies of --copy-probe: the last three copy
+    dispatches of the run (the input clones before them are smaller)."""
+    per = _counter_per_dispatch(path, counter, COPY_KERNEL)
+    last = [per[d] for d in sorted(per)[-3:]]
+    if len(last) < 3:
+        raise SystemExit(f"{path}: fewer than 3 copy dispatches; was the run made with --copy-probe?")
+    return statistics.mean(last)
+
+
+def traffic_summary(fetch_csv, write_csv, workload, command):
+    """HBM bytes per lora_fwd call of the roofline kernel(s): FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by bytes-moved / counter-reading
+    of the plain 1 GiB copy that ran in the same process."""
+    kern = ROOFLINE_KERNEL[workload]
+    f_copy = _copy_probe_kib(fetch_csv, "FETCH_SIZE") * 1024
+    w_copy = _copy_probe_kib(write_csv, "WRITE_SIZE") * 1024
+    f_scale, w_scale = COPY_PROBE_BYTES / f_copy, COPY_PROBE_BYTES / w_copy
+    fetch = [_kernel_mean(fetch_csv, "FETCH_SIZE", ROOFLINE_PATTERN[k]) for k in kern]
+    write = [_kernel_mean(write_csv, "WRITE_SIZE", ROOFLINE_PATTERN[k]) for k in kern]
+    f_k = sum(v for v, _ in fetch)
+    w_k = sum(v for v, _ in write)
+    n_f = [n for _, n in fetch]
+    n_w = [n for _, n in write]
+    M, K, Lc, r, _, _ = WORKLOADS[workload]
+    rec = {
+        "kernels": kern,
+        "workload": workload,
+        "command": command,
+        "source_digest": source_digest(KERNEL_SOURCES),
+        "copy_probe_bytes": COPY_PROBE_BYTES,
+        "copy_fetch_kib": f_copy / 1024, "copy_write_kib": w_copy / 1024,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "kernel_fetch_kib": f_k, "kernel_write_kib": w_k, "dispatches": [n_f, n_w],
+        "hbm_bytes_per_launch": f_k * 1024 * f_scale + w_k * 1024 * w_scale,
+        "algorithmic_bytes_per_launch": algorithmic_bytes(M, K, Lc, r)["fwd"],
+    }
+    rec["traffic_over_algorithmic"] = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+    with open(traffic_path(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def cpu_baseline(case, min_seconds=12.0, max_runs=1000):
     """The fp64 CPU oracle on the same batch, repeated for >= min_seconds."""
     import threadpoolctl
 
@@ -105,7 +202,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--command", default="", help="the profiled command, recorded with --traffic-summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, args.workload, args.command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -147,6 +250,8 @@ def main():
     del X0, dY0
     dA = torch.empty((K, r), dtype=torch.float32, device=dev)
     dB = torch.empty((r, Lc), dtype=torch.float32, device=dev)
+    ws0 = torch.empty(max(1, L.lora_workspace_bytes(L.LORA_OP_FWD, M, K, Lc, r, torch.bfloat16)), dtype=torch.uint8,
+                      device=dev)
     ws1 = torch.empty(L.lora_workspace_bytes(L.LORA_OP_BWD_DX_DA, M, K, Lc, r, torch.bfloat16), dtype=torch.uint8,
                       device=dev)
     ws2 = torch.empty(L.lora_workspace_bytes(L.LORA_OP_BWD_DB, M, K, Lc, r, torch.bfloat16), dtype=torch.uint8,
@@ -156,7 +261,7 @@ def main():
         s = sets[i % n_sets]
         if ev is not None:
             ev[0].record()
-        L.lora_fwd(s["X"], A_w.t(), B_w.t(), s["Y"], scale)
+        L.lora_fwd(s["X"], A_w.t(), B_w.t(), s["Y"], scale, workspace=ws0)
         if ev is not None:
             ev[1].record()
         L.lora_bwd_dx_da(s["X"].t(), s["dY"], B_w, A_w, scale, dx=s["dX"], dA=dA, workspace=ws1)
@@ -184,6 +289,14 @@ def main():
     fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
     dxda_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
     db_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+
+    if args.copy_probe:
+        src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     ab = algorithmic_bytes(M, K, Lc, r)
     step_bytes = ab["fwd"] + ab["dx_da"] + ab["db"]
@@ -215,7 +328,7 @@ def main():
             "lora_bwd_db": ab["db"] / (db_ms * 1e-3) / 1e9,
         },
         "roofline": {
-            "kernel": "fused_kernel (lora_fwd)",
+            "kernel": " + ".join(ROOFLINE_KERNEL[args.workload]) + " (lora_fwd)",
             "bound": "hbm",
             "achieved": fwd_gbs,
             "peak": HBM_PEAK_GBS,

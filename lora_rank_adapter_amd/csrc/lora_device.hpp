@@ -30,6 +30,12 @@ struct F32 {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: loops bounded by it compile to scalar branches, so the compiler can
+// keep loads in flight across iterations instead of draining at each
+// divergent loop edge.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
+
 // ---------------------------------------------------------------------------
 // Buffer-resource (V#) memory access. A raw buffer descriptor carries a base
 // address and a byte size; the hardware returns 0 for loads and drops stores

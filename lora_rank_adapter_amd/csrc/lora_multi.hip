@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
   __shared__ int sh_tok[TB];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int per_tile = p.n_slices * p.row_chunks;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
   __shared__ int sh_tok[TB];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int ti = blockIdx.x / p.total_chunks;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
                                                      const int32_t* __restrict__ token_slot,
                                                      const int32_t* __restrict__ ranks, int T, int S, int r_max,
                                                      float* __restrict__ h, int64_t hs0) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + wave_id();
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
   const int s = token_slot[t];

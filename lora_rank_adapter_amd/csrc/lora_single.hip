@@ -36,15 +36,51 @@ __device__ __forceinline__ int64_t round_up_dev(int64_t a, int64_t b) { return (
 // small utility kernels
 // ---------------------------------------------------------------------------
 
+// One weight re-layout: dst[i*ld + j] = src[i*s_i + j*s_j] for i < rows,
+// j < cols, and 0 in the padding up to dst_rows x dst_cols.
+struct PackJob {
+  const void* src;
+  int64_t s_i, s_j, rows, cols;
+  void* dst;
+  int64_t dst_rows, dst_cols, ld;
+  int64_t tiles_j, tiles;  // 32 x 32 tiles of dst: per tile row, total
+};
+struct PackArgs {
+  PackJob job[2];
+};
+
+// Up to two re-layouts in one launch (workgroups [0, job[0].tiles) take the
+// first). Each workgroup moves one 32 x 32 tile through LDS: it reads along
+// whichever source index is unit-stride and writes dst rows contiguously, so
+// a transposing pack stays coalesced on both sides.
 template <class E>
-__global__ __launch_bounds__(256) void pack_kernel(const E* __restrict__ src, int64_t s_i, int64_t s_j, int64_t rows,
-                                                   int64_t cols, E* __restrict__ dst, int64_t dst_rows,
-                                                   int64_t dst_cols, int64_t ld) {
-  const int64_t total = dst_rows * dst_cols;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const int64_t i = idx / dst_cols;
-    const int64_t j = idx - i * dst_cols;
-    dst[i * ld + j] = (i < rows && j < cols) ? src[i * s_i + j * s_j] : E(0);
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+  __shared__ E tile[32][33];
+  int64_t b = blockIdx.x;
+  const int sel = b < a.job[0].tiles ? 0 : 1;
+  if (sel) b -= a.job[0].tiles;
+  const PackJob jb = sel ? a.job[1] : a.job[0];
+  const E* __restrict__ src = static_cast<const E*>(jb.src);
+  E* __restrict__ dst = static_cast<E*>(jb.dst);
+  const int64_t ti = b / jb.tiles_j;
+  const int64_t tj = b - ti * jb.tiles_j;
+  const int tx = threadIdx.x & 31;
+  const int ty = threadIdx.x >> 5;
+  const bool along_i = jb.s_i == 1 && jb.s_j != 1;
+#pragma unroll
+  for (int k = 0; k < 32; k += 8) {
+    const int li = along_i ? tx : ty + k;
+    const int lj = along_i ? ty + k : tx;
+    const int64_t i = ti * 32 + li;
+    const int64_t j = tj * 32 + lj;
+    tile[li][lj] = (i < jb.rows && j < jb.cols) ? src[i * jb.s_i + j * jb.s_j] : E(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 32; k += 8) {
+    const int64_t i = ti * 32 + ty + k;
+    const int64_t j = tj * 32 + tx;
+    if (i < jb.dst_rows && j < jb.dst_cols) dst[i * jb.ld + j] = tile[ty + k][tx];
   }
 }
 
@@ -128,7 +164,7 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   constexpr int ES = sizeof(E);
   constexpr int CH = 4 * VEC;  // contraction values per MFMA step (4 lane groups)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
 
@@ -146,13 +182,18 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
 #pragma unroll
     for (int q = 0; q < RB; ++q) acc[b][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Each wave reduces one contiguous range of CH-wide chunks: its loads walk
+  // along the rows, which keeps the DRAM pages they open few.
   const int64_t nch = (p.Kin + CH - 1) / CH;
-  const int64_t cstep = (int64_t)NW * U;
+  const int64_t per = (nch + NW - 1) / NW;
+  const int64_t cbeg = (int64_t)wave * per;
+  const int64_t cend = (cbeg + per < nch) ? cbeg + per : nch;
+  constexpr int64_t cstep = U;
   auto load1 = [&](uint4 (&zf)[U][BMB], uint4 (&wf)[U][RB], int64_t c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t cc = c + (int64_t)NW * u;
-      const bool kok = cc < nch && cc * CH + grp * VEC < p.Kin;
+      const int64_t cc = c + u;
+      const bool kok = cc < cend && cc * CH + grp * VEC < p.Kin;
       const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
 #pragma unroll
       for (int b = 0; b < BMB; ++b) zf[u][b] = bload16(rz, kok ? zoff[b] + kb : kOOB);
@@ -170,18 +211,18 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   };
   {
     uint4 zA[U][BMB], wA[U][RB], zB[U][BMB], wB[U][RB];
-    int64_t c = wave;
-    if (c < nch) {
+    int64_t c = cbeg;
+    if (c < cend) {
       load1(zA, wA, c);
       for (;;) {
         load1(zB, wB, c + cstep);  // reads 0 past the end
         mma1(zA, wA);
         c += cstep;
-        if (c >= nch) break;
+        if (c >= cend) break;
         load1(zA, wA, c + cstep);
         mma1(zB, wB);
         c += cstep;
-        if (c >= nch) break;
+        if (c >= cend) break;
       }
     }
   }
@@ -253,7 +294,7 @@ __device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int6
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
@@ -332,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   uint4 hf[BMB][RB];
   shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf);
   if constexpr (EMIT_G) {
-    if ((threadIdx.x >> 6) == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
+    if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
   expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, 0, (p.Nout + 15) / 16, tile * p.rot, hf);
 }
@@ -346,7 +387,7 @@ __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
   f32x4_t acc[BMB][RB];
   uint4 hf[BMB][RB];
   shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf);
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   if constexpr (EMIT_G) {
     if (wave == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
@@ -403,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
   constexpr int NBS = NW * NBU;             // column blocks of this workgroup
   __shared__ wf_t w2s[NBS * RB * 64];       // [block][rank block][lane]
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int64_t nnb = (p.Nout + 15) / 16;
@@ -514,7 +555,7 @@ __global__ __launch_bounds__(64 * NW) void shrink_tok_kernel(FusedArgs p) {
   __shared__ uint4 wpan[2][NSTEP * RB * 64];  // [buffer][step][rank block][lane]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int64_t m0 = ((int64_t)blockIdx.x * NW + wave) * 16;  // this wave's token block
@@ -620,7 +661,7 @@ __global__ __launch_bounds__(64 * NW) void expand_tok_kernel(FusedArgs p) {
   using wf_t = typename WF::type;
   __shared__ wf_t w2s[NBS * RB * 64];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int64_t nnb = (p.Nout + 15) / 16;
@@ -901,11 +942,12 @@ static int pick_bmb_shrink(int64_t M, int rb) {
   return 1;
 }
 
-// Waves per workgroup: 8 while the partial-sum buffer stays <= 32 KB, else 4.
-static int pick_nw(const char* env, int rb, int bmb) {
+// Waves per workgroup: 8 while the partial-sum buffer stays <= 32 KB, else 4
+// (dflt8 = 0: 4 unless overridden; the fused kernel streams best with 4).
+static int pick_nw(const char* env, int rb, int bmb, int dflt8 = 1) {
   const int over = env_int(env, 0);
   if ((over == 4 && rb * bmb <= 16) || (over == 8 && rb * bmb <= 4)) return over;
-  return (8 * rb * bmb <= 32) ? 8 : 4;
+  return (dflt8 && 8 * rb * bmb <= 32) ? 8 : 4;
 }
 
 // Column splits of each token tile for the split expand: about `cols` output
@@ -1115,7 +1157,7 @@ struct ExpandNW {
 
 template <class Tag, bool ACCUM, bool EMIT_G>
 static void launch_fused(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  if (pick_nw("LORA_FUSED_NW", rb, bmb) == 8)
+  if (pick_nw("LORA_FUSED_NW", rb, bmb, 0) == 8)
     dispatch8<FusedNW<Tag, 8, ACCUM, EMIT_G>::template L>(rb, bmb, a, st);
   else
     dispatch8<FusedNW<Tag, 4, ACCUM, EMIT_G>::template L>(rb, bmb, a, st);
@@ -1179,20 +1221,24 @@ static void launch_tn(const TnArgs& a, int rb, hipStream_t st) {
   }
 }
 
-static void launch_pack(int32_t dtype, const void* src, int64_t s_i, int64_t s_j, int64_t rows, int64_t cols,
-                        void* dst, int64_t dst_rows, int64_t dst_cols, int64_t ld, hipStream_t st) {
-  const int64_t total = dst_rows * dst_cols;
-  if (total <= 0) return;
-  int64_t blocks = ceil_div(total, 256);
-  if (blocks > 8192) blocks = 8192;
+static PackJob pack_job(const void* src, int64_t s_i, int64_t s_j, int64_t rows, int64_t cols, void* dst,
+                        int64_t dst_rows, int64_t dst_cols, int64_t ld) {
+  PackJob j{src, s_i, s_j, rows, cols, dst, dst_rows, dst_cols, ld, ceil_div(dst_cols, 32), 0};
+  j.tiles = ceil_div(dst_rows, 32) * j.tiles_j;
+  return j;
+}
+
+// Launches the re-layouts (one or two) as a single kernel.
+static void launch_pack(int32_t dtype, const PackJob& j0, const PackJob* j1, hipStream_t st) {
+  PackArgs a{};
+  a.job[0] = j0;
+  if (j1) a.job[1] = *j1;
+  const int64_t blocks = a.job[0].tiles + a.job[1].tiles;
+  if (blocks <= 0) return;
   if (dtype == LORA_BF16)
-    hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(src), s_i, s_j, rows, cols, static_cast<uint16_t*>(dst), dst_rows,
-                       dst_cols, ld);
+    hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(pack_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       static_cast<const float*>(src), s_i, s_j, rows, cols, static_cast<float*>(dst), dst_rows,
-                       dst_cols, ld);
+    hipLaunchKernelGGL(pack_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
 }
 
 static void launch_fill_zero(const lora_mat* m, hipStream_t st) {
@@ -1333,11 +1379,13 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   FusedArgs a{};
   a.z = x->ptr;
   a.ldz = x->stride_row;
+  PackJob jobs[2];
+  int njobs = 0;
   if (a_direct) {
     a.w1 = lora_A->ptr;
     a.ldw1 = lora_A->stride_col;
   } else {
-    launch_pack(x->dtype, lora_A->ptr, lora_A->stride_col, lora_A->stride_row, r, K, w1p, rp, K, K, st);
+    jobs[njobs++] = pack_job(lora_A->ptr, lora_A->stride_col, lora_A->stride_row, r, K, w1p, rp, K, K);
     a.w1 = w1p;
     a.ldw1 = K;
   }
@@ -1345,10 +1393,11 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
     a.w2 = lora_B->ptr;
     a.ldw2 = lora_B->stride_col;
   } else {
-    launch_pack(x->dtype, lora_B->ptr, lora_B->stride_col, lora_B->stride_row, L, r, w2p, L, rp, rp, st);
+    jobs[njobs++] = pack_job(lora_B->ptr, lora_B->stride_col, lora_B->stride_row, L, r, w2p, L, rp, rp);
     a.w2 = w2p;
     a.ldw2 = rp;
   }
+  if (njobs > 0) launch_pack(x->dtype, jobs[0], njobs > 1 ? &jobs[1] : nullptr, st);
   a.out = static_cast<float*>(res->ptr);
   a.ldo = res->stride_row;
   a.M = M;
@@ -1413,8 +1462,9 @@ extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora
       !fits32((int64_t)lay.g))
     return LORA_ERR_LIMIT;
   // W1 = B^T (r x L, L contiguous); W2 = A^T (K x r, r contiguous).
-  launch_pack(xt->dtype, lora_B->ptr, lora_B->stride_col, lora_B->stride_row, r, L, w1p, rp, L, L, st);
-  launch_pack(xt->dtype, lora_A->ptr, lora_A->stride_col, lora_A->stride_row, K, r, w2p, K, rp, rp, st);
+  const PackJob jb = pack_job(lora_B->ptr, lora_B->stride_col, lora_B->stride_row, r, L, w1p, rp, L, L);
+  const PackJob ja = pack_job(lora_A->ptr, lora_A->stride_col, lora_A->stride_row, K, r, w2p, K, rp, rp);
+  launch_pack(xt->dtype, jb, &ja, st);
 
   FusedArgs a{};
   a.z = dy->ptr;
@@ -1502,7 +1552,8 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
     a.w1 = lora_A->ptr;
     a.ldw1 = lora_A->stride_row;
   } else {
-    launch_pack(xt->dtype, lora_A->ptr, lora_A->stride_row, lora_A->stride_col, r, K, w1p, rp, K, K, st);
+    launch_pack(xt->dtype, pack_job(lora_A->ptr, lora_A->stride_row, lora_A->stride_col, r, K, w1p, rp, K, K), nullptr,
+                st);
     a.w1 = w1p;
     a.ldw1 = K;
   }
