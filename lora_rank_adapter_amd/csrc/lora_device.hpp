@@ -16,6 +16,7 @@ namespace lora {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // bfloat16 inputs: 8 elements per 128-bit vector; one 16x16x32 MFMA per vector.
 struct BF16 {
@@ -29,6 +30,15 @@ struct F32 {
 };
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i receives element (i % 4) of the 4 x 16-bit pieces that lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of its group address, in that order.
+// `off` is this lane's byte offset into the __shared__ buffer `lds`.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds, int off) {
+  auto p = (__attribute__((address_space(3))) short4_t*)((char*)lds + off);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
 
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value: loops bounded by it compile to scalar branches, so the compiler can

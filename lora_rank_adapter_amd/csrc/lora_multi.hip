@@ -13,6 +13,8 @@
 // wave-level scan. Every tile touches one slot's adapter only, so its rows are
 // shared by all tokens of the tile.
 
+#include <type_traits>
+
 #include "lora_device.hpp"
 #include "lora_host.hpp"
 
@@ -309,6 +311,8 @@ struct ExpandArgs {
   const int32_t* sorted;
   const int32_t* ranks;
   int S, r_max, n_slices, total_chunks;
+  int64_t chunk_cols;  // columns per chunk (streaming kernel)
+  int64_t y_bytes;     // bytes of y a descriptor may span (streaming kernel)
   bool h_vec;  // h rows 16-byte aligned
   bool b_vec;  // b rows aligned for 4-element loads
   int64_t slice_off[kMaxSlices];
@@ -412,6 +416,292 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
   }
 }
 
+// Streaming form of expand_fused (bf16/f32 b rows 4-element aligned, h rows
+// 16-byte aligned, y below 2 GiB). A workgroup owns one tile (16*BMB tokens
+// of one slot) and a chunk of one output slice (chunk_cols columns, walked
+// 64*NBU columns per stage by the 4 waves, next stage's loads in flight while
+// the current one is multiplied). Consecutive workgroups take the chunks of
+// one tile, so the rows being updated at any time are few. Loads and stores
+// go through buffer descriptors: masked lanes (tokens past the tile, columns
+// past the slice) use an out-of-range offset.
+template <class Tag, int BMB, int RBM, int NBU>
+__global__ __launch_bounds__(256) void expand_stream_kernel(ExpandArgs p) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  constexpr int TB = 16 * BMB;
+  constexpr int NW = 4;
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int ti = blockIdx.x / p.total_chunks;
+  const int ch = blockIdx.x - ti * p.total_chunks;
+  int slice = 0;
+  while (slice + 1 < p.n_slices && ch >= p.chunk_begin[slice + 1]) ++slice;
+  const int64_t width = p.slice_w[slice];
+  const int64_t off = p.slice_off[slice];
+  const int64_t c_begin = (int64_t)(ch - p.chunk_begin[slice]) * p.chunk_cols;
+  const int64_t c_end = (c_begin + p.chunk_cols < width) ? c_begin + p.chunk_cols : width;
+
+  if (wave == 0) {
+    const Tile tl = find_tile(ti, TB, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  if (threadIdx.x < TB) sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
+  __syncthreads();
+  const float sc = p.scalings[tl.slot];
+  const int nq = (rho + 15) / 16;
+
+  // (sc * h)^T operand fragments of the tile's tokens; ranks >= rho read as 0
+  uint4 hf[BMB][RBM];
+  uint32_t yrow[BMB];
+  bool tok_ok[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) {
+    tok_ok[b] = 16 * b + col < tl.len;
+    const int t = sh_tok[16 * b + col];
+    yrow[b] = static_cast<uint32_t>((int64_t)t * p.ldy * 4 + off * 4);
+    const float* hrow = p.h + (int64_t)t * p.hs0 + (int64_t)slice * p.hs1;
+#pragma unroll
+    for (int q = 0; q < RBM; ++q) {
+      f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int j = 16 * q + 4 * grp;
+      if (tok_ok[b] && j < rho) {
+        if (j + 4 <= rho) {
+          v = ld16f(hrow + j);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < rho) v[e] = hrow[j + e];
+        }
+      }
+      v *= sc;
+      hf[b][q] = split_frag<Tag>(v);
+    }
+  }
+
+  const rsrc_t ry = make_rsrc(p.y, p.y_bytes);
+  const rsrc_t rb = make_rsrc(static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0 + off * p.bs1,
+                              width * p.bs1 * ES);
+  // column indices fit 32 bits (the host checks the descriptors' spans)
+  constexpr int kStage = NW * NBU * 16;
+  const int cb = static_cast<int>(c_begin);
+  const int ce = static_cast<int>(c_end);
+  const int nst = (ce - cb + kStage - 1) / kStage;
+  const int ldb = static_cast<int>(p.bs1);
+  auto yoff = [&](int b, int n) -> uint32_t {
+    return (tok_ok[b] && n < ce) ? yrow[b] + static_cast<uint32_t>(n) * 4u : kOOB;
+  };
+  // The column walk for NQ rank blocks (NQ = the slot's rank blocks, a
+  // wave-uniform value, so each tile runs exactly the MFMAs its rank needs).
+  auto walk = [&](auto nq_tag) {
+    constexpr int NQ = decltype(nq_tag)::value;
+    auto load2 = [&](wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
+#pragma unroll
+      for (int u = 0; u < NBU; ++u) {
+        const int nb = cb + k * kStage + (wave * NBU + u) * 16;
+        const int nrow = nb + col;
+        const bool rok = k < nst && nrow < ce;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int j0 = 16 * q + 4 * grp;
+          wv[u][q] = WF::bload(rb, rok ? static_cast<uint32_t>((nrow * ldb + j0) * ES) : kOOB, j0, rho);
+        }
+#pragma unroll
+        for (int b = 0; b < BMB; ++b)
+          cv[u][b] = __builtin_bit_cast(f32x4_t, bload16(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB));
+      }
+    };
+    auto comp2 = [&](const wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
+#pragma unroll
+      for (int u = 0; u < NBU; ++u) {
+        const int nb = cb + k * kStage + (wave * NBU + u) * 16;
+#pragma unroll
+        for (int b = 0; b < BMB; ++b) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
+          bstore16(ry, yoff(b, nb + 4 * grp), __builtin_bit_cast(uint4, cv[u][b]));
+        }
+      }
+    };
+    wf_t wvA[NBU][NQ], wvB[NBU][NQ];
+    f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
+    if (nst > 0) {
+      int k = 0;
+      load2(wvA, cvA, 0);
+      for (;;) {
+        load2(wvB, cvB, k + 1);  // masked past the last stage
+        comp2(wvA, cvA, k);
+        if (++k >= nst) break;
+        load2(wvA, cvA, k + 1);
+        comp2(wvB, cvB, k);
+        if (++k >= nst) break;
+      }
+    }
+  };
+  switch (nq) {
+    case 0: break;
+    case 1: walk(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (RBM >= 2) walk(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (RBM >= 4) walk(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (RBM >= 4) walk(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr (RBM >= 8) walk(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr (RBM >= 8) walk(std::integral_constant<int, 6>{}); break;
+    case 7: if constexpr (RBM >= 8) walk(std::integral_constant<int, 7>{}); break;
+    default: if constexpr (RBM >= 8) walk(std::integral_constant<int, 8>{}); break;
+  }
+}
+
+// Column-owner form of expand_fused (same preconditions as the streaming
+// form). A workgroup owns a piece of one slot's grouped tokens (at most
+// kOwnerTokens) and a chunk of kOwnerCols columns of one output slice. It
+// stages that slot's weight columns for the chunk in LDS once (MFMA operand
+// order, ranks >= rho zero), then each wave walks token blocks blk = wave,
+// wave + 4, ... of the piece: the block's h fragments go to registers, and the
+// block's output rows are updated across the chunk, 16 columns per MFMA tile,
+// with the next stage of output tiles loaded while the current one is
+// multiplied. The weights are read once per piece instead of once per token
+// block.
+constexpr int kOwnerTokens = 256;
+constexpr int kOwnerCols = 128;
+
+template <class Tag, int RBM>
+__global__ __launch_bounds__(256) void expand_owner_kernel(ExpandArgs p) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  constexpr int NW = 4;
+  constexpr int NCT = kOwnerCols / 16;  // column tiles of the chunk
+  constexpr int NBU = 4;                // column tiles per stage
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  __shared__ wf_t wls[NCT * RBM * 64];
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[kOwnerTokens];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int pi = blockIdx.x / p.total_chunks;
+  const int ch = blockIdx.x - pi * p.total_chunks;
+  int slice = 0;
+  while (slice + 1 < p.n_slices && ch >= p.chunk_begin[slice + 1]) ++slice;
+  const int64_t width = p.slice_w[slice];
+  const int64_t off = p.slice_off[slice];
+  const int c0 = (ch - p.chunk_begin[slice]) * kOwnerCols;
+  const int ce = (c0 + kOwnerCols < width) ? c0 + kOwnerCols : static_cast<int>(width);
+
+  if (wave == 0) {
+    const Tile tl = find_tile(pi, kOwnerTokens, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  const int nq = (rho + 15) / 16;
+  if (nq == 0) return;
+  for (int i = threadIdx.x; i < kOwnerTokens; i += 256) sh_tok[i] = (i < tl.len) ? p.sorted[tl.start + i] : 0;
+
+  // weight columns of the chunk, in operand order [column tile][rank block][lane]
+  const rsrc_t rb = make_rsrc(static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0 + off * p.bs1,
+                              width * p.bs1 * ES);
+  const int ldb = static_cast<int>(p.bs1);
+  for (int i = threadIdx.x; i < NCT * nq * 64; i += 256) {
+    const int l = i & 63;
+    const int q = (i >> 6) % nq;
+    const int ct = (i >> 6) / nq;
+    const int n = c0 + ct * 16 + (l & 15);
+    const int j0 = 16 * q + 4 * (l >> 4);
+    wls[(ct * RBM + q) * 64 + l] =
+        WF::bload(rb, n < ce ? static_cast<uint32_t>((n * ldb + j0) * ES) : kOOB, j0, rho);
+  }
+  __syncthreads();
+
+  const float sc = p.scalings[tl.slot];
+  const rsrc_t ry = make_rsrc(p.y, p.y_bytes);
+  const int nblk = (tl.len + 15) / 16;
+
+  auto walk = [&](auto nq_tag) {
+    constexpr int NQ = decltype(nq_tag)::value;
+    for (int blk = wave; blk < nblk; blk += NW) {
+      // an opaque zero keeps the weight reads below inside this loop (read
+      // from LDS per block instead of held in registers across blocks)
+      int lz;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+      const wf_t* wl = wls + lz;
+      const int tix = 16 * blk + col;
+      const bool tok_ok = tix < tl.len;
+      const int t = sh_tok[tix < kOwnerTokens ? tix : 0];
+      const uint32_t yrow = static_cast<uint32_t>((int64_t)t * p.ldy * 4 + off * 4);
+      const float* hrow = p.h + (int64_t)t * p.hs0 + (int64_t)slice * p.hs1;
+      uint4 hf[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int j = 16 * q + 4 * grp;
+        if (tok_ok && j < rho) {
+          if (j + 4 <= rho) {
+            v = ld16f(hrow + j);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j + e < rho) v[e] = hrow[j + e];
+          }
+        }
+        v *= sc;
+        hf[q] = split_frag<Tag>(v);
+      }
+      auto yoff = [&](int n) -> uint32_t { return (tok_ok && n < ce) ? yrow + static_cast<uint32_t>(n) * 4u : kOOB; };
+      f32x4_t cvA[NBU], cvB[NBU];
+      auto load = [&](f32x4_t (&cv)[NBU], int s) {
+#pragma unroll
+        for (int u = 0; u < NBU; ++u)
+          cv[u] = __builtin_bit_cast(f32x4_t, bload16(ry, s * NBU + u < NCT ? yoff(c0 + (s * NBU + u) * 16 + 4 * grp) : kOOB));
+      };
+      auto comp = [&](f32x4_t (&cv)[NBU], int s) {
+#pragma unroll
+        for (int u = 0; u < NBU; ++u) {
+          const int ct = s * NBU + u;
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u], WF::operand(wl[(ct * RBM + q) * 64 + lane]), hf[q]);
+          bstore16(ry, yoff(c0 + ct * 16 + 4 * grp), __builtin_bit_cast(uint4, cv[u]));
+        }
+      };
+      constexpr int NST = NCT / NBU;
+      load(cvA, 0);
+#pragma unroll
+      for (int s = 0; s < NST; s += 2) {
+        if (s + 1 < NST) load(cvB, s + 1);
+        comp(cvA, s);
+        if (s + 1 < NST) {
+          if (s + 2 < NST) load(cvA, s + 2);
+          comp(cvB, s + 1);
+        }
+      }
+    }
+  };
+  switch (nq) {
+    case 1: walk(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (RBM >= 2) walk(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (RBM >= 4) walk(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (RBM >= 4) walk(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr (RBM >= 8) walk(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr (RBM >= 8) walk(std::integral_constant<int, 6>{}); break;
+    case 7: if constexpr (RBM >= 8) walk(std::integral_constant<int, 7>{}); break;
+    default: if constexpr (RBM >= 8) walk(std::integral_constant<int, 8>{}); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gather_shrink: h[t, 0, j] = a[s, j, ids[t]] (exact), +0.0 for ids outside [0, V)
 // ---------------------------------------------------------------------------
@@ -485,6 +775,30 @@ static void launch_expand_b(const ExpandArgs& a, int rbm, dim3 grid, hipStream_t
     case 2: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
     default: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
+  }
+}
+
+// Streaming expand: (BMB, NBU) per rank-block count, chosen to keep the
+// weight and output fragments of two stages within the register budget.
+template <class Tag, int BMB>
+static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(tiles * a.total_chunks));
+  switch (rbm) {
+    case 1: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
+  }
+}
+
+template <class Tag>
+static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(pieces * a.total_chunks));
+  switch (rbm) {
+    case 1: hipLaunchKernelGGL((expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((expand_owner_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((expand_owner_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -605,6 +919,64 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   p.S = static_cast<int>(S);
   p.r_max = r_max;
   p.n_slices = num_slices;
+  const int rbm = rank_blocks(r_max);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Streaming kernel when its descriptors can span y and one slot's b with
+  // 32-bit offsets and the rows allow vector loads; else the general kernel.
+  // LORA_MULTI_EXPAND: 1 streaming, 2 column owner, 3 general (default: by T)
+  const int force = env_int("LORA_MULTI_EXPAND", 0);
+  const bool stream_ok = force != 3 && p.h_vec && p.b_vec && (T * y->stride_row * 4 <= kMaxBufferBytes) &&
+                         (O * b->s1 * (int64_t)es <= kMaxBufferBytes) && y->stride_row < (int64_t(1) << 30);
+  if (stream_ok && (force == 2 || (force == 0 && T >= 2048))) {
+    // many tokens: column owners, weights read once per token piece
+    p.chunk_cols = kOwnerCols;
+    int64_t off = 0;
+    int chunks = 0;
+    for (int i = 0; i < num_slices; ++i) {
+      p.slice_off[i] = off;
+      p.slice_w[i] = out_slices[i];
+      p.chunk_begin[i] = chunks;
+      chunks += static_cast<int>(ceil_div(out_slices[i], kOwnerCols));
+      off += out_slices[i];
+    }
+    p.chunk_begin[num_slices] = chunks;
+    p.total_chunks = chunks;
+    if (chunks == 0) return LORA_OK;
+    p.y_bytes = T * y->stride_row * 4;
+    const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
+    if (b->dtype == LORA_BF16)
+      launch_expand_owner<BF16>(p, rbm, pieces, st);
+    else
+      launch_expand_owner<F32>(p, rbm, pieces, st);
+    return launch_status();
+  }
+  if (stream_ok) {
+    const int bmb = (T >= 1024 && rbm <= 4) ? 2 : 1;
+    const int64_t tiles = ceil_div(T, 16 * bmb) + S;
+    // about 1024 columns per workgroup, fewer when there are few tiles
+    p.chunk_cols = tiles >= 256 ? 1024 : 256;
+    int64_t off = 0;
+    int chunks = 0;
+    for (int i = 0; i < num_slices; ++i) {
+      p.slice_off[i] = off;
+      p.slice_w[i] = out_slices[i];
+      p.chunk_begin[i] = chunks;
+      chunks += static_cast<int>(ceil_div(out_slices[i], p.chunk_cols));
+      off += out_slices[i];
+    }
+    p.chunk_begin[num_slices] = chunks;
+    p.total_chunks = chunks;
+    if (chunks == 0) return LORA_OK;
+    p.y_bytes = T * y->stride_row * 4;
+    if (b->dtype == LORA_BF16) {
+      if (bmb == 2) launch_expand_stream<BF16, 2>(p, rbm, tiles, st);
+      else launch_expand_stream<BF16, 1>(p, rbm, tiles, st);
+    } else {
+      if (bmb == 2) launch_expand_stream<F32, 2>(p, rbm, tiles, st);
+      else launch_expand_stream<F32, 1>(p, rbm, tiles, st);
+    }
+    return launch_status();
+  }
   int64_t off = 0;
   int chunks = 0;
   for (int i = 0; i < num_slices; ++i) {
@@ -618,9 +990,7 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   p.total_chunks = chunks;
   if (chunks == 0) return LORA_OK;
   const int bmb = tile_bmb(static_cast<int>(T));
-  const int rbm = rank_blocks(r_max);
   const int64_t tiles = ceil_div(T, 16 * bmb) + S;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (b->dtype == LORA_BF16)
     launch_expand<BF16>(p, bmb, rbm, tiles, st);
   else

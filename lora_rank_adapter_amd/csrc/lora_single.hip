@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ out,
 }
 
 // out(n, j) = sum over p = 0..P-1 (in that order) of part[p][n][j], j < r.
-// Loads are issued 8 partials at a time; the adds keep the p order.
+// Loads are issued 16 partials at a time; the adds keep the p order.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int P, int64_t N, int rp, int r,
                                                      float* __restrict__ out, int64_t os_n, int64_t os_j) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -105,12 +105,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
   const int64_t step = N * rp;
   float s = 0.0f;
   int pp = 0;
-  for (; pp + 8 <= P; pp += 8) {
-    float v[8];
+  for (; pp + 16 <= P; pp += 16) {
+    float v[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = src[(pp + e) * step];
+    for (int e = 0; e < 16; ++e) v[e] = src[(pp + e) * step];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = (pp + e == 0) ? v[e] : s + v[e];
+    for (int e = 0; e < 16; ++e) s = (pp + e == 0) ? v[e] : s + v[e];
   }
   for (; pp < P; ++pp) s = (pp == 0) ? src[0] : s + src[pp * step];
   out[n * os_n + j * os_j] = s;
@@ -745,7 +745,7 @@ struct TnArgs {
   float* part;     // P x N x rp
   int64_t M, N;
   int rp;
-  int64_t chunk;   // tokens per chunk, a multiple of 32
+  int64_t chunk;   // tokens per chunk, a multiple of 64
 };
 
 template <class Tag, int RB>
@@ -755,7 +755,7 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   constexpr int ES = sizeof(E);
   constexpr int NSB = 4;              // 16-column blocks per wave
   constexpr int NS = 64 * NSB;        // columns per workgroup
-  constexpr int TS = 32;              // tokens per stage
+  constexpr int TS = (ES == 2) ? 64 : 32;  // tokens per stage (bf16: two 32-token MFMA steps)
   constexpr int ROWB = NS * ES;       // LDS bytes per staged Z row
   constexpr int VPR = NS / VEC;       // 128-bit vectors per Z row
   constexpr int ZV = TS * VPR / 256;  // Z vectors per thread per stage
@@ -814,14 +814,26 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
     }
   };
 
+  // LDS byte offset of Z(row, column byte cb). bf16: the 32-byte (16-column)
+  // block index is XORed with a 4-bit row code so that the 16 rows one
+  // transposed read touches (rows 8g + j, g, j < 4) land in 16 different
+  // blocks; f32: 64-byte windows XORed with rows 4 apart.
+  auto zoff = [&](int row, int cb) -> int {
+    if constexpr (ES == 2) {
+      const int code = (row & 3) | (((row >> 3) & 3) << 2);
+      return row * ROWB + ((((cb >> 5) ^ code) << 5) | (cb & 31));
+    } else {
+      return row * ROWB + (cb ^ (((row >> SWZ_SHIFT) & 3) * SWZ_UNIT));
+    }
+  };
+
   auto store_stage = [&]() {
 #pragma unroll
     for (int i = 0; i < ZV; ++i) {
       const int v = tid + 256 * i;
       const int row = v / VPR;
       const int vc = v - row * VPR;
-      const int off = row * ROWB + ((vc * 16) ^ (((row >> SWZ_SHIFT) & 3) * SWZ_UNIT));
-      *reinterpret_cast<uint4*>(zt + off) = zr[i];
+      *reinterpret_cast<uint4*>(zt + zoff(row, vc * 16)) = zr[i];
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
@@ -830,13 +842,8 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
     }
   };
 
-  auto zval = [&](int m, int nl) -> uint32_t {
-    const int off = m * ROWB + ((nl * ES) ^ (((m >> SWZ_SHIFT) & 3) * SWZ_UNIT));
-    if constexpr (ES == 2)
-      return *reinterpret_cast<const uint16_t*>(zt + off);
-    else
-      return *reinterpret_cast<const uint32_t*>(zt + off);
-  };
+  // f32 operand element (bf16 operands use transposed reads instead)
+  auto zval = [&](int m, int nl) -> uint32_t { return *reinterpret_cast<const uint32_t*>(zt + zoff(m, nl * ES)); };
 
   const int64_t nstage = (m_end - m_begin + TS - 1) / TS;
   if (nstage > 0) load_stage(m_begin);
@@ -847,23 +854,34 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
     if (s + 1 < nstage) load_stage(m_begin + (s + 1) * TS);
 
     if constexpr (ES == 2) {
-      uint4 ghi[RB], glo[RB];
 #pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        ghi[q] = *reinterpret_cast<const uint4*>(gs + (16 * q + col) * GROWB + grp * 16);
-        glo[q] = *reinterpret_cast<const uint4*>(gs + (16 * RB + 16 * q + col) * GROWB + grp * 16);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NSB; ++nb) {
-        const int nl = (wave * NSB + nb) * 16 + col;
-        uint32_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = zval(8 * grp + e, nl);
-        const uint4 zf = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+      for (int u = 0; u < TS / 32; ++u) {
+        uint4 ghi[RB], glo[RB];
 #pragma unroll
         for (int q = 0; q < RB; ++q) {
-          mma_vec<Tag>(acc[nb][q], zf, ghi[q]);
-          mma_vec<Tag>(acc[nb][q], zf, glo[q]);
+          ghi[q] = *reinterpret_cast<const uint4*>(gs + (16 * q + col) * GROWB + u * 64 + grp * 16);
+          glo[q] = *reinterpret_cast<const uint4*>(gs + (16 * RB + 16 * q + col) * GROWB + u * 64 + grp * 16);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NSB; ++nb) {
+          // Z^T fragment: lane (col, grp) needs Z[32u + 8grp + 0..7][n0 + col]. A
+          // transposed read hands lane i of each 16-lane group element i%4 of
+          // the 8-byte pieces addressed by lanes 4e + i/4 (e < 4): lane c
+          // addresses row 32u + 8grp + 4h + c/4, columns n0 + 4(c%4) .. +3.
+          const int n0 = (wave * NSB + nb) * 16;
+          uint2 half[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = 32 * u + 8 * grp + 4 * h + (col >> 2);
+            const int off = zoff(row, (n0 + 4 * (col & 3)) * 2);
+            half[h] = lds_read_tr16(zt, off);
+          }
+          const uint4 zf = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            mma_vec<Tag>(acc[nb][q], zf, ghi[q]);
+            mma_vec<Tag>(acc[nb][q], zf, glo[q]);
+          }
         }
       }
     } else {
@@ -964,26 +982,29 @@ static int pick_split(int64_t nout) {
 // or split (shrink kernel writes it as MFMA fragments, column-split expand).
 // The split form lets several workgroups update the rows of one token tile
 // together; it wins when the output rows are long.
-static bool use_split(int64_t nout) {
-  const int over = env_int("LORA_EXPAND_MODE", 0);  // 1 fused, 2 split
-  if (over == 1) return false;
-  if (over == 2) return true;
-  return nout > 8192;
+static int pick_schedule(int64_t nout, int64_t kin) {
+  const int over = env_int("LORA_EXPAND_MODE", 0);  // 1 fused, 2 column split, 3 column owner, 4 token split
+  if (over >= 1 && over <= 4) return over;
+  return (nout > 8192 || kin > 8192) ? 3 : 1;
 }
 
-static int64_t tn_chunks_max(int64_t M, int64_t N) {
+// Token chunks of the weight-gradient kernels: about `wgs` workgroups in all,
+// at most one chunk per 64 tokens.
+static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs) {
   const int64_t slices = ceil_div(N, kTnCols);
-  int64_t P = ceil_div(512, slices);
-  const int64_t cap = ceil_div(M, 32);
+  int64_t P = ceil_div(wgs, slices);
+  const int64_t cap = ceil_div(M, 64);
   if (P > cap) P = cap;
   return P < 1 ? 1 : P;
 }
 
+static int64_t tn_chunks_max(int64_t M, int64_t N) { return tn_chunks_for(M, N, 2048); }
+
 static int64_t tn_chunk_tokens(int64_t M, int64_t N) {
-  int64_t P = tn_chunks_max(M, N);
+  int64_t P = tn_chunks_for(M, N, 512);
   const int64_t over = env_int("LORA_TN_CHUNKS", 0);
-  if (over >= 1 && over < P) P = over;
-  return round_up(ceil_div(M, P), 32);
+  if (over >= 1 && over <= tn_chunks_max(M, N)) P = over;
+  return round_up(ceil_div(M, P), 64);
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,9 +1056,10 @@ struct ExpandColsLaunch {
   static void run(FusedArgs a, hipStream_t st) {
     a.tiles = ceil_div(a.M, 16 * BMB);
     const int64_t cols = ceil_div(ceil_div(a.Nout, 16), (int64_t)NW * NBU);
-    // token groups: enough workgroups to fill the chip twice, at most one per tile
+    // token groups: at least 64 (measured best for 8-28 column slices), enough
+    // workgroups to fill the chip twice for narrow outputs, at most one per tile
     int64_t groups = env_int("LORA_COLS_GROUPS", 0);
-    if (groups <= 0) groups = ceil_div(512, cols);
+    if (groups <= 0) groups = ceil_div(512, cols) > 64 ? ceil_div(512, cols) : 64;
     if (groups > a.tiles) groups = a.tiles;
     if (groups < 1) groups = 1;
     hipLaunchKernelGGL((expand_cols_kernel<Tag, NW, RB, BMB, NBU, ACCUM>),
@@ -1186,20 +1208,21 @@ static void launch_expand_cols(const FusedArgs& a, int rb, int bmb, hipStream_t 
 }
 
 // Shrink Z against W1 and expand into the output, fused or split (see
-// use_split); with EMIT_G also writes the planes for the gradient kernels.
+// pick_schedule); with EMIT_G also writes the planes for the gradient kernels.
 template <class Tag, bool ACCUM, bool EMIT_G>
 static void run_shrink_expand(FusedArgs a, int rb, hipStream_t st) {
-  if (env_int("LORA_EXPAND_MODE", 0) == 4) {
+  const int mode = pick_schedule(a.Nout, a.Kin);
+  if (mode == 4) {
     launch_shrink_tok<Tag, EMIT_G, true>(a, rb, st);
     launch_expand_tok<Tag, ACCUM>(a, rb, st);
     return;
   }
-  if (env_int("LORA_EXPAND_MODE", 0) == 3) {
+  if (mode == 3) {
     launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
     launch_expand_cols<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, 8), st);
     return;
   }
-  if (use_split(a.Nout)) {
+  if (mode == 2) {
     launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
     a.nsplit = pick_split(a.Nout);
     launch_expand<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, a.nsplit), st);
@@ -1294,14 +1317,14 @@ static SingleLayout layout_for(int op, int64_t M, int64_t K, int64_t L, int r, i
   } else if (op == LORA_OP_BWD_DX_DA) {
     s.w1 = static_cast<size_t>(rp * L) * es;  // B as r x L
     s.w2 = static_cast<size_t>(K * rp) * es;  // A as K x r
-    s.ldg = round_up(M > 0 ? M : 1, 32);
+    s.ldg = round_up(M > 0 ? M : 1, 64);
     s.g = static_cast<size_t>(4 * rp * s.ldg);
     s.P = tn_chunks_max(M, K);
     s.part = static_cast<size_t>(s.P * K * rp) * 4;
     s.frag = frag;
   } else {
     s.w1 = static_cast<size_t>(rp * K) * es;  // A as r x K
-    s.ldg = round_up(M > 0 ? M : 1, 32);
+    s.ldg = round_up(M > 0 ? M : 1, 64);
     s.g = static_cast<size_t>(4 * rp * s.ldg);
     s.P = tn_chunks_max(M, L);
     s.part = static_cast<size_t>(s.P * L * rp) * 4;

@@ -111,6 +111,32 @@ def test_expand_fused(case):
     assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
 
 
+@pytest.mark.parametrize("mode", [1, 2, 3])
+@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
+def test_expand_every_schedule(case, mode, monkeypatch):
+    """Each expand_fused kernel (streaming, column owner, general) on the same
+    cases: parity, inactive rows untouched, NaN padding never read."""
+    monkeypatch.setenv("LORA_MULTI_EXPAND", str(mode))
+    test_expand_fused(case)
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_expand_schedules_integer_exact(mode, monkeypatch):
+    monkeypatch.setenv("LORA_MULTI_EXPAND", str(mode))
+    note(f"expand integer-exact schedule {mode}")
+    m = _case("prefill-like", 0, 96, (64, 32), 12, 32, (8, 16, 32), 0.0, "bf16", int_exact=True)
+    addr, ranks = _addr(m)
+    act, spec = _spec_mask(m)
+    rng = np.random.default_rng(9)
+    hin = rng.integers(-2, 3, size=(m.T, m.num_slices, m.r_max)).astype(np.float32)
+    hin[~spec] = np.nan
+    y = f32(m.y0)
+    L.lora_expand_fused(f32(hin), dev(m.b, "bf16"), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    want = oracle.expand_fused(hin, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max)
+    assert same_bits(host(y), want.astype(np.float32))
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_shrink_then_expand(case):
     m = _case(*case)
