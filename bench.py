@@ -195,6 +195,84 @@ def cpu_baseline(case, min_seconds=12.0, max_runs=1000):
     }
 
 
+def multi_lora_figures(dev, reps=20):
+    """Kernel times of the slot-addressed ops on the decode and prefill
+    workloads (routing from synth's seeded laws; values drawn on the device
+    with the same laws), with their algorithmic bytes: activations once per
+    active token, each used slot's live adapter rows once, h once, y read and
+    written for active tokens."""
+    import numpy as np
+    import torch
+
+    import lora_rank_adapter_amd as L
+    import synth
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+
+    def timed(f, n):
+        f(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            f(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    out = {}
+    rng4 = np.random.default_rng(4)
+    ts4, rk4 = synth.decode_routing(256, 32, 64, (0, 8, 16, 32, 64), 0.1, rng4)
+    ts5, rk5, _lengths, _rng5 = synth.config5_routing()
+    for name, ts_np, rk_np, K, slices, r_max in (
+            ("decode-T256-K4096-qkv-S32-rmax64", ts4, rk4, 4096, (4096, 1024, 1024), 64),
+            ("prefill-K8192-qkv-S128-rmax128", ts5, rk5, 8192, (8192, 1024, 1024), 128)):
+        T, S, n, SO = ts_np.shape[0], rk_np.shape[0], len(slices), sum(slices)
+        nsets = 3 if T > 4096 else 1
+        ts = torch.from_numpy(ts_np).to(dev)
+        rk = torch.from_numpy(rk_np).to(dev)
+        xs = [torch.randn((T, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(nsets)]
+        a = (torch.randn((S, n * r_max, K), device=dev, generator=gen) / K ** 0.5).to(torch.bfloat16)
+        b = (torch.randn((S, SO, r_max), device=dev, generator=gen) / 8).to(torch.bfloat16)
+        sc = torch.rand(S, device=dev, generator=gen) * 1.5 + 0.5
+        ys = [torch.randn((T, SO), device=dev, generator=gen) for _ in range(nsets)]
+        h = torch.zeros((T, n, r_max), device=dev)
+        addr = L.Addressing(ts, S)
+        t_group = timed(lambda i: L.lora_addressing_build(addr, rk, r_max), reps)
+        t_shrink = timed(lambda i: L.lora_shrink(xs[i % nsets], a, addr, rk, n, r_max, h=h), reps)
+        t_expand = timed(lambda i: L.lora_expand_fused(h, b, addr, rk, sc, ys[i % nsets], slices, r_max), reps)
+        rho = np.clip(rk_np, 0, r_max)
+        act = (ts_np >= 0) & (ts_np < S) & (rho[np.clip(ts_np, 0, S - 1)] > 0)
+        used = np.unique(ts_np[act])
+        na = int(act.sum())
+        live = int(rho[used].sum())
+        rho_sum = int(rho[ts_np[act]].sum())
+        sh_bytes = na * 2 * K + 2 * K * n * live + 4 * n * rho_sum
+        ex_bytes = 4 * n * rho_sum + 2 * SO * live + 8 * SO * na
+        out[name] = {
+            "tokens": T, "active_tokens": na, "used_slots": int(len(used)),
+            "grouping_us": t_group,
+            "shrink_us": t_shrink, "shrink_gbs": sh_bytes / t_shrink / 1e3,
+            "expand_fused_us": t_expand, "expand_fused_gbs": ex_bytes / t_expand / 1e3,
+            "expand_fused_frac": ex_bytes / t_expand / 1e3 / HBM_PEAK_GBS,
+        }
+        del xs, a, b, ys, h
+    # gather_shrink over the 128256-row embedding adapter table (4.2 GB, rank index contiguous)
+    T, S, r_max, V = ts5.shape[0], 128, 128, 128256
+    tab = torch.randn((S, V, r_max), device=dev, generator=gen).to(torch.bfloat16).permute(0, 2, 1)
+    ids = torch.randint(0, V, (T,), device=dev, generator=gen, dtype=torch.int32)
+    ids[torch.rand(T, device=dev, generator=gen) < 0.05] = -1
+    rk = torch.from_numpy(rk5).to(dev)
+    addr = L.lora_addressing_build(L.Addressing(torch.from_numpy(ts5).to(dev), S), rk, r_max)
+    h = torch.zeros((T, 1, r_max), device=dev)
+    out["gather_shrink-V128256-S128-rmax128"] = {
+        "tokens": T, "us": timed(lambda i: L.lora_gather_shrink(ids, tab, addr, rk, r_max, h=h), reps)}
+    del tab
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +281,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-multi", action="store_true", help="skip the multi-adapter serving figures")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="", help="the profiled command, recorded with --traffic-summary")
     args = ap.parse_args()
@@ -338,6 +417,10 @@ def main():
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(case),
     }
+    if not args.no_multi:
+        del sets
+        torch.cuda.empty_cache()
+        out["multi_lora"] = multi_lora_figures(dev)
     print(json.dumps(out), flush=True)
 
 

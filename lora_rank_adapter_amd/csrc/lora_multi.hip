@@ -179,6 +179,7 @@ struct ShrinkArgs {
   const int32_t* ranks;
   int64_t K;
   int S, r_max, n_slices, row_chunks;
+  int64_t x_bytes;  // bytes of x a descriptor may span (GEMM kernel)
   bool h_vec;  // h rows 16-byte aligned (strides multiples of 4)
 };
 
@@ -291,6 +292,142 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
           if (j + e < rho) hrow[j + e] = s[e];
       }
     }
+  }
+}
+
+// GEMM form of shrink for bf16 inputs (x and one slot's a within 2 GiB
+// descriptors, h rows 16-byte aligned). A workgroup of 8 waves owns a piece
+// of up to 128 grouped tokens of one slot; wave w owns token block w. The
+// rank rows of all slices are handled as (slice, 16-row rank block) pairs, up
+// to kPairs per pass (one pass unless the slot's rank exceeds 16*kPairs/n):
+// every 64-feature chunk of the pass's adapter rows is staged once in LDS
+// (double buffered, one barrier per chunk) and shared by the 8 token blocks,
+// while each wave streams its own tokens' features from HBM. x is read once
+// per pass, the adapter once per piece.
+constexpr int kPairs = 16;
+constexpr int kShrinkTokens = 128;
+
+__global__ __launch_bounds__(512) void shrink_gemm_kernel(ShrinkArgs p) {
+  constexpr int NW = 8;
+  constexpr int KC = 64;                  // features per chunk (two MFMA steps)
+  constexpr int kAE = kPairs * 2 * 64 / (64 * NW);  // adapter-tile entries per thread
+  __shared__ uint4 als[2][kPairs * 2 * 64];  // [buf][pair][step][lane]
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[kShrinkTokens];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  if (wave == 0) {
+    const Tile tl = find_tile(blockIdx.x, kShrinkTokens, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  const int nq = (rho + 15) / 16;
+  if (nq == 0) return;
+  if (threadIdx.x < kShrinkTokens)
+    sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
+  __syncthreads();
+
+  const int tix = 16 * wave + col;
+  const bool tok_ok = tix < tl.len;
+  const bool blk_any = 16 * wave < tl.len;
+  const int t = sh_tok[tix];
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+  const rsrc_t ra = make_rsrc(static_cast<const uint16_t*>(p.a) + (int64_t)tl.slot * p.as0,
+                              (int64_t)p.n_slices * p.r_max * p.as1 * 2);
+  const uint32_t xrow = tok_ok ? static_cast<uint32_t>((int64_t)t * p.ldx * 2) : kOOB;
+  const int K = static_cast<int>(p.K);
+  const int nch = (K + KC - 1) / KC;
+  const int npairs = p.n_slices * nq;
+
+  for (int p0 = 0; p0 < npairs; p0 += kPairs) {
+    const int rp = (npairs - p0 < kPairs) ? npairs - p0 : kPairs;
+    // this thread's share of the chunk's adapter tile: entries e = tid + 512*i,
+    // e -> (pair, step, lane) in operand order
+    uint4 areg[kAE];
+    uint32_t aoff[kAE];
+    int ak[kAE];  // feature offset of the entry within a chunk
+    bool aok[kAE];
+#pragma unroll
+    for (int i = 0; i < kAE; ++i) {
+      const int e = threadIdx.x + 512 * i;
+      const int pr = e >> 7;
+      const int l = e & 63;
+      const int stp = (e >> 6) & 1;
+      aok[i] = pr < rp;
+      const int pg = p0 + pr;
+      const int sl = pg / nq;
+      const int q = pg - sl * nq;
+      const int row = 16 * q + (l & 15);
+      ak[i] = stp * 32 + (l >> 4) * 8;
+      aoff[i] = (aok[i] && row < rho)
+                    ? static_cast<uint32_t>(((int64_t)(sl * p.r_max + row) * p.as1 + stp * 32 + (l >> 4) * 8) * 2)
+                    : kOOB;
+    }
+    auto load_a = [&](int c) {
+#pragma unroll
+      for (int i = 0; i < kAE; ++i)
+        areg[i] = bload16(ra, (aoff[i] != kOOB && c * KC + ak[i] < K) ? aoff[i] + static_cast<uint32_t>(c * KC * 2)
+                                                                           : kOOB);
+    };
+    uint4 xr[2];
+    auto load_x = [&](int c) {
+#pragma unroll
+      for (int stp = 0; stp < 2; ++stp) {
+        const int k = c * KC + stp * 32 + grp * 8;
+        xr[stp] = bload16(rx, (xrow != kOOB && k < K) ? xrow + static_cast<uint32_t>(k * 2) : kOOB);
+      }
+    };
+    f32x4_t acc[kPairs];
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_a(0);
+    load_x(0);
+    for (int c = 0; c < nch; ++c) {
+      uint4* buf = als[c & 1];
+#pragma unroll
+      for (int i = 0; i < kAE; ++i)
+        if (aok[i]) buf[threadIdx.x + 512 * i] = areg[i];
+      const uint4 x0 = xr[0], x1 = xr[1];
+      __syncthreads();
+      load_a(c + 1);  // masked past the last chunk
+      load_x(c + 1);
+      if (blk_any) {
+#pragma unroll
+        for (int pr = 0; pr < kPairs; ++pr) {
+          if (pr < rp) {
+            mma_vec<BF16>(acc[pr], buf[(pr * 2 + 0) * 64 + lane], x0);
+            mma_vec<BF16>(acc[pr], buf[(pr * 2 + 1) * 64 + lane], x1);
+          }
+        }
+      }
+    }
+    // h[t][slice][16q + 4grp + i] = acc[pr][i] for rank rows below rho
+    if (tok_ok) {
+#pragma unroll
+      for (int pr = 0; pr < kPairs; ++pr) {
+        if (pr < rp) {
+          const int pg = p0 + pr;
+          const int sl = pg / nq;
+          const int j = 16 * (pg - sl * nq) + 4 * grp;
+          float* hrow = p.h + (int64_t)t * p.hs0 + (int64_t)sl * p.hs1;
+          if (j + 4 <= rho) {
+            st16f(hrow + j, acc[pr]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j + e < rho) hrow[j + e] = acc[pr][e];
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next pass rewrites both buffers
   }
 }
 
@@ -869,6 +1006,20 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
   p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // LORA_MULTI_SHRINK: 1 GEMM form, 2 general. Default: general. (The GEMM
+  // form reads x once instead of once per slice and rank chunk, but with one
+  // chunk of prefetch and a barrier per chunk it is latency-bound and measures
+  // slower on the prefill workload: 456 vs 382 us.)
+  const int force = env_int("LORA_MULTI_SHRINK", 2);
+  const bool gemm_ok = force != 2 && x->dtype == LORA_BF16 && p.h_vec && K % 8 == 0 &&
+                       T * x->stride_row * 2 <= kMaxBufferBytes &&
+                       (int64_t)num_slices * r_max * a->s1 * 2 <= kMaxBufferBytes && K < (int64_t(1) << 30);
+  if (gemm_ok && force == 1) {
+    p.x_bytes = T * x->stride_row * 2;
+    const int64_t pieces = ceil_div(T, kShrinkTokens) + S;
+    hipLaunchKernelGGL(shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
+    return launch_status();
+  }
   if (x->dtype == LORA_BF16)
     launch_shrink<BF16>(p, bmb, rb, tiles, st);
   else

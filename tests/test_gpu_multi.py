@@ -91,6 +91,32 @@ def test_shrink(case):
     assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
+def test_shrink_every_schedule(case, mode, monkeypatch):
+    """Both shrink kernels (GEMM form with the adapter staged in LDS, general)
+    on the same cases, including a feature count that is not a multiple of
+    the GEMM form's 64-feature chunk."""
+    monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
+    test_shrink(case)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_shrink_schedules_integer_exact(mode, monkeypatch):
+    monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
+    note(f"shrink integer-exact schedule {mode}")
+    m = _case("prefill-like", 0, 200, (64, 32), 12, 48, (8, 16, 48), 0.0, "bf16", int_exact=True)
+    addr, ranks = _addr(m)
+    act, spec = _spec_mask(m)
+    h = torch.full((m.T, m.num_slices, m.r_max), SENTINEL, dtype=torch.float32, device=DEV)
+    L.lora_shrink(dev(m.x, "bf16"), dev(m.a, "bf16"), addr, ranks, m.num_slices, m.r_max, h=h)
+    torch.cuda.synchronize()
+    want = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max)
+    got = host(h)
+    assert np.all(got[~spec] == SENTINEL)
+    assert same_bits(got[spec], want[spec].astype(np.float32))
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_expand_fused(case):
     m = _case(*case)
