@@ -79,10 +79,15 @@ def algorithmic_bytes(M, K, L, r, es=2):
 
 
 def source_digest(paths):
+    """Digest of the kernel sources with comments and blank space removed, so
+    that a comment-only edit keeps counter records valid."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -12,6 +12,19 @@
 // into tiles of TB tokens; tile k of the batch is found from counts[] with a
 // wave-level scan. Every tile touches one slot's adapter only, so its rows are
 // shared by all tokens of the tile.
+//
+// Kernels:
+//   group_kernel               stable counting sort (one 1024-thread workgroup)
+//   slot_shrink_kernel         shrink, one workgroup per (tile, slice, rank chunk)
+//   slot_shrink_gemm_kernel    shrink with the adapter chunk staged in LDS and
+//                              shared by 8 token blocks (selectable)
+//   slot_expand_owner_kernel   expand for many tokens: a token piece x column
+//                              chunk per workgroup, weights staged once in LDS
+//   slot_expand_stream_kernel  expand for few tokens: tile x column chunk,
+//                              weights from L2, two stages of outputs in flight
+//   slot_expand_kernel         expand for any layout (unaligned rows, y or b
+//                              beyond 2 GiB)
+//   gather_kernel              exact one-hot shrink, one wave per token
 
 #include <type_traits>
 
@@ -184,7 +197,7 @@ struct ShrinkArgs {
 };
 
 template <class Tag, int BMB, int RB>
-__global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
+__global__ __launch_bounds__(256) void slot_shrink_kernel(ShrinkArgs p) {
   using E = typename Tag::elem;
   constexpr int VEC = Tag::VEC;
   constexpr int CH = 4 * VEC;
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
 constexpr int kPairs = 16;
 constexpr int kShrinkTokens = 128;
 
-__global__ __launch_bounds__(512) void shrink_gemm_kernel(ShrinkArgs p) {
+__global__ __launch_bounds__(512) void slot_shrink_gemm_kernel(ShrinkArgs p) {
   constexpr int NW = 8;
   constexpr int KC = 64;                  // features per chunk (two MFMA steps)
   constexpr int kAE = kPairs * 2 * 64 / (64 * NW);  // adapter-tile entries per thread
@@ -461,7 +474,7 @@ constexpr int kExpandNBU = 4;                  // 16-column blocks per wave
 constexpr int kExpandCols = 64 * kExpandNBU;   // columns per workgroup
 
 template <class Tag, int BMB, int RBM>
-__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
+__global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
   constexpr int TB = 16 * BMB;
   constexpr int NBU = kExpandNBU;
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
 // go through buffer descriptors: masked lanes (tokens past the tile, columns
 // past the slice) use an out-of-range offset.
 template <class Tag, int BMB, int RBM, int NBU>
-__global__ __launch_bounds__(256) void expand_stream_kernel(ExpandArgs p) {
+__global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
   constexpr int TB = 16 * BMB;
@@ -712,7 +725,7 @@ constexpr int kOwnerTokens = 256;
 constexpr int kOwnerCols = 128;
 
 template <class Tag, int RBM>
-__global__ __launch_bounds__(256) void expand_owner_kernel(ExpandArgs p) {
+__global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
   constexpr int NW = 4;
@@ -894,24 +907,24 @@ static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, h
   const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
   if (bmb == 4) {
     if (rb == 4)
-      hipLaunchKernelGGL((shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((shrink_kernel<Tag, 4, 1>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 4, 1>), grid, dim3(256), 0, st, a);
   } else {
     if (rb == 4)
-      hipLaunchKernelGGL((shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
   }
 }
 
 template <class Tag, int BMB>
 static void launch_expand_b(const ExpandArgs& a, int rbm, dim3 grid, hipStream_t st) {
   switch (rbm) {
-    case 1: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -921,10 +934,10 @@ template <class Tag, int BMB>
 static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.total_chunks));
   switch (rbm) {
-    case 1: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((expand_stream_kernel<Tag, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -932,10 +945,10 @@ template <class Tag>
 static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(pieces * a.total_chunks));
   switch (rbm) {
-    case 1: hipLaunchKernelGGL((expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((expand_owner_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((expand_owner_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -1017,7 +1030,7 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   if (gemm_ok && force == 1) {
     p.x_bytes = T * x->stride_row * 2;
     const int64_t pieces = ceil_div(T, kShrinkTokens) + S;
-    hipLaunchKernelGGL(shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
+    hipLaunchKernelGGL(slot_shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
     return launch_status();
   }
   if (x->dtype == LORA_BF16)

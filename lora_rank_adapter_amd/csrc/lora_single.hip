@@ -19,6 +19,14 @@
 //                 second weight W2 and adding into (or overwriting) the
 //                 output with 128-bit accesses. Optionally it also writes s*H
 //                 (transposed, hi/lo planes) for the weight-gradient kernels.
+//   shrink_kernel the same shrink alone, writing s*H as gradient planes and/or
+//                 MFMA fragments for the split expands below.
+//   expand_cols_kernel  column-owner expand (outputs wider than 8192 or long
+//                 feature axes): a workgroup stages its W2 column slice in LDS
+//                 once and walks token tiles.
+//   expand_kernel, shrink_tok_kernel, expand_tok_kernel  further schedules
+//                 (column split; token-split waves with W panels in LDS),
+//                 selectable with LORA_EXPAND_MODE.
 //   tn_kernel     weight-gradient partial sums over a chunk of tokens:
 //                 part[p][n][j] = sum_m Z[m][n] * G[j][m]. Z tiles are staged
 //                 in LDS (XOR-swizzled rows) and read transposed.
@@ -151,9 +159,9 @@ struct FusedArgs {
 
 // ---- shrink of one token tile --------------------------------------------
 // H^T (rank x tokens) = W1 * Z^T over the whole feature axis for the tile's
-// 16*BMB tokens. Wave w takes contraction chunks w, w+NW, ...; U chunks per
-// pipeline stage, two stages in flight; the NW partial sums are reduced
-// through LDS in a fixed order. On return every wave holds s*H (acc) and its
+// 16*BMB tokens. Wave w takes the w-th contiguous range of contraction chunks;
+// U chunks per pipeline stage, two stages in flight; the NW partial sums are
+// reduced through LDS in a fixed order. On return every wave holds s*H (acc) and its
 // MFMA operand form (hf). Rows past M (Z) or past r (W1) lie outside their
 // buffer descriptors and read as zero.
 template <class Tag, int NW, int RB, int BMB, int U>
