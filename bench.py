@@ -341,7 +341,7 @@ def main():
     ws2 = torch.empty(L.lora_workspace_bytes(L.LORA_OP_BWD_DB, M, K, Lc, r, torch.bfloat16), dtype=torch.uint8,
                       device=dev)
 
-    def step(i, ev=None):
+    def step(i, ev=None, fwd_only_events=False):
         s = sets[i % n_sets]
         if ev is not None:
             ev[0].record()
@@ -349,30 +349,37 @@ def main():
         if ev is not None:
             ev[1].record()
         L.lora_bwd_dx_da(s["X"].t(), s["dY"], B_w, A_w, scale, dx=s["dX"], dA=dA, workspace=ws1)
-        if ev is not None:
+        if ev is not None and not fwd_only_events:
             ev[2].record()
         L.lora_bwd_db(A_w, s["X"].t(), s["dY"], scale, dB=dB, workspace=ws2)
-        if ev is not None:
+        if ev is not None and not fwd_only_events:
             ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # timed region: whole steps; events only around the forward (the roofline
+    # kernel's launch), on the stream it runs on (torch's current stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs[i], fwd_only_events=True)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
-    dxda_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
-    db_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+    # per-call split of the backward (informative), from a separate pass
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+    for i in range(10):
+        step(i, evb[i])
+    torch.cuda.synchronize()
+    dxda_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evb)
+    db_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evb)
 
     if args.copy_probe:
         src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)

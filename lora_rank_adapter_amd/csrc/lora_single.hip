@@ -155,6 +155,7 @@ struct FusedArgs {
   int64_t nbs;
   int64_t tiles;
   int rot;
+  int rows_out;  // fused kernel: row-linear output access (expand_tile_rows) or MFMA layout
 };
 
 // ---- shrink of one token tile --------------------------------------------
@@ -369,12 +370,112 @@ __device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int6
   }
 }
 
+// ---- expand with row-linear output access ----------------------------------
+// Same product as expand_tile, but the output is read and written one row
+// segment at a time: each stage's MFMA products (16 columns x 16 tokens per
+// tile, in MFMA layout) go to this wave's LDS tile, and lanes then take 16-byte
+// pieces of whole rows (CW/4 lanes per row of the stage's CW columns), add
+// the output row-linearly (ACCUM) and store it. Row segments of 512 bytes per
+// instruction pair reach HBM as whole lines, which streams markedly faster
+// than the 64-byte-per-row pieces of the MFMA layout when one workgroup owns
+// a token tile's full rows. The LDS tile is private to the wave (LDS
+// instructions of one wave complete in order), so no barrier is needed.
+template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
+__device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0, int64_t rot,
+                                                 const uint4 (&hf)[BMB][RB], float* obuf) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  constexpr int CW = 16 * NBU;        // columns per wave per stage
+  constexpr int LDW = CW + 4;         // LDS row pitch (floats)
+  constexpr int LPR = CW / 4;         // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;       // rows per instruction
+  constexpr int NI = 16 * BMB / RPI;  // row instructions per stage
+  static_assert(64 % LPR == 0 && (16 * BMB) % RPI == 0, "stage shape");
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int lr = lane / LPR;          // row within an instruction
+  const int lc = (lane % LPR) * 4;    // column within the stage
+  const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
+  const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
+  const int64_t nb_end = (p.Nout + 15) / 16;
+  const int64_t gstep = (int64_t)NW * NBU;
+  const int64_t nst = (nb_end + gstep - 1) / gstep;
+  const int64_t r0 = nst > 0 ? rot % nst : 0;
+  auto stage_nb = [&](int64_t k) -> int64_t {  // first column block of this wave in stage k
+    if (k >= nst) return nb_end;
+    const int64_t st = (k + r0 < nst) ? k + r0 : k + r0 - nst;
+    return st * gstep + (int64_t)wave * NBU;
+  };
+  // output offset of this lane's piece in row instruction i of the stage at nb0
+  auto ooff = [&](int i, int64_t nb0) -> uint32_t {
+    const int64_t n = nb0 * 16 + lc;
+    const int row = RPI * i + lr;
+    return (nb0 < nb_end && n < p.Nout) ? static_cast<uint32_t>(((int64_t)row * p.ldo + n) * 4) : kOOB;
+  };
+  auto load2 = [&](wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0) {
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+      const int64_t nb = nb0 + u;
+      const int64_t nrow = (nb < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int j0 = 16 * q + 4 * grp;
+        wv[u][q] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (ACCUM)
+        cv[i] = __builtin_bit_cast(f32x4_t, bload16(ro, ooff(i, nb0)));
+      else
+        cv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto comp2 = [&](const wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0) {
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) {
+        f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < RB; ++q) mma_rank16<Tag>(pr, WF::operand(wv[u][q]), hf[b][q]);
+        // lane holds columns 16u + 4grp .. +3 of token 16b + col
+        *reinterpret_cast<f32x4_t*>(obuf + (16 * b + col) * LDW + 16 * u + 4 * grp) = pr;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(obuf + (RPI * i + lr) * LDW + lc);
+      bstore16(ro, ooff(i, nb0), __builtin_bit_cast(uint4, cv[i] + pr));
+    }
+  };
+  wf_t wvA[NBU][RB], wvB[NBU][RB];
+  f32x4_t cvA[NI], cvB[NI];
+  if (nst > 0) {
+    int64_t k = 0;
+    load2(wvA, cvA, stage_nb(0));
+    for (;;) {
+      load2(wvB, cvB, stage_nb(k + 1));  // reads 0 past the end
+      comp2(wvA, cvA, stage_nb(k));
+      if (++k >= nst) break;
+      load2(wvA, cvA, stage_nb(k + 1));
+      comp2(wvB, cvB, stage_nb(k));
+      if (++k >= nst) break;
+    }
+  }
+}
+
 // Fused shrink -> expand: one workgroup per token tile, the rank intermediate
 // never leaves registers and LDS (optionally also written as planes for the
 // gradient kernels).
-template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G>
+template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G, bool ROWS>
 __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   __shared__ f32x4_t red[NW][BMB * RB][64];
+  __shared__ float obuf[ROWS ? NW : 1][ROWS ? 16 * BMB * (16 * NBU + 4) : 1];
   const int64_t tile = blockIdx.x;
   const int64_t m0 = tile * (16 * BMB);
   f32x4_t acc[BMB][RB];
@@ -383,7 +484,10 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   if constexpr (EMIT_G) {
     if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
-  expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, 0, (p.Nout + 15) / 16, tile * p.rot, hf);
+  if constexpr (ROWS)
+    expand_tile_rows<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, tile * p.rot, hf, obuf[wave_id()]);
+  else
+    expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, 0, (p.Nout + 15) / 16, tile * p.rot, hf);
 }
 
 // Shrink only: s*H of each token tile, written as gradient-kernel planes
@@ -1026,8 +1130,12 @@ struct FusedLaunch {
     // kernels that write planes cover every token row below ldg (zeros past M)
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    hipLaunchKernelGGL((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G>), dim3((unsigned)a.tiles),
-                       dim3(64 * NW), 0, st, a);
+    if (a.rows_out)
+      hipLaunchKernelGGL((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, true>), dim3((unsigned)a.tiles),
+                         dim3(64 * NW), 0, st, a);
+    else
+      hipLaunchKernelGGL((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, false>), dim3((unsigned)a.tiles),
+                         dim3(64 * NW), 0, st, a);
   }
 };
 
@@ -1237,6 +1345,7 @@ static void run_shrink_expand(FusedArgs a, int rb, hipStream_t st) {
   } else {
     a.nsplit = 1;
     a.rot = env_int("LORA_FUSED_ROT", 1);
+    a.rows_out = env_int("LORA_FUSED_ROWS", 1);
     launch_fused<Tag, ACCUM, EMIT_G>(a, rb, pick_bmb_expand("LORA_FUSED_BMB", a.M, rb, 1), st);
   }
 }
