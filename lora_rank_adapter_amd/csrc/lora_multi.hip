@@ -462,7 +462,8 @@ struct ExpandArgs {
   const int32_t* ranks;
   int S, r_max, n_slices, total_chunks;
   int64_t chunk_cols;  // columns per chunk (streaming kernel)
-  int64_t y_bytes;     // bytes of y a descriptor may span (streaming kernel)
+  int64_t y_bytes;     // bytes of y a descriptor may span (streaming and owner kernels)
+  int64_t h_bytes;     // bytes of h a descriptor may span (owner kernel)
   bool h_vec;  // h rows 16-byte aligned
   bool b_vec;  // b rows aligned for 4-element loads
   int64_t slice_off[kMaxSlices];
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
 // with the next stage of output tiles loaded while the current one is
 // multiplied. The weights are read once per piece instead of once per token
 // block.
-constexpr int kOwnerTokens = 256;
+constexpr int kOwnerTokens = 1024;
 constexpr int kOwnerCols = 128;
 
 template <class Tag, int RBM>
@@ -730,10 +731,10 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   constexpr int ES = sizeof(E);
   constexpr int NW = 4;
   constexpr int NCT = kOwnerCols / 16;  // column tiles of the chunk
-  constexpr int NBU = 4;                // column tiles per stage
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
   __shared__ wf_t wls[NCT * RBM * 64];
+  __shared__ float obuf[NW][16 * (NCT * 16 + 4)];
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[kOwnerTokens];
 
@@ -781,63 +782,75 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   const rsrc_t ry = make_rsrc(p.y, p.y_bytes);
   const int nblk = (tl.len + 15) / 16;
 
+  // Row-linear output: a block's 16 rows x 128 columns are read and written
+  // as 512-byte row segments (32 lanes per row, 2 rows per instruction); the
+  // MFMA products reach that layout through the wave's LDS tile.
+  constexpr int LPR = NCT * 16 / 4;  // lanes per row
+  constexpr int RPI = 64 / LPR;      // rows per instruction
+  constexpr int NI = 16 / RPI;       // row instructions per block
+  constexpr int LDW = NCT * 16 + 4;  // LDS row pitch (floats)
+  float* ob = obuf[wave];
+  const int lr = lane / LPR;
+  const int lc = (lane % LPR) * 4;
+  const bool col_ok = c0 + lc < ce;
+  const rsrc_t rh = make_rsrc(p.h, p.h_bytes);
+  struct Blk {
+    f32x4_t cv[NI];   // output rows (row-linear pieces)
+    uint32_t yo[NI];  // their offsets (kOOB when masked)
+  };
+  auto load_blk = [&](Blk& B, int blk) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tix = 16 * blk + RPI * i + lr;
+      const bool ok = blk < nblk && tix < tl.len && col_ok;
+      const int t = sh_tok[ok ? tix : 0];
+      B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * 4) : kOOB;
+      B.cv[i] = __builtin_bit_cast(f32x4_t, bload16(ry, B.yo[i]));
+    }
+  };
   auto walk = [&](auto nq_tag) {
     constexpr int NQ = decltype(nq_tag)::value;
-    for (int blk = wave; blk < nblk; blk += NW) {
-      // an opaque zero keeps the weight reads below inside this loop (read
-      // from LDS per block instead of held in registers across blocks)
+    auto comp_blk = [&](Blk& B, int blk) {
+      if (blk >= nblk) return;
+      // an opaque zero keeps the weight reads below inside the block loop
+      // (read from LDS per block instead of held in registers across blocks)
       int lz;
       asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
       const wf_t* wl = wls + lz;
       const int tix = 16 * blk + col;
       const bool tok_ok = tix < tl.len;
-      const int t = sh_tok[tix < kOwnerTokens ? tix : 0];
-      const uint32_t yrow = static_cast<uint32_t>((int64_t)t * p.ldy * 4 + off * 4);
-      const float* hrow = p.h + (int64_t)t * p.hs0 + (int64_t)slice * p.hs1;
+      const int t = sh_tok[tok_ok ? tix : 0];
+      const uint32_t hbase = static_cast<uint32_t>(((int64_t)t * p.hs0 + (int64_t)slice * p.hs1) * 4);
       uint4 hf[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int j = 16 * q + 4 * grp;
-        if (tok_ok && j < rho) {
-          if (j + 4 <= rho) {
-            v = ld16f(hrow + j);
-          } else {
+        f32x4_t v = __builtin_bit_cast(f32x4_t, bload16(rh, (tok_ok && j < rho) ? hbase + j * 4 : kOOB));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (j + e < rho) v[e] = hrow[j + e];
-          }
-        }
+        for (int e = 0; e < 4; ++e) v[e] = (j + e < rho) ? v[e] : 0.f;  // padding may hold NaN
         v *= sc;
         hf[q] = split_frag<Tag>(v);
       }
-      auto yoff = [&](int n) -> uint32_t { return (tok_ok && n < ce) ? yrow + static_cast<uint32_t>(n) * 4u : kOOB; };
-      f32x4_t cvA[NBU], cvB[NBU];
-      auto load = [&](f32x4_t (&cv)[NBU], int s) {
 #pragma unroll
-        for (int u = 0; u < NBU; ++u)
-          cv[u] = __builtin_bit_cast(f32x4_t, bload16(ry, s * NBU + u < NCT ? yoff(c0 + (s * NBU + u) * 16 + 4 * grp) : kOOB));
-      };
-      auto comp = [&](f32x4_t (&cv)[NBU], int s) {
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NBU; ++u) {
-          const int ct = s * NBU + u;
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u], WF::operand(wl[(ct * RBM + q) * 64 + lane]), hf[q]);
-          bstore16(ry, yoff(c0 + ct * 16 + 4 * grp), __builtin_bit_cast(uint4, cv[u]));
-        }
-      };
-      constexpr int NST = NCT / NBU;
-      load(cvA, 0);
-#pragma unroll
-      for (int s = 0; s < NST; s += 2) {
-        if (s + 1 < NST) load(cvB, s + 1);
-        comp(cvA, s);
-        if (s + 1 < NST) {
-          if (s + 2 < NST) load(cvA, s + 2);
-          comp(cvB, s + 1);
-        }
+        for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(pr, WF::operand(wl[(ct * RBM + q) * 64 + lane]), hf[q]);
+        *reinterpret_cast<f32x4_t*>(ob + col * LDW + ct * 16 + 4 * grp) = pr;
       }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(ob + (RPI * i + lr) * LDW + lc);
+        bstore16(ry, B.yo[i], __builtin_bit_cast(uint4, B.cv[i] + pr));
+      }
+    };
+    Blk A, Bb;
+    load_blk(A, wave);
+    for (int blk = wave; blk < nblk; blk += 2 * NW) {
+      load_blk(Bb, blk + NW);  // masked past the last block
+      comp_blk(A, blk);
+      load_blk(A, blk + 2 * NW);
+      comp_blk(Bb, blk + NW);
     }
   };
   switch (nq) {
@@ -1091,7 +1104,8 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   const int force = env_int("LORA_MULTI_EXPAND", 0);
   const bool stream_ok = force != 3 && p.h_vec && p.b_vec && (T * y->stride_row * 4 <= kMaxBufferBytes) &&
                          (O * b->s1 * (int64_t)es <= kMaxBufferBytes) && y->stride_row < (int64_t(1) << 30);
-  if (stream_ok && (force == 2 || (force == 0 && T >= 2048))) {
+  const bool owner_ok = stream_ok && T * h->s0 * 4 <= kMaxBufferBytes;
+  if (owner_ok && (force == 2 || (force == 0 && T >= 2048))) {
     // many tokens: column owners, weights read once per token piece
     p.chunk_cols = kOwnerCols;
     int64_t off = 0;
@@ -1107,6 +1121,7 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
     p.total_chunks = chunks;
     if (chunks == 0) return LORA_OK;
     p.y_bytes = T * y->stride_row * 4;
+    p.h_bytes = T * h->s0 * 4;
     const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
     if (b->dtype == LORA_BF16)
       launch_expand_owner<BF16>(p, rbm, pieces, st);

@@ -1091,13 +1091,15 @@ static int pick_split(int64_t nout) {
 }
 
 // Forward / dX strategy: fused (rank intermediate only in registers and LDS)
-// or split (shrink kernel writes it as MFMA fragments, column-split expand).
-// The split form lets several workgroups update the rows of one token tile
-// together; it wins when the output rows are long.
+// or split (shrink kernel writes it as MFMA fragments for a separate expand).
 static int pick_schedule(int64_t nout, int64_t kin) {
   const int over = env_int("LORA_EXPAND_MODE", 0);  // 1 fused, 2 column split, 3 column owner, 4 token split
   if (over >= 1 && over <= 4) return over;
-  return (nout > 8192 || kin > 8192) ? 3 : 1;
+  // fused (row-linear output) unless the contraction is long: then the
+  // separate shrink plus column-owner expand measures faster (dX of an
+  // MLP-up layer: contraction over 14336 features)
+  (void)nout;
+  return kin > 8192 ? 3 : 1;
 }
 
 // Token chunks of the weight-gradient kernels: about `wgs` workgroups in all,
