@@ -49,19 +49,18 @@ WORKLOADS = {
 DEFAULT_WORKLOAD = "single-bf16-M8192-K4096-L4096-r16"
 
 # The kernels the roofline entry is about, per workload: what lora_fwd
-# launches at that shape (weights used in place, so no packing launch). At
-# M8192 K4096 L4096 r16 that is the one fused shrink+expand kernel; at the
-# 14336-wide output the call is a shrink launch followed by an expand launch.
+# launches at that shape (weights used in place, so no packing launch): the
+# one fused shrink+expand kernel.
 ROOFLINE_KERNEL = {
     "single-bf16-M8192-K4096-L4096-r16": ["fused_kernel"],
-    "single-bf16-M16384-K4096-L14336-r64": ["shrink_kernel", "expand_kernel"],
+    "single-bf16-M16384-K4096-L14336-r64": ["fused_kernel"],
 }
 # How those launches are told apart from the same templates' backward
 # instances in a profile: the forward ones accumulate into Y (ACCUM = true,
-# EMIT_G = false in fused_kernel / expand_kernel; EMIT_G = false, EMIT_F = true
-# in shrink_kernel).
+# EMIT_G = false in fused_kernel, followed by its output-layout flag, and in
+# expand_kernel; EMIT_G = false, EMIT_F = true in shrink_kernel).
 ROOFLINE_PATTERN = {
-    "fused_kernel": r"\bfused_kernel<.*, true, false>",
+    "fused_kernel": r"\bfused_kernel<.*, true, false, (true|false)>",
     "shrink_kernel": r"\bshrink_kernel<.*, false, true>",
     "expand_kernel": r"\bexpand_kernel<.*, true>",
 }
