@@ -10,9 +10,10 @@ Infinity Cache.
 
 Prints ONE JSON line with the throughput (tokens/s over the whole step), the
 step's algorithmic HBM bandwidth, a roofline entry for the dominant kernel
-(the fused forward: algorithmic bytes / its average duration measured with
-HIP events on its stream), and the CPU oracle's throughput on the same
-workload as a baseline.
+(the fused forward: algorithmic bytes / its average launch duration, from
+HIP events that the kernel's own dispatch stamps on its stream during the
+timed steps; see lora_timing_* in include/lora.h), and the CPU oracle's
+throughput on the same workload as a baseline.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py ... --copy-probe      (adds 1 GiB plain copies after the
@@ -340,43 +341,52 @@ def main():
     ws2 = torch.empty(L.lora_workspace_bytes(L.LORA_OP_BWD_DB, M, K, Lc, r, torch.bfloat16), dtype=torch.uint8,
                       device=dev)
 
-    def step(i, ev=None, fwd_only_events=False):
+    def step(i, ev=None, time_fwd_kernel=False):
         s = sets[i % n_sets]
         if ev is not None:
             ev[0].record()
+        if time_fwd_kernel:
+            L.lora_timing_resume()
         L.lora_fwd(s["X"], A_w.t(), B_w.t(), s["Y"], scale, workspace=ws0)
+        if time_fwd_kernel:
+            L.lora_timing_pause()
         if ev is not None:
             ev[1].record()
         L.lora_bwd_dx_da(s["X"].t(), s["dY"], B_w, A_w, scale, dx=s["dX"], dA=dA, workspace=ws1)
-        if ev is not None and not fwd_only_events:
+        if ev is not None:
             ev[2].record()
         L.lora_bwd_db(A_w, s["X"].t(), s["dY"], scale, dB=dB, workspace=ws2)
-        if ev is not None and not fwd_only_events:
+        if ev is not None:
             ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: whole steps; events only around the forward (the roofline
-    # kernel's launch), on the stream it runs on (torch's current stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: whole steps between two events on torch's current stream
+    # (the stream the library launches on). The forward's kernels are launched
+    # with the library's kernel timing on: HIP events that their dispatch
+    # stamps at kernel start and end (the roofline kernel's launch duration).
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    L.lora_timing_begin()
+    L.lora_timing_pause()
     t_begin.record()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i], fwd_only_events=True)
+        step(args.warmup + i, time_fwd_kernel=True)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
-    # per-call split of the backward (informative), from a separate pass
+    fwd_kernel_total_ms, fwd_launches = L.lora_timing_read()
+    fwd_kernel_ms = fwd_kernel_total_ms / args.steps      # kernel time per lora_fwd call
+    # per-call split (events around each call, informative), from a separate pass
     evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
     for i in range(10):
         step(i, evb[i])
     torch.cuda.synchronize()
+    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evb)
     dxda_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evb)
     db_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evb)
 
@@ -392,6 +402,7 @@ def main():
     step_bytes = ab["fwd"] + ab["dx_da"] + ab["db"]
     step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     fwd_gbs = ab["fwd"] / (fwd_ms * 1e-3) / 1e9
+    fwd_kernel_gbs = ab["fwd"] / (fwd_kernel_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(args.workload)
 
     out = {
@@ -420,11 +431,14 @@ def main():
         "roofline": {
             "kernel": " + ".join(ROOFLINE_KERNEL[args.workload]) + " (lora_fwd)",
             "bound": "hbm",
-            "achieved": fwd_gbs,
+            "achieved": fwd_kernel_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": fwd_gbs / HBM_PEAK_GBS,
+            "frac": fwd_kernel_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
+            "kernel_us": fwd_kernel_ms * 1e3,
+            "launches_per_call": fwd_launches / args.steps,
+            "algorithmic_bytes": ab["fwd"],
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(case),
     }

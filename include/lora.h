@@ -113,6 +113,29 @@ enum { LORA_OP_FWD = 0, LORA_OP_BWD_DX_DA = 1, LORA_OP_BWD_DB = 2 };
 /* ABI version (LORA_ABI_VERSION) of the loaded library. */
 int lora_abi_version(void);
 
+/*
+ * Kernel timing, for measurement tools (not one of the LoRA operations).
+ * While recording, every kernel the library launches is dispatched with
+ * hipExtLaunchKernel and a pair of HIP events that the dispatch stamps at the
+ * kernel's start and end, so a duration covers the kernel alone, without the
+ * command-processor latency that event records around a call add.
+ *   lora_timing_begin   forgets earlier records and starts recording.
+ *   lora_timing_pause   stops recording (launches run untimed);
+ *   lora_timing_resume  starts it again, keeping the records.
+ *   lora_timing_read    waits for every recorded kernel to finish and returns
+ *                       the sum of their durations (ms) and their number;
+ *                       -1 for NULL outputs, -7 if an event query fails.
+ * The state is process-wide: launches from any thread or stream while
+ * recording are included. Events are created (once, then reused) on the
+ * device current at the first timed launch, so one recording session must
+ * time launches on one device. Records stay valid until the next
+ * lora_timing_begin.
+ */
+int lora_timing_begin(void);
+int lora_timing_pause(void);
+int lora_timing_resume(void);
+int lora_timing_read(double* total_ms, int64_t* launches);
+
 /* Static text for a status code. */
 const char* lora_status_string(int status);
 

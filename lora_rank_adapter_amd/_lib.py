@@ -90,6 +90,10 @@ SIGNATURES = {
                                          ctypes.c_int32, ctypes.c_void_p]),
     "lora_gather_shrink": (ctypes.c_int, [ctypes.c_void_p, _P(LoraT3), _P(LoraAddressing), ctypes.c_void_p,
                                           ctypes.c_int32, _P(LoraT3), ctypes.c_void_p]),
+    "lora_timing_begin": (ctypes.c_int, []),
+    "lora_timing_pause": (ctypes.c_int, []),
+    "lora_timing_resume": (ctypes.c_int, []),
+    "lora_timing_read": (ctypes.c_int, [_P(ctypes.c_double), _P(ctypes.c_int64)]),
 }
 
 _lock = threading.Lock()

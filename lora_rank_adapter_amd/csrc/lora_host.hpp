@@ -2,6 +2,7 @@
 // before any launch), sizes, workspace carving and launch-error mapping.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -67,6 +68,22 @@ struct Carver {
 inline int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH;
+}
+
+// Kernel timing for measurement tools (lora_timing_* entry points): true,
+// with a pair of events, when the next launch is to be timed.
+bool timing_take(hipEvent_t* start, hipEvent_t* stop);
+
+// Launches a kernel. While kernel timing records, the launch goes through
+// hipExtLaunchKernel with a pair of events that the dispatch itself stamps
+// at the kernel's start and end (no marker packets around it).
+template <class... P, class... A>
+inline void launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, A... args) {
+  hipEvent_t e0, e1;
+  if (timing_take(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0u, args...);
+  else
+    kernel<<<grid, block, shmem, st>>>(args...);
 }
 
 // Optional tile overrides for tuning sweeps (unset in normal use).

@@ -920,24 +920,24 @@ static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, h
   const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
   if (bmb == 4) {
     if (rb == 4)
-      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
+      launch((slot_shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 4, 1>), grid, dim3(256), 0, st, a);
+      launch((slot_shrink_kernel<Tag, 4, 1>), grid, dim3(256), 0, st, a);
   } else {
     if (rb == 4)
-      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
+      launch((slot_shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((slot_shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
+      launch((slot_shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
   }
 }
 
 template <class Tag, int BMB>
 static void launch_expand_b(const ExpandArgs& a, int rbm, dim3 grid, hipStream_t st) {
   switch (rbm) {
-    case 1: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((slot_expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_kernel<Tag, BMB, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -947,10 +947,10 @@ template <class Tag, int BMB>
 static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.total_chunks));
   switch (rbm) {
-    case 1: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((slot_expand_stream_kernel<Tag, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_stream_kernel<Tag, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_stream_kernel<Tag, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_stream_kernel<Tag, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_stream_kernel<Tag, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -958,10 +958,10 @@ template <class Tag>
 static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(pieces * a.total_chunks));
   switch (rbm) {
-    case 1: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((slot_expand_owner_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_owner_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_owner_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -984,7 +984,7 @@ extern "C" int lora_addressing_build(const lora_addressing* addr, const int32_t*
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
   if (addr->S > 0 && !addr->counts) return LORA_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, st, addr->token_slot, addr->T, addr->S, ranks, r_max,
+  launch(group_kernel, dim3(1), dim3(1024), 0, st, addr->token_slot, addr->T, addr->S, ranks, r_max,
                      addr->counts, addr->offsets, addr->sorted_tokens);
   return launch_status();
 }
@@ -1043,7 +1043,7 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   if (gemm_ok && force == 1) {
     p.x_bytes = T * x->stride_row * 2;
     const int64_t pieces = ceil_div(T, kShrinkTokens) + S;
-    hipLaunchKernelGGL(slot_shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
+    launch(slot_shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
     return launch_status();
   }
   if (x->dtype == LORA_BF16)
@@ -1193,11 +1193,11 @@ extern "C" int lora_gather_shrink(const int32_t* ids, const lora_t3* a, const lo
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(ceil_div(T, 4)));
   if (a->dtype == LORA_BF16)
-    hipLaunchKernelGGL(gather_kernel<uint16_t>, grid, dim3(256), 0, st, ids, static_cast<const uint16_t*>(a->ptr),
+    launch(gather_kernel<uint16_t>, grid, dim3(256), 0, st, ids, static_cast<const uint16_t*>(a->ptr),
                        a->s0, a->s1, a->s2, V, addr->token_slot, ranks, static_cast<int>(T), static_cast<int>(S),
                        r_max, static_cast<float*>(h->ptr), h->s0);
   else
-    hipLaunchKernelGGL(gather_kernel<float>, grid, dim3(256), 0, st, ids, static_cast<const float*>(a->ptr), a->s0,
+    launch(gather_kernel<float>, grid, dim3(256), 0, st, ids, static_cast<const float*>(a->ptr), a->s0,
                        a->s1, a->s2, V, addr->token_slot, ranks, static_cast<int>(T), static_cast<int>(S), r_max,
                        static_cast<float*>(h->ptr), h->s0);
   return launch_status();

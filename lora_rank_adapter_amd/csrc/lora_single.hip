@@ -33,6 +33,10 @@
 //   reduce_kernel fixed-order sum of the partials into the strided output.
 //   pack_kernel   lays a small weight out in the orientation a kernel needs.
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include "lora_device.hpp"
 #include "lora_host.hpp"
 
@@ -1133,10 +1137,10 @@ struct FusedLaunch {
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
     if (a.rows_out)
-      hipLaunchKernelGGL((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, true>), dim3((unsigned)a.tiles),
+      launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, true>), dim3((unsigned)a.tiles),
                          dim3(64 * NW), 0, st, a);
     else
-      hipLaunchKernelGGL((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, false>), dim3((unsigned)a.tiles),
+      launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, false>), dim3((unsigned)a.tiles),
                          dim3(64 * NW), 0, st, a);
   }
 };
@@ -1147,7 +1151,7 @@ struct ShrinkLaunch {
     using S = FusedShape<RB, BMB>;
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    hipLaunchKernelGGL((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F>), dim3((unsigned)a.tiles),
+    launch((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F>), dim3((unsigned)a.tiles),
                        dim3(64 * NW), 0, st, a);
   }
 };
@@ -1161,7 +1165,7 @@ struct ExpandLaunch {
     a.nbs = round_up(ceil_div(nnb, a.nsplit), (int64_t)NW * S::NBU);  // whole workgroup stages
     a.nsplit = static_cast<int>(ceil_div(nnb, a.nbs));
     const dim3 grid(static_cast<unsigned>(round_up(a.tiles, 8) * a.nsplit));
-    hipLaunchKernelGGL((expand_kernel<Tag, NW, RB, BMB, S::NBU, ACCUM>), grid, dim3(64 * NW), 0, st, a);
+    launch((expand_kernel<Tag, NW, RB, BMB, S::NBU, ACCUM>), grid, dim3(64 * NW), 0, st, a);
   }
 };
 
@@ -1180,7 +1184,7 @@ struct ExpandColsLaunch {
     if (groups <= 0) groups = ceil_div(512, cols) > 64 ? ceil_div(512, cols) : 64;
     if (groups > a.tiles) groups = a.tiles;
     if (groups < 1) groups = 1;
-    hipLaunchKernelGGL((expand_cols_kernel<Tag, NW, RB, BMB, NBU, ACCUM>),
+    launch((expand_cols_kernel<Tag, NW, RB, BMB, NBU, ACCUM>),
                        dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st, a);
   }
 };
@@ -1196,10 +1200,10 @@ static void launch_shrink_tok(FusedArgs a, int rb, hipStream_t st) {
   const dim3 block(64 * NW);
   // two panel buffers of KP features x 16*RB ranks: <= 64 KB of LDS (bf16)
   switch (rb) {
-    case 1: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 1, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 2, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 4, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((shrink_tok_kernel<Tag, NW, 8, 4 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    case 1: launch((shrink_tok_kernel<Tag, NW, 1, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    case 2: launch((shrink_tok_kernel<Tag, NW, 2, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    case 4: launch((shrink_tok_kernel<Tag, NW, 4, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
+    default: launch((shrink_tok_kernel<Tag, NW, 8, 4 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
   }
 }
 
@@ -1217,7 +1221,7 @@ static void launch_expand_tok(FusedArgs a, int rb, hipStream_t st) {
     if (groups <= 0) groups = ceil_div(512, cols);
     if (groups > ntile) groups = ntile;
     if (groups < 1) groups = 1;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st,
+    launch(kern, dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st,
                        a);
   };
   const int nbs_env = env_int("LORA_TOK_NBS", 0);
@@ -1356,10 +1360,10 @@ template <class Tag>
 static void launch_tn(const TnArgs& a, int rb, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(ceil_div(a.N, kTnCols)), static_cast<unsigned>(ceil_div(a.M, a.chunk)));
   switch (rb) {
-    case 1: hipLaunchKernelGGL((tn_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((tn_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((tn_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((tn_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((tn_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((tn_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((tn_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
+    default: launch((tn_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -1378,9 +1382,9 @@ static void launch_pack(int32_t dtype, const PackJob& j0, const PackJob* j1, hip
   const int64_t blocks = a.job[0].tiles + a.job[1].tiles;
   if (blocks <= 0) return;
   if (dtype == LORA_BF16)
-    hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
+    launch(pack_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(pack_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
+    launch(pack_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
 }
 
 static void launch_fill_zero(const lora_mat* m, hipStream_t st) {
@@ -1388,7 +1392,7 @@ static void launch_fill_zero(const lora_mat* m, hipStream_t st) {
   if (total <= 0) return;
   int64_t blocks = ceil_div(total, 256);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+  launch(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                      static_cast<float*>(m->ptr), m->rows, m->cols, m->stride_row, m->stride_col);
 }
 
@@ -1396,7 +1400,7 @@ static void launch_reduce(const float* part, int P, int64_t N, int rp, int r, fl
                           hipStream_t st) {
   const int64_t total = N * r;
   if (total <= 0) return;
-  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(ceil_div(total, 256))), dim3(256), 0, st, part, P, N,
+  launch(reduce_kernel, dim3(static_cast<unsigned>(ceil_div(total, 256))), dim3(256), 0, st, part, P, N,
                      rp, r, out, os_n, os_j);
 }
 
@@ -1451,11 +1455,77 @@ static SingleLayout layout_for(int op, int64_t M, int64_t K, int64_t L, int r, i
   return s;
 }
 
+// ---------------------------------------------------------------------------
+// kernel timing (measurement tools)
+// ---------------------------------------------------------------------------
+
+namespace {
+struct EventPair {
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+std::atomic<bool> g_timing_on{false};
+std::vector<EventPair> g_timing_events;  // reused across recording sessions
+size_t g_timing_used = 0;                // pairs handed out since lora_timing_begin
+}  // namespace
+
+bool timing_take(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_timing_on.load(std::memory_order_relaxed)) return false;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (!g_timing_on.load(std::memory_order_relaxed)) return false;
+  if (g_timing_used == g_timing_events.size()) {
+    EventPair e{};
+    if (hipEventCreate(&e.start) != hipSuccess) return false;
+    if (hipEventCreate(&e.stop) != hipSuccess) {
+      (void)hipEventDestroy(e.start);
+      return false;
+    }
+    g_timing_events.push_back(e);
+  }
+  *start = g_timing_events[g_timing_used].start;
+  *stop = g_timing_events[g_timing_used].stop;
+  ++g_timing_used;
+  return true;
+}
+
 }  // namespace lora
 
 using namespace lora;
 
 extern "C" int lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+extern "C" int lora_timing_begin(void) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  g_timing_used = 0;
+  g_timing_on.store(true);
+  return LORA_OK;
+}
+
+extern "C" int lora_timing_pause(void) {
+  g_timing_on.store(false);
+  return LORA_OK;
+}
+
+extern "C" int lora_timing_resume(void) {
+  g_timing_on.store(true);
+  return LORA_OK;
+}
+
+extern "C" int lora_timing_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return LORA_ERR_NULL;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  double sum = 0.0;
+  for (size_t i = 0; i < g_timing_used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timing_events[i].stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timing_events[i].start, g_timing_events[i].stop) != hipSuccess)
+      return LORA_ERR_LAUNCH;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = static_cast<int64_t>(g_timing_used);
+  return LORA_OK;
+}
 
 extern "C" const char* lora_status_string(int status) {
   switch (status) {

@@ -174,3 +174,26 @@ def lora_gather_shrink(ids: torch.Tensor, a: torch.Tensor, addr: Addressing, ran
                                                        _ptr(ranks), int(r_max), ctypes.byref(t3(h)),
                                                        _stream(ids.device)))
     return h
+
+
+def lora_timing_begin() -> None:
+    """Start recording kernel durations (forgets earlier records)."""
+    check("lora_timing_begin", _lib.load().lora_timing_begin())
+
+
+def lora_timing_pause() -> None:
+    """Stop recording; later launches run untimed."""
+    check("lora_timing_pause", _lib.load().lora_timing_pause())
+
+
+def lora_timing_resume() -> None:
+    """Record again, keeping the earlier records."""
+    check("lora_timing_resume", _lib.load().lora_timing_resume())
+
+
+def lora_timing_read() -> tuple[float, int]:
+    """Waits for the recorded kernels; returns (sum of their durations in ms, number of launches)."""
+    total = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    check("lora_timing_read", _lib.load().lora_timing_read(ctypes.byref(total), ctypes.byref(n)))
+    return total.value, n.value

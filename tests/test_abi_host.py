@@ -49,6 +49,19 @@ def test_version_and_status_strings(lib):
     assert b"workspace" in lib.lora_status_string(-6)
 
 
+def test_timing_calls_without_launches(lib):
+    assert lib.lora_timing_begin() == 0
+    assert lib.lora_timing_pause() == 0
+    assert lib.lora_timing_resume() == 0
+    total = ctypes.c_double(-1.0)
+    n = ctypes.c_int64(-1)
+    assert lib.lora_timing_read(ctypes.byref(total), ctypes.byref(n)) == 0
+    assert (total.value, n.value) == (0.0, 0)
+    assert lib.lora_timing_read(None, ctypes.byref(n)) == -1
+    assert lib.lora_timing_read(ctypes.byref(total), None) == -1
+    assert lib.lora_timing_pause() == 0
+
+
 def test_workspace_bytes(lib):
     f = lib.lora_workspace_bytes
     assert f(1, 8192, 4096, 4096, 16, 1) > 0

@@ -141,6 +141,37 @@ def test_deterministic_reruns():
         assert same_bits(a, b)
 
 
+def test_kernel_timing_records_each_launch():
+    """Timed launches (hipExtLaunchKernel with events) give the same bits as
+    untimed ones, one record per kernel; pausing stops the records."""
+    note("kernel timing")
+    c = synth.single_adapter(600, 1024, 768, 16, seed=61, dtype="bf16", scale=2.0, y0="normal")
+    X, A_w, B_w, dY = _upload(c, "bf16")
+    y_plain = f32(c.Y0)
+    L.lora_fwd(X, A_w.t(), B_w.t(), y_plain, 2.0)
+    dx_plain, dA_plain = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, 2.0)
+    torch.cuda.synchronize()
+    y_timed = f32(c.Y0)
+    torch.cuda.synchronize()
+    L.lora_timing_begin()
+    L.lora_fwd(X, A_w.t(), B_w.t(), y_timed, 2.0)
+    L.lora_timing_pause()
+    ms_fwd, n_fwd = L.lora_timing_read()
+    assert n_fwd == 1 and 0.0 < ms_fwd < 1000.0
+    L.lora_timing_resume()
+    dx_t, dA_t = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, 2.0)
+    L.lora_timing_pause()
+    L.lora_fwd(X, A_w.t(), B_w.t(), f32(c.Y0), 2.0)   # untimed
+    ms_all, n_all = L.lora_timing_read()
+    assert n_all >= 3 and ms_all > ms_fwd               # dx/dA take at least two kernels
+    assert same_bits(host(y_timed), host(y_plain))
+    assert same_bits(host(dx_t), host(dx_plain))
+    assert same_bits(host(dA_t), host(dA_plain))
+    L.lora_timing_begin()
+    L.lora_timing_pause()
+    assert L.lora_timing_read() == (0.0, 0)
+
+
 def test_empty_and_degenerate():
     note("empty")
     dv = torch.device("cuda:0")
