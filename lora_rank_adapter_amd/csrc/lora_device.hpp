@@ -40,6 +40,18 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* lds, int off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
 }
 
+// A wave-uniform value below 2^31 as a scalar-register int.
+__device__ __forceinline__ int uniform_int(int64_t v) {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(v));
+}
+
+// Keeps the instruction scheduler from moving instructions across this
+// point. Software-pipelined loops put one between issuing the next stage's
+// loads and computing on the current stage, so that the loads stay in flight
+// during the computation (the wait before it then covers only the current
+// stage).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value: loops bounded by it compile to scalar branches, so the compiler can
 // keep loads in flight across iterations instead of draining at each

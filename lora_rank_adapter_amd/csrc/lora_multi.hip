@@ -686,16 +686,19 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
     };
     wf_t wvA[NBU][NQ], wvB[NBU][NQ];
     f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
+    // two stages in flight; a stage past the last loads nothing and its
+    // columns (>= ce) store nothing, so the loop body has no exit in the middle
     if (nst > 0) {
-      int k = 0;
       load2(wvA, cvA, 0);
-      for (;;) {
-        load2(wvB, cvB, k + 1);  // masked past the last stage
+      for (int k = 0; k < nst; k += 2) {
+        load2(wvB, cvB, k + 1);
+        sched_fence();
         comp2(wvA, cvA, k);
-        if (++k >= nst) break;
-        load2(wvA, cvA, k + 1);
-        comp2(wvB, cvB, k);
-        if (++k >= nst) break;
+        sched_fence();
+        load2(wvA, cvA, k + 2);
+        sched_fence();
+        comp2(wvB, cvB, k + 1);
+        sched_fence();
       }
     }
   };
@@ -810,8 +813,9 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   };
   auto walk = [&](auto nq_tag) {
     constexpr int NQ = decltype(nq_tag)::value;
+    // a block past the last loads nothing and stores nothing (every offset
+    // is masked), so it needs no branch around it
     auto comp_blk = [&](Blk& B, int blk) {
-      if (blk >= nblk) return;
       // an opaque zero keeps the weight reads below inside the block loop
       // (read from LDS per block instead of held in registers across blocks)
       int lz;
@@ -848,9 +852,13 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
     load_blk(A, wave);
     for (int blk = wave; blk < nblk; blk += 2 * NW) {
       load_blk(Bb, blk + NW);  // masked past the last block
+      sched_fence();
       comp_blk(A, blk);
+      sched_fence();
       load_blk(A, blk + 2 * NW);
+      sched_fence();
       comp_blk(Bb, blk + NW);
+      sched_fence();
     }
   };
   switch (nq) {

@@ -223,19 +223,22 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
         for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], wf[u][q], zf[u][b]);
   };
   {
+    // Two register stages of U chunks: the loads of the next stage are in
+    // flight while the current one is multiplied. The loop body has no exit in
+    // the middle: with an odd stage count the last pass multiplies a stage
+    // of zeros (every load past this wave's range reads 0).
     uint4 zA[U][BMB], wA[U][RB], zB[U][BMB], wB[U][RB];
-    int64_t c = cbeg;
-    if (c < cend) {
-      load1(zA, wA, c);
-      for (;;) {
-        load1(zB, wB, c + cstep);  // reads 0 past the end
+    if (cbeg < cend) {
+      load1(zA, wA, cbeg);
+      for (int64_t c = cbeg; c < cend; c += 2 * cstep) {
+        load1(zB, wB, c + cstep);
+        sched_fence();
         mma1(zA, wA);
-        c += cstep;
-        if (c >= cend) break;
-        load1(zA, wA, c + cstep);
+        sched_fence();
+        load1(zA, wA, c + 2 * cstep);
+        sched_fence();
         mma1(zB, wB);
-        c += cstep;
-        if (c >= cend) break;
+        sched_fence();
       }
     }
   }
@@ -312,17 +315,17 @@ __device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int6
   const int grp = lane >> 4;
   const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
   const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
-  const int64_t gstep = (int64_t)NW * NBU;
-  const int64_t nst = (nb_end - nb_begin + gstep - 1) / gstep;
-  const int64_t r0 = nst > 0 ? rot % nst : 0;
+  constexpr int gstep = NW * NBU;
+  const int nst = uniform_int((nb_end - nb_begin + gstep - 1) / gstep);
+  const int r0 = nst > 0 ? uniform_int(rot % nst) : 0;
   uint32_t orow[BMB];
 #pragma unroll
   for (int b = 0; b < BMB; ++b) orow[b] = static_cast<uint32_t>((16 * b + col) * p.ldo * 4);
   // first column block of this wave in stage k (nb_end when k is past the end)
-  auto stage_nb = [&](int64_t k) -> int64_t {
-    if (k >= nst) return nb_end;
-    const int64_t st = (k + r0 < nst) ? k + r0 : k + r0 - nst;
-    return nb_begin + st * gstep + (int64_t)wave * NBU;
+  auto stage_nb = [&](int k) -> int64_t {
+    const int kk = k + r0;
+    const int64_t v = nb_begin + (kk - (kk >= nst ? nst : 0)) * gstep + wave * NBU;
+    return k < nst ? v : nb_end;
   };
   auto ooff = [&](int b, int64_t nb) -> uint32_t {
     const int64_t ncol = nb * 16 + 4 * grp;
@@ -358,18 +361,22 @@ __device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int6
       }
     }
   };
+  // two stages in flight; stages past the end read zeros and store nothing,
+  // so the loop body needs no exit in the middle (an odd stage count ends
+  // with one such stage)
   wf_t wvA[NBU][RB], wvB[NBU][RB];
   f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
   if (nst > 0) {
-    int64_t k = 0;
     load2(wvA, cvA, stage_nb(0));
-    for (;;) {
-      load2(wvB, cvB, stage_nb(k + 1));  // reads 0 past the end
+    for (int k = 0; k < nst; k += 2) {
+      load2(wvB, cvB, stage_nb(k + 1));
+      sched_fence();
       comp2(wvA, cvA, stage_nb(k));
-      if (++k >= nst) break;
-      load2(wvA, cvA, stage_nb(k + 1));
-      comp2(wvB, cvB, stage_nb(k));
-      if (++k >= nst) break;
+      sched_fence();
+      load2(wvA, cvA, stage_nb(k + 2));
+      sched_fence();
+      comp2(wvB, cvB, stage_nb(k + 1));
+      sched_fence();
     }
   }
 }
@@ -406,13 +413,15 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
   const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
   const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
   const int64_t nb_end = (p.Nout + 15) / 16;
-  const int64_t gstep = (int64_t)NW * NBU;
-  const int64_t nst = (nb_end + gstep - 1) / gstep;
-  const int64_t r0 = nst > 0 ? rot % nst : 0;
-  auto stage_nb = [&](int64_t k) -> int64_t {  // first column block of this wave in stage k
-    if (k >= nst) return nb_end;
-    const int64_t st = (k + r0 < nst) ? k + r0 : k + r0 - nst;
-    return st * gstep + (int64_t)wave * NBU;
+  constexpr int gstep = NW * NBU;
+  // stage bookkeeping in scalar registers (a 64-bit division would leave it
+  // in vector registers and turn the selects below into branches)
+  const int nst = uniform_int((nb_end + gstep - 1) / gstep);
+  const int r0 = nst > 0 ? uniform_int(rot % nst) : 0;
+  auto stage_nb = [&](int k) -> int64_t {  // first column block of this wave in stage k
+    const int kk = k + r0;
+    const int v = (kk - (kk >= nst ? nst : 0)) * gstep + wave * NBU;
+    return k < nst ? v : nb_end;
   };
   // output offset of this lane's piece in row instruction i of the stage at nb0
   auto ooff = [&](int i, int64_t nb0) -> uint32_t {
@@ -457,18 +466,20 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
       bstore16(ro, ooff(i, nb0), __builtin_bit_cast(uint4, cv[i] + pr));
     }
   };
+  // two stages in flight; stages past the end read zeros and store nothing
   wf_t wvA[NBU][RB], wvB[NBU][RB];
   f32x4_t cvA[NI], cvB[NI];
   if (nst > 0) {
-    int64_t k = 0;
     load2(wvA, cvA, stage_nb(0));
-    for (;;) {
-      load2(wvB, cvB, stage_nb(k + 1));  // reads 0 past the end
+    for (int k = 0; k < nst; k += 2) {
+      load2(wvB, cvB, stage_nb(k + 1));
+      sched_fence();
       comp2(wvA, cvA, stage_nb(k));
-      if (++k >= nst) break;
-      load2(wvA, cvA, stage_nb(k + 1));
-      comp2(wvB, cvB, stage_nb(k));
-      if (++k >= nst) break;
+      sched_fence();
+      load2(wvA, cvA, stage_nb(k + 2));
+      sched_fence();
+      comp2(wvB, cvB, stage_nb(k + 1));
+      sched_fence();
     }
   }
 }
@@ -636,18 +647,19 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
   };
   uint4 hfA[BMB][RB], hfB[BMB][RB];
   f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
-  int64_t t = blockIdx.y;
-  if (t < p.tiles) {
-    load_tile(hfA, cvA, t);
-    for (;;) {
-      load_tile(hfB, cvB, t + gstride);  // reads 0 past the last tile
+  // two tiles in flight; a tile past the last reads zeros and stores nothing
+  // (empty output descriptor), so the loop body has no exit in the middle
+  if (blockIdx.y < p.tiles) {
+    load_tile(hfA, cvA, blockIdx.y);
+    for (int64_t t = blockIdx.y; t < p.tiles; t += 2 * gstride) {
+      load_tile(hfB, cvB, t + gstride);
+      sched_fence();
       comp_tile(hfA, cvA, t);
-      t += gstride;
-      if (t >= p.tiles) break;
-      load_tile(hfA, cvA, t + gstride);
-      comp_tile(hfB, cvB, t);
-      t += gstride;
-      if (t >= p.tiles) break;
+      sched_fence();
+      load_tile(hfA, cvA, t + 2 * gstride);
+      sched_fence();
+      comp_tile(hfB, cvB, t + gstride);
+      sched_fence();
     }
   }
 }
@@ -833,18 +845,18 @@ __global__ __launch_bounds__(64 * NW) void expand_tok_kernel(FusedArgs p) {
   };
   uint4 hfA[RB], hfB[RB];
   f32x4_t cvA[NBS], cvB[NBS];
-  int64_t t = blockIdx.y;
-  if (t < ntile) {
-    load_tile(hfA, cvA, t);
-    for (;;) {
-      load_tile(hfB, cvB, t + gstride);  // reads 0 past the last tile
+  // two tiles in flight; a tile past the last reads zeros and stores nothing
+  if (blockIdx.y < ntile) {
+    load_tile(hfA, cvA, blockIdx.y);
+    for (int64_t t = blockIdx.y; t < ntile; t += 2 * gstride) {
+      load_tile(hfB, cvB, t + gstride);
+      sched_fence();
       comp_tile(hfA, cvA, t);
-      t += gstride;
-      if (t >= ntile) break;
-      load_tile(hfA, cvA, t + gstride);
-      comp_tile(hfB, cvB, t);
-      t += gstride;
-      if (t >= ntile) break;
+      sched_fence();
+      load_tile(hfA, cvA, t + 2 * gstride);
+      sched_fence();
+      comp_tile(hfB, cvB, t + gstride);
+      sched_fence();
     }
   }
 }
@@ -967,7 +979,11 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
     __syncthreads();
     store_stage();
     __syncthreads();
-    if (s + 1 < nstage) load_stage(m_begin + (s + 1) * TS);
+    // the next stage's loads stay in flight during this stage's products;
+    // past the last stage they read zeros (Z rows past the chunk) and are
+    // never stored
+    load_stage(m_begin + (s + 1) * TS);
+    sched_fence();
 
     if constexpr (ES == 2) {
 #pragma unroll
