@@ -16,6 +16,8 @@
 // Kernels:
 //   group_kernel               stable counting sort (one 1024-thread workgroup)
 //   slot_shrink_kernel         shrink, one workgroup per (tile, slice, rank chunk)
+//   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
+//                              descriptor loads and two register stages
 //   slot_shrink_gemm_kernel    shrink with the adapter chunk staged in LDS and
 //                              shared by 8 token blocks (selectable)
 //   slot_expand_owner_kernel   expand for many tokens: a token piece x column
@@ -303,6 +305,150 @@ __global__ __launch_bounds__(256) void slot_shrink_kernel(ShrinkArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (j + e < rho) hrow[j + e] = s[e];
+      }
+    }
+  }
+}
+
+// Pipelined form of slot_shrink_kernel (same grid and reduction): every wave
+// contracts one contiguous range of the feature axis, the loads go through
+// buffer descriptors (masked lanes use kOOB, no branches), and U chunks of the
+// next stage are in flight while the current stage is multiplied. Needs x and
+// one slot's adapter rows within 2 GiB descriptors (the host checks).
+template <class Tag, int BMB, int RB, int U>
+__global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
+  using E = typename Tag::elem;
+  constexpr int VEC = Tag::VEC;
+  constexpr int ES = sizeof(E);
+  constexpr int CH = 4 * VEC;  // features per MFMA step
+  constexpr int TB = 16 * BMB;
+  __shared__ f32x4_t red[4][BMB * RB][64];
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The per_tile
+  // workgroups of one token tile (its slices and rank chunks) all get ids
+  // with the same residue, so they run on one XCD and re-read the tile's
+  // x rows from that XCD's L2. The grid is padded to a multiple of 8 tiles;
+  // tile numbers past the last tile find no slot and exit.
+  const int per_tile = p.n_slices * p.row_chunks;
+  const int kx = static_cast<int>(blockIdx.x >> 3);
+  const int ti = (kx / per_tile) * 8 + static_cast<int>(blockIdx.x & 7);
+  const int rem = kx % per_tile;
+  const int slice = rem / p.row_chunks;
+  const int j0 = (rem - slice * p.row_chunks) * 16 * RB;
+
+  if (wave == 0) {
+    const Tile tl = find_tile(ti, TB, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  if (j0 >= rho) return;
+  if (threadIdx.x < TB) sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
+  __syncthreads();
+
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+  const rsrc_t ra = make_rsrc(static_cast<const E*>(p.a) + (int64_t)tl.slot * p.as0,
+                              (int64_t)p.n_slices * p.r_max * p.as1 * ES);
+  uint32_t xoff[BMB];
+  bool bany[BMB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) {
+    const bool ok = 16 * b + col < tl.len;
+    xoff[b] = ok ? static_cast<uint32_t>(((int64_t)sh_tok[16 * b + col] * p.ldx + grp * VEC) * ES) : kOOB;
+    bany[b] = 16 * b < tl.len;
+  }
+  uint32_t aoff[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) {
+    const int j = j0 + 16 * q + col;
+    aoff[q] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + grp * VEC) * ES) : kOOB;
+  }
+
+  f32x4_t acc[BMB][RB];
+#pragma unroll
+  for (int b = 0; b < BMB; ++b)
+#pragma unroll
+    for (int q = 0; q < RB; ++q) acc[b][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = static_cast<int>((p.K + CH - 1) / CH);
+  const int per = (nch + 3) / 4;
+  const int cbeg = wave * per;
+  const int cend = (cbeg + per < nch) ? cbeg + per : nch;
+  const int K = static_cast<int>(p.K);
+  auto load = [&](uint4 (&xf)[U][BMB], uint4 (&af)[U][RB], int c) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cc = c + u;
+      const bool kok = cc < cend && cc * CH + grp * VEC < K;
+      const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);  // < x row bytes when kok
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) xf[u][b] = bload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
+#pragma unroll
+      for (int q = 0; q < RB; ++q) af[u][q] = bload16(ra, (kok && aoff[q] != kOOB) ? aoff[q] + kb : kOOB);
+    }
+  };
+  auto mma = [&](const uint4 (&xf)[U][BMB], const uint4 (&af)[U][RB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < BMB; ++b)
+        if (bany[b]) {
+#pragma unroll
+          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], af[u][q], xf[u][b]);
+        }
+  };
+  // two register stages; the loop body has no exit in the middle (an odd
+  // stage count ends with a stage of zeros)
+  {
+    uint4 xA[U][BMB], aA[U][RB], xB[U][BMB], aB[U][RB];
+    if (cbeg < cend) {
+      load(xA, aA, cbeg);
+      for (int c = cbeg; c < cend; c += 2 * U) {
+        load(xB, aB, c + U);
+        sched_fence();
+        mma(xA, aA);
+        sched_fence();
+        load(xA, aA, c + 2 * U);
+        sched_fence();
+        mma(xB, aB);
+        sched_fence();
+      }
+    }
+  }
+
+#pragma unroll
+  for (int b = 0; b < BMB; ++b)
+#pragma unroll
+    for (int q = 0; q < RB; ++q) red[wave][b * RB + q][lane] = acc[b][q];
+  __syncthreads();
+  // wave w stores token blocks w, w+4, ...
+#pragma unroll
+  for (int b = 0; b < BMB; ++b) {
+    if ((b & 3) != wave) continue;
+    if (16 * b + col >= tl.len) continue;
+    float* hrow = p.h + (int64_t)sh_tok[16 * b + col] * p.hs0 + (int64_t)slice * p.hs1;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int i = b * RB + q;
+      f32x4_t sum = red[0][i][lane];
+      sum += red[1][i][lane];
+      sum += red[2][i][lane];
+      sum += red[3][i][lane];
+      const int j = j0 + 16 * q + 4 * grp;
+      if (p.h_vec && j + 4 <= rho) {
+        st16f(hrow + j, sum);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < rho) hrow[j + e] = sum[e];
       }
     }
   }
@@ -924,8 +1070,23 @@ static int check_addressing(const lora_addressing* addr, const int32_t* ranks) {
 static int tile_bmb(int T) { return T >= 1024 ? 4 : 1; }
 
 template <class Tag>
-static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, hipStream_t st) {
+static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, bool pipe, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
+  if (pipe) {
+    const dim3 pgrid(static_cast<unsigned>(round_up(tiles, 8) * a.n_slices * a.row_chunks));
+    if (bmb == 4) {
+      if (rb == 4)
+        launch((slot_shrink_pipe_kernel<Tag, 4, 4, 2>), pgrid, dim3(256), 0, st, a);
+      else
+        launch((slot_shrink_pipe_kernel<Tag, 4, 1, 2>), pgrid, dim3(256), 0, st, a);
+    } else {
+      if (rb == 4)
+        launch((slot_shrink_pipe_kernel<Tag, 1, 4, 2>), pgrid, dim3(256), 0, st, a);
+      else
+        launch((slot_shrink_pipe_kernel<Tag, 1, 1, 4>), pgrid, dim3(256), 0, st, a);
+    }
+    return;
+  }
   if (bmb == 4) {
     if (rb == 4)
       launch((slot_shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
@@ -1040,24 +1201,26 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
   p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // LORA_MULTI_SHRINK: 1 GEMM form, 2 general. Default: general. (The GEMM
+  // LORA_MULTI_SHRINK: 1 GEMM form, 2 general, 3 pipelined general (the
+  // default where x and one slot's adapter fit 2 GiB descriptors). The GEMM
   // form reads x once instead of once per slice and rank chunk, but with one
   // chunk of prefetch and a barrier per chunk it is latency-bound and measures
-  // slower on the prefill workload: 456 vs 382 us.)
-  const int force = env_int("LORA_MULTI_SHRINK", 2);
-  const bool gemm_ok = force != 2 && x->dtype == LORA_BF16 && p.h_vec && K % 8 == 0 &&
-                       T * x->stride_row * 2 <= kMaxBufferBytes &&
-                       (int64_t)num_slices * r_max * a->s1 * 2 <= kMaxBufferBytes && K < (int64_t(1) << 30);
+  // slower on the prefill workload.
+  const int force = env_int("LORA_MULTI_SHRINK", 3);
+  const bool desc_ok = T * x->stride_row * (int64_t)es <= kMaxBufferBytes &&
+                       (int64_t)num_slices * r_max * a->s1 * (int64_t)es <= kMaxBufferBytes && K < (int64_t(1) << 30);
+  p.x_bytes = T * x->stride_row * (int64_t)es;
+  const bool gemm_ok = desc_ok && x->dtype == LORA_BF16 && p.h_vec && K % 8 == 0;
   if (gemm_ok && force == 1) {
-    p.x_bytes = T * x->stride_row * 2;
     const int64_t pieces = ceil_div(T, kShrinkTokens) + S;
     launch(slot_shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
     return launch_status();
   }
+  const bool pipe = desc_ok && force != 2;
   if (x->dtype == LORA_BF16)
-    launch_shrink<BF16>(p, bmb, rb, tiles, st);
+    launch_shrink<BF16>(p, bmb, rb, tiles, pipe, st);
   else
-    launch_shrink<F32>(p, bmb, rb, tiles, st);
+    launch_shrink<F32>(p, bmb, rb, tiles, pipe, st);
   return launch_status();
 }
 

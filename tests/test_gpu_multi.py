@@ -91,17 +91,17 @@ def test_shrink(case):
     assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2, 3])
 @pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
 def test_shrink_every_schedule(case, mode, monkeypatch):
-    """Both shrink kernels (GEMM form with the adapter staged in LDS, general)
-    on the same cases, including a feature count that is not a multiple of
-    the GEMM form's 64-feature chunk."""
+    """Every shrink kernel (GEMM form with the adapter staged in LDS, general,
+    pipelined general) on the same cases, including a feature count that is
+    not a multiple of the GEMM form's 64-feature chunk."""
     monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
     test_shrink(case)
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2, 3])
 def test_shrink_schedules_integer_exact(mode, monkeypatch):
     monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
     note(f"shrink integer-exact schedule {mode}")
