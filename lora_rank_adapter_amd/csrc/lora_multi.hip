@@ -310,6 +310,8 @@ __global__ __launch_bounds__(256) void slot_shrink_kernel(ShrinkArgs p) {
   }
 }
 
+constexpr int kShrinkGroup = 4;  // token tiles per XCD group (pipelined shrink)
+
 // Pipelined form of slot_shrink_kernel (same grid and reduction): every wave
 // contracts one contiguous range of the feature axis, the loads go through
 // buffer descriptors (masked lanes use kOOB, no branches), and U chunks of the
@@ -330,15 +332,19 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
-  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The per_tile
-  // workgroups of one token tile (its slices and rank chunks) all get ids
-  // with the same residue, so they run on one XCD and re-read the tile's
-  // x rows from that XCD's L2. The grid is padded to a multiple of 8 tiles;
-  // tile numbers past the last tile find no slot and exit.
+  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). Groups of
+  // kShrinkGroup consecutive token tiles (mostly tiles of one slot) go to one
+  // XCD, and within a group the workgroups of one (slice, rank chunk) follow
+  // each other: the adapter rows are re-read by the group's tiles and each
+  // tile's x rows by its slice and rank-chunk workgroups while they are in
+  // that XCD's L2. The grid is padded to a multiple of 8 groups; tile numbers
+  // past the last tile find no slot and exit.
   const int per_tile = p.n_slices * p.row_chunks;
   const int kx = static_cast<int>(blockIdx.x >> 3);
-  const int ti = (kx / per_tile) * 8 + static_cast<int>(blockIdx.x & 7);
-  const int rem = kx % per_tile;
+  const int gw = kShrinkGroup * per_tile;  // workgroups per group
+  const int r2 = kx % gw;
+  const int ti = ((kx / gw) * 8 + static_cast<int>(blockIdx.x & 7)) * kShrinkGroup + r2 % kShrinkGroup;
+  const int rem = r2 / kShrinkGroup;
   const int slice = rem / p.row_chunks;
   const int j0 = (rem - slice * p.row_chunks) * 16 * RB;
 
@@ -1073,7 +1079,7 @@ template <class Tag>
 static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, bool pipe, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
   if (pipe) {
-    const dim3 pgrid(static_cast<unsigned>(round_up(tiles, 8) * a.n_slices * a.row_chunks));
+    const dim3 pgrid(static_cast<unsigned>(round_up(tiles, 8 * kShrinkGroup) * a.n_slices * a.row_chunks));
     if (bmb == 4) {
       if (rb == 4)
         launch((slot_shrink_pipe_kernel<Tag, 4, 4, 2>), pgrid, dim3(256), 0, st, a);
