@@ -15,6 +15,7 @@
 //
 // Kernels:
 //   group_kernel               stable counting sort (one 1024-thread workgroup)
+//   group_chunk_kernel         the same with one workgroup per 1024-token chunk
 //   slot_shrink_kernel         shrink, one workgroup per (tile, slice, rank chunk)
 //   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
 //                              descriptor loads and two register stages
@@ -130,6 +131,149 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
     __syncthreads();
     if (leader) wcnt[wave][key] = 0;
     __syncthreads();
+  }
+}
+
+// Key of token t: its slot if active, else S (inactive).
+__device__ __forceinline__ int group_key(const int32_t* __restrict__ token_slot, const int* rho, int t, int T, int S) {
+  int key = S;
+  if (t < T) {
+    const int s = token_slot[t];
+    if (s >= 0 && s < S && rho[s] > 0) key = s;
+  }
+  return key;
+}
+
+// Lanes of the wave that hold the same key as this lane (bit l = lane l),
+// from one ballot per key bit; a single ballot when the whole wave holds one
+// key (the usual case for tokens of one request). Needs all 64 lanes active.
+__device__ __forceinline__ uint64_t key_peers(int key, int nbits) {
+  const int k0 = __builtin_amdgcn_readfirstlane(key);
+  if (__ballot(key == k0) == ~0ull) return ~0ull;
+  uint64_t peers = ~0ull;
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool on = (key >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    peers &= on ? bal : ~bal;
+  }
+  return peers;
+}
+
+// The same stable counting sort with one workgroup per chunk of 1024 tokens
+// (for T up to kGroupChunkMaxT). Every workgroup counts all T tokens itself:
+// the total per slot gives the offsets (workgroup 0 writes counts and
+// offsets), the count over the chunks before its own gives where its tokens
+// of each slot start. It then places its chunk's tokens as group_kernel does.
+// Counting uses one LDS atomic per distinct key of each wave.
+constexpr int kGroupKeys = 32;  // token chunks (of 1024) the chunked grouping holds in registers
+constexpr int kGroupChunkMaxT = 1024 * kGroupKeys;
+__global__ __launch_bounds__(1024) void group_chunk_kernel(const int32_t* __restrict__ token_slot, int T, int S,
+                                                           const int32_t* __restrict__ ranks, int r_max,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_tokens) {
+  __shared__ int rho[kMaxSlots];
+  __shared__ int cnt[kMaxSlots + 1];   // all tokens
+  __shared__ int pre[kMaxSlots + 1];   // tokens of the chunks before this one
+  __shared__ int base[kMaxSlots + 1];
+  __shared__ int wcnt[16][kMaxSlots + 1];
+  __shared__ int wsum[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c0 = static_cast<int>(blockIdx.x) * 1024;
+  if (tid < S) rho[tid] = clamp_rank(ranks[tid], r_max);
+  for (int i = tid; i <= S; i += 1024) {
+    cnt[i] = 0;
+    pre[i] = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) wcnt[w][i] = 0;
+  }
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) <= S) ++nbits;  // keys 0..S (S = inactive)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // Histograms in per-wave rows of wcnt (the lane that leads a key in its
+  // wave adds the key's count: no two lanes write one entry, no atomics).
+  // All kGroupKeys token chunks are loaded into registers at once; chunk j
+  // takes part while j*1024 < T (uniform, so every lane joins the ballots).
+  int keys[kGroupKeys];
+#pragma unroll
+  for (int j = 0; j < kGroupKeys; ++j) {
+    const int t = j * 1024 + tid;
+    keys[j] = (t < T) ? token_slot[t] : -1;
+  }
+  const int nchunk = (T + 1023) / 1024;
+  auto count_range = [&](int ja, int jb) {
+#pragma unroll
+    for (int j = 0; j < kGroupKeys; ++j) {
+      if (j >= ja && j < jb) {
+        const int sj = keys[j];
+        const int k = (sj >= 0 && sj < S && rho[sj] > 0) ? sj : S;
+        const uint64_t peers = key_peers(k, nbits);
+        if ((peers & lt_mask) == 0 && k < S) wcnt[wave][k] += __popcll(peers);
+      }
+    }
+  };
+  auto sum_rows = [&](int* out) {
+    for (int i = tid; i < S; i += 1024) {
+      int v = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) v += wcnt[w][i];
+      out[i] = v;
+    }
+  };
+  const int bx = static_cast<int>(blockIdx.x);
+  count_range(0, bx);  // the chunks before this one
+  __syncthreads();
+  sum_rows(pre);
+  __syncthreads();
+  count_range(bx, nchunk);  // the rest: the rows now hold every token
+  __syncthreads();
+  sum_rows(cnt);
+  __syncthreads();
+  for (int i = tid; i <= S; i += 1024) {
+#pragma unroll
+    for (int w = 0; w < 16; ++w) wcnt[w][i] = 0;
+  }
+  __syncthreads();
+
+  // exclusive scan of the totals (S <= 1024: one value per thread)
+  const int c = (tid < S) ? cnt[tid] : 0;
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int excl = before + incl - c;
+  if (tid < S) base[tid] = excl + pre[tid];
+  if (blockIdx.x == 0) {
+    if (tid < S) {
+      counts[tid] = c;
+      offsets[tid] = excl;
+    }
+    if (tid == S - 1) offsets[S] = excl + c;
+    if (S == 0 && tid == 0) offsets[0] = 0;
+  }
+  __syncthreads();
+
+  // stable placement of this chunk's tokens
+  const int t = c0 + tid;
+  const int key = group_key(token_slot, rho, t, T, S);
+  const uint64_t peers = key_peers(key, nbits);
+  const int rank_in_wave = __popcll(peers & lt_mask);
+  if ((peers & lt_mask) == 0) wcnt[wave][key] = __popcll(peers);
+  __syncthreads();
+  if (key < S) {
+    int pos = base[key] + rank_in_wave;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][key];
+    sorted_tokens[pos] = t;
   }
 }
 
@@ -1159,8 +1303,17 @@ extern "C" int lora_addressing_build(const lora_addressing* addr, const int32_t*
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
   if (addr->S > 0 && !addr->counts) return LORA_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  launch(group_kernel, dim3(1), dim3(1024), 0, st, addr->token_slot, addr->T, addr->S, ranks, r_max,
-                     addr->counts, addr->offsets, addr->sorted_tokens);
+  // LORA_GROUP: 1 one workgroup, 2 one workgroup per 1024-token chunk
+  // (default up to kGroupChunkMaxT tokens)
+  const int mode = env_int("LORA_GROUP", 2);
+  if (mode == 2 && addr->T <= kGroupChunkMaxT) {
+    const int chunks = addr->T > 0 ? static_cast<int>(ceil_div(addr->T, 1024)) : 1;
+    launch(group_chunk_kernel, dim3(static_cast<unsigned>(chunks)), dim3(1024), 0, st, addr->token_slot, addr->T,
+           addr->S, ranks, r_max, addr->counts, addr->offsets, addr->sorted_tokens);
+  } else {
+    launch(group_kernel, dim3(1), dim3(1024), 0, st, addr->token_slot, addr->T, addr->S, ranks, r_max,
+           addr->counts, addr->offsets, addr->sorted_tokens);
+  }
   return launch_status();
 }
 

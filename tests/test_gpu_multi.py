@@ -74,6 +74,48 @@ def test_grouping_bitwise(case):
     assert np.array_equal(host(addr.sorted_tokens)[:n], sorted_tokens)
 
 
+def _grouping_inputs(kind, rng):
+    if kind == "chunk-multiple":
+        T, S = 4096, 40
+        ts = rng.integers(0, S, T).astype(np.int32)
+    elif kind == "bursty":
+        ts, _, _ = synth.prefill_routing(40, 96, (8, 16), rng, median=300.0, sigma=0.8, cap=2048)
+        T, S = ts.shape[0], 96
+    elif kind == "many-slots":
+        T, S = 5000, 1000
+        ts = rng.integers(-5, S + 5, T).astype(np.int32)
+    elif kind == "max-chunked":
+        T, S = 32768, 200
+        ts = np.repeat(rng.integers(-2, S, 128), 256).astype(np.int32)
+    elif kind == "all-inactive":
+        T, S = 3000, 8
+        ts = np.full(T, -1, np.int32)
+    else:  # "beyond-chunked" (more tokens than the chunked kernel takes)
+        T, S = 70000, 64
+        ts = rng.integers(0, S + 2, T).astype(np.int32)
+    ranks = rng.choice(np.asarray([0, 4, 16, 64], np.int32), S).astype(np.int32)
+    return ts, ranks
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("kind", ["chunk-multiple", "bursty", "many-slots", "max-chunked", "all-inactive",
+                                  "beyond-chunked"])
+def test_grouping_schedules_bitwise(kind, mode, monkeypatch):
+    """Both grouping kernels (one workgroup; one workgroup per 1024-token
+    chunk) against the stable sort of the oracle."""
+    monkeypatch.setenv("LORA_GROUP", str(mode))
+    rng = np.random.default_rng(77)
+    ts, ranks = _grouping_inputs(kind, rng)
+    S = ranks.shape[0]
+    note(f"grouping schedule {mode} {kind} T={ts.shape[0]} S={S}")
+    addr = L.lora_addressing_build(L.Addressing(torch.from_numpy(ts).to(DEV), S), torch.from_numpy(ranks).to(DEV), 64)
+    torch.cuda.synchronize()
+    counts, offsets, sorted_tokens, n = oracle.group_tokens(ts, ranks, 64)
+    assert np.array_equal(host(addr.counts)[:S], counts)
+    assert np.array_equal(host(addr.offsets), offsets)
+    assert np.array_equal(host(addr.sorted_tokens)[:n], sorted_tokens)
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_shrink(case):
     m = _case(*case)
