@@ -21,6 +21,9 @@
 //                              descriptor loads and two register stages
 //   slot_shrink_gemm_kernel    shrink with the adapter chunk staged in LDS and
 //                              shared by 8 token blocks (selectable)
+//   slot_shrink_rows_kernel    shrink for many tokens: a 128-token tile x up to
+//                              256 adapter rows (all slices) per workgroup, x
+//                              staged once in LDS, waves split the rows
 //   slot_expand_owner_kernel   expand for many tokens: a token piece x column
 //                              chunk per workgroup, weights staged once in LDS
 //   slot_expand_stream_kernel  expand for few tokens: tile x column chunk,
@@ -338,6 +341,7 @@ struct ShrinkArgs {
   const int32_t* ranks;
   int64_t K;
   int S, r_max, n_slices, row_chunks;
+  int row_groups;   // row-split kernel: workgroups per token tile (16 rank-block pairs each)
   int64_t x_bytes;  // bytes of x a descriptor may span (GEMM kernel)
   bool h_vec;  // h rows 16-byte aligned (strides multiples of 4)
 };
@@ -737,6 +741,207 @@ __global__ __launch_bounds__(512) void slot_shrink_gemm_kernel(ShrinkArgs p) {
       }
     }
     __syncthreads();  // the next pass rewrites both buffers
+  }
+}
+
+// Row-split shrink for bf16 inputs (x and one slot's a within 2 GiB
+// descriptors). A workgroup owns a tile of up to 128 grouped tokens of one
+// slot against up to 16 (slice, 16-row rank block) pairs: 256 adapter rows
+// over every slice at once (a slot with more pairs gets further row-group
+// workgroups). Wave w takes pairs w, w+4, w+8 and w+12 of its row group over
+// the whole feature axis, so no partial sums are exchanged between waves.
+// The tile's x rows are fetched once per stage of 32*U features by the whole
+// workgroup into a double-buffered LDS tile (in MFMA operand order, so every
+// fragment read is one conflict-free 1 KB access), while each wave streams
+// its own pairs' adapter rows from global memory in two register stages. Each
+// x fragment feeds NP MFMAs and each adapter fragment eight. Compared with one
+// workgroup per (tile, slice, rank chunk), a tile's x rows reach the CU once
+// per row group instead of once per slice and rank chunk, and each adapter
+// row is shared by 128 tokens instead of 64.
+// Tiles go to the XCDs in groups of kRowsGroup consecutive tiles (mostly
+// tiles of one slot) with a tile's row-group workgroups next to each other,
+// so adapter and x rows are re-read from that XCD's L2.
+constexpr int kRowsGroup = 4;
+
+template <int TT, int U, int NP>
+__device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile& tl, int rho, rsrc_t rx, rsrc_t ra,
+                                                 const uint32_t (&xoff)[TT * U / 4], const bool (&bany)[TT],
+                                                 const uint32_t (&aoff)[4], const int (&psl)[4], const int (&pj)[4],
+                                                 const int* tok, uint4* lds) {
+  constexpr int XV = TT * U / 4;     // x vectors per thread per stage
+  constexpr int BUFV = TT * U * 64;  // 16-byte entries per LDS buffer
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int K = static_cast<int>(p.K);
+  const int nstage = (K + 32 * U - 1) / (32 * U);
+  f32x4_t acc[TT][NP];
+#pragma unroll
+  for (int b = 0; b < TT; ++b)
+#pragma unroll
+    for (int i = 0; i < NP; ++i) acc[b][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // entry v = tid + 256*i of a stage: token row 16*(v / 64U) + (v & 15),
+  // features 32*u + 8*g of the stage with u = (v / 64) % U, g = (v / 16) % 4;
+  // its LDS slot is v itself (operand order: block, step, lane)
+  auto load_x = [&](uint4 (&xs)[XV], int st) {
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int v = tid + 256 * i;
+      const int u = (v >> 6) & (U - 1);
+      const int g = (v >> 4) & 3;
+      const bool kok = st < nstage && (st * U + u) * 32 + g * 8 < K;
+      xs[i] = bload16(rx, (kok && xoff[i] != kOOB) ? xoff[i] + static_cast<uint32_t>(st * U) * 64u : kOOB);
+    }
+  };
+  auto store_x = [&](const uint4 (&xs)[XV], int buf) {
+#pragma unroll
+    for (int i = 0; i < XV; ++i) lds[buf * BUFV + tid + 256 * i] = xs[i];
+  };
+  auto load_a = [&](uint4 (&af)[U][NP], int st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cc = st * U + u;
+      const bool kok = st < nstage && cc * 32 + grp * 8 < K;
+      const uint32_t kb = static_cast<uint32_t>(cc) * 64u;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) af[u][i] = bload16(ra, (kok && aoff[i] != kOOB) ? aoff[i] + kb : kOOB);
+    }
+  };
+  auto mma = [&](const uint4 (&af)[U][NP], int buf) {
+    if constexpr (NP > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < TT; ++b)
+          if (bany[b]) {
+            const uint4 xf = lds[buf * BUFV + (b * U + u) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) mma_vec<BF16>(acc[b][i], af[u][i], xf);
+          }
+    }
+  };
+  // Stage s: x in LDS buffer s & 1, adapter fragments in register set s & 1.
+  // Stage s+1's x is stored after stage s is multiplied (its buffer was last
+  // read before the previous barrier) and stage s+2's loads are issued then.
+  // Stages past the end load zeros and add nothing, so the loop body needs no
+  // exit in the middle.
+  uint4 xs[XV];
+  uint4 aA[U][NP], aB[U][NP];
+  load_x(xs, 0);
+  load_a(aA, 0);
+  store_x(xs, 0);
+  load_x(xs, 1);
+  load_a(aB, 1);
+  __syncthreads();
+  for (int st = 0; st < nstage; st += 2) {
+    mma(aA, 0);
+    sched_fence();
+    load_a(aA, st + 2);
+    store_x(xs, 1);
+    load_x(xs, st + 2);
+    __syncthreads();
+    mma(aB, 1);
+    sched_fence();
+    load_a(aB, st + 3);
+    store_x(xs, 0);
+    load_x(xs, st + 3);
+    __syncthreads();
+  }
+  // lane holds rank rows pj + 4grp .. +3 of token 16b + col for each pair
+#pragma unroll
+  for (int b = 0; b < TT; ++b) {
+    if (16 * b + col >= tl.len) continue;
+    const int64_t t = tok[16 * b + col];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float* hrow = p.h + t * p.hs0 + (int64_t)psl[i] * p.hs1;
+      const int j = pj[i] + 4 * grp;
+      if (p.h_vec && j + 4 <= rho) {
+        st16f(hrow + j, acc[b][i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < rho) hrow[j + e] = acc[b][i][e];
+      }
+    }
+  }
+}
+
+template <int TT, int U>
+__global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
+  static_assert(TT * U >= 4 && (U & (U - 1)) == 0, "stage shape");
+  constexpr int TB = 16 * TT;
+  constexpr int XV = TT * U / 4;
+  __shared__ uint4 lds[2 * TT * U * 64];
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[TB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  // workgroup -> (tile, row group): ids go round-robin over the 8 XCDs
+  const int rgs = p.row_groups;
+  const int kx = static_cast<int>(blockIdx.x >> 3);
+  const int gw = kRowsGroup * rgs;
+  const int r2 = kx % gw;
+  const int ti = ((kx / gw) * 8 + static_cast<int>(blockIdx.x & 7)) * kRowsGroup + r2 % kRowsGroup;
+  const int rg = r2 / kRowsGroup;
+  if (wave == 0) {
+    const Tile tl = find_tile(ti, TB, p.counts, p.offsets, p.S);
+    if (lane == 0) sh_tile = tl;
+  }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
+  const int nq = (rho + 15) >> 4;
+  const int npairs = p.n_slices * nq;
+  const int pbeg = 16 * rg;
+  if (pbeg >= npairs) return;  // uniform over the workgroup
+  if (tid < TB) sh_tok[tid] = (tid < tl.len) ? p.sorted[tl.start + tid] : 0;
+  __syncthreads();
+  // this wave's pairs: pbeg + wave + 4i for i < npw (waves without pairs still
+  // load their share of x and take part in every barrier)
+  const int avail = npairs - pbeg - wave;
+  const int npw = uniform_int(avail <= 0 ? 0 : (((avail + 3) >> 2) < 4 ? ((avail + 3) >> 2) : 4));
+
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+  const rsrc_t ra = make_rsrc(static_cast<const uint16_t*>(p.a) + (int64_t)tl.slot * p.as0,
+                              (int64_t)p.n_slices * p.r_max * p.as1 * 2);
+  uint32_t xoff[XV];
+#pragma unroll
+  for (int i = 0; i < XV; ++i) {
+    const int v = tid + 256 * i;
+    const int row = 16 * (v / (64 * U)) + (v & 15);
+    const int u = (v >> 6) & (U - 1);
+    const int g = (v >> 4) & 3;
+    xoff[i] = row < tl.len ? static_cast<uint32_t>(((int64_t)sh_tok[row] * p.ldx + u * 32 + g * 8) * 2) : kOOB;
+  }
+  bool bany[TT];
+#pragma unroll
+  for (int b = 0; b < TT; ++b) bany[b] = 16 * b < tl.len;
+  uint32_t aoff[4];
+  int psl[4], pj[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pg = pbeg + wave + 4 * i;
+    const int sl = pg / nq;
+    const int q = pg - sl * nq;
+    const int j = 16 * q + col;
+    psl[i] = sl;
+    pj[i] = 16 * q;
+    aoff[i] = (i < npw && j < rho)
+                  ? static_cast<uint32_t>(((int64_t)(sl * p.r_max + j) * p.as1 + (lane >> 4) * 8) * 2)
+                  : kOOB;
+  }
+  switch (npw) {
+    case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
+    case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
+    case 2: shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
+    case 3: shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
+    default: shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
   }
 }
 
@@ -1360,22 +1565,38 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
   p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // LORA_MULTI_SHRINK: 1 GEMM form, 2 general, 3 pipelined general (the
-  // default where x and one slot's adapter fit 2 GiB descriptors). The GEMM
-  // form reads x once instead of once per slice and rank chunk, but with one
-  // chunk of prefetch and a barrier per chunk it is latency-bound and measures
+  // Schedule (LORA_MULTI_SHRINK overrides it for tuning sweeps): the
+  // row-split kernel for bf16 batches of 1024 tokens or more (4; 5-7 are its
+  // other tile shapes), the pipelined general kernel for fewer tokens or f32
+  // (3), the general kernel where x or one slot's adapter exceeds a 2 GiB
+  // descriptor (2). The GEMM form (1) reads x once per pass but, with one
+  // chunk of prefetch and a barrier per chunk, is latency-bound and measures
   // slower on the prefill workload.
-  const int force = env_int("LORA_MULTI_SHRINK", 3);
+  const int force = env_int("LORA_MULTI_SHRINK", 0);
   const bool desc_ok = T * x->stride_row * (int64_t)es <= kMaxBufferBytes &&
                        (int64_t)num_slices * r_max * a->s1 * (int64_t)es <= kMaxBufferBytes && K < (int64_t(1) << 30);
   p.x_bytes = T * x->stride_row * (int64_t)es;
   const bool gemm_ok = desc_ok && x->dtype == LORA_BF16 && p.h_vec && K % 8 == 0;
-  if (gemm_ok && force == 1) {
+  const int mode = force >= 1 && force <= 7 ? force : (x->dtype == LORA_BF16 && T >= 1024 ? 4 : 3);
+  if (desc_ok && x->dtype == LORA_BF16 && mode >= 4) {
+    const int tt = mode <= 5 ? 8 : 4;
+    p.row_groups = static_cast<int>(ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 16));
+    const int64_t rtiles = ceil_div(T, 16 * tt) + S;
+    const dim3 grid(static_cast<unsigned>(round_up(rtiles, 8 * kRowsGroup) * p.row_groups));
+    switch (mode) {
+      case 4: launch((slot_shrink_rows_kernel<8, 2>), grid, dim3(256), 0, st, p); break;
+      case 5: launch((slot_shrink_rows_kernel<8, 4>), grid, dim3(256), 0, st, p); break;
+      case 6: launch((slot_shrink_rows_kernel<4, 2>), grid, dim3(256), 0, st, p); break;
+      default: launch((slot_shrink_rows_kernel<4, 4>), grid, dim3(256), 0, st, p); break;
+    }
+    return launch_status();
+  }
+  if (gemm_ok && mode == 1) {
     const int64_t pieces = ceil_div(T, kShrinkTokens) + S;
     launch(slot_shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
     return launch_status();
   }
-  const bool pipe = desc_ok && force != 2;
+  const bool pipe = desc_ok && mode != 2;
   if (x->dtype == LORA_BF16)
     launch_shrink<BF16>(p, bmb, rb, tiles, pipe, st);
   else

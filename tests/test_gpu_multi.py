@@ -133,17 +133,23 @@ def test_shrink(case):
     assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3])
+# LORA_MULTI_SHRINK: 1 GEMM form, 2 general, 3 pipelined general, 4-7 row-split
+# (x tile staged in LDS: 128-token tiles with stages of 64 or 128 features, then 64-token tiles)
+SHRINK_MODES = [1, 2, 3, 4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("mode", SHRINK_MODES)
 @pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
 def test_shrink_every_schedule(case, mode, monkeypatch):
     """Every shrink kernel (GEMM form with the adapter staged in LDS, general,
-    pipelined general) on the same cases, including a feature count that is
-    not a multiple of the GEMM form's 64-feature chunk."""
+    pipelined general, row-split) on the same cases, including a feature count
+    that is not a multiple of the 32- and 64-feature steps, ranks that are not
+    multiples of 16 and a slot with more than 16 (slice, rank block) pairs."""
     monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
     test_shrink(case)
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3])
+@pytest.mark.parametrize("mode", SHRINK_MODES)
 def test_shrink_schedules_integer_exact(mode, monkeypatch):
     monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
     note(f"shrink integer-exact schedule {mode}")
