@@ -386,9 +386,9 @@ def main():
     for i in range(10):
         step(i, evb[i])
     torch.cuda.synchronize()
-    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evb)
-    dxda_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evb)
-    db_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evb)
+    fwd_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evb)
+    dxda_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evb)
+    db_ms = statistics.median(e[2].elapsed_time(e[3]) for e in evb)
 
     if args.copy_probe:
         src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
