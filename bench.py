@@ -262,6 +262,27 @@ def multi_lora_figures(dev, reps=20):
             "expand_fused_us": t_expand, "expand_fused_gbs": ex_bytes / t_expand / 1e3,
             "expand_fused_frac": ex_bytes / t_expand / 1e3 / HBM_PEAK_GBS,
         }
+        if T <= 4096:
+            # a decode step's three calls back to back, eagerly and as one
+            # captured HIP graph replayed per step (no host sync or
+            # data-dependent shape in them, so a serving loop can capture them)
+            def seq(i):
+                L.lora_addressing_build(addr, rk, r_max)
+                L.lora_shrink(xs[i % nsets], a, addr, rk, n, r_max, h=h)
+                L.lora_expand_fused(h, b, addr, rk, sc, ys[i % nsets], slices, r_max)
+
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                seq(0)
+            torch.cuda.current_stream(dev).wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                seq(0)
+            out[name]["step_eager_us"] = timed(seq, reps)
+            out[name]["step_graph_us"] = timed(lambda i: graph.replay(), reps)
+            del graph
         del xs, a, b, ys, h
     # gather_shrink over the 128256-row embedding adapter table (4.2 GB, rank index contiguous)
     T, S, r_max, V = ts5.shape[0], 128, 128, 128256
