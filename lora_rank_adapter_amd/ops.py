@@ -127,6 +127,15 @@ class Addressing:
         self.offsets = torch.empty(self.S + 1, dtype=torch.int32, device=dev)
         self.sorted_tokens = torch.empty(max(self.T, 1), dtype=torch.int32, device=dev)
 
+    @classmethod
+    def from_arrays(cls, token_slot: torch.Tensor, S: int, counts: torch.Tensor, offsets: torch.Tensor,
+                    sorted_tokens: torch.Tensor) -> "Addressing":
+        """An addressing over arrays the caller already holds (e.g. built by an earlier call)."""
+        a = cls.__new__(cls)
+        a.token_slot, a.T, a.S = token_slot, int(token_slot.shape[0]), int(S)
+        a.counts, a.offsets, a.sorted_tokens = counts, offsets, sorted_tokens
+        return a
+
     def struct(self) -> LoraAddressing:
         return LoraAddressing(_ptr(self.token_slot), self.T, self.S, _ptr(self.counts), _ptr(self.offsets),
                               _ptr(self.sorted_tokens))
