@@ -544,7 +544,7 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
       const bool kok = cc < cend && cc * CH + grp * VEC < K;
       const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);  // < x row bytes when kok
 #pragma unroll
-      for (int b = 0; b < BMB; ++b) xf[u][b] = bload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
+      for (int b = 0; b < BMB; ++b) xf[u][b] = sload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
 #pragma unroll
       for (int q = 0; q < RB; ++q) af[u][q] = bload16(ra, (kok && aoff[q] != kOOB) ? aoff[q] + kb : kOOB);
     }
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(512) void slot_shrink_gemm_kernel(ShrinkArgs p) {
 #pragma unroll
       for (int stp = 0; stp < 2; ++stp) {
         const int k = c * KC + stp * 32 + grp * 8;
-        xr[stp] = bload16(rx, (xrow != kOOB && k < K) ? xrow + static_cast<uint32_t>(k * 2) : kOOB);
+        xr[stp] = sload16(rx, (xrow != kOOB && k < K) ? xrow + static_cast<uint32_t>(k * 2) : kOOB);
       }
     };
     f32x4_t acc[kPairs];
@@ -792,7 +792,7 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
       const int u = (v >> 6) & (U - 1);
       const int g = (v >> 4) & 3;
       const bool kok = st < nstage && (st * U + u) * 32 + g * 8 < K;
-      xs[i] = bload16(rx, (kok && xoff[i] != kOOB) ? xoff[i] + static_cast<uint32_t>(st * U) * 64u : kOOB);
+      xs[i] = sload16(rx, (kok && xoff[i] != kOOB) ? xoff[i] + static_cast<uint32_t>(st * U) * 64u : kOOB);
     }
   };
   auto store_x = [&](const uint4 (&xs)[XV], int buf) {
@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
         }
 #pragma unroll
         for (int b = 0; b < BMB; ++b)
-          cv[u][b] = __builtin_bit_cast(f32x4_t, bload16(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB));
+          cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB));
       }
     };
     auto comp2 = [&](const wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
@@ -1181,7 +1181,7 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
         for (int b = 0; b < BMB; ++b) {
 #pragma unroll
           for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
-          bstore16(ry, yoff(b, nb + 4 * grp), __builtin_bit_cast(uint4, cv[u][b]));
+          sstore16(ry, yoff(b, nb + 4 * grp), __builtin_bit_cast(uint4, cv[u][b]));
         }
       }
     };
@@ -1309,7 +1309,7 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
       const bool ok = blk < nblk && tix < tl.len && col_ok;
       const int t = sh_tok[ok ? tix : 0];
       B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * 4) : kOOB;
-      B.cv[i] = __builtin_bit_cast(f32x4_t, bload16(ry, B.yo[i]));
+      B.cv[i] = __builtin_bit_cast(f32x4_t, sload16(ry, B.yo[i]));
     }
   };
   auto walk = [&](auto nq_tag) {
@@ -1346,7 +1346,7 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(ob + (RPI * i + lr) * LDW + lc);
-        bstore16(ry, B.yo[i], __builtin_bit_cast(uint4, B.cv[i] + pr));
+        sstore16(ry, B.yo[i], __builtin_bit_cast(uint4, B.cv[i] + pr));
       }
     };
     Blk A, Bb;

@@ -209,7 +209,7 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
       const bool kok = cc < cend && cc * CH + grp * VEC < p.Kin;
       const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
 #pragma unroll
-      for (int b = 0; b < BMB; ++b) zf[u][b] = bload16(rz, kok ? zoff[b] + kb : kOOB);
+      for (int b = 0; b < BMB; ++b) zf[u][b] = sload16(rz, kok ? zoff[b] + kb : kOOB);
 #pragma unroll
       for (int q = 0; q < RB; ++q) wf[u][q] = bload16(rw1, kok ? woff[q] + kb : kOOB);
     }
@@ -344,7 +344,7 @@ __device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int6
 #pragma unroll
       for (int b = 0; b < BMB; ++b) {
         if constexpr (ACCUM)
-          cv[u][b] = __builtin_bit_cast(f32x4_t, bload16(ro, ooff(b, nb)));
+          cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ro, ooff(b, nb)));
         else
           cv[u][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
@@ -357,7 +357,7 @@ __device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int6
       for (int b = 0; b < BMB; ++b) {
 #pragma unroll
         for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
-        bstore16(ro, ooff(b, nb0 + u), __builtin_bit_cast(uint4, cv[u][b]));
+        sstore16(ro, ooff(b, nb0 + u), __builtin_bit_cast(uint4, cv[u][b]));
       }
     }
   };
@@ -443,7 +443,7 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if constexpr (ACCUM)
-        cv[i] = __builtin_bit_cast(f32x4_t, bload16(ro, ooff(i, nb0)));
+        cv[i] = __builtin_bit_cast(f32x4_t, sload16(ro, ooff(i, nb0)));
       else
         cv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -463,7 +463,7 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(obuf + (RPI * i + lr) * LDW + lc);
-      bstore16(ro, ooff(i, nb0), __builtin_bit_cast(uint4, cv[i] + pr));
+      sstore16(ro, ooff(i, nb0), __builtin_bit_cast(uint4, cv[i] + pr));
     }
   };
   // two stages in flight; stages past the end read zeros and store nothing
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
           const uint32_t off = (nb < nnb && ncol < p.Nout)
                                    ? static_cast<uint32_t>(((16 * b + col) * p.ldo + ncol) * 4)
                                    : kOOB;
-          cv[u][b] = __builtin_bit_cast(f32x4_t, bload16(ro, off));
+          cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ro, off));
         }
       }
     } else {
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
         for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(w[q]), hf[b][q]);
         const uint32_t off =
             (nb < nnb && ncol < p.Nout) ? static_cast<uint32_t>(((16 * b + col) * p.ldo + ncol) * 4) : kOOB;
-        bstore16(ro, off, __builtin_bit_cast(uint4, cv[u][b]));
+        sstore16(ro, off, __builtin_bit_cast(uint4, cv[u][b]));
       }
     }
   };
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(64 * NW) void shrink_tok_kernel(FusedArgs p) {
 #pragma unroll
     for (int c = 0; c < NSTEP; ++c) {
       const int64_t k = pan * KP + c * CH + grp * VEC;
-      zf[c] = bload16(rz, (pan < npan && k < p.Kin) ? zrow + static_cast<uint32_t>((pan * KP + c * CH) * ES) : kOOB);
+      zf[c] = sload16(rz, (pan < npan && k < p.Kin) ? zrow + static_cast<uint32_t>((pan * KP + c * CH) * ES) : kOOB);
     }
   };
   f32x4_t acc[RB];
@@ -827,7 +827,7 @@ __global__ __launch_bounds__(64 * NW) void expand_tok_kernel(FusedArgs p) {
     if constexpr (ACCUM) {
       const rsrc_t ro = make_rsrc(p.out + blk * 16 * p.ldo, ok ? (p.M - blk * 16) * p.ldo * 4 : 0);
 #pragma unroll
-      for (int u = 0; u < NBS; ++u) cv[u] = __builtin_bit_cast(f32x4_t, bload16(ro, coff[u]));
+      for (int u = 0; u < NBS; ++u) cv[u] = __builtin_bit_cast(f32x4_t, sload16(ro, coff[u]));
     } else {
 #pragma unroll
       for (int u = 0; u < NBS; ++u) cv[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -840,7 +840,7 @@ __global__ __launch_bounds__(64 * NW) void expand_tok_kernel(FusedArgs p) {
     for (int u = 0; u < NBS; ++u) {
 #pragma unroll
       for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u], WF::operand(w2s[(u * RB + q) * 64 + lane]), hf[q]);
-      bstore16(ro, coff[u], __builtin_bit_cast(uint4, cv[u]));
+      sstore16(ro, coff[u], __builtin_bit_cast(uint4, cv[u]));
     }
   };
   uint4 hfA[RB], hfB[RB];
@@ -931,7 +931,7 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
       const int row = v / VPR;
       const int vc = v - row * VPR;
       const int64_t n = n_base + (int64_t)vc * VEC;
-      zr[i] = bload16(rz, n < p.N ? static_cast<uint32_t>(((m0 - m_begin + row) * p.ldz + n) * ES) : kOOB);
+      zr[i] = sload16(rz, n < p.N ? static_cast<uint32_t>(((m0 - m_begin + row) * p.ldz + n) * ES) : kOOB);
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
