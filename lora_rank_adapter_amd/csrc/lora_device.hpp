@@ -93,15 +93,18 @@ __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, uint4 v) {
 // displace each other and the reused operands (weights, the rank intermediate)
 // in the caches. On the MI355X a plain y += x stream over the forward's
 // tensors (bf16 x, fp32 y) runs at 6.4 TB/s with non-temporal loads and stores
-// against 5.8 TB/s without. Weights and intermediates keep the default policy.
+// against 5.8 TB/s without; in the LoRA kernels nt on both is needed (nt loads
+// with default stores lose most of the gain), and the system-scope bit (sc1)
+// on the stores adds about 1% more. Weights and intermediates keep the default
+// policy. Cache-policy operand bits on gfx950: 1 sc0, 2 nt, 16 sc1.
 #ifndef LORA_STREAM_LOAD_POLICY
 #define LORA_STREAM_LOAD_POLICY 2
 #endif
 #ifndef LORA_STREAM_STORE_POLICY
-#define LORA_STREAM_STORE_POLICY 2
+#define LORA_STREAM_STORE_POLICY 18
 #endif
-constexpr int kStreamLoadPolicy = LORA_STREAM_LOAD_POLICY;    // 2: nt on gfx950
-constexpr int kStreamStorePolicy = LORA_STREAM_STORE_POLICY;  // 2: nt on gfx950
+constexpr int kStreamLoadPolicy = LORA_STREAM_LOAD_POLICY;    // nt
+constexpr int kStreamStorePolicy = LORA_STREAM_STORE_POLICY;  // nt | sc1
 
 __device__ __forceinline__ uint4 sload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStreamLoadPolicy));
