@@ -169,9 +169,24 @@ struct FusedArgs {
 // reduced through LDS in a fixed order. On return every wave holds s*H (acc) and its
 // MFMA operand form (hf). Rows past M (Z) or past r (W1) lie outside their
 // buffer descriptors and read as zero.
+// LDS of shrink_tile: the NW partial sums (after the feature loop) share
+// their memory with the per-wave row-linear stream staging tiles (during it;
+// bf16 only: the wave's 16*BMB stream rows of one stage, rows padded by 16
+// bytes so that the 16 rows one fragment read touches fall in distinct banks).
+template <class Tag, int NW, int RB, int BMB, int U>
+struct ShrinkStage {
+  static constexpr int ES = sizeof(typename Tag::elem);
+  static constexpr bool LIN = ES == 2;
+  static constexpr int SROW = U * 4 * Tag::VEC * ES;  // bytes of a row per stage
+  static constexpr int PITCH = SROW + 16;
+  static constexpr int BYTES = LIN ? 16 * BMB * PITCH : 0;  // per wave
+  static constexpr int RED = NW * BMB * RB * 64 * 16;
+  static constexpr int TOTAL = (NW * BYTES > RED) ? NW * BYTES : RED;
+};
+
 template <class Tag, int NW, int RB, int BMB, int U>
 __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x4_t (*red)[BMB * RB][64],
-                                            f32x4_t (&acc)[BMB][RB], uint4 (&hf)[BMB][RB]) {
+                                            f32x4_t (&acc)[BMB][RB], uint4 (&hf)[BMB][RB], char* stage) {
   using E = typename Tag::elem;
   constexpr int VEC = Tag::VEC;
   constexpr int ES = sizeof(E);
@@ -180,12 +195,33 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
+  // bf16 streams are loaded row-linearly (each instruction covers whole row
+  // segments of the stage: SROW bytes of 64/LPR rows) into this wave's LDS
+  // tile and read back in MFMA operand order; in MFMA order every instruction
+  // would touch 16 rows x 64 bytes, half of each 128-byte line.
+  using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
+  constexpr bool LIN = SS::LIN;
+  constexpr int LPR = SS::SROW / 16;                 // lanes per row
+  constexpr int RPI = LIN ? 64 / LPR : 16;           // rows per row-linear load
+  constexpr int ZN = LIN ? 16 * BMB / RPI : BMB;     // stream vectors per lane and step group
+  static_assert(!LIN || (64 % LPR == 0 && (16 * BMB) % RPI == 0 && ZN * RPI == 16 * BMB), "stage shape");
 
   const rsrc_t rz = make_rsrc(static_cast<const E*>(p.z) + m0 * p.ldz, (p.M - m0) * p.ldz * ES);
   const rsrc_t rw1 = make_rsrc(p.w1, (int64_t)p.r * p.ldw1 * ES);
   uint32_t zoff[BMB];
 #pragma unroll
   for (int b = 0; b < BMB; ++b) zoff[b] = static_cast<uint32_t>(((16 * b + col) * p.ldz + grp * VEC) * ES);
+  // row-linear form: lane -> row i*RPI + lane/LPR, 16-byte piece lane%LPR of
+  // the stage's row segment (step piece/4, lane group piece%4)
+  const int lpiece = lane % LPR;
+  const int lstep = lpiece >> 2;
+  const int lgrp = lpiece & 3;
+  uint32_t lrow[LIN ? ZN : 1];
+  if constexpr (LIN) {
+#pragma unroll
+    for (int i = 0; i < ZN; ++i)
+      lrow[i] = static_cast<uint32_t>(((i * RPI + lane / LPR) * p.ldz + lgrp * VEC) * ES);
+  }
   uint32_t woff[RB];
 #pragma unroll
   for (int q = 0; q < RB; ++q) woff[q] = static_cast<uint32_t>(((int64_t)(16 * q + col) * p.ldw1 + grp * VEC) * ES);
@@ -202,32 +238,57 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   const int64_t cbeg = (int64_t)wave * per;
   const int64_t cend = (cbeg + per < nch) ? cbeg + per : nch;
   constexpr int64_t cstep = U;
-  auto load1 = [&](uint4 (&zf)[U][BMB], uint4 (&wf)[U][RB], int64_t c) {
+  // zf: LIN: ZN row-linear vectors of the stage; else [u][b] MFMA fragments
+  auto load1 = [&](uint4 (&zf)[U][ZN], uint4 (&wf)[U][RB], int64_t c) {
+    if constexpr (LIN) {
+      const int64_t cc = c + lstep;
+      const bool kok = cc < cend && cc * CH + lgrp * VEC < p.Kin;
+      const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
+#pragma unroll
+      for (int i = 0; i < ZN; ++i) zf[0][i] = sload16(rz, kok ? lrow[i] + kb : kOOB);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t cc = c + u;
       const bool kok = cc < cend && cc * CH + grp * VEC < p.Kin;
       const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
+      if constexpr (!LIN) {
 #pragma unroll
-      for (int b = 0; b < BMB; ++b) zf[u][b] = sload16(rz, kok ? zoff[b] + kb : kOOB);
+        for (int b = 0; b < BMB; ++b) zf[u][b] = sload16(rz, kok ? zoff[b] + kb : kOOB);
+      }
 #pragma unroll
       for (int q = 0; q < RB; ++q) wf[u][q] = bload16(rw1, kok ? woff[q] + kb : kOOB);
     }
   };
-  auto mma1 = [&](const uint4 (&zf)[U][BMB], const uint4 (&wf)[U][RB]) {
+  auto mma1 = [&](const uint4 (&zf)[U][ZN], const uint4 (&wf)[U][RB]) {
+    if constexpr (LIN) {
+      // the stage's rows into this wave's tile, then fragments in operand order
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int i = 0; i < ZN; ++i)
+        *reinterpret_cast<uint4*>(stage + (i * RPI + lane / LPR) * SS::PITCH + lpiece * 16) = zf[0][i];
 #pragma unroll
-      for (int b = 0; b < BMB; ++b)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], wf[u][q], zf[u][b]);
+        for (int b = 0; b < BMB; ++b) {
+          const uint4 z = *reinterpret_cast<const uint4*>(stage + (16 * b + col) * SS::PITCH + (u * 4 + grp) * 16);
+#pragma unroll
+          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], wf[u][q], z);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < BMB; ++b)
+#pragma unroll
+          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], wf[u][q], zf[u][b]);
+    }
   };
   {
     // Two register stages of U chunks: the loads of the next stage are in
     // flight while the current one is multiplied. The loop body has no exit in
     // the middle: with an odd stage count the last pass multiplies a stage
     // of zeros (every load past this wave's range reads 0).
-    uint4 zA[U][BMB], wA[U][RB], zB[U][BMB], wB[U][RB];
+    uint4 zA[U][ZN], wA[U][RB], zB[U][ZN], wB[U][RB];
     if (cbeg < cend) {
       load1(zA, wA, cbeg);
       for (int64_t c = cbeg; c < cend; c += 2 * cstep) {
@@ -242,6 +303,8 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
       }
     }
   }
+  // the staging tiles share their memory with the partial sums
+  if constexpr (LIN) __syncthreads();
 
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
@@ -489,13 +552,15 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 // gradient kernels).
 template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G, bool ROWS>
 __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
-  __shared__ f32x4_t red[NW][BMB * RB][64];
+  using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
+  __shared__ __attribute__((aligned(16))) char shr[SS::TOTAL];
   __shared__ float obuf[ROWS ? NW : 1][ROWS ? 16 * BMB * (16 * NBU + 4) : 1];
+  auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   const int64_t tile = blockIdx.x;
   const int64_t m0 = tile * (16 * BMB);
   f32x4_t acc[BMB][RB];
   uint4 hf[BMB][RB];
-  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf);
+  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf, shr + wave_id() * SS::BYTES);
   if constexpr (EMIT_G) {
     if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
@@ -509,11 +574,13 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
 // (EMIT_G) and/or expand fragments (EMIT_F).
 template <class Tag, int NW, int RB, int BMB, int U, bool EMIT_G, bool EMIT_F>
 __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
-  __shared__ f32x4_t red[NW][BMB * RB][64];
+  using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
+  __shared__ __attribute__((aligned(16))) char shr[SS::TOTAL];
+  auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   const int64_t m0 = (int64_t)blockIdx.x * (16 * BMB);
   f32x4_t acc[BMB][RB];
   uint4 hf[BMB][RB];
-  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf);
+  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf, shr + wave_id() * SS::BYTES);
   const int wave = wave_id();
   if constexpr (EMIT_G) {
     if (wave == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
