@@ -751,8 +751,9 @@ __global__ __launch_bounds__(512) void slot_shrink_gemm_kernel(ShrinkArgs p) {
 // workgroups). Wave w takes pairs w, w+4, w+8 and w+12 of its row group over
 // the whole feature axis, so no partial sums are exchanged between waves.
 // The tile's x rows are fetched once per stage of 32*U features by the whole
-// workgroup into a double-buffered LDS tile (in MFMA operand order, so every
-// fragment read is one conflict-free 1 KB access), while each wave streams
+// workgroup, row-linearly (each load instruction covers whole row segments),
+// into a double-buffered LDS tile with padded rows (every fragment read is
+// conflict-free), while each wave streams
 // its own pairs' adapter rows from global memory in two register stages. Each
 // x fragment feeds NP MFMAs and each adapter fragment eight. Compared with one
 // workgroup per (tile, slice, rank chunk), a tile's x rows reach the CU once
@@ -767,9 +768,13 @@ template <int TT, int U, int NP>
 __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile& tl, int rho, rsrc_t rx, rsrc_t ra,
                                                  const uint32_t (&xoff)[TT * U / 4], const bool (&bany)[TT],
                                                  const uint32_t (&aoff)[4], const int (&psl)[4], const int (&pj)[4],
-                                                 const int* tok, uint4* lds) {
+                                                 const int* tok, char* lds, char* alds) {
   constexpr int XV = TT * U / 4;     // x vectors per thread per stage
-  constexpr int BUFV = TT * U * 64;  // 16-byte entries per LDS buffer
+  constexpr int NA = NP * U;         // adapter vectors per lane and stage (row-linear)
+  constexpr int ARPI = 64 / (4 * U);  // adapter rows per load instruction
+  constexpr int LPR = 4 * U;         // 16-byte pieces of a row per stage
+  constexpr int PITCH = 64 * U + 16;  // LDS row pitch: the 16 rows of a fragment read fall in distinct banks
+  constexpr int BUFB = 16 * TT * PITCH;  // bytes per LDS buffer
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int col = lane & 15;
@@ -782,41 +787,67 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[b][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // entry v = tid + 256*i of a stage: token row 16*(v / 64U) + (v & 15),
-  // features 32*u + 8*g of the stage with u = (v / 64) % U, g = (v / 16) % 4;
-  // its LDS slot is v itself (operand order: block, step, lane)
+  // entry v = tid + 256*i of a stage: token row v / 4U, 16-byte piece v % 4U
+  // of the row's stage segment (features 32*u + 8*g with u = piece / 4,
+  // g = piece % 4): each load instruction covers whole row segments; the
+  // piece goes to LDS at row * PITCH + piece * 16
   auto load_x = [&](uint4 (&xs)[XV], int st) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
       const int v = tid + 256 * i;
-      const int u = (v >> 6) & (U - 1);
-      const int g = (v >> 4) & 3;
+      const int u = (v % LPR) >> 2;
+      const int g = v & 3;
       const bool kok = st < nstage && (st * U + u) * 32 + g * 8 < K;
       xs[i] = sload16(rx, (kok && xoff[i] != kOOB) ? xoff[i] + static_cast<uint32_t>(st * U) * 64u : kOOB);
     }
   };
   auto store_x = [&](const uint4 (&xs)[XV], int buf) {
 #pragma unroll
-    for (int i = 0; i < XV; ++i) lds[buf * BUFV + tid + 256 * i] = xs[i];
-  };
-  auto load_a = [&](uint4 (&af)[U][NP], int st) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int cc = st * U + u;
-      const bool kok = st < nstage && cc * 32 + grp * 8 < K;
-      const uint32_t kb = static_cast<uint32_t>(cc) * 64u;
-#pragma unroll
-      for (int i = 0; i < NP; ++i) af[u][i] = bload16(ra, (kok && aoff[i] != kOOB) ? aoff[i] + kb : kOOB);
+    for (int i = 0; i < XV; ++i) {
+      const int v = tid + 256 * i;
+      *reinterpret_cast<uint4*>(lds + buf * BUFB + (v / LPR) * PITCH + (v % LPR) * 16) = xs[i];
     }
   };
-  auto mma = [&](const uint4 (&af)[U][NP], int buf) {
+  // This wave's adapter rows (16 per pair) are loaded row-linearly too: load
+  // i covers rows i*ARPI .. +ARPI-1 (pair i*ARPI/16), lane -> row lane / 4U,
+  // 16-byte piece lane % 4U; the pieces go to the wave's LDS tile and the
+  // fragments are read back from it.
+  const int apiece = lane % LPR;
+  const int astep = apiece >> 2;
+  const int agrp = apiece & 3;
+  uint32_t aro[NA > 0 ? NA : 1];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = i * ARPI + lane / LPR;  // row of the wave's tile
+    const int pr = (i * ARPI) / 16;         // its pair (compile-time per i)
+    const int j = pj[pr] + (row & 15);
+    aro[i] = j < rho ? static_cast<uint32_t>(((int64_t)(psl[pr] * p.r_max + j) * p.as1 + agrp * 8) * 2) : kOOB;
+  }
+  auto load_a = [&](uint4 (&al)[NA > 0 ? NA : 1], int st) {
+    const int cc = st * U + astep;
+    const bool kok = st < nstage && cc * 32 + agrp * 8 < K;
+    const uint32_t kb = static_cast<uint32_t>(cc) * 64u;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) al[i] = bload16(ra, (kok && aro[i] != kOOB) ? aro[i] + kb : kOOB);
+  };
+  auto mma = [&](const uint4 (&al)[NA > 0 ? NA : 1], int buf) {
     if constexpr (NP > 0) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        *reinterpret_cast<uint4*>(alds + (i * ARPI + lane / LPR) * PITCH + apiece * 16) = al[i];
+      uint4 af[U][NP];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          af[u][i] = *reinterpret_cast<const uint4*>(alds + (16 * i + col) * PITCH + (u * 4 + grp) * 16);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int b = 0; b < TT; ++b)
           if (bany[b]) {
-            const uint4 xf = lds[buf * BUFV + (b * U + u) * 64 + lane];
+            const uint4 xf =
+                *reinterpret_cast<const uint4*>(lds + buf * BUFB + (16 * b + col) * PITCH + (u * 4 + grp) * 16);
 #pragma unroll
             for (int i = 0; i < NP; ++i) mma_vec<BF16>(acc[b][i], af[u][i], xf);
           }
@@ -828,7 +859,7 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
   // Stages past the end load zeros and add nothing, so the loop body needs no
   // exit in the middle.
   uint4 xs[XV];
-  uint4 aA[U][NP], aB[U][NP];
+  uint4 aA[NA > 0 ? NA : 1], aB[NA > 0 ? NA : 1];
   load_x(xs, 0);
   load_a(aA, 0);
   store_x(xs, 0);
@@ -874,7 +905,8 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   static_assert(TT * U >= 4 && (U & (U - 1)) == 0, "stage shape");
   constexpr int TB = 16 * TT;
   constexpr int XV = TT * U / 4;
-  __shared__ uint4 lds[2 * TT * U * 64];
+  __shared__ __attribute__((aligned(16))) char lds[2 * 16 * TT * (64 * U + 16)];
+  __shared__ __attribute__((aligned(16))) char alds[4][64 * (64 * U + 16)];  // per wave: 4 pairs x 16 rows
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
   const int tid = threadIdx.x;
@@ -914,9 +946,9 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
 #pragma unroll
   for (int i = 0; i < XV; ++i) {
     const int v = tid + 256 * i;
-    const int row = 16 * (v / (64 * U)) + (v & 15);
-    const int u = (v >> 6) & (U - 1);
-    const int g = (v >> 4) & 3;
+    const int row = v / (4 * U);
+    const int u = (v % (4 * U)) >> 2;
+    const int g = v & 3;
     xoff[i] = row < tl.len ? static_cast<uint32_t>(((int64_t)sh_tok[row] * p.ldx + u * 32 + g * 8) * 2) : kOOB;
   }
   bool bany[TT];
@@ -937,11 +969,11 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
                   : kOOB;
   }
   switch (npw) {
-    case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
-    case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
-    case 2: shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
-    case 3: shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
-    default: shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds); break;
+    case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 2: shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 3: shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
+    default: shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
   }
 }
 
