@@ -170,16 +170,17 @@ struct FusedArgs {
 // MFMA operand form (hf). Rows past M (Z) or past r (W1) lie outside their
 // buffer descriptors and read as zero.
 // LDS of shrink_tile: the NW partial sums (after the feature loop) share
-// their memory with the per-wave row-linear stream staging tiles (during it;
-// bf16 only: the wave's 16*BMB stream rows of one stage, rows padded by 16
-// bytes so that the 16 rows one fragment read touches fall in distinct banks).
+// their memory with the per-wave row-linear staging tiles (during it; bf16
+// only: the wave's 16*BMB stream rows and 16*RB weight rows of one stage,
+// rows padded by 16 bytes so that the 16 rows one fragment read touches fall
+// in distinct banks).
 template <class Tag, int NW, int RB, int BMB, int U>
 struct ShrinkStage {
   static constexpr int ES = sizeof(typename Tag::elem);
   static constexpr bool LIN = ES == 2;
   static constexpr int SROW = U * 4 * Tag::VEC * ES;  // bytes of a row per stage
   static constexpr int PITCH = SROW + 16;
-  static constexpr int BYTES = LIN ? 16 * BMB * PITCH : 0;  // per wave
+  static constexpr int BYTES = LIN ? 16 * (BMB + RB) * PITCH : 0;  // per wave: stream rows, then weight rows
   static constexpr int RED = NW * BMB * RB * 64 * 16;
   static constexpr int TOTAL = (NW * BYTES > RED) ? NW * BYTES : RED;
 };
@@ -204,7 +205,9 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   constexpr int LPR = SS::SROW / 16;                 // lanes per row
   constexpr int RPI = LIN ? 64 / LPR : 16;           // rows per row-linear load
   constexpr int ZN = LIN ? 16 * BMB / RPI : BMB;     // stream vectors per lane and step group
-  static_assert(!LIN || (64 % LPR == 0 && (16 * BMB) % RPI == 0 && ZN * RPI == 16 * BMB), "stage shape");
+  constexpr int WN = LIN ? 16 * RB / RPI : RB;       // weight vectors per lane and step group
+  static_assert(!LIN || (64 % LPR == 0 && (16 * BMB) % RPI == 0 && ZN * RPI == 16 * BMB && WN * RPI == 16 * RB),
+                "stage shape");
 
   const rsrc_t rz = make_rsrc(static_cast<const E*>(p.z) + m0 * p.ldz, (p.M - m0) * p.ldz * ES);
   const rsrc_t rw1 = make_rsrc(p.w1, (int64_t)p.r * p.ldw1 * ES);
@@ -225,6 +228,13 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   uint32_t woff[RB];
 #pragma unroll
   for (int q = 0; q < RB; ++q) woff[q] = static_cast<uint32_t>(((int64_t)(16 * q + col) * p.ldw1 + grp * VEC) * ES);
+  // weight rows past r lie outside rw1 and read as zero
+  uint32_t lwrow[LIN ? WN : 1];
+  if constexpr (LIN) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i)
+      lwrow[i] = static_cast<uint32_t>(((int64_t)(i * RPI + lane / LPR) * p.ldw1 + lgrp * VEC) * ES);
+  }
 
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
@@ -238,41 +248,53 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   const int64_t cbeg = (int64_t)wave * per;
   const int64_t cend = (cbeg + per < nch) ? cbeg + per : nch;
   constexpr int64_t cstep = U;
-  // zf: LIN: ZN row-linear vectors of the stage; else [u][b] MFMA fragments
-  auto load1 = [&](uint4 (&zf)[U][ZN], uint4 (&wf)[U][RB], int64_t c) {
+  // LIN: zf[0] holds the stage's ZN row-linear stream vectors and wf[0] its
+  // WN row-linear weight vectors; else [u][b] and [u][q] MFMA fragments
+  auto load1 = [&](uint4 (&zf)[U][ZN], uint4 (&wf)[U][WN], int64_t c) {
     if constexpr (LIN) {
       const int64_t cc = c + lstep;
       const bool kok = cc < cend && cc * CH + lgrp * VEC < p.Kin;
       const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
 #pragma unroll
       for (int i = 0; i < ZN; ++i) zf[0][i] = sload16(rz, kok ? lrow[i] + kb : kOOB);
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t cc = c + u;
-      const bool kok = cc < cend && cc * CH + grp * VEC < p.Kin;
-      const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
-      if constexpr (!LIN) {
+      for (int i = 0; i < WN; ++i) wf[0][i] = bload16(rw1, kok ? lwrow[i] + kb : kOOB);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t cc = c + u;
+        const bool kok = cc < cend && cc * CH + grp * VEC < p.Kin;
+        const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
 #pragma unroll
         for (int b = 0; b < BMB; ++b) zf[u][b] = sload16(rz, kok ? zoff[b] + kb : kOOB);
-      }
 #pragma unroll
-      for (int q = 0; q < RB; ++q) wf[u][q] = bload16(rw1, kok ? woff[q] + kb : kOOB);
+        for (int q = 0; q < RB; ++q) wf[u][q] = bload16(rw1, kok ? woff[q] + kb : kOOB);
+      }
     }
   };
-  auto mma1 = [&](const uint4 (&zf)[U][ZN], const uint4 (&wf)[U][RB]) {
+  auto mma1 = [&](const uint4 (&zf)[U][ZN], const uint4 (&wf)[U][WN]) {
     if constexpr (LIN) {
-      // the stage's rows into this wave's tile, then fragments in operand order
+      // the stage's rows into this wave's tile (stream rows, then weight
+      // rows), then fragments in operand order
 #pragma unroll
       for (int i = 0; i < ZN; ++i)
         *reinterpret_cast<uint4*>(stage + (i * RPI + lane / LPR) * SS::PITCH + lpiece * 16) = zf[0][i];
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+        *reinterpret_cast<uint4*>(stage + (16 * BMB + i * RPI + lane / LPR) * SS::PITCH + lpiece * 16) = wf[0][i];
+      uint4 w[U][RB];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < RB; ++q)
+          w[u][q] = *reinterpret_cast<const uint4*>(stage + (16 * (BMB + q) + col) * SS::PITCH + (u * 4 + grp) * 16);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int b = 0; b < BMB; ++b) {
           const uint4 z = *reinterpret_cast<const uint4*>(stage + (16 * b + col) * SS::PITCH + (u * 4 + grp) * 16);
 #pragma unroll
-          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], wf[u][q], z);
+          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], w[u][q], z);
         }
     } else {
 #pragma unroll
@@ -288,7 +310,7 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
     // flight while the current one is multiplied. The loop body has no exit in
     // the middle: with an odd stage count the last pass multiplies a stage
     // of zeros (every load past this wave's range reads 0).
-    uint4 zA[U][ZN], wA[U][RB], zB[U][ZN], wB[U][RB];
+    uint4 zA[U][ZN], wA[U][WN], zB[U][ZN], wB[U][WN];
     if (cbeg < cend) {
       load1(zA, wA, cbeg);
       for (int64_t c = cbeg; c < cend; c += 2 * cstep) {
@@ -1160,10 +1182,14 @@ static int pick_bmb_dx(int64_t M, int rb) {
 }
 
 // Token blocks per shrink tile (rb * bmb <= 16): large tiles share each weight
-// chunk among more tokens, while keeping >= 256 workgroups.
+// chunk among more tokens, while keeping >= 256 workgroups. At rank <= 16 the
+// weight rows are few and staged row-linearly with the stream, and 16-token
+// tiles (twice the workgroups) measure faster (8192 x 4096, rank 16: 34.8
+// against 36.7 us for the X*A shrink of lora_bwd_db).
 static int pick_bmb_shrink(int64_t M, int rb) {
   int bmb = env_int("LORA_SHRINK_BMB", 0);
   if ((bmb == 1 || bmb == 2 || bmb == 4) && bmb * rb <= 16) return bmb;
+  if (rb == 1) return 1;
   for (int c : {4, 2}) {
     if (c * rb <= 16 && ceil_div(M, 16 * c) >= 256) return c;
   }
