@@ -1330,22 +1330,34 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   const int lc = (lane % LPR) * 4;
   const bool col_ok = c0 + lc < ce;
   const rsrc_t rh = make_rsrc(p.h, p.h_bytes);
-  struct Blk {
-    f32x4_t cv[NI];   // output rows (row-linear pieces)
-    uint32_t yo[NI];  // their offsets (kOOB when masked)
-  };
-  auto load_blk = [&](Blk& B, int blk) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tix = 16 * blk + RPI * i + lr;
-      const bool ok = blk < nblk && tix < tl.len && col_ok;
-      const int t = sh_tok[ok ? tix : 0];
-      B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * 4) : kOOB;
-      B.cv[i] = __builtin_bit_cast(f32x4_t, sload16(ry, B.yo[i]));
-    }
-  };
   auto walk = [&](auto nq_tag) {
     constexpr int NQ = decltype(nq_tag)::value;
+    struct Blk {
+      f32x4_t cv[NI];   // output rows (row-linear pieces)
+      uint32_t yo[NI];  // their offsets (kOOB when masked)
+      f32x4_t hv[NQ];   // the block's h values (MFMA operand rows)
+    };
+    // a block's output rows and its h values are loaded one block ahead of
+    // their use (h from L2: its latency would otherwise stall every block)
+    auto load_blk = [&](Blk& B, int blk) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int tix = 16 * blk + RPI * i + lr;
+        const bool ok = blk < nblk && tix < tl.len && col_ok;
+        const int t = sh_tok[ok ? tix : 0];
+        B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * 4) : kOOB;
+        B.cv[i] = __builtin_bit_cast(f32x4_t, sload16(ry, B.yo[i]));
+      }
+      const int tix = 16 * blk + col;
+      const bool tok_ok = blk < nblk && tix < tl.len;
+      const int t = sh_tok[tok_ok ? tix : 0];
+      const uint32_t hbase = static_cast<uint32_t>(((int64_t)t * p.hs0 + (int64_t)slice * p.hs1) * 4);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int j = 16 * q + 4 * grp;
+        B.hv[q] = __builtin_bit_cast(f32x4_t, bload16(rh, (tok_ok && j < rho) ? hbase + j * 4 : kOOB));
+      }
+    };
     // a block past the last loads nothing and stores nothing (every offset
     // is masked), so it needs no branch around it
     auto comp_blk = [&](Blk& B, int blk) {
@@ -1354,15 +1366,11 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
       int lz;
       asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
       const wf_t* wl = wls + lz;
-      const int tix = 16 * blk + col;
-      const bool tok_ok = tix < tl.len;
-      const int t = sh_tok[tok_ok ? tix : 0];
-      const uint32_t hbase = static_cast<uint32_t>(((int64_t)t * p.hs0 + (int64_t)slice * p.hs1) * 4);
       uint4 hf[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int j = 16 * q + 4 * grp;
-        f32x4_t v = __builtin_bit_cast(f32x4_t, bload16(rh, (tok_ok && j < rho) ? hbase + j * 4 : kOOB));
+        f32x4_t v = B.hv[q];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (j + e < rho) ? v[e] : 0.f;  // padding may hold NaN
         v *= sc;
