@@ -472,7 +472,21 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
   constexpr int ES = sizeof(E);
   constexpr int CH = 4 * VEC;  // features per MFMA step
   constexpr int TB = 16 * BMB;
-  __shared__ f32x4_t red[4][BMB * RB][64];
+  // bf16: x rows and adapter rows loaded row-linearly (whole row segments of
+  // the stage per instruction) into a per-wave LDS tile (rows padded by 16
+  // bytes), fragments read back conflict-free; the tiles share their memory
+  // with the partial sums (one barrier after the feature loop)
+  constexpr bool LIN = ES == 2;
+  constexpr int SROW = U * CH * ES;
+  constexpr int PITCH = SROW + 16;
+  constexpr int LPR = SROW / 16;
+  constexpr int RPI = LIN ? 64 / LPR : 16;
+  constexpr int ZN = LIN ? 16 * BMB / RPI : BMB;
+  constexpr int WN = LIN ? 16 * RB / RPI : RB;
+  constexpr int SBYTES = LIN ? 16 * (BMB + RB) * PITCH : 0;
+  constexpr int RBYTES = 4 * BMB * RB * 64 * 16;
+  __shared__ __attribute__((aligned(16))) char shr[4 * SBYTES > RBYTES ? 4 * SBYTES : RBYTES];
+  auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
 
@@ -526,6 +540,24 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
     aoff[q] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + grp * VEC) * ES) : kOOB;
   }
 
+  const int lpiece = lane % LPR;
+  const int lstep = lpiece >> 2;
+  const int lgrp = lpiece & 3;
+  uint32_t lx[LIN ? ZN : 1], la[LIN ? WN : 1];
+  if constexpr (LIN) {
+#pragma unroll
+    for (int i = 0; i < ZN; ++i) {
+      const int row = i * RPI + lane / LPR;
+      lx[i] = row < tl.len ? static_cast<uint32_t>(((int64_t)sh_tok[row] * p.ldx + lgrp * VEC) * ES) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int j = j0 + i * RPI + lane / LPR;
+      la[i] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + lgrp * VEC) * ES) : kOOB;
+    }
+  }
+  char* stage = shr + wave * SBYTES;
+
   f32x4_t acc[BMB][RB];
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
@@ -537,32 +569,68 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
   const int cbeg = wave * per;
   const int cend = (cbeg + per < nch) ? cbeg + per : nch;
   const int K = static_cast<int>(p.K);
-  auto load = [&](uint4 (&xf)[U][BMB], uint4 (&af)[U][RB], int c) {
+  // LIN: xf[0] holds the stage's ZN row-linear x vectors, af[0] its WN
+  // adapter vectors; else [u][b] and [u][q] MFMA fragments
+  auto load = [&](uint4 (&xf)[U][ZN], uint4 (&af)[U][WN], int c) {
+    if constexpr (LIN) {
+      const int cc = c + lstep;
+      const bool kok = cc < cend && cc * CH + lgrp * VEC < K;
+      const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int cc = c + u;
-      const bool kok = cc < cend && cc * CH + grp * VEC < K;
-      const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);  // < x row bytes when kok
+      for (int i = 0; i < ZN; ++i) xf[0][i] = sload16(rx, (kok && lx[i] != kOOB) ? lx[i] + kb : kOOB);
 #pragma unroll
-      for (int b = 0; b < BMB; ++b) xf[u][b] = sload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
+      for (int i = 0; i < WN; ++i) af[0][i] = bload16(ra, (kok && la[i] != kOOB) ? la[i] + kb : kOOB);
+    } else {
 #pragma unroll
-      for (int q = 0; q < RB; ++q) af[u][q] = bload16(ra, (kok && aoff[q] != kOOB) ? aoff[q] + kb : kOOB);
+      for (int u = 0; u < U; ++u) {
+        const int cc = c + u;
+        const bool kok = cc < cend && cc * CH + grp * VEC < K;
+        const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);  // < x row bytes when kok
+#pragma unroll
+        for (int b = 0; b < BMB; ++b) xf[u][b] = sload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
+#pragma unroll
+        for (int q = 0; q < RB; ++q) af[u][q] = bload16(ra, (kok && aoff[q] != kOOB) ? aoff[q] + kb : kOOB);
+      }
     }
   };
-  auto mma = [&](const uint4 (&xf)[U][BMB], const uint4 (&af)[U][RB]) {
+  auto mma = [&](const uint4 (&xf)[U][ZN], const uint4 (&af)[U][WN]) {
+    if constexpr (LIN) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int i = 0; i < ZN; ++i)
+        *reinterpret_cast<uint4*>(stage + (i * RPI + lane / LPR) * PITCH + lpiece * 16) = xf[0][i];
 #pragma unroll
-      for (int b = 0; b < BMB; ++b)
-        if (bany[b]) {
+      for (int i = 0; i < WN; ++i)
+        *reinterpret_cast<uint4*>(stage + (16 * BMB + i * RPI + lane / LPR) * PITCH + lpiece * 16) = af[0][i];
+      uint4 w[U][RB];
 #pragma unroll
-          for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], af[u][q], xf[u][b]);
-        }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < RB; ++q)
+          w[u][q] = *reinterpret_cast<const uint4*>(stage + (16 * (BMB + q) + col) * PITCH + (u * 4 + grp) * 16);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < BMB; ++b)
+          if (bany[b]) {
+            const uint4 z = *reinterpret_cast<const uint4*>(stage + (16 * b + col) * PITCH + (u * 4 + grp) * 16);
+#pragma unroll
+            for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], w[u][q], z);
+          }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < BMB; ++b)
+          if (bany[b]) {
+#pragma unroll
+            for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], af[u][q], xf[u][b]);
+          }
+    }
   };
   // two register stages; the loop body has no exit in the middle (an odd
   // stage count ends with a stage of zeros)
   {
-    uint4 xA[U][BMB], aA[U][RB], xB[U][BMB], aB[U][RB];
+    uint4 xA[U][ZN], aA[U][WN], xB[U][ZN], aB[U][WN];
     if (cbeg < cend) {
       load(xA, aA, cbeg);
       for (int c = cbeg; c < cend; c += 2 * U) {
@@ -577,6 +645,7 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
       }
     }
   }
+  if constexpr (LIN) __syncthreads();  // the staging tiles share their memory with the partial sums
 
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
