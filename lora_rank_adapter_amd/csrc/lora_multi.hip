@@ -836,7 +836,7 @@ constexpr int kRowsGroup = 4;
 template <int TT, int U, int NP>
 __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile& tl, int rho, rsrc_t rx, rsrc_t ra,
                                                  const uint32_t (&xoff)[TT * U / 4], const bool (&bany)[TT],
-                                                 const uint32_t (&aoff)[4], const int (&psl)[4], const int (&pj)[4],
+                                                 const int (&psl)[4], const int (&pj)[4],
                                                  const int* tok, char* lds, char* alds) {
   constexpr int XV = TT * U / 4;     // x vectors per thread per stage
   constexpr int NA = NP * U;         // adapter vectors per lane and stage (row-linear)
@@ -981,7 +981,6 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
-  const int col = lane & 15;
   // workgroup -> (tile, row group): ids go round-robin over the 8 XCDs
   const int rgs = p.row_groups;
   const int kx = static_cast<int>(blockIdx.x >> 3);
@@ -1023,26 +1022,21 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   bool bany[TT];
 #pragma unroll
   for (int b = 0; b < TT; ++b) bany[b] = 16 * b < tl.len;
-  uint32_t aoff[4];
+  // this wave's pairs: slice and first rank row (rows at or past rho read 0)
   int psl[4], pj[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int pg = pbeg + wave + 4 * i;
     const int sl = pg / nq;
-    const int q = pg - sl * nq;
-    const int j = 16 * q + col;
     psl[i] = sl;
-    pj[i] = 16 * q;
-    aoff[i] = (i < npw && j < rho)
-                  ? static_cast<uint32_t>(((int64_t)(sl * p.r_max + j) * p.as1 + (lane >> 4) * 8) * 2)
-                  : kOOB;
+    pj[i] = 16 * (pg - sl * nq);
   }
   switch (npw) {
-    case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
-    case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
-    case 2: shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
-    case 3: shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
-    default: shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, aoff, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 2: shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 3: shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    default: shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
   }
 }
 
