@@ -11,14 +11,18 @@
 // Kernels:
 //   fused_kernel  one workgroup owns 16*BMB tokens: it contracts the streamed
 //                 operand Z (X or dY) with the first weight W1 over all of Z's
-//                 features (the four waves split the feature axis, MFMA
-//                 partial sums are reduced through LDS in a fixed order), so
-//                 the rank-r intermediate H exists only in registers/LDS; then
-//                 every wave holds s*H as bf16 hi+lo MFMA operands and the
-//                 waves walk the output columns together, multiplying by the
-//                 second weight W2 and adding into (or overwriting) the
-//                 output with 128-bit accesses. Optionally it also writes s*H
-//                 (transposed, hi/lo planes) for the weight-gradient kernels.
+//                 features (the four waves split the feature axis; bf16 rows
+//                 of Z and W1 are loaded row-linearly into a per-wave LDS tile
+//                 and read back as MFMA fragments; partial sums are reduced
+//                 through LDS in a fixed order), so the rank-r intermediate H
+//                 exists only in registers/LDS; then every wave holds s*H as
+//                 bf16 hi+lo MFMA operands and the waves walk the output
+//                 columns together, multiplying by the second weight W2 and
+//                 adding into (or overwriting) the output, whose row segments
+//                 are read and written row-linearly through a per-wave LDS
+//                 tile. Optionally it also writes s*H (transposed, hi/lo
+//                 planes) for the weight-gradient kernels. Streamed tensors
+//                 are loaded and stored with the non-temporal cache policy.
 //   shrink_kernel the same shrink alone, writing s*H as gradient planes and/or
 //                 MFMA fragments for the split expands below.
 //   expand_cols_kernel  column-owner expand (outputs wider than 8192 or long
