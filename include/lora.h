@@ -259,6 +259,25 @@ int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing*
                       int32_t r_max, void* stream);
 
 /*
+ * Multi-adapter linear target (LoraOpsBackend.apply_linear_: shrink then
+ * expand into y, for a linear target; the page lets a backend fuse them):
+ *   x, a       as for lora_shrink.
+ *   b, scalings, y, out_slices
+ *              as for lora_expand_fused (num_slices = number of out_slices).
+ *   h          T x num_slices x r_max float32 WORKSPACE owned by the caller,
+ *              with the layout rules of both calls; it receives the rank
+ *              intermediate (entries of inactive tokens and past a slot's
+ *              rank are left as they were).
+ *   y[t, slice i] += scalings[slot(t)] * (x[t] @ a[s, slice i]^T) @ b[s, slice i]^T
+ *   for active t on slot s (ranks as in the two calls). Runs the shrink and
+ *   the expand back to back on the stream. The arguments of both are checked
+ *   before either launches: a failing call launches nothing.
+ */
+int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora_t3* b, const lora_addressing* addr,
+                      const int32_t* ranks, const float* scalings, const lora_mat* y, const int64_t* out_slices,
+                      int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream);
+
+/*
  * Multi-adapter one-hot shrink (LoraOpsBackend.gather_shrink:
  * h[t] = a[slot(t)][:, ids[t]], the shrink of a token's one-hot):
  *   ids  int32[T] device.

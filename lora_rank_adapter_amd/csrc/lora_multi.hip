@@ -1625,8 +1625,9 @@ extern "C" int lora_addressing_build(const lora_addressing* addr, const int32_t*
   return launch_status();
 }
 
-extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
-                           int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream) {
+// Host-side argument checks of lora_shrink (status; nothing is launched).
+static int shrink_checks(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
+                         int32_t num_slices, int32_t r_max, const lora_t3* h) {
   if (!x || !a || !h) return LORA_ERR_NULL;
   int rc = check_addressing(addr, ranks);
   if (rc != LORA_OK) return rc;
@@ -1644,6 +1645,15 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   if (a->s2 != 1 || (a->s1 * (int64_t)es) % 16 != 0 || (a->s0 * (int64_t)es) % 16 != 0 || !aligned(a->ptr, 16))
     return LORA_ERR_STRIDE;
   if (h->s2 != 1) return LORA_ERR_STRIDE;
+  return LORA_OK;
+}
+
+extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
+                           int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream) {
+  const int rc = shrink_checks(x, a, addr, ranks, num_slices, r_max, h);
+  if (rc != LORA_OK) return rc;
+  const int64_t T = addr->T, S = addr->S, K = x->cols;
+  const size_t es = elem_size(x->dtype);
   if (T == 0 || S == 0) return LORA_OK;
   const int bmb = tile_bmb(static_cast<int>(T));
   const int rb = (T >= 1024) ? 4 : 1;
@@ -1707,9 +1717,11 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   return launch_status();
 }
 
-extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing* addr,
-                                 const int32_t* ranks, const float* scalings, const lora_mat* y,
-                                 const int64_t* out_slices, int32_t num_slices, int32_t r_max, void* stream) {
+// Host-side argument checks of lora_expand_fused (status; nothing is
+// launched); *O_out = sum of the slice widths.
+static int expand_checks(const lora_t3* h, const lora_t3* b, const lora_addressing* addr, const int32_t* ranks,
+                         const float* scalings, const lora_mat* y, const int64_t* out_slices, int32_t num_slices,
+                         int32_t r_max, int64_t* O_out) {
   if (!h || !b || !y || !out_slices) return LORA_ERR_NULL;
   int rc = check_addressing(addr, ranks);
   if (rc != LORA_OK) return rc;
@@ -1727,9 +1739,20 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   if (h->dtype != LORA_F32 || !float_dtype_ok(b->dtype) || y->dtype != LORA_F32) return LORA_ERR_DTYPE;
   if ((T > 0 && !h->ptr) || (S * O > 0 && !b->ptr) || (T * O > 0 && !y->ptr) || (S > 0 && !scalings))
     return LORA_ERR_NULL;
-  const size_t es = elem_size(b->dtype);
   if (h->s2 != 1 || b->s2 != 1) return LORA_ERR_STRIDE;
   if (T * O > 0 && check_rowmajor_stream(y) != LORA_OK) return LORA_ERR_STRIDE;
+  *O_out = O;
+  return LORA_OK;
+}
+
+extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing* addr,
+                                 const int32_t* ranks, const float* scalings, const lora_mat* y,
+                                 const int64_t* out_slices, int32_t num_slices, int32_t r_max, void* stream) {
+  int64_t O = 0;
+  const int rc = expand_checks(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, &O);
+  if (rc != LORA_OK) return rc;
+  const int64_t T = addr->T, S = addr->S;
+  const size_t es = elem_size(b->dtype);
   if (T == 0 || S == 0 || O == 0) return LORA_OK;
   ExpandArgs p{};
   p.h = static_cast<const float*>(h->ptr);
@@ -1829,6 +1852,23 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   else
     launch_expand<F32>(p, bmb, rbm, tiles, st);
   return launch_status();
+}
+
+// LoraOpsBackend.apply_linear_: the shrink into the caller's h, then the
+// expand into y, on one stream. Both operations' arguments are checked
+// before either launches.
+extern "C" int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora_t3* b, const lora_addressing* addr,
+                                 const int32_t* ranks, const float* scalings, const lora_mat* y,
+                                 const int64_t* out_slices, int32_t num_slices, int32_t r_max, const lora_t3* h,
+                                 void* stream) {
+  int rc = shrink_checks(x, a, addr, ranks, num_slices, r_max, h);
+  if (rc != LORA_OK) return rc;
+  int64_t O = 0;
+  rc = expand_checks(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, &O);
+  if (rc != LORA_OK) return rc;
+  rc = lora_shrink(x, a, addr, ranks, num_slices, r_max, h, stream);
+  if (rc != LORA_OK) return rc;
+  return lora_expand_fused(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, stream);
 }
 
 extern "C" int lora_gather_shrink(const int32_t* ids, const lora_t3* a, const lora_addressing* addr,

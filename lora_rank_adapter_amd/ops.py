@@ -173,6 +173,22 @@ def lora_expand_fused(h: torch.Tensor, b: torch.Tensor, addr: Addressing, ranks:
     return y
 
 
+def lora_apply_linear(x: torch.Tensor, y: torch.Tensor, a: torch.Tensor, b: torch.Tensor, addr: Addressing,
+                      ranks: torch.Tensor, scalings: torch.Tensor, out_slices, r_max: int,
+                      h: torch.Tensor | None = None) -> torch.Tensor:
+    """y[t, slice i] += scalings[slot(t)] * (x[t] @ a[slot(t), slice i]^T) @ b[slot(t), slice i]^T, in place
+    (shrink then expand; h [T x num_slices x r_max] float32 is the rank intermediate's workspace). Returns y."""
+    lib = _lib.load()
+    n = len(out_slices)
+    if h is None:
+        h = torch.empty((x.shape[0], n, r_max), dtype=torch.float32, device=x.device)
+    sl = (ctypes.c_int64 * n)(*[int(v) for v in out_slices])
+    check("lora_apply_linear", lib.lora_apply_linear(
+        ctypes.byref(mat(x)), ctypes.byref(t3(a)), ctypes.byref(t3(b)), ctypes.byref(addr.struct()), _ptr(ranks),
+        _ptr(scalings), ctypes.byref(mat(y)), sl, n, int(r_max), ctypes.byref(t3(h)), _stream(x.device)))
+    return y
+
+
 def lora_gather_shrink(ids: torch.Tensor, a: torch.Tensor, addr: Addressing, ranks: torch.Tensor, r_max: int,
                        h: torch.Tensor | None = None) -> torch.Tensor:
     """h[t, 0, j] = a[slot(t), j, ids[t]] for j < rank (+0.0 for ids outside [0, V)). Returns h [T x 1 x r_max]."""

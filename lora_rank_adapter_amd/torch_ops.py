@@ -97,10 +97,8 @@ def _(h, b, token_slot, counts, offsets, sorted_tokens, ranks, scalings, y, out_
 def apply_(x: torch.Tensor, y: torch.Tensor, a: torch.Tensor, b: torch.Tensor, token_slot: torch.Tensor,
            counts: torch.Tensor, offsets: torch.Tensor, sorted_tokens: torch.Tensor, ranks: torch.Tensor,
            scalings: torch.Tensor, out_slices: list[int], r_max: int) -> None:
-    addr = _addr(token_slot, counts, offsets, sorted_tokens)
-    h = torch.empty((x.shape[0], len(out_slices), r_max), dtype=torch.float32, device=x.device)
-    ops.lora_shrink(x, a, addr, ranks, len(out_slices), r_max, h=h)
-    ops.lora_expand_fused(h, b, addr, ranks, scalings, y, out_slices, r_max)
+    ops.lora_apply_linear(x, y, a, b, _addr(token_slot, counts, offsets, sorted_tokens), ranks, scalings,
+                          out_slices, r_max)
 
 
 @apply_.register_fake

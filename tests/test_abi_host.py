@@ -182,6 +182,17 @@ def test_multi_validation(lib):
     assert expand(y_=m(T, 48, dtype=1)) == -3
     assert expand(h_=LoraT3(FAKE, 0, 0, T, 2, r_max, 2 * r_max, 1, 2)) == -4      # rank index not contiguous
 
+    def apply(x_=x, y_=y, h_=h, slices=sl, n=2):
+        return lib.lora_apply_linear(ctypes.byref(x_), ctypes.byref(a), ctypes.byref(b), ctypes.byref(addr),
+                                     ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.byref(y_), slices, n, r_max,
+                                     ctypes.byref(h_), None)
+
+    # the shrink's and the expand's checks both run before any launch
+    assert apply(h_=LoraT3(FAKE, 1, 0, T, 2, r_max, 2 * r_max, r_max, 1)) == -3       # h must be float32
+    assert apply(slices=(ctypes.c_int64 * 2)(32, 20)) == -2                            # expand: widths vs y
+    assert apply(y_=m(T, 48, dtype=1)) == -3                                           # expand: y float32
+    assert apply(x_=m(T, K + 8)) == -2                                                 # shrink: x vs a
+
     ah = LoraT3(FAKE, 1, 0, S, r_max, 1000, r_max * 1000, 1000, 1)
     h1 = LoraT3(FAKE, 0, 0, T, 1, r_max, r_max, r_max, 1)
     assert lib.lora_gather_shrink(None, ctypes.byref(ah), ctypes.byref(addr), ctypes.c_void_p(FAKE), r_max,

@@ -228,6 +228,30 @@ def test_shrink_then_expand(case):
     assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
 
 
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_apply_linear(case):
+    """lora_apply_linear (shrink then expand in one call, h as the caller's
+    workspace) gives the bits of the two separate calls and the oracle's
+    apply_linear within tolerance; inactive rows stay bitwise untouched."""
+    m = _case(*case)
+    dtype = case[-1]
+    note(f"apply_linear {case[0]}")
+    addr, ranks = _addr(m)
+    x, a, b, sc = dev(m.x, dtype), dev(m.a, dtype), dev(m.b, dtype), f32(m.scalings)
+    h_ref = L.lora_shrink(x, a, addr, ranks, m.num_slices, m.r_max)
+    y_ref = f32(m.y0)
+    L.lora_expand_fused(h_ref, b, addr, ranks, sc, y_ref, m.out_slices, m.r_max)
+    y = f32(m.y0)
+    L.lora_apply_linear(x, y, a, b, addr, ranks, sc, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert same_bits(got, host(y_ref))
+    want = oracle.apply_linear(m.x, m.y0, m.a, m.b, m.token_slot, m.ranks, m.scalings, m.out_slices, m.r_max)
+    act, _ = _spec_mask(m)
+    assert same_bits(got[~act], m.y0[~act])
+    assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_integer_exact_bitwise(dtype):
     note(f"multi integer-exact {dtype}")
