@@ -1060,6 +1060,8 @@ struct ExpandArgs {
   int64_t chunk_cols;  // columns per chunk (streaming kernel)
   int64_t y_bytes;     // bytes of y a descriptor may span (streaming and owner kernels)
   int64_t h_bytes;     // bytes of h a descriptor may span (owner kernel)
+  int xcd_group;       // owner kernel: consecutive work items per XCD group
+  int n_work;          // owner kernel: pieces x total_chunks work items
   bool h_vec;  // h rows 16-byte aligned
   bool b_vec;  // b rows aligned for 4-element loads
   int64_t slice_off[kMaxSlices];
@@ -1323,6 +1325,7 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
 // block.
 constexpr int kOwnerTokens = 1024;
 constexpr int kOwnerCols = 128;
+constexpr int kOwnerGroup = 4;  // consecutive work items per XCD group
 
 template <class Tag, int RBM>
 __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
@@ -1341,8 +1344,17 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int pi = blockIdx.x / p.total_chunks;
-  const int ch = blockIdx.x - pi * p.total_chunks;
+  // workgroup -> work item (piece, chunk): ids go round-robin over the 8
+  // XCDs; the k-th workgroup of XCD x takes item ((k / G) * 8 + x) * G + k % G,
+  // so G consecutive chunks of a piece (which read the same h rows) share an
+  // XCD's L2. A bijection onto [0, gridDim.x); the grid is padded to a
+  // multiple of 8 G and the items past n_work exit.
+  const int G = p.xcd_group;
+  const int kx = static_cast<int>(blockIdx.x >> 3);
+  const int item = ((kx / G) * 8 + static_cast<int>(blockIdx.x & 7)) * G + kx % G;
+  if (item >= p.n_work) return;
+  const int pi = item / p.total_chunks;
+  const int ch = item - pi * p.total_chunks;
   int slice = 0;
   while (slice + 1 < p.n_slices && ch >= p.chunk_begin[slice + 1]) ++slice;
   const int64_t width = p.slice_w[slice];
@@ -1583,7 +1595,8 @@ static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream
 
 template <class Tag>
 static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(pieces * a.total_chunks));
+  a.n_work = static_cast<int>(pieces * a.total_chunks);
+  const dim3 grid(static_cast<unsigned>(a.xcd_group == 1 ? a.n_work : round_up(a.n_work, 8 * a.xcd_group)));
   switch (rbm) {
     case 1: launch((slot_expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
     case 2: launch((slot_expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
@@ -1800,6 +1813,8 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
     p.y_bytes = T * y->stride_row * 4;
     p.h_bytes = T * h->s0 * 4;
     const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
+    const int64_t grp = env_int("LORA_OWNER_GROUP", 0);
+    p.xcd_group = grp >= 1 && grp <= 128 ? static_cast<int>(grp) : kOwnerGroup;
     if (b->dtype == LORA_BF16)
       launch_expand_owner<BF16>(p, rbm, pieces, st);
     else

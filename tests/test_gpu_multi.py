@@ -211,6 +211,28 @@ def test_expand_schedules_integer_exact(mode, monkeypatch):
     assert same_bits(host(y), want.astype(np.float32))
 
 
+@pytest.mark.parametrize("group", [1, 3, 4, 16])
+def test_expand_owner_xcd_groups_integer_exact(group, monkeypatch):
+    """The column-owner expand maps workgroups to (token piece, column chunk)
+    items in XCD groups of any size; the grid is padded to a multiple of 8
+    groups and the padding exits. Every group size must give the exact
+    result (14 pieces x 5 chunks: no size here divides the item count)."""
+    monkeypatch.setenv("LORA_MULTI_EXPAND", "2")
+    monkeypatch.setenv("LORA_OWNER_GROUP", str(group))
+    note(f"owner expand, XCD group {group}")
+    m = _case("prefill-like", 0, 96, (384, 128, 64), 12, 32, (8, 16, 32), 0.0, "bf16", seed=4, int_exact=True)
+    addr, ranks = _addr(m)
+    act, spec = _spec_mask(m)
+    rng = np.random.default_rng(10)
+    hin = rng.integers(-2, 3, size=(m.T, m.num_slices, m.r_max)).astype(np.float32)
+    hin[~spec] = np.nan
+    y = f32(m.y0)
+    L.lora_expand_fused(f32(hin), dev(m.b, "bf16"), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    want = oracle.expand_fused(hin, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max)
+    assert same_bits(host(y), want.astype(np.float32))
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_shrink_then_expand(case):
     m = _case(*case)
