@@ -25,7 +25,8 @@
 //                              256 adapter rows (all slices) per workgroup, x
 //                              staged once in LDS, waves split the rows
 //   slot_expand_owner_kernel   expand for many tokens: a token piece x column
-//                              chunk per workgroup, weights staged once in LDS
+//                              chunk per workgroup, weights staged once in LDS,
+//                              a piece's chunks grouped per XCD
 //   slot_expand_stream_kernel  expand for few tokens: tile x column chunk,
 //                              weights from L2, two stages of outputs in flight
 //   slot_expand_kernel         expand for any layout (unaligned rows, y or b
