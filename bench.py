@@ -75,7 +75,7 @@ def algorithmic_bytes(M, K, L, r, es=2):
     fwd = M * (es * K + 8 * L) + es * r * (K + L)
     dxda = M * (es * L + 4 * K + es * K) + es * r * (K + L) + 4 * K * r
     db = M * (es * K + es * L) + es * r * K + 4 * r * L
-    return {"fwd": fwd, "dx_da": dxda, "db": db}
+    return {"fwd": fwd, "dx_da": dxda, "db": db, "dx_da_accumulate": dxda + 4 * M * K}
 
 
 def source_digest(paths):
@@ -391,6 +391,8 @@ def main():
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # events for the timed forward launches exist before the timed region
+    L.lora_timing_reserve(4 * args.steps)
     L.lora_timing_begin()
     L.lora_timing_pause()
     t_begin.record()
@@ -410,6 +412,16 @@ def main():
     fwd_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evb)
     dxda_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evb)
     db_ms = statistics.median(e[2].elapsed_time(e[3]) for e in evb)
+    # the accumulating variant of lora_bwd_dx_da (dX added to the base layer's
+    # gradient), outside the step: events around each call on the same sets
+    eva = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    for i in range(10):
+        s_ = sets[i % n_sets]
+        eva[i][0].record()
+        L.lora_bwd_dx_da_accumulate(s_["X"].t(), s_["dY"], B_w, A_w, scale, s_["dX"], dA=dA, workspace=ws1)
+        eva[i][1].record()
+    torch.cuda.synchronize()
+    dxda_acc_ms = statistics.median(e[0].elapsed_time(e[1]) for e in eva)
 
     if args.copy_probe:
         src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
@@ -443,11 +455,13 @@ def main():
                    "scale": scale, "outputs": "fp32", "rotating_input_sets": n_sets},
         "hbm_gbs": step_gbs,
         "hbm_frac": step_gbs / HBM_PEAK_GBS,
-        "per_call_ms": {"lora_fwd": fwd_ms, "lora_bwd_dx_da": dxda_ms, "lora_bwd_db": db_ms},
+        "per_call_ms": {"lora_fwd": fwd_ms, "lora_bwd_dx_da": dxda_ms, "lora_bwd_db": db_ms,
+                        "lora_bwd_dx_da_accumulate": dxda_acc_ms},
         "per_call_algorithmic_gbs": {
             "lora_fwd": fwd_gbs,
             "lora_bwd_dx_da": ab["dx_da"] / (dxda_ms * 1e-3) / 1e9,
             "lora_bwd_db": ab["db"] / (db_ms * 1e-3) / 1e9,
+            "lora_bwd_dx_da_accumulate": ab["dx_da_accumulate"] / (dxda_acc_ms * 1e-3) / 1e9,
         },
         "roofline": {
             "kernel": " + ".join(ROOFLINE_KERNEL[args.workload]) + " (lora_fwd)",

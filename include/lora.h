@@ -125,6 +125,10 @@ int lora_abi_version(void);
  *   lora_timing_read    waits for every recorded kernel to finish and returns
  *                       the sum of their durations (ms) and their number;
  *                       -1 for NULL outputs, -7 if an event query fails.
+ *   lora_timing_reserve creates event pairs up front until `pairs` exist (on
+ *                       the current device), so that timed launches reuse
+ *                       them instead of creating events while being timed;
+ *                       -2 for a negative count, -7 if creation fails.
  * The state is process-wide: launches from any thread or stream while
  * recording are included. Events are created (once, then reused) on the
  * device current at the first timed launch, so one recording session must
@@ -135,6 +139,7 @@ int lora_timing_begin(void);
 int lora_timing_pause(void);
 int lora_timing_resume(void);
 int lora_timing_read(double* total_ms, int64_t* launches);
+int lora_timing_reserve(int64_t pairs);
 
 /* Static text for a status code. */
 const char* lora_status_string(int status);
@@ -197,6 +202,20 @@ int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_mat* lora_B, 
 int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B, const lora_mat* lora_A,
                    float scale, const lora_mat* dx, const lora_mat* dA, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * lora_bwd_dx_da with dx accumulated instead of overwritten (the page's
+ * wrapper takes a dtype for its outputs and leaves open whether dx is a fresh
+ * buffer; a training step usually adds the adapter's input gradient to the
+ * base layer's, which this does without a separate add over M x K):
+ *   dx += scale * (dy @ lora_B) @ lora_A, every element read once and written
+ *   once (float32 add of the float32 product); dA is overwritten as in
+ *   lora_bwd_dx_da. Same arguments, layouts, workspace and errors; with M or
+ *   L zero dx is left unchanged and dA set to zero.
+ */
+int lora_bwd_dx_da_accumulate(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B,
+                              const lora_mat* lora_A, float scale, const lora_mat* dx, const lora_mat* dA,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Single-adapter backward for lora_B (lora_db_kernel: AXT = A x X^T;

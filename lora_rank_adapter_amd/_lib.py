@@ -80,6 +80,9 @@ SIGNATURES = {
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "lora_bwd_dx_da": (ctypes.c_int, [_P(LoraMat), _P(LoraMat), _P(LoraMat), _P(LoraMat), ctypes.c_float,
                                       _P(LoraMat), _P(LoraMat), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "lora_bwd_dx_da_accumulate": (ctypes.c_int, [_P(LoraMat), _P(LoraMat), _P(LoraMat), _P(LoraMat),
+                                                 ctypes.c_float, _P(LoraMat), _P(LoraMat), ctypes.c_void_p,
+                                                 ctypes.c_size_t, ctypes.c_void_p]),
     "lora_bwd_db": (ctypes.c_int, [_P(LoraMat), _P(LoraMat), _P(LoraMat), ctypes.c_float, _P(LoraMat),
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "lora_addressing_build": (ctypes.c_int, [_P(LoraAddressing), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
@@ -97,6 +100,7 @@ SIGNATURES = {
     "lora_timing_pause": (ctypes.c_int, []),
     "lora_timing_resume": (ctypes.c_int, []),
     "lora_timing_read": (ctypes.c_int, [_P(ctypes.c_double), _P(ctypes.c_int64)]),
+    "lora_timing_reserve": (ctypes.c_int, [ctypes.c_int64]),
 }
 
 _lock = threading.Lock()

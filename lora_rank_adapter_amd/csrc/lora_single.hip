@@ -1626,6 +1626,21 @@ extern "C" int lora_timing_begin(void) {
   return LORA_OK;
 }
 
+extern "C" int lora_timing_reserve(int64_t pairs) {
+  if (pairs < 0) return LORA_ERR_SHAPE;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  while (static_cast<int64_t>(g_timing_events.size()) < pairs) {
+    EventPair e{};
+    if (hipEventCreate(&e.start) != hipSuccess) return LORA_ERR_LAUNCH;
+    if (hipEventCreate(&e.stop) != hipSuccess) {
+      (void)hipEventDestroy(e.start);
+      return LORA_ERR_LAUNCH;
+    }
+    g_timing_events.push_back(e);
+  }
+  return LORA_OK;
+}
+
 extern "C" int lora_timing_pause(void) {
   g_timing_on.store(false);
   return LORA_OK;
@@ -1751,9 +1766,10 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   return launch_status();
 }
 
-extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B, const lora_mat* lora_A,
-                              float scale, const lora_mat* dx, const lora_mat* dA, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+// dX overwritten (accumulate = false) or added to (true); dA always overwritten.
+static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B, const lora_mat* lora_A,
+                     float scale, const lora_mat* dx, const lora_mat* dA, void* workspace, size_t workspace_bytes,
+                     void* stream, bool accumulate) {
   if (!xt || !dy || !lora_B || !lora_A || !dx || !dA) return LORA_ERR_NULL;
   if (!valid_dims(xt) || !valid_dims(dy) || !valid_dims(lora_B) || !valid_dims(lora_A) || !valid_dims(dx) ||
       !valid_dims(dA))
@@ -1777,7 +1793,7 @@ extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (K == 0) return LORA_OK;
   if (M == 0 || L == 0) {
-    launch_fill_zero(dx, st);
+    if (!accumulate) launch_fill_zero(dx, st);
     launch_fill_zero(dA, st);
     return launch_status();
   }
@@ -1833,15 +1849,33 @@ extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora
   t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
   if (xt->dtype == LORA_BF16) {
-    run_shrink_expand<BF16, false, true>(a, rb, st);
+    if (accumulate)
+      run_shrink_expand<BF16, true, true>(a, rb, st);
+    else
+      run_shrink_expand<BF16, false, true>(a, rb, st);
     launch_tn<BF16>(t, rb, st);
   } else {
-    run_shrink_expand<F32, false, true>(a, rb, st);
+    if (accumulate)
+      run_shrink_expand<F32, true, true>(a, rb, st);
+    else
+      run_shrink_expand<F32, false, true>(a, rb, st);
     launch_tn<F32>(t, rb, st);
   }
   launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dA->ptr), dA->stride_row,
                 dA->stride_col, st);
   return launch_status();
+}
+
+extern "C" int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B, const lora_mat* lora_A,
+                              float scale, const lora_mat* dx, const lora_mat* dA, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return bwd_dx_da(xt, dy, lora_B, lora_A, scale, dx, dA, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int lora_bwd_dx_da_accumulate(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B,
+                                         const lora_mat* lora_A, float scale, const lora_mat* dx, const lora_mat* dA,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_dx_da(xt, dy, lora_B, lora_A, scale, dx, dA, workspace, workspace_bytes, stream, true);
 }
 
 extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lora_mat* dy, float scale,

@@ -37,7 +37,14 @@ def t3(t: torch.Tensor) -> LoraT3:
                   t.stride(0), t.stride(1), t.stride(2))
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device):
+    """torch's current stream on `device` as a raw pointer."""
+    if _raw_stream is not None:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        return ctypes.c_void_p(_raw_stream(idx))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -50,8 +57,9 @@ def lora_workspace_bytes(op: int, M: int, K: int, L: int, r: int, dtype: torch.d
 
 
 def _workspace(op, M, K, L, r, dtype, device, workspace):
-    need = lora_workspace_bytes(op, M, K, L, r, dtype)
+    # a caller's workspace is passed with its size; the library checks it
     if workspace is None:
+        need = lora_workspace_bytes(op, M, K, L, r, dtype)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return workspace, workspace.numel()
 
@@ -89,6 +97,25 @@ def lora_bwd_dx_da(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lor
         dA = torch.empty((K, r), dtype=torch.float32, device=dy.device)
     ws, nbytes = _workspace(_lib.LORA_OP_BWD_DX_DA, M, K, L, r, dy.dtype, dy.device, workspace)
     check("lora_bwd_dx_da", lib.lora_bwd_dx_da(
+        ctypes.byref(mat(xt)), ctypes.byref(mat(dy)), ctypes.byref(mat(lora_B)), ctypes.byref(mat(lora_A)),
+        float(scale), ctypes.byref(mat(dx)), ctypes.byref(mat(dA)), _ptr(ws), nbytes, _stream(dy.device)))
+    return dx, dA
+
+
+def lora_bwd_dx_da_accumulate(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lora_A: torch.Tensor,
+                              scale: float, dx: torch.Tensor, dA: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None):
+    """dx += scale * (dy @ lora_B) @ lora_A (dx: M x K float32, added to in
+    place); dA = scale * xt @ (dy @ lora_B) as in lora_bwd_dx_da.
+    Returns (dx, dA)."""
+    lib = _lib.load()
+    K, M = xt.shape
+    L = dy.shape[1]
+    r = lora_B.shape[1]
+    if dA is None:
+        dA = torch.empty((K, r), dtype=torch.float32, device=dy.device)
+    ws, nbytes = _workspace(_lib.LORA_OP_BWD_DX_DA, M, K, L, r, dy.dtype, dy.device, workspace)
+    check("lora_bwd_dx_da_accumulate", lib.lora_bwd_dx_da_accumulate(
         ctypes.byref(mat(xt)), ctypes.byref(mat(dy)), ctypes.byref(mat(lora_B)), ctypes.byref(mat(lora_A)),
         float(scale), ctypes.byref(mat(dx)), ctypes.byref(mat(dA)), _ptr(ws), nbytes, _stream(dy.device)))
     return dx, dA
@@ -214,6 +241,12 @@ def lora_timing_pause() -> None:
 def lora_timing_resume() -> None:
     """Record again, keeping the earlier records."""
     check("lora_timing_resume", _lib.load().lora_timing_resume())
+
+
+def lora_timing_reserve(pairs: int) -> None:
+    """Create event pairs up front (on the current device) so that timed
+    launches do not create events while being timed."""
+    check("lora_timing_reserve", _lib.load().lora_timing_reserve(int(pairs)))
 
 
 def lora_timing_read() -> tuple[float, int]:

@@ -124,18 +124,20 @@ def test_bwd_validation(lib):
     dB = m(r, L_, dtype=0)
     need = lib.lora_workspace_bytes(1, M, K, L_, r, 1)
 
-    def dxda(xt_=xt, dy_=dy, B_=Bw, A_=Aw, dx_=dx, dA_=dA, ws=FAKE, nb=need):
-        return lib.lora_bwd_dx_da(ctypes.byref(xt_), ctypes.byref(dy_), ctypes.byref(B_), ctypes.byref(A_), 1.0,
-                                  ctypes.byref(dx_), ctypes.byref(dA_), ctypes.c_void_p(ws) if ws else None, nb, None)
+    for fn in (lib.lora_bwd_dx_da, lib.lora_bwd_dx_da_accumulate):
+        def dxda(xt_=xt, dy_=dy, B_=Bw, A_=Aw, dx_=dx, dA_=dA, ws=FAKE, nb=need):
+            return fn(ctypes.byref(xt_), ctypes.byref(dy_), ctypes.byref(B_), ctypes.byref(A_), 1.0,
+                      ctypes.byref(dx_), ctypes.byref(dA_), ctypes.c_void_p(ws) if ws else None, nb, None)
 
-    assert dxda(ws=0) == -6
-    assert dxda(nb=need - 1) == -6
-    assert dxda(ws=FAKE + 64) == -6                           # workspace must be 256-byte aligned
-    assert dxda(xt_=m(K, M)) == -4                            # xt must be a view of row-major x
-    assert dxda(dy_=m(M, L_ + 8)) == -2
-    assert dxda(dA_=m(K, r, dtype=1)) == -3
-    assert dxda(B_=m(L_, 200), A_=m(200, K)) == -2             # dA shape disagrees with rank 200
-    assert dxda(B_=m(L_, 0), A_=m(0, K), dA_=m(K, 0, dtype=0)) == -5
+        assert dxda(ws=0) == -6
+        assert dxda(nb=need - 1) == -6
+        assert dxda(ws=FAKE + 64) == -6                       # workspace must be 256-byte aligned
+        assert dxda(xt_=m(K, M)) == -4                        # xt must be a view of row-major x
+        assert dxda(dy_=m(M, L_ + 8)) == -2
+        assert dxda(dA_=m(K, r, dtype=1)) == -3
+        assert dxda(dx_=m(M, K, dtype=1)) == -3               # dx is float32 (read and written when accumulating)
+        assert dxda(B_=m(L_, 200), A_=m(200, K)) == -2         # dA shape disagrees with rank 200
+        assert dxda(B_=m(L_, 0), A_=m(0, K), dA_=m(K, 0, dtype=0)) == -5
 
     def db(A_=Aw, xt_=xt, dy_=dy, dB_=dB, ws=FAKE, nb=lib.lora_workspace_bytes(2, M, K, L_, r, 1)):
         return lib.lora_bwd_db(ctypes.byref(A_), ctypes.byref(xt_), ctypes.byref(dy_), 1.0, ctypes.byref(dB_),

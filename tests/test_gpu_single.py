@@ -172,6 +172,59 @@ def test_kernel_timing_records_each_launch():
     assert L.lora_timing_read() == (0.0, 0)
 
 
+@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[5], CASES[7], CASES[8], CASES[9]], ids=_ids)
+def test_bwd_dx_accumulate(case):
+    """lora_bwd_dx_da_accumulate adds the input gradient into dx (a base
+    layer's gradient of the same scale) and overwrites dA: compared with the
+    oracle on the added delta, like the forward."""
+    M, K, L_, r, dtype, s = case
+    note(f"bwd dx accumulate {case}")
+    c = synth.single_adapter(M, K, L_, r, seed=300 + M, dtype=dtype, scale=s)
+    X, A_w, B_w, dY = _upload(c, dtype)
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    rms = float(np.sqrt(np.mean(odx * odx)))
+    dx0 = (np.random.default_rng(M).standard_normal((M, K)) * rms).astype(np.float32)
+    dx = f32(dx0)
+    out, dA = L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dx)
+    torch.cuda.synchronize()
+    assert out is dx
+    assert oracle.rel_frobenius(host(dx) - dx0, odx) <= tol(dtype)
+    assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_dx_accumulate_integer_exact(dtype):
+    """Integer inputs and an integer dx: every sum is exact, so dx must equal
+    dx0 + the oracle's dX bit for bit."""
+    note(f"bwd dx accumulate integer-exact {dtype}")
+    M, K, L_, r, s = 96, 256, 200, 16, 2.0
+    c = synth.single_adapter(M, K, L_, r, seed=32, dtype=dtype, scale=s, int_exact=True)
+    X, A_w, B_w, dY = _upload(c, dtype)
+    dx0 = np.random.default_rng(5).integers(-8, 9, size=(M, K)).astype(np.float32)
+    dx = f32(dx0)
+    _, dA = L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dx)
+    torch.cuda.synchronize()
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    assert same_bits(host(dx), (dx0 + odx).astype(np.float32))
+    assert same_bits(host(dA), odA.astype(np.float32))
+
+
+def test_bwd_dx_accumulate_empty_contraction():
+    """L = 0: nothing to add, dx keeps its bits; dA is zero."""
+    note("bwd dx accumulate, L = 0")
+    dv = torch.device("cuda:0")
+    bf = torch.bfloat16
+    x = torch.randn((24, 64), device=dv).to(bf)
+    a_w = torch.randn((8, 64), device=dv).to(bf)
+    b_w = torch.empty((0, 8), dtype=bf, device=dv)
+    dy = torch.empty((24, 0), dtype=bf, device=dv)
+    dx0 = torch.randn((24, 64), device=dv)
+    dx = dx0.clone()
+    _, dA = L.lora_bwd_dx_da_accumulate(x.t(), dy, b_w, a_w, 1.0, dx, dA=torch.full((64, 8), 7.0, device=dv))
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx0) and not dA.any()
+
+
 def test_empty_and_degenerate():
     note("empty")
     dv = torch.device("cuda:0")
@@ -240,7 +293,13 @@ def test_full_size_configs(cfg):
     dB = L.lora_bwd_db(A_w, X.t(), dY, c.scale)
     torch.cuda.synchronize()
     odx_rows, _ = oracle.lora_bwd_dx_da(c.X[rows].T, c.dY[rows], c.B.T, c.A.T, c.scale)
-    assert oracle.rel_frobenius(host(dx[torch.from_numpy(rows).to(X.device)]), odx_rows) <= tol(dtype)
+    rows_d = torch.from_numpy(rows).to(X.device)
+    assert oracle.rel_frobenius(host(dx[rows_d]), odx_rows) <= tol(dtype)
+    # the accumulating variant adds the same gradient once more
+    base = host(dx[rows_d])
+    L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, c.scale, dx, dA=torch.empty_like(dA))
+    torch.cuda.synchronize()
+    assert oracle.rel_frobenius(host(dx[rows_d]) - base, odx_rows) <= tol(dtype)
     # dA and dB contract over every token
     _, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, c.scale)
     assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
@@ -267,6 +326,11 @@ def test_every_schedule_matches_oracle(mode, monkeypatch):
         odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
         assert oracle.rel_frobenius(host(dx), odx) <= tol(dtype)
         assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
+        # the accumulating dX through the same schedule, added onto the result above
+        base = host(dx)
+        L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dx)
+        torch.cuda.synchronize()
+        assert oracle.rel_frobenius(host(dx) - base, odx) <= tol(dtype)
 
 
 @pytest.mark.parametrize("bmb", [1, 2, 4])
