@@ -18,6 +18,7 @@ Ops (the addressing arrays are passed as the tensors of lora_addressing):
   gather_shrink(ids, a, token_slot, counts, offsets, sorted_tokens, ranks, r_max) -> h
   lora_fwd_(x, lora_A, lora_B, res, scale)                 [res += scale * (x @ lora_A) @ lora_B]
   lora_bwd_dx_da(xt, dy, lora_B, lora_A, scale) -> (dx, dA)
+  lora_bwd_dx_da_accumulate_(xt, dy, lora_B, lora_A, scale, dx) -> dA  [dx += scale * (dy @ lora_B) @ lora_A]
   lora_bwd_db(lora_A, xt, dy, scale) -> dB
   lora_delta(x, A_w, B_w, scale) -> scale * (x @ A_w^T) @ B_w^T  (float32, differentiable)
 
@@ -143,6 +144,17 @@ def lora_bwd_dx_da(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lor
 def _(xt, dy, lora_B, lora_A, scale):
     K, M = xt.shape
     return dy.new_empty((M, K), dtype=torch.float32), dy.new_empty((K, lora_B.shape[1]), dtype=torch.float32)
+
+
+@torch.library.custom_op(f"{_NS}::lora_bwd_dx_da_accumulate_", mutates_args=("dx",), device_types="cuda")
+def lora_bwd_dx_da_accumulate_(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lora_A: torch.Tensor,
+                               scale: float, dx: torch.Tensor) -> torch.Tensor:
+    return ops.lora_bwd_dx_da_accumulate(xt, dy, lora_B, lora_A, scale, dx)[1]
+
+
+@lora_bwd_dx_da_accumulate_.register_fake
+def _(xt, dy, lora_B, lora_A, scale, dx):
+    return dy.new_empty((xt.shape[0], lora_B.shape[1]), dtype=torch.float32)
 
 
 @torch.library.custom_op(f"{_NS}::lora_bwd_db", mutates_args=(), device_types="cuda")

@@ -113,6 +113,7 @@ def test_opcheck_single_adapter_ops():
     cases = [
         (OPS.lora_fwd_, (x, A_w.t(), B_w.t(), torch.zeros((M, L_), device=DEV), s)),
         (OPS.lora_bwd_dx_da, (x.t(), dy, B_w, A_w, s)),
+        (OPS.lora_bwd_dx_da_accumulate_, (x.t(), dy, B_w, A_w, s, torch.randn((M, K_), device=DEV))),
         (OPS.lora_bwd_db, (A_w, x.t(), dy, s)),
         (OPS.lora_delta, (x.clone().requires_grad_(), A_w.clone().requires_grad_(), B_w.clone().requires_grad_(),
                           s)),
@@ -146,3 +147,20 @@ def test_lora_delta_forward_and_gradients(dtype):
     assert oracle.rel_frobenius(host(x.grad.float()), odx) <= gtol
     assert oracle.rel_frobenius(host(A_w.grad.float()).T, odA) <= gtol
     assert oracle.rel_frobenius(host(B_w.grad.float()).T, odB) <= gtol
+
+
+def test_dx_accumulate_op_matches_direct_call_bitwise():
+    M, K_, L_, r, s = 150, 264, 200, 16, 0.5
+    note("dx accumulate op vs direct call")
+    c = synth.single_adapter(M, K_, L_, r, seed=79, dtype="bf16", scale=s)
+    x = dev(c.X, "bf16")
+    A_w = dev(np.ascontiguousarray(c.A.T), "bf16")
+    B_w = dev(np.ascontiguousarray(c.B.T), "bf16")
+    dy = dev(c.dY, "bf16")
+    dx0 = torch.randn((M, K_), device=DEV)
+    d1 = dx0.clone()
+    _, dA1 = L.lora_bwd_dx_da_accumulate(x.t(), dy, B_w, A_w, s, d1)
+    d2 = dx0.clone()
+    dA2 = OPS.lora_bwd_dx_da_accumulate_(x.t(), dy, B_w, A_w, s, d2)
+    torch.cuda.synchronize()
+    assert same_bits(host(d2), host(d1)) and same_bits(host(dA2), host(dA1))

@@ -40,6 +40,7 @@ def test_schemas_declare_in_place_outputs():
     assert _written(OPS.expand_) == ["y"]
     assert _written(OPS.apply_) == ["y"]
     assert _written(OPS.lora_fwd_) == ["res"]
+    assert _written(OPS.lora_bwd_dx_da_accumulate_) == ["dx"]
     for name in ("addressing", "shrink", "gather_shrink", "lora_bwd_dx_da", "lora_bwd_db", "lora_delta"):
         assert _written(getattr(OPS, name)) == [], name
 
@@ -82,6 +83,8 @@ def test_fake_shapes_single_adapter_and_backward_formula():
         dy = torch.empty(M, L_, dtype=torch.bfloat16, device="cuda")
         dx, dA = OPS.lora_bwd_dx_da(x.t(), dy, B_w, A_w, 2.0)
         assert dx.shape == (M, K_) and dA.shape == (K_, r) and dx.dtype == dA.dtype == torch.float32
+        dA2 = OPS.lora_bwd_dx_da_accumulate_(x.t(), dy, B_w, A_w, 2.0, torch.empty(M, K_, device="cuda"))
+        assert dA2.shape == (K_, r) and dA2.dtype == torch.float32
         dB = OPS.lora_bwd_db(A_w, x.t(), dy, 2.0)
         assert dB.shape == (r, L_) and dB.dtype == torch.float32
         res = torch.empty(M, L_, dtype=torch.float32, device="cuda")
