@@ -34,7 +34,7 @@
  *     pages' wrappers default to dtype=torch.float32).
  *   - Data anomalies that the host cannot see (slot ids outside [0, S), ranks
  *     outside [0, r_max], token ids outside [0, V)) are defined behaviour, not
- *     errors: such tokens, rank rows or ids contribute nothing.
+ *     errors: such tokens, rank rows or ids add no term.
  */
 #ifndef LORA_MI355X_LORA_H
 #define LORA_MI355X_LORA_H
@@ -177,7 +177,13 @@ size_t lora_workspace_bytes(int op, int64_t M, int64_t K, int64_t L, int32_t r, 
  *   per 16 tokens and 16 ranks, and several workgroups per token tile expand
  *   disjoint column ranges). Both give the same results up to float32
  *   summation order.
- *   workspace: lora_workspace_bytes(LORA_OP_FWD, ...) bytes, required.
+ *   workspace: lora_workspace_bytes(LORA_OP_FWD, ...) bytes (an upper bound
+ *   over all layouts). It is needed only when a weight must be packed (a
+ *   layout other than the two read in place) or the split schedule runs
+ *   (K > 8192); otherwise the call uses none and workspace may be NULL with
+ *   workspace_bytes 0, as for the page's lora_forward_wrapper, which takes
+ *   only x, lora_A, lora_B, res and scale. LORA_ERR_WORKSPACE when one is
+ *   needed and missing or too small.
  */
 int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_mat* lora_B, const lora_mat* res,
              float scale, void* workspace, size_t workspace_bytes, void* stream);
@@ -232,8 +238,8 @@ int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lora_mat* dy, 
 
 /*
  * Token-to-slot grouping (the addressing every multi-adapter op takes; the
- * M* page requires the ops to run with no host sync and no data-dependent
- * shape, so the grouping runs on the device). Writes addr->counts, offsets
+ * M* page's ops neither wait on the host nor size anything from device data,
+ * so the grouping runs on the device). Writes addr->counts, offsets
  * and sorted_tokens from addr->token_slot and ranks[S] (device int32).
  *   1 <= r_max <= 128; 0 <= S <= 1024 (LORA_ERR_LIMIT above); T >= 0.
  */
@@ -297,8 +303,8 @@ int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora_t3* b, con
                       int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream);
 
 /*
- * Multi-adapter one-hot shrink (LoraOpsBackend.gather_shrink:
- * h[t] = a[slot(t)][:, ids[t]], the shrink of a token's one-hot):
+ * Multi-adapter embedding gather (LoraOpsBackend.gather_shrink:
+ * h[t] = a[slot(t)][:, ids[t]], i.e. column ids[t] of the token's adapter):
  *   ids  int32[T] device.
  *   a    S x r_max x V, bf16 or f32, any strides (64-bit offsets; a table
  *        stored with the rank index contiguous, s1 = 1, is read coalesced).

@@ -1,13 +1,13 @@
 """ctypes view of the C ABI declared in include/lora.h.
 
-Loads the in-tree ``liblora_mi355x.so``; if it has not been built yet it is
-built first (hipcc). There is no other implementation behind these calls:
-when the library cannot be built or loaded, every op raises.
+Loads the in-tree ``liblora_mi355x.so``; if it is missing, or was built from
+other sources than the ones in the tree (the build records a digest of them),
+it is built first (hipcc). There is no other implementation behind these
+calls: when the library cannot be built or loaded, every op raises.
 """
 from __future__ import annotations
 
 import ctypes
-import os
 import threading
 
 from . import build as _build
@@ -112,12 +112,13 @@ def library_path() -> str:
 
 
 def load() -> ctypes.CDLL:
-    """Load (building first if absent) the HIP library and bind every symbol."""
+    """Load the HIP library (building it first when it is absent or stale) and
+    bind every symbol."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_build.LIB_PATH):
+        if _build.is_stale():
             _build.build()
         lib = ctypes.CDLL(_build.LIB_PATH)
         for name, (res, args) in SIGNATURES.items():

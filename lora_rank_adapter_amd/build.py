@@ -6,6 +6,7 @@ disabled, then linked into one shared library next to this file.
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import shutil
 import subprocess
@@ -16,6 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "liblora_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+DIGEST_PATH = LIB_PATH + ".digest"   # digest of the sources the library was built from
 SOURCES = ["lora_single.hip", "lora_multi.hip"]
 HEADERS = ["lora_device.hpp", "lora_host.hpp"]
 
@@ -46,6 +48,27 @@ def _compile(src: str) -> str:
     return obj
 
 
+def source_digest() -> str:
+    """Digest of every source, header and compiler flag the library is built
+    from (contents, not file times: a copied tree keeps it)."""
+    h = hashlib.sha256(" ".join(HIPCC_FLAGS).encode())
+    deps = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "lora.h")]
+    for d in deps:
+        h.update(os.path.basename(d).encode())
+        with open(d, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def built_digest():
+    """The digest recorded by the last build, or None."""
+    try:
+        with open(DIGEST_PATH) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
 def build(verbose: bool = False) -> str:
     """Compile all sources and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -56,19 +79,19 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    digest = source_digest()
     os.replace(tmp, LIB_PATH)
+    with open(DIGEST_PATH, "w") as f:
+        f.write(digest + "\n")
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH
 
 
 def is_stale() -> bool:
-    """True when the library is missing or older than a source or header."""
-    if not os.path.exists(LIB_PATH):
-        return True
-    t = os.path.getmtime(LIB_PATH)
-    deps = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "lora.h")]
-    return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
+    """True when the library is missing or was built from other sources than
+    the ones in the tree now."""
+    return not os.path.exists(LIB_PATH) or built_digest() != source_digest()
 
 
 if __name__ == "__main__":

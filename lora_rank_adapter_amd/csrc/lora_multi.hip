@@ -2,9 +2,9 @@
 // "mstar.engine.resources.lora.ops", class LoraOpsBackend):
 //   shrink:        h[t] = x[t] @ a[slot(t)]^T          (per output slice)
 //   expand_fused:  y[t, slice i] += sc[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T
-//   gather_shrink: h[t] = a[slot(t)][:, ids[t]]        (the one-hot shrink)
-// plus the token-to-slot grouping that every op reads. The page requires the
-// ops to run with no host sync and no data-dependent shape: grids are sized
+//   gather_shrink: h[t] = a[slot(t)][:, ids[t]]        (one column of the slot's adapter)
+// plus the token-to-slot grouping that every op reads. The page's ops never
+// wait on the host and never size anything from device data: grids are sized
 // from host-known bounds (T, S, slice widths) and each workgroup finds its
 // work on the device, exiting early when there is none.
 //
@@ -31,7 +31,7 @@
 //                              weights from L2, two stages of outputs in flight
 //   slot_expand_kernel         expand for any layout (unaligned rows, y or b
 //                              beyond 2 GiB)
-//   gather_kernel              exact one-hot shrink, one wave per token
+//   gather_kernel              exact column gather, one wave per token
 
 #include <type_traits>
 

@@ -1718,9 +1718,12 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   const bool b_direct = lora_B->stride_row == 1 && r % 4 == 0 && lora_B->stride_col >= r &&
                         lora_B->stride_col % 4 == 0 && aligned(lora_B->ptr, 4 * es);
   const SingleLayout lay = layout_for(LORA_OP_FWD, M, K, L, static_cast<int>(r), x->dtype);
-  if (!workspace || !aligned(workspace, 256)) return LORA_ERR_WORKSPACE;
-  if (workspace_bytes < lay.total()) return LORA_ERR_WORKSPACE;
-  Carver cv(workspace);
+  // Weights read in place and the fused schedule use no workspace: the
+  // caller may then pass none.
+  const bool needs_ws = !a_direct || !b_direct || pick_schedule(L, K) != 1;
+  if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total()))
+    return LORA_ERR_WORKSPACE;
+  Carver cv(needs_ws ? workspace : nullptr);
   void* w1p = cv.take(lay.w1);
   void* w2p = cv.take(lay.w2);
   uint4* frag = static_cast<uint4*>(cv.take(lay.frag));

@@ -1,10 +1,10 @@
 """PyTorch custom ops over the LoRA library (namespace ``lora_amd``).
 
-The M* ops page exposes the shrink and the expand as custom ops so that
-torch.compile sees one opaque node each, with the expand declaring that it adds
-into y in place (mutates_args) so functionalization keeps every read of y on
-the right side of the add; it also has the pair as one op for a linear target,
-and checks the fake (shape) implementations on a CPU. The same here, over the
+On the M* ops page the shrink and the expand are custom ops, each one opaque
+node under torch.compile; the expand lists y among its mutated arguments, so
+functionalization orders the reads of y before and after the in-place update
+correctly; the pair also exists as one op for a linear target, and the fake
+(shape) implementations are checked on a CPU. The same here, over the
 HIP library: each op's only kernel is the library call on a CUDA (ROCm)
 device; there is no CPU kernel, so calling an op with CPU tensors raises
 NotImplementedError instead of computing anything elsewhere. The fake

@@ -24,6 +24,7 @@ from .lora_oracle import (  # noqa: F401
     lora_bwd_db,
     group_tokens,
     active_mask,
+    token_ranks,
     shrink,
     expand_fused,
     gather_shrink,

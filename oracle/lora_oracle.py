@@ -55,10 +55,9 @@ def rel_frobenius(got, want) -> float:
 def lora_fwd(x, lora_A, lora_B, res, scale):
     """Forward, in the frame of the lora_forward_kernel / lora_forward_wrapper
     entries: x is M x K, lora_A is K x N, lora_B is N x L (N = rank), res is
-    M x L. The kernel computes D = A x B x C and adds it to the output; the
-    inner_kernel entry forms the scaled product of x and lora_A, and the
-    block_vector_mul entry multiplies that by lora_B and adds the result to
-    the output.
+    M x L. Three matrices are multiplied in a row and the product is added
+    into res (lora_forward_kernel); inner_kernel supplies the first, scaled
+    product and block_vector_mul the second one together with the add.
 
     Returns res + scale * (x @ lora_A) @ lora_B as a new float64 array.
     """
@@ -77,8 +76,9 @@ def lora_bwd_dx_da(xt, dy, lora_B, lora_A, scale):
     S = in-features), dy is M x K (K = out-features), lora_B is K x N, lora_A
     is N x L (L = in-features, N = rank).
 
-    The kernel forms DYB = DY x B and DX = DY * B * A; the product with xt
-    that gives dlora_A is reduced over the M tokens in the wrapper.
+    lora_da_dx_kernel produces the rank-sized product of dy and lora_B and,
+    from it, the input gradient; the gradient of lora_A is a sum over the M
+    tokens of xt times that product, which the wrapper entry carries out.
 
     Returns (dx, dlora_A): dx = scale * DYB @ lora_A (M x L) and
     dlora_A = scale * xt @ DYB (S x N, i.e. in-features x rank).
@@ -117,18 +117,28 @@ def _clamped_ranks(ranks, r_max):
     return [min(max(int(v), 0), int(r_max)) for v in np.asarray(ranks).ravel()]
 
 
-def active_mask(token_slot, ranks, r_max) -> np.ndarray:
-    """True for tokens whose slot is in [0, S) and has clamped rank > 0.
+def token_ranks(token_slot, ranks, r_max) -> np.ndarray:
+    """Effective rank of each token: the rank of its slot clamped to
+    [0, r_max] when the slot id lies in [0, S), else 0.
 
-    A token on the zero adapter (a rank-0 slot) or on a slot id outside
-    [0, S) contributes nothing."""
+    The page names the addressing and the per-slot ranks but not what an
+    out-of-range slot id or rank means; the reading taken is that such a
+    token, or a token on a rank-0 slot (the zero adapter), adds no term, and
+    that a rank outside [0, r_max] is clamped into it."""
     token_slot = np.asarray(token_slot).ravel()
     rho = _clamped_ranks(ranks, r_max)
     S = len(rho)
-    out = np.zeros(token_slot.shape[0], dtype=bool)
+    out = np.zeros(token_slot.shape[0], dtype=np.int64)
     for t, s in enumerate(token_slot.tolist()):
-        out[t] = 0 <= s < S and rho[s] > 0
+        if 0 <= s < S:
+            out[t] = rho[s]
     return out
+
+
+def active_mask(token_slot, ranks, r_max) -> np.ndarray:
+    """True for the tokens that contribute: effective rank (see
+    :func:`token_ranks`) above zero."""
+    return token_ranks(token_slot, ranks, r_max) > 0
 
 
 def group_tokens(token_slot, ranks, r_max):
@@ -229,13 +239,13 @@ def expand_fused(h, b, token_slot, ranks, scalings, y, out_slices, r_max, tokens
 
 
 def gather_shrink(ids, a, token_slot, ranks, r_max, tokens=None, a_is_bf16_bits=False):
-    """h[t] = a[slot(t)][:, ids[t]], the shrink of a token's one-hot
-    (LoraOpsBackend.gather_shrink).
+    """Column ids[t] of the token's adapter (LoraOpsBackend.gather_shrink):
+    what the shrink would give for a one-hot input row.
 
     ``a`` is indexable as a[s, j, v] (S x r_max x V, any strides). For an
     active token t on slot s with rank rho: h[t, 0, j] = a[s, j, ids[t]] for
-    j < rho when 0 <= ids[t] < V, and +0.0 when the id lies outside [0, V)
-    (such an id contributes nothing). Other entries are written as 0.
+    j < rho when 0 <= ids[t] < V; an id outside [0, V) selects no column, so
+    those entries are +0.0. Other entries are written as 0.
 
     Returns a float64 array T x 1 x r_max.
     """

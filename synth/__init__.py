@@ -115,15 +115,30 @@ class SingleAdapterCase:
 
 def single_adapter(M: int, K: int, L: int, r: int, *, seed: int, dtype: str = "bf16",
                    scale: float = 2.0, y0: str = "zero", int_exact: bool = False,
-                   name: str = "") -> SingleAdapterCase:
+                   density=None, name: str = "") -> SingleAdapterCase:
     """Draw X, A, B, dY (and Y0) in that order from ``default_rng(seed)``.
 
     Laws: X, dY ~ N(0,1); A ~ N(0, 1/K); B ~ N(0, 1/r); Y0 = 0 or ~N(0,1).
     ``int_exact`` draws every input uniformly from {-2,...,2} instead (exact in
     bf16; with small enough shapes every fp32 partial sum is then exact).
+    ``density`` = (d_X, d_A, d_B, d_dY) with ``int_exact`` draws sparse
+    values instead: each element is nonzero with its matrix's probability,
+    then +1 or -1 with equal odds (Y0 stays on {-2,...,2}); full-size shapes
+    keep their sums small this way.
     """
     rng = np.random.default_rng(seed)
-    if int_exact:
+    if int_exact and density is not None:
+        dens = iter(density)
+
+        def draw(shape, _sigma):
+            p = next(dens, None)
+            if p is None:      # Y0
+                return rng.integers(-2, 3, size=shape).astype(np.float32)
+            nz = rng.random(shape, dtype=np.float32) < np.float32(p)
+            sign = rng.integers(0, 2, size=shape, dtype=np.int8)
+            return np.where(nz, np.where(sign == 1, np.float32(1.0), np.float32(-1.0)),
+                            np.float32(0.0)).astype(np.float32)
+    elif int_exact:
         def draw(shape, _sigma):
             return rng.integers(-2, 3, size=shape).astype(np.float32)
     else:

@@ -368,11 +368,132 @@ def pin_grouping_is_stable_sort(group, seed=24):
             assert all(int(ts[t]) == s for t in seg)
 
 
+def pin_golden_active(token_ranks, active_mask, group):
+    """Hand-worked addressing with a negative rank, a rank above r_max, a
+    rank-0 slot and slot ids S, -1, -7 and 1000."""
+    g = _load("active_tiny.json")
+    ts = np.asarray(g["token_slot"], np.int32)
+    ranks = np.asarray(g["ranks"], np.int32)
+    assert [int(v) for v in token_ranks(ts, ranks, g["r_max"])] == g["token_ranks"], "golden token ranks"
+    assert [bool(v) for v in active_mask(ts, ranks, g["r_max"])] == g["active"], "golden active mask"
+    counts, offsets, sorted_tokens, n_active = group(ts, ranks, g["r_max"])
+    assert list(counts) == g["counts"] and list(offsets) == g["offsets"], "golden grouping"
+    assert list(sorted_tokens[:n_active]) == g["sorted_tokens"] and n_active == g["n_active"]
+
+
+def _literal_rank(ts_t, ranks, r_max):
+    """The reading written out with Python conditionals, one token at a time."""
+    S = len(ranks)
+    if ts_t < 0 or ts_t >= S:
+        return 0
+    v = int(ranks[ts_t])
+    if v < 0:
+        return 0
+    if v > r_max:
+        return r_max
+    return v
+
+
+def pin_active_mask(token_ranks, active_mask, group, seed=25):
+    """Effective ranks against the reading written out per token with plain
+    conditionals, on random slot ids and ranks well outside their ranges; the
+    active mask against the grouping (a token is active iff the grouping lists
+    it)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for (T, S, r_max) in [(1, 1, 1), (64, 6, 4), (400, 33, 16), (0, 2, 3)]:
+        wild = rng.integers(-2 * r_max - 3, 2 * r_max + 4, S).astype(np.int32)
+        inside = rng.integers(1, r_max + 1, S).astype(np.int32)     # every slot active
+        for ranks in (wild, inside):
+            ts = rng.integers(-S - 3, 2 * S + 3, T).astype(np.int32)
+            edge = np.asarray([S, -1, -S, S - 1, 0, S + 1, -S - 1], np.int32)[:T]
+            ts[:edge.shape[0]] = edge                                # the bounds of [0, S)
+            cases.append((T, S, r_max, ranks, ts))
+    for (T, S, r_max, ranks, ts) in cases:
+        rho = [int(v) for v in token_ranks(ts, ranks, r_max)]
+        assert rho == [_literal_rank(int(t), ranks, r_max) for t in ts.tolist()], "effective ranks"
+        act = np.asarray(active_mask(ts, ranks, r_max), bool)
+        assert act.shape == (T,)
+        assert list(act) == [v > 0 for v in rho], "active iff effective rank > 0"
+        _, _, sorted_tokens, n_active = group(ts, ranks, r_max)
+        assert sorted(int(t) for t in sorted_tokens[:n_active]) == [t for t in range(T) if act[t]], \
+            "active tokens = tokens the grouping lists"
+
+
+def pin_golden_bf16(conv):
+    """bf16 bit patterns -> values on the hand-worked golden patterns."""
+    g = _load("bf16_bits.json")
+    bits = np.asarray([int(c["bits"], 16) for c in g["cases"]], np.uint16)
+    got = np.asarray(conv(bits), np.float64)
+    for c, v in zip(g["cases"], got.tolist()):
+        want = float(c["value"])
+        if math.isnan(want):
+            assert math.isnan(v), (c["bits"], v)
+        else:
+            assert v == want and math.copysign(1.0, v) == math.copysign(1.0, want), (c["bits"], v, want)
+
+
+def pin_bf16_closed_form(conv):
+    """Every one of the 65536 bf16 patterns against the format's closed form
+    (sign, biased exponent, fraction), computed with math.ldexp."""
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):          # signalling-NaN patterns
+        got = np.asarray(conv(every), np.float64)
+    for b in range(65536):
+        sgn, e, f = (b >> 15) & 1, (b >> 7) & 0xFF, b & 0x7F
+        v = float(got[b])
+        if e == 255:
+            assert (math.isnan(v) if f else (v == (-math.inf if sgn else math.inf))), hex(b)
+            continue
+        mag = math.ldexp(f / 128.0, -126) if e == 0 else math.ldexp(1.0 + f / 128.0, e - 127)
+        assert v == (-mag if sgn else mag) and math.copysign(1.0, v) == (-1.0 if sgn else 1.0), hex(b)
+
+
+def pin_golden_apply(apply):
+    """apply_linear on the hand-worked multi-adapter example gives its y."""
+    g = _load("multi_tiny.json")
+    x, a, b, y0 = (_arr(g[k]) for k in ("x", "a", "b", "y0"))
+    y = apply(x, y0, a, b, np.asarray(g["token_slot"], np.int32), np.asarray(g["ranks"], np.int32),
+              np.asarray(g["scalings"], np.float64), g["out_slices"], g["r_max"])
+    _bitwise(y, _arr(g["y"]), "golden apply_linear y")
+
+
+def pin_apply_linear_brute(apply, seed=26):
+    """Literal sums of the composed definition, y[t, off_i + c] = y0 +
+    sc[s] * sum_j (sum_k x[t,k] a[s, i*r_max + j, k]) b[s, off_i + c, j], on
+    tiny cases with NaN padding, out-of-range slots and clamped ranks."""
+    rng = np.random.default_rng(seed)
+    for (T, K, out_slices, S, r_max) in [(6, 4, (2, 3), 3, 2), (11, 3, (1, 1, 2), 4, 3)]:
+        ranks = rng.integers(-1, r_max + 2, S).astype(np.int32)
+        ts, ranks, x, a, b, sc, y0 = _rand_multi(rng, T, K, out_slices, S, r_max, ranks=ranks)
+        y = np.asarray(apply(x, y0, a, b, ts, ranks, sc, out_slices, r_max))
+        offs = [sum(out_slices[:i]) for i in range(len(out_slices) + 1)]
+        for t in range(T):
+            rho = _literal_rank(int(ts[t]), ranks, r_max)
+            if rho == 0:
+                _bitwise(y[t], y0[t], "apply_linear: inactive row untouched")
+                continue
+            s = int(ts[t])
+            for i in range(len(out_slices)):
+                for c in range(offs[i], offs[i + 1]):
+                    acc = 0.0
+                    for j in range(rho):
+                        hj = 0.0
+                        for k in range(K):
+                            hj += x[t][k] * a[s][i * r_max + j][k]
+                        acc += hj * b[s][c][j]
+                    want = y0[t][c] + sc[s] * acc
+                    assert abs(y[t, c] - want) <= 1e-13 * (1 + abs(want)), "brute apply_linear"
+        assert np.isfinite(y).all(), "NaN padding leaked into y"
+
+
 ALL_SINGLE = ("pin_golden_single", "pin_fwd_dense_identity", "pin_fwd_special_cases",
               "pin_bwd_finite_differences", "pin_bwd_euler", "pin_bwd_dense_chain",
               "pin_single_brute_force", "pin_single_integer_exact")
 ALL_MULTI = ("pin_golden_multi", "pin_golden_gather", "pin_golden_grouping", "pin_multi_brute_force",
-             "pin_multi_reduces_to_single", "pin_gather_is_onehot_shrink", "pin_grouping_is_stable_sort")
+             "pin_multi_reduces_to_single", "pin_gather_is_onehot_shrink", "pin_grouping_is_stable_sort",
+             "pin_golden_active", "pin_active_mask", "pin_golden_apply", "pin_apply_linear_brute")
+ALL_FORMAT = ("pin_golden_bf16", "pin_bf16_closed_form")
 
 
 def run_all(o):
@@ -392,7 +513,12 @@ def run_all(o):
     pin_multi_reduces_to_single(o.lora_fwd, o.shrink, o.expand_fused)
     pin_gather_is_onehot_shrink(o.gather_shrink, o.shrink)
     pin_grouping_is_stable_sort(o.group_tokens)
-
+    pin_golden_active(o.token_ranks, o.active_mask, o.group_tokens)
+    pin_active_mask(o.token_ranks, o.active_mask, o.group_tokens)
+    pin_golden_apply(o.apply_linear)
+    pin_apply_linear_brute(o.apply_linear)
+    pin_golden_bf16(o.bf16_bits_to_f64)
+    pin_bf16_closed_form(o.bf16_bits_to_f64)
 
 
 def pin_calls(o):
@@ -413,6 +539,12 @@ def pin_calls(o):
         ("multi_reduces_to_single", lambda: pin_multi_reduces_to_single(o.lora_fwd, o.shrink, o.expand_fused)),
         ("gather_is_onehot_shrink", lambda: pin_gather_is_onehot_shrink(o.gather_shrink, o.shrink)),
         ("grouping_is_stable_sort", lambda: pin_grouping_is_stable_sort(o.group_tokens)),
+        ("golden_active", lambda: pin_golden_active(o.token_ranks, o.active_mask, o.group_tokens)),
+        ("active_mask", lambda: pin_active_mask(o.token_ranks, o.active_mask, o.group_tokens)),
+        ("golden_apply", lambda: pin_golden_apply(o.apply_linear)),
+        ("apply_linear_brute", lambda: pin_apply_linear_brute(o.apply_linear)),
+        ("golden_bf16", lambda: pin_golden_bf16(o.bf16_bits_to_f64)),
+        ("bf16_closed_form", lambda: pin_bf16_closed_form(o.bf16_bits_to_f64)),
     ]
 
 

@@ -103,11 +103,15 @@ def test_fwd_validation(lib):
     assert fwd(lib, m(M, K, sr=K + 2), A, B, res) == -4                    # row pitch not 16-byte aligned
     assert fwd(lib, m(M, 132), m(132, r, sr=1, sc=132), B, res) == -2      # K not a multiple of 8 (bf16)
     assert fwd(lib, x, A, m(r, 98, sr=1, sc=r), m(M, 98, dtype=0)) == -2   # L not a multiple of 4
-    # the forward needs its workspace (weight packing, split schedule)
-    assert fwd(lib, x, A, B, res) == -6
-    assert fwd(lib, x, m(K, r), B, res) == -6
+    # the forward needs its workspace when it packs a weight or runs the split
+    # schedule (contractions longer than 8192); weights read in place with the
+    # fused schedule need none (that call launches: covered by a GPU test)
+    assert fwd(lib, x, m(K, r), B, res) == -6                               # A packed
+    assert fwd(lib, x, A, m(r, L_), res) == -6                              # B packed
     assert fwd(lib, x, m(K, r), B, res, ctypes.c_void_p(FAKE), 16) == -6
-    assert fwd(lib, x, A, B, res, ctypes.c_void_p(FAKE + 128), 1 << 20) == -6   # not 256-byte aligned
+    assert fwd(lib, x, m(K, r), B, res, ctypes.c_void_p(FAKE + 128), 1 << 20) == -6   # not 256-byte aligned
+    Kl = 8200
+    assert fwd(lib, m(M, Kl), m(Kl, r, sr=1, sc=Kl), B, res) == -6          # split schedule
     # empty problems launch nothing and succeed
     assert fwd(lib, m(0, K), A, B, m(0, L_, dtype=0)) == 0
     assert fwd(lib, m(M, 0), m(0, r, sr=1, sc=1), B, res) == 0

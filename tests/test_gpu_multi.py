@@ -53,12 +53,12 @@ def _addr(m):
 
 
 def _spec_mask(m):
-    """Entries of h the page specifies: active tokens, j < rank."""
-    act = oracle.active_mask(m.token_slot, m.ranks, m.r_max)
-    spec = np.zeros((m.T, m.num_slices, m.r_max), bool)
-    for t in np.nonzero(act)[0]:
-        rho = min(int(m.ranks[m.token_slot[t]]), m.r_max)
-        spec[t, :, :rho] = True
+    """Entries of h the page specifies: active tokens, j below the token's
+    effective rank (the oracle's pinned token_ranks)."""
+    rho = oracle.token_ranks(m.token_slot, m.ranks, m.r_max)
+    act = rho > 0
+    spec = np.arange(m.r_max)[None, None, :] < rho[:, None, None]
+    spec = np.broadcast_to(spec, (m.T, m.num_slices, m.r_max)).copy()
     return act, spec
 
 
@@ -316,10 +316,9 @@ def test_gather_shrink_bitwise(dtype, layout):
     torch.cuda.synchronize()
     want = oracle.gather_shrink(ids, table, ts, ranks, r_max)
     got = host(h)
-    act = oracle.active_mask(ts, ranks, r_max)
-    spec = np.zeros((T, 1, r_max), bool)
-    for t in np.nonzero(act)[0]:
-        spec[t, 0, :ranks[ts[t]]] = True
+    rho = oracle.token_ranks(ts, ranks, r_max)
+    act = rho > 0
+    spec = (np.arange(r_max)[None, None, :] < rho[:, None, None]).repeat(1, axis=1)
     assert same_bits(got[spec], want[spec].astype(np.float32))
     assert np.all(got[~spec] == SENTINEL)
     invalid = act & ((ids < 0) | (ids >= V))
@@ -346,21 +345,26 @@ def test_bad_arguments():
     assert e.value.status == -2
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("cfg", ["config4", "config5"])
-def test_full_size_shrink_expand(cfg):
-    m = getattr(synth, cfg)()
+def _full_size_check(m):
     note(f"full size {m.name} T={m.T}")
     addr, ranks = _addr(m)
     counts, offsets, sorted_tokens, n = oracle.group_tokens(m.token_slot, m.ranks, m.r_max)
     torch.cuda.synchronize()
+    assert np.array_equal(host(addr.counts)[:m.S], counts)
+    assert np.array_equal(host(addr.offsets), offsets)
     assert np.array_equal(host(addr.sorted_tokens)[:n], sorted_tokens)
     h = L.lora_shrink(dev(m.x, "bf16"), dev(m.a, "bf16"), addr, ranks, m.num_slices, m.r_max)
     y = f32(m.y0)
     L.lora_expand_fused(h, dev(m.b, "bf16"), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
     torch.cuda.synchronize()
+    # sampled tokens: the ends, random ones, and the first and last token of
+    # every slot the batch uses (so every slot's rank, clamped or not, is seen)
     rng = np.random.default_rng(1)
-    toks = np.unique(np.concatenate([[0, m.T - 1], rng.integers(0, m.T, 200)]))
+    per_slot = []
+    for s in np.unique(m.token_slot):
+        idx = np.nonzero(m.token_slot == s)[0]
+        per_slot += [idx[0], idx[-1]]
+    toks = np.unique(np.concatenate([[0, m.T - 1], rng.integers(0, m.T, 200), per_slot]))
     act, spec = _spec_mask(m)
     hw = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max, tokens=toks)
     hg = host(h)
@@ -370,6 +374,30 @@ def test_full_size_shrink_expand(cfg):
     a_t = act[toks]
     assert same_bits(got[~a_t], m.y0[toks][~a_t])
     assert oracle.rel_frobenius(got[a_t] - m.y0[toks][a_t], want[a_t] - m.y0[toks][a_t]) <= 2e-3
+    return act
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["config4", "config5"])
+def test_full_size_shrink_expand(cfg):
+    _full_size_check(getattr(synth, cfg)())
+
+
+@pytest.mark.slow
+def test_full_size_rank_clamp():
+    """The prefill workload's routing with the ranks of four used slots moved
+    outside [0, r_max] (-3, r_max + 5, 2^30, -2^30): ranks are clamped into
+    [0, r_max], so two of those slots use all 128 rank rows and the tokens of
+    the other two are inactive and leave y untouched."""
+    ts, ranks, _lengths, rng = synth.config5_routing()
+    used = np.unique(ts)
+    ranks = ranks.copy()
+    ranks[used[:4]] = [-3, 128 + 5, 1 << 30, -(1 << 30)]
+    m = synth.multi_lora(ts, ranks, 8192, (8192, 1024, 1024), 128, rng=rng, name="cfg5-rank-clamp")
+    act = _full_size_check(m)
+    rho = oracle.token_ranks(m.token_slot, m.ranks, m.r_max)
+    assert (rho[np.isin(m.token_slot, used[[1, 2]])] == 128).all()
+    assert not act[np.isin(m.token_slot, used[[0, 3]])].any()
 
 
 @pytest.mark.slow

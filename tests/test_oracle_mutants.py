@@ -12,7 +12,8 @@ from tests import oracle_pins as P
 
 def _ns(**over):
     base = {k: getattr(O, k) for k in ("lora_fwd", "lora_bwd_dx_da", "lora_bwd_db", "group_tokens",
-                                       "shrink", "expand_fused", "gather_shrink")}
+                                       "shrink", "expand_fused", "gather_shrink", "token_ranks",
+                                       "active_mask", "apply_linear", "bf16_bits_to_f64")}
     base.update(over)
     return types.SimpleNamespace(**base)
 
@@ -125,7 +126,86 @@ def gather_wraps_negative_ids(ids, a, token_slot, ranks, r_max, tokens=None, a_i
     return O.gather_shrink(ids, a, token_slot, ranks, r_max, tokens, a_is_bf16_bits)
 
 
+# --- addressing, apply_linear and bf16 mutants -----------------------------
+
+def ranks_slot_le_S(token_slot, ranks, r_max):
+    # slot id S read as the last slot (an off-by-one bound)
+    ts = np.asarray(token_slot).ravel().copy()
+    S = len(np.asarray(ranks).ravel())
+    ts[ts == S] = S - 1
+    return O.token_ranks(ts, ranks, r_max)
+
+
+def ranks_negative_slot_wraps(token_slot, ranks, r_max):
+    # negative slot ids index from the end, as Python lists do
+    ts = np.asarray(token_slot).ravel().copy()
+    S = len(np.asarray(ranks).ravel())
+    ts[(ts < 0) & (ts >= -S)] += S
+    return O.token_ranks(ts, ranks, r_max)
+
+
+def ranks_unclamped_above(token_slot, ranks, r_max):
+    # a rank above r_max counted raw
+    return O.token_ranks(token_slot, ranks, 10 ** 6)
+
+
+def ranks_abs_negative(token_slot, ranks, r_max):
+    # a negative rank taken by magnitude instead of clamped to 0
+    return O.token_ranks(token_slot, np.abs(np.asarray(ranks)), r_max)
+
+
+def active_zero_adapter(token_slot, ranks, r_max):
+    # rank-0 slots counted as active (>= instead of >)
+    ts = np.asarray(token_slot).ravel()
+    S = len(np.asarray(ranks).ravel())
+    return (ts >= 0) & (ts < S)
+
+
+def active_mask_of(rank_fn):
+    return lambda token_slot, ranks, r_max: rank_fn(token_slot, ranks, r_max) > 0
+
+
+def apply_no_scaling(x, y, a, b, token_slot, ranks, scalings, out_slices, r_max, tokens=None):
+    return O.apply_linear(x, y, a, b, token_slot, ranks, np.ones(len(ranks)), out_slices, r_max, tokens)
+
+
+def apply_swapped_slices(x, y, a, b, token_slot, ranks, scalings, out_slices, r_max, tokens=None):
+    h = O.shrink(x, a, token_slot, ranks, len(out_slices), r_max, tokens=tokens)
+    if h.shape[1] > 1:
+        h = h[:, ::-1, :]
+    return O.expand_fused(h, b, token_slot, ranks, scalings, y, out_slices, r_max, tokens=tokens)
+
+
+def apply_touches_inactive(x, y, a, b, token_slot, ranks, scalings, out_slices, r_max, tokens=None):
+    return O.apply_linear(x, y, a, b, token_slot, ranks, scalings, out_slices, r_max, tokens) + 0.0
+
+
+def bf16_shift15(bits):
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+
+
+def bf16_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_drops_sign(bits):
+    return np.abs(O.bf16_bits_to_f64(bits))
+
+
 MUTANTS = {
+    "ranks_slot_le_S": dict(token_ranks=ranks_slot_le_S, active_mask=active_mask_of(ranks_slot_le_S)),
+    "ranks_negative_slot_wraps": dict(token_ranks=ranks_negative_slot_wraps,
+                                      active_mask=active_mask_of(ranks_negative_slot_wraps)),
+    "ranks_unclamped_above": dict(token_ranks=ranks_unclamped_above),
+    "ranks_abs_negative": dict(token_ranks=ranks_abs_negative, active_mask=active_mask_of(ranks_abs_negative)),
+    "active_zero_adapter": dict(active_mask=active_zero_adapter),
+    "apply_no_scaling": dict(apply_linear=apply_no_scaling),
+    "apply_swapped_slices": dict(apply_linear=apply_swapped_slices),
+    "apply_touches_inactive": dict(apply_linear=apply_touches_inactive),
+    "bf16_shift15": dict(bf16_bits_to_f64=bf16_shift15),
+    "bf16_as_fp16": dict(bf16_bits_to_f64=bf16_as_fp16),
+    "bf16_drops_sign": dict(bf16_bits_to_f64=bf16_drops_sign),
     "fwd_no_scale": dict(lora_fwd=fwd_no_scale),
     "fwd_overwrites": dict(lora_fwd=fwd_overwrites),
     "fwd_squared_scale": dict(lora_fwd=fwd_squared_scale),

@@ -65,6 +65,30 @@ def test_grouping_is_stable_sort():
     P.pin_grouping_is_stable_sort(oracle.group_tokens)
 
 
+def test_golden_active():
+    P.pin_golden_active(oracle.token_ranks, oracle.active_mask, oracle.group_tokens)
+
+
+def test_active_mask():
+    P.pin_active_mask(oracle.token_ranks, oracle.active_mask, oracle.group_tokens)
+
+
+def test_golden_apply_linear():
+    P.pin_golden_apply(oracle.apply_linear)
+
+
+def test_apply_linear_brute_force():
+    P.pin_apply_linear_brute(oracle.apply_linear)
+
+
+def test_golden_bf16_widening():
+    P.pin_golden_bf16(oracle.bf16_bits_to_f64)
+
+
+def test_bf16_widening_closed_form():
+    P.pin_bf16_closed_form(oracle.bf16_bits_to_f64)
+
+
 def test_apply_linear_is_shrink_then_expand():
     import numpy as np
     rng = np.random.default_rng(31)
