@@ -1,9 +1,11 @@
 """Benchmark of the LoRA hot path on one MI355X.
 
 One step = one single-adapter forward + backward pass over a batch:
-lora_fwd (Y += s*(X*A)*B), lora_bwd_dx_da (dX, dA), lora_bwd_db (dB), on the
-bf16-in / fp32-out workload M = 8192 tokens (4 x 2048), K = L = 4096, rank 16,
-s = 2.0 (synthetic seeded data, see synth/). Inputs are resident in HBM before
+lora_fwd (Y += s*(X*A)*B), lora_bwd_dx_da (dX, dA), lora_bwd_db (dB), by
+default on the largest bf16-in / fp32-out workload, the MLP-up shape M = 16384
+tokens, K = 4096, L = 14336, rank 64, s = 0.5 (synthetic seeded data, see
+synth/); --workload selects the 8192 x 4096 x 4096, rank 16 one instead.
+Inputs are resident in HBM before
 the timed region; several copies of the streamed tensors rotate so that
 successive steps do not read the previous step's data from the 256 MB
 Infinity Cache.
@@ -47,7 +49,7 @@ WORKLOADS = {
     "single-bf16-M8192-K4096-L4096-r16": (8192, 4096, 4096, 16, 2.0, 2),
     "single-bf16-M16384-K4096-L14336-r64": (16384, 4096, 14336, 64, 0.5, 3),
 }
-DEFAULT_WORKLOAD = "single-bf16-M8192-K4096-L4096-r16"
+DEFAULT_WORKLOAD = "single-bf16-M16384-K4096-L14336-r64"
 
 # The kernels the roofline entry is about, per workload: what lora_fwd
 # launches at that shape (weights used in place, so no packing launch): the
@@ -175,37 +177,148 @@ def traffic_summary(fetch_csv, write_csv, workload, command):
     print(json.dumps(rec))
 
 
-def cpu_baseline(case, min_seconds=12.0, max_runs=1000):
-    """The fp64 CPU oracle on the same batch, repeated for >= min_seconds."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Hardware counters the --counter-summary tables use (one rocprofv3 --pmc pass:
+# 7 SQ counters and GRBM_GUI_ACTIVE, within one pass's limits).
+PMC_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"]
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
+
+
+def counter_summary(csv_path, name, command):
+    """Per kernel (mean over its dispatches), with the kernel's busy cycles
+    G = GRBM_GUI_ACTIVE / 8 (the counter collection sums the GUI-active
+    cycles of the 8 XCDs, each with its own GRBM): MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (G * SIMDs); mean resident waves per CU =
+    4 * SQ_WAVE_CYCLES / (G * CUs) (SQ_WAVE_CYCLES counts in units of 4
+    cycles); bf16 MFMA TFLOP/s = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 / (G at
+    2.4 GHz); LDS bank-conflict cycles per LDS instruction cycle =
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    per = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = (row["Kernel_Name"], int(row["Dispatch_Id"]))
+            d = per.setdefault(key, {})
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    kernels = {}
+    for (kname, _), d in per.items():
+        kernels.setdefault(kname, []).append(d)
+    lines = [f"# Hardware counters: {name}", "", "Command (from the repository root; outputs under gpurun_out/):", "",
+             "```", command, "```", "",
+             "Counters: " + ", ".join(PMC_COUNTERS) + ". Per kernel, means over its dispatches:",
+             "G = GRBM_GUI_ACTIVE / 8 (the collection sums the 8 XCDs' GUI-active cycles; G / 2.4 GHz "
+             "matches the kernel-trace duration); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (G x 1024 SIMDs); "
+             "waves/CU = 4 x SQ_WAVE_CYCLES / (G x 256 CUs); bf16 MFMA TFLOP/s = 512 x "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 / (G / 2.4 GHz); LDS conflict = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel | dispatches | µs (G / 2.4 GHz) | MFMA busy | waves/CU | bf16 MFMA TFLOP/s | LDS conflict |",
+             "|---|---|---|---|---|---|---|"]
+    rows = []
+    for kname, ds in kernels.items():
+        if not kname.startswith("void lora::") and not kname.startswith("lora::"):
+            continue
+
+        def mean(c):
+            return statistics.mean(d.get(c, 0.0) for d in ds)
+        gui = mean("GRBM_GUI_ACTIVE") / XCD_NUM
+        if gui <= 0:
+            continue
+        us = gui / 2.4e3
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (gui * SIMD_NUM)
+        waves = 4.0 * mean("SQ_WAVE_CYCLES") / (gui * CU_NUM)
+        tflops = 512.0 * mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") / (us * 1e-6) / 1e12
+        lds = mean("SQ_LDS_IDX_ACTIVE")
+        conf = mean("SQ_LDS_BANK_CONFLICT") / lds if lds > 0 else 0.0
+        short = re.sub(r"^void ", "", kname).replace("(lora::FusedArgs)", "").replace("(lora::TnArgs)", "")
+        short = re.sub(r"\(.*\)$", "", short)
+        rows.append((us, f"| `{short[:90]}` | {len(ds)} | {us:.1f} | {busy:.3f} | {waves:.2f} | {tflops:.1f} | "
+                         f"{conf:.3f} |"))
+    lines += [r for _, r in sorted(rows, reverse=True)]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats_summary(csv_path, name, command):
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run as a table."""
+    with open(csv_path, newline="") as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# rocprofv3 kernel statistics: {name}", "", "Command (from the repository root; outputs under "
+             "gpurun_out/):", "", "```", command, "```", "",
+             "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        kname = re.sub(r"^void ", "", r["Name"])
+        kname = re.sub(r"\((lora::)?\w+Args\)$", "", kname)
+        lines.append(f"| `{kname[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(case, budget_s=8.0):
+    """The float64 CPU oracle (numpy, as it stands) on a bounded sample of the
+    batch: the first `tokens` rows of X, dY and Y0 with the full weights, one
+    forward + lora_bwd_dx_da + lora_bwd_db per run, median over repeated runs
+    for about `budget_s` seconds; on every thread the host's BLAS uses, then on
+    one. Tokens/s scale linearly with the sample (every op is per-token work
+    plus the token sums of dA and dB)."""
     import threadpoolctl
 
     import oracle
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
-        t0 = time.perf_counter()
-        oracle.lora_fwd(case.X, case.A, case.B, case.Y0, case.scale)
-        oracle.lora_bwd_dx_da(case.X.T, case.dY, case.B.T, case.A.T, case.scale)
-        oracle.lora_bwd_db(case.A.T, case.X.T, case.dY, case.scale)
-        times.append(time.perf_counter() - t0)
-    med = statistics.median(times)
+
+    def measure(tokens):
+        X, dY, Y0 = case.X[:tokens], case.dY[:tokens], case.Y0[:tokens]
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 200):
+            t0 = time.perf_counter()
+            oracle.lora_fwd(X, case.A, case.B, Y0, case.scale)
+            oracle.lora_bwd_dx_da(X.T, dY, case.B.T, case.A.T, case.scale)
+            oracle.lora_bwd_db(case.A.T, X.T, dY, case.scale)
+            times.append(time.perf_counter() - t0)
+        return tokens / statistics.median(times), len(times), sum(times)
+
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    n_all = min(case.M, 2048)
+    v_all, runs_all, t_all = measure(n_all)
+    n_one = min(case.M, 256)
+    with threadpoolctl.threadpool_limits(1):
+        v_one, runs_one, t_one = measure(n_one)
     return {
-        "value": case.M / med,
+        "value": v_all,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"whole batch ({case.M} tokens), fwd+bwd_dx_da+bwd_db in float64 numpy, "
-                  f"median of {len(times)} runs ({sum(times):.1f} s total)",
+        "sample": f"first {n_all} of {case.M} tokens (full weights), fwd + bwd_dx_da + bwd_db in float64 "
+                  f"numpy, median of {runs_all} runs ({t_all:.1f} s)",
+        "one_core": {"value": v_one, "unit": "tokens/s", "cores": 1,
+                     "sample": f"first {n_one} tokens, median of {runs_one} runs ({t_one:.1f} s)"},
+        "host": {"nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(), "cpu_model": _cpu_model()},
     }
 
 
-def multi_lora_figures(dev, reps=20):
+def multi_lora_figures(dev, reps=20, graph=True):
     """Kernel times of the slot-addressed ops on the decode and prefill
     workloads (routing from synth's seeded laws; values drawn on the device
     with the same laws), with their algorithmic bytes: activations once per
     active token, each used slot's live adapter rows once, h once, y read and
-    written for active tokens."""
+    written for active tokens. Whole input sets (x, adapters, y, h) rotate, at
+    least 1 GB of them, so that no repetition finds the previous one's data in
+    the 256 MB Infinity Cache."""
     import numpy as np
     import torch
 
@@ -234,19 +347,23 @@ def multi_lora_figures(dev, reps=20):
             ("decode-T256-K4096-qkv-S32-rmax64", ts4, rk4, 4096, (4096, 1024, 1024), 64),
             ("prefill-K8192-qkv-S128-rmax128", ts5, rk5, 8192, (8192, 1024, 1024), 128)):
         T, S, n, SO = ts_np.shape[0], rk_np.shape[0], len(slices), sum(slices)
-        nsets = 3 if T > 4096 else 1
+        set_bytes = 2 * T * K + 2 * S * n * r_max * K + 2 * S * SO * r_max + 4 * T * SO + 4 * T * n * r_max
+        nsets = max(2, min(24, -(-(1 << 30) // set_bytes)))
         ts = torch.from_numpy(ts_np).to(dev)
         rk = torch.from_numpy(rk_np).to(dev)
         xs = [torch.randn((T, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(nsets)]
-        a = (torch.randn((S, n * r_max, K), device=dev, generator=gen) / K ** 0.5).to(torch.bfloat16)
-        b = (torch.randn((S, SO, r_max), device=dev, generator=gen) / 8).to(torch.bfloat16)
+        as_ = [(torch.randn((S, n * r_max, K), device=dev, generator=gen) / K ** 0.5).to(torch.bfloat16)
+               for _ in range(nsets)]
+        bs = [(torch.randn((S, SO, r_max), device=dev, generator=gen) / 8).to(torch.bfloat16) for _ in range(nsets)]
         sc = torch.rand(S, device=dev, generator=gen) * 1.5 + 0.5
         ys = [torch.randn((T, SO), device=dev, generator=gen) for _ in range(nsets)]
-        h = torch.zeros((T, n, r_max), device=dev)
+        hs = [torch.zeros((T, n, r_max), device=dev) for _ in range(nsets)]
         addr = L.Addressing(ts, S)
         t_group = timed(lambda i: L.lora_addressing_build(addr, rk, r_max), reps)
-        t_shrink = timed(lambda i: L.lora_shrink(xs[i % nsets], a, addr, rk, n, r_max, h=h), reps)
-        t_expand = timed(lambda i: L.lora_expand_fused(h, b, addr, rk, sc, ys[i % nsets], slices, r_max), reps)
+        t_shrink = timed(lambda i: L.lora_shrink(xs[i % nsets], as_[i % nsets], addr, rk, n, r_max,
+                                                 h=hs[i % nsets]), reps)
+        t_expand = timed(lambda i: L.lora_expand_fused(hs[i % nsets], bs[i % nsets], addr, rk, sc, ys[i % nsets],
+                                                       slices, r_max), reps)
         rho = np.clip(rk_np, 0, r_max)
         act = (ts_np >= 0) & (ts_np < S) & (rho[np.clip(ts_np, 0, S - 1)] > 0)
         used = np.unique(ts_np[act])
@@ -256,20 +373,21 @@ def multi_lora_figures(dev, reps=20):
         sh_bytes = na * 2 * K + 2 * K * n * live + 4 * n * rho_sum
         ex_bytes = 4 * n * rho_sum + 2 * SO * live + 8 * SO * na
         out[name] = {
-            "tokens": T, "active_tokens": na, "used_slots": int(len(used)),
+            "tokens": T, "active_tokens": na, "used_slots": int(len(used)), "rotating_input_sets": nsets,
             "grouping_us": t_group,
             "shrink_us": t_shrink, "shrink_gbs": sh_bytes / t_shrink / 1e3,
             "expand_fused_us": t_expand, "expand_fused_gbs": ex_bytes / t_expand / 1e3,
             "expand_fused_frac": ex_bytes / t_expand / 1e3 / HBM_PEAK_GBS,
         }
-        if T <= 4096:
+        if T <= 4096 and graph:
             # a decode step's three calls back to back, eagerly and as one
             # captured HIP graph replayed per step (no host sync or
             # data-dependent shape in them, so a serving loop can capture them)
             def seq(i):
+                j = i % nsets
                 L.lora_addressing_build(addr, rk, r_max)
-                L.lora_shrink(xs[i % nsets], a, addr, rk, n, r_max, h=h)
-                L.lora_expand_fused(h, b, addr, rk, sc, ys[i % nsets], slices, r_max)
+                L.lora_shrink(xs[j], as_[j], addr, rk, n, r_max, h=hs[j])
+                L.lora_expand_fused(hs[j], bs[j], addr, rk, sc, ys[j], slices, r_max)
 
             side = torch.cuda.Stream(device=dev)
             side.wait_stream(torch.cuda.current_stream(dev))
@@ -283,7 +401,7 @@ def multi_lora_figures(dev, reps=20):
             out[name]["step_eager_us"] = timed(seq, reps)
             out[name]["step_graph_us"] = timed(lambda i: graph.replay(), reps)
             del graph
-        del xs, a, b, ys, h
+        del xs, as_, bs, ys, hs
     # gather_shrink over the 128256-row embedding adapter table (4.2 GB, rank index contiguous)
     T, S, r_max, V = ts5.shape[0], 128, 128, 128256
     tab = torch.randn((S, V, r_max), device=dev, generator=gen).to(torch.bfloat16).permute(0, 2, 1)
@@ -308,11 +426,27 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-adapter serving figures")
+    ap.add_argument("--multi-only", action="store_true",
+                    help="only the multi-adapter serving figures (no single-adapter step)")
+    ap.add_argument("--multi-reps", type=int, default=20, help="repetitions per multi-adapter figure")
+    ap.add_argument("--no-graph", action="store_true", help="skip the decode step's HIP-graph replays")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="summarise a rocprofv3 --pmc counter_collection.csv (MFMA busy, occupancy, LDS "
+                         "bank conflicts per kernel) into profiles/")
+    ap.add_argument("--summary-name", default="", help="file name stem for --counter-summary / --stats-summary")
+    ap.add_argument("--stats-summary", metavar="CSV",
+                    help="summarise a rocprofv3 --kernel-trace --stats kernel_stats.csv into profiles/")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="", help="the profiled command, recorded with --traffic-summary")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, args.workload, args.command)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.summary_name, args.command)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary, args.summary_name, args.command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -333,6 +467,10 @@ def main():
         sys.exit(1)
     L.load_library()
     dev = torch.device("cuda:0")
+    if args.multi_only:
+        print(json.dumps({"multi_lora": multi_lora_figures(dev, reps=args.multi_reps, graph=not args.no_graph)}),
+              flush=True)
+        return
     M, K, Lc, r, scale, seed = WORKLOADS[args.workload]
     case = synth.single_adapter(M, K, Lc, r, seed=seed, dtype="bf16", scale=scale, name=args.workload)
 
@@ -480,7 +618,7 @@ def main():
     if not args.no_multi:
         del sets
         torch.cuda.empty_cache()
-        out["multi_lora"] = multi_lora_figures(dev)
+        out["multi_lora"] = multi_lora_figures(dev, reps=args.multi_reps, graph=not args.no_graph)
     print(json.dumps(out), flush=True)
 
 

@@ -1158,10 +1158,16 @@ constexpr int kTnCols = 256;  // columns per tn_kernel workgroup
 // (2 VGPRs) and BMB output tiles (4 VGPRs) per column block; keep a stage
 // near 48 VGPRs. A shrink stage holds U*(BMB+RB) 16-byte vectors.
 constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+#ifndef LORA_SHRINK_VB
+#define LORA_SHRINK_VB 8
+#endif
+#ifndef LORA_EXPAND_VB
+#define LORA_EXPAND_VB 48
+#endif
 template <int RB, int BMB>
 struct FusedShape {
-  static constexpr int U = (8 / (BMB + RB)) > 0 ? (8 / (BMB + RB)) : 1;
-  static constexpr int NBU = pow2_floor(48 / (2 * RB + 4 * BMB));
+  static constexpr int U = (LORA_SHRINK_VB / (BMB + RB)) > 0 ? pow2_floor(LORA_SHRINK_VB / (BMB + RB)) : 1;
+  static constexpr int NBU = pow2_floor(LORA_EXPAND_VB / (2 * RB + 4 * BMB));
 };
 
 // Token blocks per fused/expand tile (rb * bmb <= 8).
