@@ -5,7 +5,6 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "../../include/lora.h"
 
@@ -84,13 +83,6 @@ inline void launch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, 
     hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0u, args...);
   else
     kernel<<<grid, block, shmem, st>>>(args...);
-}
-
-// Optional tile overrides for tuning sweeps (unset in normal use).
-inline int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
 }
 
 }  // namespace lora

@@ -19,8 +19,6 @@
 //   slot_shrink_kernel         shrink, one workgroup per (tile, slice, rank chunk)
 //   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
 //                              descriptor loads and two register stages
-//   slot_shrink_gemm_kernel    shrink with the adapter chunk staged in LDS and
-//                              shared by 8 token blocks (selectable)
 //   slot_shrink_rows_kernel    shrink for many tokens: a 128-token tile x up to
 //                              256 adapter rows (all slices) per workgroup, x
 //                              staged once in LDS, waves split the rows
@@ -678,142 +676,6 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
   }
 }
 
-// GEMM form of shrink for bf16 inputs (x and one slot's a within 2 GiB
-// descriptors, h rows 16-byte aligned). A workgroup of 8 waves owns a piece
-// of up to 128 grouped tokens of one slot; wave w owns token block w. The
-// rank rows of all slices are handled as (slice, 16-row rank block) pairs, up
-// to kPairs per pass (one pass unless the slot's rank exceeds 16*kPairs/n):
-// every 64-feature chunk of the pass's adapter rows is staged once in LDS
-// (double buffered, one barrier per chunk) and shared by the 8 token blocks,
-// while each wave streams its own tokens' features from HBM. x is read once
-// per pass, the adapter once per piece.
-constexpr int kPairs = 16;
-constexpr int kShrinkTokens = 128;
-
-__global__ __launch_bounds__(512) void slot_shrink_gemm_kernel(ShrinkArgs p) {
-  constexpr int NW = 8;
-  constexpr int KC = 64;                  // features per chunk (two MFMA steps)
-  constexpr int kAE = kPairs * 2 * 64 / (64 * NW);  // adapter-tile entries per thread
-  __shared__ uint4 als[2][kPairs * 2 * 64];  // [buf][pair][step][lane]
-  __shared__ Tile sh_tile;
-  __shared__ int sh_tok[kShrinkTokens];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  if (wave == 0) {
-    const Tile tl = find_tile(blockIdx.x, kShrinkTokens, p.counts, p.offsets, p.S);
-    if (lane == 0) sh_tile = tl;
-  }
-  __syncthreads();
-  const Tile tl = sh_tile;
-  if (tl.slot < 0) return;
-  const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
-  const int nq = (rho + 15) / 16;
-  if (nq == 0) return;
-  if (threadIdx.x < kShrinkTokens)
-    sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
-  __syncthreads();
-
-  const int tix = 16 * wave + col;
-  const bool tok_ok = tix < tl.len;
-  const bool blk_any = 16 * wave < tl.len;
-  const int t = sh_tok[tix];
-  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
-  const rsrc_t ra = make_rsrc(static_cast<const uint16_t*>(p.a) + (int64_t)tl.slot * p.as0,
-                              (int64_t)p.n_slices * p.r_max * p.as1 * 2);
-  const uint32_t xrow = tok_ok ? static_cast<uint32_t>((int64_t)t * p.ldx * 2) : kOOB;
-  const int K = static_cast<int>(p.K);
-  const int nch = (K + KC - 1) / KC;
-  const int npairs = p.n_slices * nq;
-
-  for (int p0 = 0; p0 < npairs; p0 += kPairs) {
-    const int rp = (npairs - p0 < kPairs) ? npairs - p0 : kPairs;
-    // this thread's share of the chunk's adapter tile: entries e = tid + 512*i,
-    // e -> (pair, step, lane) in operand order
-    uint4 areg[kAE];
-    uint32_t aoff[kAE];
-    int ak[kAE];  // feature offset of the entry within a chunk
-    bool aok[kAE];
-#pragma unroll
-    for (int i = 0; i < kAE; ++i) {
-      const int e = threadIdx.x + 512 * i;
-      const int pr = e >> 7;
-      const int l = e & 63;
-      const int stp = (e >> 6) & 1;
-      aok[i] = pr < rp;
-      const int pg = p0 + pr;
-      const int sl = pg / nq;
-      const int q = pg - sl * nq;
-      const int row = 16 * q + (l & 15);
-      ak[i] = stp * 32 + (l >> 4) * 8;
-      aoff[i] = (aok[i] && row < rho)
-                    ? static_cast<uint32_t>(((int64_t)(sl * p.r_max + row) * p.as1 + stp * 32 + (l >> 4) * 8) * 2)
-                    : kOOB;
-    }
-    auto load_a = [&](int c) {
-#pragma unroll
-      for (int i = 0; i < kAE; ++i)
-        areg[i] = bload16(ra, (aoff[i] != kOOB && c * KC + ak[i] < K) ? aoff[i] + static_cast<uint32_t>(c * KC * 2)
-                                                                           : kOOB);
-    };
-    uint4 xr[2];
-    auto load_x = [&](int c) {
-#pragma unroll
-      for (int stp = 0; stp < 2; ++stp) {
-        const int k = c * KC + stp * 32 + grp * 8;
-        xr[stp] = sload16(rx, (xrow != kOOB && k < K) ? xrow + static_cast<uint32_t>(k * 2) : kOOB);
-      }
-    };
-    f32x4_t acc[kPairs];
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    load_a(0);
-    load_x(0);
-    for (int c = 0; c < nch; ++c) {
-      uint4* buf = als[c & 1];
-#pragma unroll
-      for (int i = 0; i < kAE; ++i)
-        if (aok[i]) buf[threadIdx.x + 512 * i] = areg[i];
-      const uint4 x0 = xr[0], x1 = xr[1];
-      __syncthreads();
-      load_a(c + 1);  // masked past the last chunk
-      load_x(c + 1);
-      if (blk_any) {
-#pragma unroll
-        for (int pr = 0; pr < kPairs; ++pr) {
-          if (pr < rp) {
-            mma_vec<BF16>(acc[pr], buf[(pr * 2 + 0) * 64 + lane], x0);
-            mma_vec<BF16>(acc[pr], buf[(pr * 2 + 1) * 64 + lane], x1);
-          }
-        }
-      }
-    }
-    // h[t][slice][16q + 4grp + i] = acc[pr][i] for rank rows below rho
-    if (tok_ok) {
-#pragma unroll
-      for (int pr = 0; pr < kPairs; ++pr) {
-        if (pr < rp) {
-          const int pg = p0 + pr;
-          const int sl = pg / nq;
-          const int j = 16 * (pg - sl * nq) + 4 * grp;
-          float* hrow = p.h + (int64_t)t * p.hs0 + (int64_t)sl * p.hs1;
-          if (j + 4 <= rho) {
-            st16f(hrow + j, acc[pr]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (j + e < rho) hrow[j + e] = acc[pr][e];
-          }
-        }
-      }
-    }
-    __syncthreads();  // the next pass rewrites both buffers
-  }
-}
-
 // Row-split shrink for bf16 inputs (x and one slot's a within 2 GiB
 // descriptors). A workgroup owns a tile of up to 128 grouped tokens of one
 // slot against up to 16 (slice, 16-row rank block) pairs: 256 adapter rows
@@ -1061,7 +923,6 @@ struct ExpandArgs {
   int64_t chunk_cols;  // columns per chunk (streaming kernel)
   int64_t y_bytes;     // bytes of y a descriptor may span (streaming and owner kernels)
   int64_t h_bytes;     // bytes of h a descriptor may span (owner kernel)
-  int xcd_group;       // owner kernel: consecutive work items per XCD group
   int n_work;          // owner kernel: pieces x total_chunks work items
   bool h_vec;  // h rows 16-byte aligned
   bool b_vec;  // b rows aligned for 4-element loads
@@ -1350,7 +1211,7 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   // so G consecutive chunks of a piece (which read the same h rows) share an
   // XCD's L2. A bijection onto [0, gridDim.x); the grid is padded to a
   // multiple of 8 G and the items past n_work exit.
-  const int G = p.xcd_group;
+  constexpr int G = kOwnerGroup;
   const int kx = static_cast<int>(blockIdx.x >> 3);
   const int item = ((kx / G) * 8 + static_cast<int>(blockIdx.x & 7)) * G + kx % G;
   if (item >= p.n_work) return;
@@ -1597,7 +1458,7 @@ static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream
 template <class Tag>
 static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
   a.n_work = static_cast<int>(pieces * a.total_chunks);
-  const dim3 grid(static_cast<unsigned>(a.xcd_group == 1 ? a.n_work : round_up(a.n_work, 8 * a.xcd_group)));
+  const dim3 grid(static_cast<unsigned>(round_up(a.n_work, 8 * kOwnerGroup)));
   switch (rbm) {
     case 1: launch((slot_expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
     case 2: launch((slot_expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
@@ -1625,10 +1486,9 @@ extern "C" int lora_addressing_build(const lora_addressing* addr, const int32_t*
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
   if (addr->S > 0 && !addr->counts) return LORA_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // LORA_GROUP: 1 one workgroup, 2 one workgroup per 1024-token chunk
-  // (default up to kGroupChunkMaxT tokens)
-  const int mode = env_int("LORA_GROUP", 2);
-  if (mode == 2 && addr->T <= kGroupChunkMaxT) {
+  // one workgroup per 1024-token chunk up to kGroupChunkMaxT tokens (each
+  // holds every token's key in registers), one workgroup beyond
+  if (addr->T <= kGroupChunkMaxT) {
     const int chunks = addr->T > 0 ? static_cast<int>(ceil_div(addr->T, 1024)) : 1;
     launch(group_chunk_kernel, dim3(static_cast<unsigned>(chunks)), dim3(1024), 0, st, addr->token_slot, addr->T,
            addr->S, ranks, r_max, addr->counts, addr->offsets, addr->sorted_tokens);
@@ -1692,38 +1552,22 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
   p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Schedule (LORA_MULTI_SHRINK overrides it for tuning sweeps): the
-  // row-split kernel for bf16 batches of 1024 tokens or more (4; 5-7 are its
-  // other tile shapes), the pipelined general kernel for fewer tokens or f32
-  // (3), the general kernel where x or one slot's adapter exceeds a 2 GiB
-  // descriptor (2). The GEMM form (1) reads x once per pass but, with one
-  // chunk of prefetch and a barrier per chunk, is latency-bound and measures
-  // slower on the prefill workload.
-  const int force = env_int("LORA_MULTI_SHRINK", 0);
+  // Schedule, from the shapes: the row-split kernel for bf16 batches of 1024
+  // tokens or more; the pipelined kernel for fewer tokens or f32; the general
+  // kernel (no buffer descriptors) where x or one slot's adapter spans more
+  // than a 2 GiB descriptor.
   const bool desc_ok = T * x->stride_row * (int64_t)es <= kMaxBufferBytes &&
                        (int64_t)num_slices * r_max * a->s1 * (int64_t)es <= kMaxBufferBytes && K < (int64_t(1) << 30);
   p.x_bytes = T * x->stride_row * (int64_t)es;
-  const bool gemm_ok = desc_ok && x->dtype == LORA_BF16 && p.h_vec && K % 8 == 0;
-  const int mode = force >= 1 && force <= 7 ? force : (x->dtype == LORA_BF16 && T >= 1024 ? 4 : 3);
-  if (desc_ok && x->dtype == LORA_BF16 && mode >= 4) {
-    const int tt = mode <= 5 ? 8 : 4;
+  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024) {
+    constexpr int tt = 8;  // 16-token blocks per row-split tile
     p.row_groups = static_cast<int>(ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 16));
     const int64_t rtiles = ceil_div(T, 16 * tt) + S;
     const dim3 grid(static_cast<unsigned>(round_up(rtiles, 8 * kRowsGroup) * p.row_groups));
-    switch (mode) {
-      case 4: launch((slot_shrink_rows_kernel<8, 2>), grid, dim3(256), 0, st, p); break;
-      case 5: launch((slot_shrink_rows_kernel<8, 4>), grid, dim3(256), 0, st, p); break;
-      case 6: launch((slot_shrink_rows_kernel<4, 2>), grid, dim3(256), 0, st, p); break;
-      default: launch((slot_shrink_rows_kernel<4, 4>), grid, dim3(256), 0, st, p); break;
-    }
+    launch((slot_shrink_rows_kernel<tt, 2>), grid, dim3(256), 0, st, p);
     return launch_status();
   }
-  if (gemm_ok && mode == 1) {
-    const int64_t pieces = ceil_div(T, kShrinkTokens) + S;
-    launch(slot_shrink_gemm_kernel, dim3(static_cast<unsigned>(pieces)), dim3(512), 0, st, p);
-    return launch_status();
-  }
-  const bool pipe = desc_ok && mode != 2;
+  const bool pipe = desc_ok;
   if (x->dtype == LORA_BF16)
     launch_shrink<BF16>(p, bmb, rb, tiles, pipe, st);
   else
@@ -1789,14 +1633,14 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   p.n_slices = num_slices;
   const int rbm = rank_blocks(r_max);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Streaming kernel when its descriptors can span y and one slot's b with
-  // 32-bit offsets and the rows allow vector loads; else the general kernel.
-  // LORA_MULTI_EXPAND: 1 streaming, 2 column owner, 3 general (default: by T)
-  const int force = env_int("LORA_MULTI_EXPAND", 0);
-  const bool stream_ok = force != 3 && p.h_vec && p.b_vec && (T * y->stride_row * 4 <= kMaxBufferBytes) &&
+  // Schedule, from the shapes: the column-owner kernel for 2048 tokens or
+  // more, the streaming kernel for fewer, both when their descriptors can
+  // span y, h and one slot's b with 32-bit offsets and the rows of h and b
+  // allow vector loads; else the general kernel.
+  const bool stream_ok = p.h_vec && p.b_vec && (T * y->stride_row * 4 <= kMaxBufferBytes) &&
                          (O * b->s1 * (int64_t)es <= kMaxBufferBytes) && y->stride_row < (int64_t(1) << 30);
   const bool owner_ok = stream_ok && T * h->s0 * 4 <= kMaxBufferBytes;
-  if (owner_ok && (force == 2 || (force == 0 && T >= 2048))) {
+  if (owner_ok && T >= 2048) {
     // many tokens: column owners, weights read once per token piece
     p.chunk_cols = kOwnerCols;
     int64_t off = 0;
@@ -1814,8 +1658,6 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
     p.y_bytes = T * y->stride_row * 4;
     p.h_bytes = T * h->s0 * 4;
     const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
-    const int64_t grp = env_int("LORA_OWNER_GROUP", 0);
-    p.xcd_group = grp >= 1 && grp <= 128 ? static_cast<int>(grp) : kOwnerGroup;
     if (b->dtype == LORA_BF16)
       launch_expand_owner<BF16>(p, rbm, pieces, st);
     else

@@ -24,13 +24,10 @@
 //                 planes) for the weight-gradient kernels. Streamed tensors
 //                 are loaded and stored with the non-temporal cache policy.
 //   shrink_kernel the same shrink alone, writing s*H as gradient planes and/or
-//                 MFMA fragments for the split expands below.
-//   expand_cols_kernel  column-owner expand (outputs wider than 8192 or long
-//                 feature axes): a workgroup stages its W2 column slice in LDS
+//                 MFMA fragments for the column-owner expand below.
+//   expand_cols_kernel  column-owner expand (contractions longer than 8192
+//                 features): a workgroup stages its W2 column slice in LDS
 //                 once and walks token tiles.
-//   expand_kernel, shrink_tok_kernel, expand_tok_kernel  further schedules
-//                 (column split; token-split waves with W panels in LDS),
-//                 selectable with LORA_EXPAND_MODE.
 //   tn_kernel     weight-gradient partial sums over a chunk of tokens:
 //                 part[p][n][j] = sum_m Z[m][n] * G[j][m]. Z tiles are staged
 //                 in LDS (XOR-swizzled rows) and read transposed.
@@ -157,13 +154,7 @@ struct FusedArgs {
   int64_t M, Kin, Nout;
   int r, rp;
   float scale;
-  // expand work split: nsplit workgroups per token tile, nbs 16-column blocks
-  // each; tiles = token tiles present; rot = column-walk rotation per tile
-  int nsplit;
-  int64_t nbs;
-  int64_t tiles;
-  int rot;
-  int rows_out;  // fused kernel: row-linear output access (expand_tile_rows) or MFMA layout
+  int64_t tiles;  // token tiles present
 };
 
 // ---- shrink of one token tile --------------------------------------------
@@ -383,103 +374,22 @@ __device__ __forceinline__ void emit_planes(const FusedArgs& p, int64_t m0, cons
   }
 }
 
-// ---- expand of one token tile over a column range -----------------------
-// out^T tile (16 columns x 16 tokens) (+)= W2 * (s*H)^T for the 16-column
-// blocks [nb_begin, nb_end). Wave w takes NBU consecutive blocks per stage
-// (the NW waves cover NW*NBU adjacent blocks together); two stages in flight.
-// The stage order is rotated by `rot` so that tiles in flight at the same
-// time do not walk the same column offsets in lockstep. Output rows past M lie
-// outside the output descriptor (loads read 0, stores are dropped); columns
-// past the range use kOOB.
-template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
-__device__ __forceinline__ void expand_tile(const FusedArgs& p, int64_t m0, int64_t nb_begin, int64_t nb_end,
-                                            int64_t rot, const uint4 (&hf)[BMB][RB]) {
-  using E = typename Tag::elem;
-  constexpr int ES = sizeof(E);
-  using WF = WFrag<Tag>;
-  using wf_t = typename WF::type;
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
-  const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
-  constexpr int gstep = NW * NBU;
-  const int nst = uniform_int((nb_end - nb_begin + gstep - 1) / gstep);
-  const int r0 = nst > 0 ? uniform_int(rot % nst) : 0;
-  uint32_t orow[BMB];
-#pragma unroll
-  for (int b = 0; b < BMB; ++b) orow[b] = static_cast<uint32_t>((16 * b + col) * p.ldo * 4);
-  // first column block of this wave in stage k (nb_end when k is past the end)
-  auto stage_nb = [&](int k) -> int64_t {
-    const int kk = k + r0;
-    const int64_t v = nb_begin + (kk - (kk >= nst ? nst : 0)) * gstep + wave * NBU;
-    return k < nst ? v : nb_end;
-  };
-  auto ooff = [&](int b, int64_t nb) -> uint32_t {
-    const int64_t ncol = nb * 16 + 4 * grp;
-    return (nb < nb_end && ncol < p.Nout) ? orow[b] + static_cast<uint32_t>(ncol * 4) : kOOB;
-  };
-  auto load2 = [&](wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NBU][BMB], int64_t nb0) {
-#pragma unroll
-    for (int u = 0; u < NBU; ++u) {
-      const int64_t nb = nb0 + u;
-      const int64_t nrow = (nb < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const int j0 = 16 * q + 4 * grp;
-        wv[u][q] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
-      }
-#pragma unroll
-      for (int b = 0; b < BMB; ++b) {
-        if constexpr (ACCUM)
-          cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ro, ooff(b, nb)));
-        else
-          cv[u][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-  auto comp2 = [&](const wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NBU][BMB], int64_t nb0) {
-#pragma unroll
-    for (int u = 0; u < NBU; ++u) {
-#pragma unroll
-      for (int b = 0; b < BMB; ++b) {
-#pragma unroll
-        for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
-        sstore16(ro, ooff(b, nb0 + u), __builtin_bit_cast(uint4, cv[u][b]));
-      }
-    }
-  };
-  // two stages in flight; stages past the end read zeros and store nothing,
-  // so the loop body needs no exit in the middle (an odd stage count ends
-  // with one such stage)
-  wf_t wvA[NBU][RB], wvB[NBU][RB];
-  f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
-  if (nst > 0) {
-    load2(wvA, cvA, stage_nb(0));
-    for (int k = 0; k < nst; k += 2) {
-      load2(wvB, cvB, stage_nb(k + 1));
-      sched_fence();
-      comp2(wvA, cvA, stage_nb(k));
-      sched_fence();
-      load2(wvA, cvA, stage_nb(k + 2));
-      sched_fence();
-      comp2(wvB, cvB, stage_nb(k + 1));
-      sched_fence();
-    }
-  }
-}
-
-// ---- expand with row-linear output access ----------------------------------
-// Same product as expand_tile, but the output is read and written one row
-// segment at a time: each stage's MFMA products (16 columns x 16 tokens per
-// tile, in MFMA layout) go to this wave's LDS tile, and lanes then take 16-byte
-// pieces of whole rows (CW/4 lanes per row of the stage's CW columns), add
-// the output row-linearly (ACCUM) and store it. Row segments of 512 bytes per
-// instruction pair reach HBM as whole lines, which streams markedly faster
-// than the 64-byte-per-row pieces of the MFMA layout when one workgroup owns
-// a token tile's full rows. The LDS tile is private to the wave (LDS
-// instructions of one wave complete in order), so no barrier is needed.
+// ---- expand of one token tile over all output columns ----------------------
+// out^T tile (16 columns x 16 tokens) (+)= W2 * (s*H)^T for every 16-column
+// block; wave w takes NBU consecutive blocks per stage (the NW waves cover
+// NW*NBU adjacent blocks together), two stages in flight, and the stage walk
+// starts at stage `rot` (mod the stage count) so that tiles in flight at the
+// same time do not walk the same column offsets in lockstep. The output is
+// read and written one row segment at a time: each stage's MFMA products (16
+// columns x 16 tokens per tile, in MFMA layout) go to this wave's LDS tile,
+// and lanes then take 16-byte pieces of whole rows (CW/4 lanes per row of the
+// stage's CW columns), add the output row-linearly (ACCUM) and store it. Row
+// segments of 512 bytes per instruction pair reach HBM as whole lines, which
+// streams markedly faster than the 64-byte-per-row pieces of the MFMA layout
+// when one workgroup owns a token tile's full rows. The LDS tile is private to
+// the wave (LDS instructions of one wave complete in order), so no barrier is
+// needed. Output rows past M lie outside the output descriptor (loads read 0,
+// stores are dropped).
 template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
 __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0, int64_t rot,
                                                  const uint4 (&hf)[BMB][RB], float* obuf) {
@@ -576,11 +486,11 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 // Fused shrink -> expand: one workgroup per token tile, the rank intermediate
 // never leaves registers and LDS (optionally also written as planes for the
 // gradient kernels).
-template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G, bool ROWS>
+template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G>
 __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
   __shared__ __attribute__((aligned(16))) char shr[SS::TOTAL];
-  __shared__ float obuf[ROWS ? NW : 1][ROWS ? 16 * BMB * (16 * NBU + 4) : 1];
+  __shared__ float obuf[NW][16 * BMB * (16 * NBU + 4)];
   auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   const int64_t tile = blockIdx.x;
   const int64_t m0 = tile * (16 * BMB);
@@ -590,10 +500,7 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   if constexpr (EMIT_G) {
     if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
-  if constexpr (ROWS)
-    expand_tile_rows<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, tile * p.rot, hf, obuf[wave_id()]);
-  else
-    expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, 0, (p.Nout + 15) / 16, tile * p.rot, hf);
+  expand_tile_rows<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, tile, hf, obuf[wave_id()]);
 }
 
 // Shrink only: s*H of each token tile, written as gradient-kernel planes
@@ -620,32 +527,6 @@ __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
         for (int q = 0; q < RB; ++q) p.frag[((m0 / 16 + b) * RB + q) * 64 + lane] = hf[b][q];
     }
   }
-}
-
-// Column-split expand from fragments: nsplit workgroups per token tile, each
-// over nbs column blocks. Workgroups are dispatched round-robin over the 8
-// XCDs (id mod 8); ids are mapped so that the splits of one tile run on the
-// same XCD in consecutive slots, which keeps the tile's fragments in that
-// XCD's L2 and the rows being updated at any time few and adjacent.
-template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
-__global__ __launch_bounds__(64 * NW) void expand_kernel(FusedArgs p) {
-  const int64_t bid = blockIdx.x;
-  const int64_t xcd = bid & 7;
-  const int64_t kk = bid >> 3;
-  const int64_t tile = (kk / p.nsplit) * 8 + xcd;
-  const int64_t split = kk % p.nsplit;
-  if (tile >= p.tiles) return;
-  const int64_t m0 = tile * (16 * BMB);
-  const int lane = threadIdx.x & 63;
-  uint4 hf[BMB][RB];
-#pragma unroll
-  for (int b = 0; b < BMB; ++b)
-#pragma unroll
-    for (int q = 0; q < RB; ++q) hf[b][q] = p.frag[((m0 / 16 + b) * RB + q) * 64 + lane];
-  const int64_t nnb = (p.Nout + 15) / 16;
-  const int64_t nb_begin = split * p.nbs;
-  const int64_t nb_end = (nb_begin + p.nbs < nnb) ? nb_begin + p.nbs : nnb;
-  expand_tile<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, nb_begin, nb_end, 0, hf);
 }
 
 // Column-owner expand. Workgroup (c, g) owns the 16-column blocks
@@ -745,203 +626,6 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
   if (blockIdx.y < p.tiles) {
     load_tile(hfA, cvA, blockIdx.y);
     for (int64_t t = blockIdx.y; t < p.tiles; t += 2 * gstride) {
-      load_tile(hfB, cvB, t + gstride);
-      sched_fence();
-      comp_tile(hfA, cvA, t);
-      sched_fence();
-      load_tile(hfA, cvA, t + 2 * gstride);
-      sched_fence();
-      comp_tile(hfB, cvB, t + gstride);
-      sched_fence();
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Token-split shrink: wave w of the workgroup owns the 16-token block
-// tile*NW + w and contracts it over the whole feature axis, so no cross-wave
-// reduction is needed. The first weight is staged in LDS one panel of KP
-// features at a time (MFMA operand order, double-buffered) and shared by all
-// waves; each wave streams its own stream rows one panel ahead of use.
-// ---------------------------------------------------------------------------
-template <class Tag, int NW, int RB, int KP, bool EMIT_G, bool EMIT_F>
-__global__ __launch_bounds__(64 * NW) void shrink_tok_kernel(FusedArgs p) {
-  using E = typename Tag::elem;
-  constexpr int VEC = Tag::VEC;
-  constexpr int ES = sizeof(E);
-  constexpr int CH = 4 * VEC;             // features per MFMA step
-  constexpr int NSTEP = KP / CH;          // steps per panel
-  constexpr int PVEC = RB * 16 * KP / VEC;  // 16-byte weight vectors per panel
-  constexpr int PV = (PVEC + 64 * NW - 1) / (64 * NW);
-  __shared__ uint4 wpan[2][NSTEP * RB * 64];  // [buffer][step][rank block][lane]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int64_t m0 = ((int64_t)blockIdx.x * NW + wave) * 16;  // this wave's token block
-  const rsrc_t rz = make_rsrc(static_cast<const E*>(p.z) + m0 * p.ldz, (p.M - m0) * p.ldz * ES);
-  const rsrc_t rw1 = make_rsrc(p.w1, (int64_t)p.r * p.ldw1 * ES);
-  const uint32_t zrow = static_cast<uint32_t>((col * p.ldz + grp * VEC) * ES);
-  const int64_t npan = (p.Kin + KP - 1) / KP;
-
-  // weight panel: thread vector i -> rank row j, features kk..kk+VEC-1 of the panel
-  uint4 wreg[PV];
-  auto load_panel = [&](int64_t pan) {
-#pragma unroll
-    for (int v = 0; v < PV; ++v) {
-      const int i = threadIdx.x + v * 64 * NW;
-      const int j = i / (KP / VEC);
-      const int kk = (i - j * (KP / VEC)) * VEC;
-      const int64_t k = pan * KP + kk;
-      const bool ok = i < PVEC && pan < npan && k < p.Kin;
-      wreg[v] = bload16(rw1, ok ? static_cast<uint32_t>(((int64_t)j * p.ldw1 + k) * ES) : kOOB);
-    }
-  };
-  auto store_panel = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < PV; ++v) {
-      const int i = threadIdx.x + v * 64 * NW;
-      if (i < PVEC) {
-        const int j = i / (KP / VEC);
-        const int kk = (i - j * (KP / VEC)) * VEC;
-        const int c = kk / CH;
-        const int g = (kk - c * CH) / VEC;
-        wpan[buf][(c * RB + (j >> 4)) * 64 + g * 16 + (j & 15)] = wreg[v];
-      }
-    }
-  };
-  uint4 zA[NSTEP], zB[NSTEP];
-  auto load_z = [&](uint4 (&zf)[NSTEP], int64_t pan) {
-#pragma unroll
-    for (int c = 0; c < NSTEP; ++c) {
-      const int64_t k = pan * KP + c * CH + grp * VEC;
-      zf[c] = sload16(rz, (pan < npan && k < p.Kin) ? zrow + static_cast<uint32_t>((pan * KP + c * CH) * ES) : kOOB);
-    }
-  };
-  f32x4_t acc[RB];
-#pragma unroll
-  for (int q = 0; q < RB; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto comp = [&](const uint4 (&zf)[NSTEP], int buf) {
-#pragma unroll
-    for (int c = 0; c < NSTEP; ++c)
-#pragma unroll
-      for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[q], wpan[buf][(c * RB + q) * 64 + lane], zf[c]);
-  };
-
-  // prologue: panel 0 into LDS, stream rows of panel 0 in flight
-  load_panel(0);
-  load_z(zA, 0);
-  store_panel(0);
-  __syncthreads();
-  for (int64_t pan = 0; pan < npan; pan += 2) {
-    // panel pan (buffer 0, rows zA) is ready; fetch panel pan+1
-    load_panel(pan + 1);
-    load_z(zB, pan + 1);
-    comp(zA, 0);
-    store_panel(1);
-    __syncthreads();
-    if (pan + 1 >= npan) break;
-    load_panel(pan + 2);
-    load_z(zA, pan + 2);
-    comp(zB, 1);
-    store_panel(0);
-    __syncthreads();
-  }
-
-  uint4 hf[RB];
-#pragma unroll
-  for (int q = 0; q < RB; ++q) {
-    acc[q] *= p.scale;
-    hf[q] = split_frag<Tag>(acc[q]);
-  }
-  if constexpr (EMIT_G) {
-    const f32x4_t (&a1)[1][RB] = reinterpret_cast<const f32x4_t (&)[1][RB]>(acc);
-    const uint4 (&h1)[1][RB] = reinterpret_cast<const uint4 (&)[1][RB]>(hf);
-    emit_planes<Tag, RB, 1>(p, m0, a1, h1);
-  }
-  if constexpr (EMIT_F) {
-    if (m0 < round_up_dev(p.M, 64)) {
-#pragma unroll
-      for (int q = 0; q < RB; ++q) p.frag[((m0 / 16) * RB + q) * 64 + lane] = hf[q];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Token-split column-owner expand: workgroup (c, g) owns the 16-column blocks
-// [c*NBS, (c+1)*NBS) with its W2 slice in LDS (MFMA operand order); wave w
-// updates token block tile*NW + w of the tiles g, g+G, ...; the output tiles
-// of the next token tile are loaded while the current one is computed.
-// ---------------------------------------------------------------------------
-template <class Tag, int NW, int RB, int NBS, bool ACCUM>
-__global__ __launch_bounds__(64 * NW) void expand_tok_kernel(FusedArgs p) {
-  using E = typename Tag::elem;
-  constexpr int ES = sizeof(E);
-  using WF = WFrag<Tag>;
-  using wf_t = typename WF::type;
-  __shared__ wf_t w2s[NBS * RB * 64];
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int64_t nnb = (p.Nout + 15) / 16;
-  const int64_t nb_base = (int64_t)blockIdx.x * NBS;
-  {
-    const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
-    for (int i = threadIdx.x; i < NBS * RB * 64; i += 64 * NW) {
-      const int l = i & 63;
-      const int q = (i >> 6) % RB;
-      const int nbl = (i >> 6) / RB;
-      const int64_t nb = nb_base + nbl;
-      const int64_t n = nb * 16 + (l & 15);
-      const int j0 = 16 * q + 4 * (l >> 4);
-      const int64_t nrow = (nb < nnb && n < p.Nout) ? n : p.Nout;  // p.Nout: outside rw2
-      w2s[i] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
-    }
-  }
-  __syncthreads();
-  const int64_t nblk = (p.M + 15) / 16;     // 16-token blocks present
-  const int64_t ntile = (nblk + NW - 1) / NW;
-  const int64_t gstride = gridDim.y;
-  uint32_t coff[NBS];
-#pragma unroll
-  for (int u = 0; u < NBS; ++u) {
-    const int64_t nb = nb_base + u;
-    const int64_t ncol = nb * 16 + 4 * grp;
-    coff[u] = (nb < nnb && ncol < p.Nout) ? static_cast<uint32_t>((col * p.ldo + ncol) * 4) : kOOB;
-  }
-  auto block_of = [&](int64_t t) -> int64_t { return t * NW + wave; };
-  auto load_tile = [&](uint4 (&hf)[RB], f32x4_t (&cv)[NBS], int64_t t) {
-    const int64_t blk = block_of(t);
-    const bool ok = t < ntile && blk < nblk;
-#pragma unroll
-    for (int q = 0; q < RB; ++q) hf[q] = ok ? p.frag[(blk * RB + q) * 64 + lane] : zero4();
-    if constexpr (ACCUM) {
-      const rsrc_t ro = make_rsrc(p.out + blk * 16 * p.ldo, ok ? (p.M - blk * 16) * p.ldo * 4 : 0);
-#pragma unroll
-      for (int u = 0; u < NBS; ++u) cv[u] = __builtin_bit_cast(f32x4_t, sload16(ro, coff[u]));
-    } else {
-#pragma unroll
-      for (int u = 0; u < NBS; ++u) cv[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  auto comp_tile = [&](const uint4 (&hf)[RB], f32x4_t (&cv)[NBS], int64_t t) {
-    const int64_t blk = block_of(t);
-    const rsrc_t ro = make_rsrc(p.out + blk * 16 * p.ldo, blk < nblk ? (p.M - blk * 16) * p.ldo * 4 : 0);
-#pragma unroll
-    for (int u = 0; u < NBS; ++u) {
-#pragma unroll
-      for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u], WF::operand(w2s[(u * RB + q) * 64 + lane]), hf[q]);
-      sstore16(ro, coff[u], __builtin_bit_cast(uint4, cv[u]));
-    }
-  };
-  uint4 hfA[RB], hfB[RB];
-  f32x4_t cvA[NBS], cvB[NBS];
-  // two tiles in flight; a tile past the last reads zeros and stores nothing
-  if (blockIdx.y < ntile) {
-    load_tile(hfA, cvA, blockIdx.y);
-    for (int64_t t = blockIdx.y; t < ntile; t += 2 * gstride) {
       load_tile(hfB, cvB, t + gstride);
       sched_fence();
       comp_tile(hfA, cvA, t);
@@ -1142,16 +826,10 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// host-side launch helpers
+// host-side schedule plan and launch helpers
 // ---------------------------------------------------------------------------
 
 constexpr int kTnCols = 256;  // columns per tn_kernel workgroup
-
-// ---------------------------------------------------------------------------
-// tile and strategy choices (host). Every (rank blocks, token blocks) pair a
-// chooser returns has a kernel instance in the dispatch switches below. The
-// LORA_* environment variables override the defaults for tuning sweeps only.
-// ---------------------------------------------------------------------------
 
 // Stage sizes: U contraction chunks (shrink) and NBU column blocks (expand)
 // per pipeline stage. A bf16 expand stage holds RB weight fragments
@@ -1170,35 +848,48 @@ struct FusedShape {
   static constexpr int NBU = pow2_floor(LORA_EXPAND_VB / (2 * RB + 4 * BMB));
 };
 
-// Token blocks per fused/expand tile (rb * bmb <= 8).
-static int pick_bmb_expand(const char* env, int64_t M, int rb, int64_t wgs_per_tile) {
-  int bmb = env_int(env, 0);
-  if ((bmb == 1 || bmb == 2 || bmb == 4) && bmb * rb <= 8) return bmb;
+// ---------------------------------------------------------------------------
+// Schedule plan. Every choice follows from the shapes alone (no run-time
+// tuning, no environment); each branch is reached by shape in the parity
+// tests. Measured on the MI355X (rocprofv3 kernel traces):
+//
+//  - contraction <= 8192 features: fused_kernel (one launch, the rank
+//    intermediate stays on chip), 4 waves. Token blocks (16 tokens each) per
+//    tile: forward 4 or 2 while rb*bmb <= 8 and the grid keeps >= 512
+//    workgroups, else 1; dX (no output loads) 2 at rank <= 16 while >= 256
+//    workgroups, else 1 (8192 x 4096, rank 16: 63.6 against 67.0 us).
+//  - contraction > 8192 features (the dX of an MLP-up layer contracts over
+//    its 14336 outputs): shrink_kernel writes s*H as MFMA fragments, then
+//    expand_cols_kernel (column owner, W2 slice staged in LDS once) updates
+//    the output; measured faster there than the fused kernel.
+//  - shrink tiles: 16*bmb tokens with bmb 4 or 2 while rb*bmb <= 16 and
+//    >= 256 workgroups; 1 at rank <= 16 (twice the workgroups measure faster
+//    there: 34.8 against 36.7 us for the X*A shrink at 8192 x 4096, rank 16);
+//    8 waves while the cross-wave partial-sum buffer stays <= 32 KB, else 4.
+//  - column-owner expand: token blocks as the fused forward with 8
+//    workgroups per tile counted; token groups >= 64 and enough to fill the
+//    chip twice for narrow outputs, at most one per tile.
+//  - weight-gradient token chunks: about 512 workgroups in all, at most one
+//    chunk per 64 tokens (P = 32 at 8192 x 4096 measured best: 16 chunks
+//    16.5, 64 chunks 16.7 us against 15.1 us).
+// ---------------------------------------------------------------------------
+
+constexpr int64_t kFusedMaxContraction = 8192;
+
+struct SinglePlan {
+  bool fused;        // fused_kernel, else shrink_kernel + expand_cols_kernel
+  int bmb;           // token blocks per fused tile, or per expand_cols tile
+  int bmb_shrink;    // token blocks per shrink_kernel tile (its waves: launch_shrink)
+};
+
+static int bmb_expand(int64_t M, int rb, int64_t wgs_per_tile) {
   for (int c : {4, 2}) {
     if (c * rb <= 8 && ceil_div(M, 16 * c) * wgs_per_tile >= 512) return c;
   }
   return 1;
 }
 
-// Token blocks per tile of the fused dX kernel (no output loads): 32-token
-// tiles at rank <= 16 while they still give >= 256 workgroups (measured on
-// 8192 tokens x 4096 features, rank 16: 63.6 us against 67.0 us with 16-token
-// tiles, where the forward, which also loads its output, is slower with 32);
-// LORA_DX_BMB overrides.
-static int pick_bmb_dx(int64_t M, int rb) {
-  const int bmb = env_int("LORA_DX_BMB", 0);
-  if ((bmb == 1 || bmb == 2 || bmb == 4) && bmb * rb <= 8) return bmb;
-  return (rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1;
-}
-
-// Token blocks per shrink tile (rb * bmb <= 16): large tiles share each weight
-// chunk among more tokens, while keeping >= 256 workgroups. At rank <= 16 the
-// weight rows are few and staged row-linearly with the stream, and 16-token
-// tiles (twice the workgroups) measure faster (8192 x 4096, rank 16: 34.8
-// against 36.7 us for the X*A shrink of lora_bwd_db).
-static int pick_bmb_shrink(int64_t M, int rb) {
-  int bmb = env_int("LORA_SHRINK_BMB", 0);
-  if ((bmb == 1 || bmb == 2 || bmb == 4) && bmb * rb <= 16) return bmb;
+static int bmb_shrink(int64_t M, int rb) {
   if (rb == 1) return 1;
   for (int c : {4, 2}) {
     if (c * rb <= 16 && ceil_div(M, 16 * c) >= 256) return c;
@@ -1206,34 +897,35 @@ static int pick_bmb_shrink(int64_t M, int rb) {
   return 1;
 }
 
-// Waves per workgroup: 8 while the partial-sum buffer stays <= 32 KB, else 4
-// (dflt8 = 0: 4 unless overridden; the fused kernel streams best with 4).
-static int pick_nw(const char* env, int rb, int bmb, int dflt8 = 1) {
-  const int over = env_int(env, 0);
-  if ((over == 4 && rb * bmb <= 16) || (over == 8 && rb * bmb <= 4)) return over;
-  return (dflt8 && 8 * rb * bmb <= 32) ? 8 : 4;
+// Column blocks per expand_cols workgroup: NW * NBU with the W2 slice in at
+// most 64 KB of LDS (bf16 fragments take 8 bytes per lane, f32 16).
+template <class Tag, int RB>
+struct ColsShape {
+  static constexpr int NW = 4;
+  static constexpr int WBYTES = (sizeof(typename Tag::elem) == 2) ? 8 : 16;
+  static constexpr int NBU0 = 65536 / (NW * RB * 64 * WBYTES);
+  static constexpr int NBU = NBU0 >= 8 ? 8 : (NBU0 >= 4 ? 4 : (NBU0 >= 2 ? 2 : 1));
+};
+
+// forward (expand accumulates into its output) or dX (no output loads);
+// kin = contraction of the shrink, nout = width of the expand.
+static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int rb) {
+  SinglePlan p{};
+  p.fused = kin <= kFusedMaxContraction;
+  p.bmb_shrink = bmb_shrink(M, rb);
+  if (p.fused)
+    p.bmb = forward ? bmb_expand(M, rb, 1) : ((rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1);
+  else
+    p.bmb = bmb_expand(M, rb, 8);
+  return p;
 }
 
-// Column splits of each token tile for the split expand: about `cols` output
-// columns per workgroup.
-static int pick_split(int64_t nout) {
-  const int64_t cols = env_int("LORA_SPLIT_COLS", 512);
-  int64_t s = ceil_div(nout, cols > 16 ? cols : 16);
-  const int64_t nnb = ceil_div(nout, 16);
-  if (s > nnb) s = nnb;
-  return s < 1 ? 1 : static_cast<int>(s);
-}
-
-// Forward / dX strategy: fused (rank intermediate only in registers and LDS)
-// or split (shrink kernel writes it as MFMA fragments for a separate expand).
-static int pick_schedule(int64_t nout, int64_t kin) {
-  const int over = env_int("LORA_EXPAND_MODE", 0);  // 1 fused, 2 column split, 3 column owner, 4 token split
-  if (over >= 1 && over <= 4) return over;
-  // fused (row-linear output) unless the contraction is long: then the
-  // separate shrink plus column-owner expand measures faster (dX of an
-  // MLP-up layer: contraction over 14336 features)
-  (void)nout;
-  return kin > 8192 ? 3 : 1;
+// Token groups of the column-owner expand: >= 64 and enough workgroups to
+// fill the chip twice for narrow outputs, at most one per tile.
+static int64_t cols_groups(int64_t cols, int64_t tiles) {
+  int64_t groups = ceil_div(512, cols) > 64 ? ceil_div(512, cols) : 64;
+  if (groups > tiles) groups = tiles;
+  return groups < 1 ? 1 : groups;
 }
 
 // Token chunks of the weight-gradient kernels: about `wgs` workgroups in all,
@@ -1246,14 +938,7 @@ static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs) {
   return P < 1 ? 1 : P;
 }
 
-static int64_t tn_chunks_max(int64_t M, int64_t N) { return tn_chunks_for(M, N, 2048); }
-
-static int64_t tn_chunk_tokens(int64_t M, int64_t N) {
-  int64_t P = tn_chunks_for(M, N, 512);
-  const int64_t over = env_int("LORA_TN_CHUNKS", 0);
-  if (over >= 1 && over <= tn_chunks_max(M, N)) P = over;
-  return round_up(ceil_div(M, P), 64);
-}
+static int64_t tn_chunk_tokens(int64_t M, int64_t N) { return round_up(ceil_div(M, tn_chunks_for(M, N, 512)), 64); }
 
 // ---------------------------------------------------------------------------
 // kernel dispatch
@@ -1266,12 +951,8 @@ struct FusedLaunch {
     // kernels that write planes cover every token row below ldg (zeros past M)
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    if (a.rows_out)
-      launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, true>), dim3((unsigned)a.tiles),
-                         dim3(64 * NW), 0, st, a);
-    else
-      launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G, false>), dim3((unsigned)a.tiles),
-                         dim3(64 * NW), 0, st, a);
+    launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G>), dim3((unsigned)a.tiles), dim3(64 * NW), 0,
+           st, a);
   }
 };
 
@@ -1281,99 +962,22 @@ struct ShrinkLaunch {
     using S = FusedShape<RB, BMB>;
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    launch((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F>), dim3((unsigned)a.tiles),
-                       dim3(64 * NW), 0, st, a);
+    launch((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F>), dim3((unsigned)a.tiles), dim3(64 * NW), 0, st,
+           a);
   }
 };
 
-template <class Tag, int NW, int RB, int BMB, bool ACCUM>
-struct ExpandLaunch {
-  static void run(FusedArgs a, hipStream_t st) {
-    using S = FusedShape<RB, BMB>;
-    a.tiles = ceil_div(a.M, 16 * BMB);
-    const int64_t nnb = ceil_div(a.Nout, 16);
-    a.nbs = round_up(ceil_div(nnb, a.nsplit), (int64_t)NW * S::NBU);  // whole workgroup stages
-    a.nsplit = static_cast<int>(ceil_div(nnb, a.nbs));
-    const dim3 grid(static_cast<unsigned>(round_up(a.tiles, 8) * a.nsplit));
-    launch((expand_kernel<Tag, NW, RB, BMB, S::NBU, ACCUM>), grid, dim3(64 * NW), 0, st, a);
-  }
-};
-
-template <class Tag, int NW, int RB, int BMB, bool ACCUM>
+template <class Tag, int RB, int BMB, bool ACCUM>
 struct ExpandColsLaunch {
-  // column blocks per workgroup: NW * NBU with the W2 slice <= 64 KB of LDS
-  static constexpr int WBYTES = (sizeof(typename Tag::elem) == 2) ? 8 : 16;
-  static constexpr int NBU0 = 65536 / (NW * RB * 64 * WBYTES);
-  static constexpr int NBU = NBU0 >= 8 ? 8 : (NBU0 >= 4 ? 4 : (NBU0 >= 2 ? 2 : 1));
   static void run(FusedArgs a, hipStream_t st) {
+    using C = ColsShape<Tag, RB>;
     a.tiles = ceil_div(a.M, 16 * BMB);
-    const int64_t cols = ceil_div(ceil_div(a.Nout, 16), (int64_t)NW * NBU);
-    // token groups: at least 64 (measured best for 8-28 column slices), enough
-    // workgroups to fill the chip twice for narrow outputs, at most one per tile
-    int64_t groups = env_int("LORA_COLS_GROUPS", 0);
-    if (groups <= 0) groups = ceil_div(512, cols) > 64 ? ceil_div(512, cols) : 64;
-    if (groups > a.tiles) groups = a.tiles;
-    if (groups < 1) groups = 1;
-    launch((expand_cols_kernel<Tag, NW, RB, BMB, NBU, ACCUM>),
-                       dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st, a);
+    const int64_t cols = ceil_div(ceil_div(a.Nout, 16), (int64_t)C::NW * C::NBU);
+    launch((expand_cols_kernel<Tag, C::NW, RB, BMB, C::NBU, ACCUM>),
+           dim3(static_cast<unsigned>(cols), static_cast<unsigned>(cols_groups(cols, a.tiles))), dim3(64 * C::NW), 0,
+           st, a);
   }
 };
-
-// Token-split shrink: NW = 8 waves (128 tokens per workgroup); KP features
-// per weight panel, panel <= 32 KB of LDS per buffer.
-template <class Tag, bool EMIT_G, bool EMIT_F>
-static void launch_shrink_tok(FusedArgs a, int rb, hipStream_t st) {
-  constexpr int NW = 8;
-  constexpr int CHB = 4 * Tag::VEC;  // features per MFMA step
-  const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
-  const dim3 grid(static_cast<unsigned>(ceil_div(ceil_div(rows, 16), NW)));
-  const dim3 block(64 * NW);
-  // two panel buffers of KP features x 16*RB ranks: <= 64 KB of LDS (bf16)
-  switch (rb) {
-    case 1: launch((shrink_tok_kernel<Tag, NW, 1, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-    case 2: launch((shrink_tok_kernel<Tag, NW, 2, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-    case 4: launch((shrink_tok_kernel<Tag, NW, 4, 8 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-    default: launch((shrink_tok_kernel<Tag, NW, 8, 4 * CHB, EMIT_G, EMIT_F>), grid, block, 0, st, a); break;
-  }
-}
-
-// Token-split expand: NW = 8 waves, NBS column blocks per workgroup with the
-// W2 slice <= 16 KB of LDS; token groups fill the chip about twice.
-template <class Tag, bool ACCUM>
-static void launch_expand_tok(FusedArgs a, int rb, hipStream_t st) {
-  constexpr int NW = 8;
-  constexpr int WB = (sizeof(typename Tag::elem) == 2) ? 8 : 16;  // bytes per weight fragment lane
-  const int64_t nblk = ceil_div(a.M, 16);
-  const int64_t ntile = ceil_div(nblk, NW);
-  auto go = [&](auto kern, int nbs) {
-    const int64_t cols = ceil_div(ceil_div(a.Nout, 16), nbs);
-    int64_t groups = env_int("LORA_TOK_GROUPS", 0);
-    if (groups <= 0) groups = ceil_div(512, cols);
-    if (groups > ntile) groups = ntile;
-    if (groups < 1) groups = 1;
-    launch(kern, dim3(static_cast<unsigned>(cols), static_cast<unsigned>(groups)), dim3(64 * NW), 0, st,
-                       a);
-  };
-  const int nbs_env = env_int("LORA_TOK_NBS", 0);
-  switch (rb) {
-    case 1:
-      if (nbs_env == 4) go(expand_tok_kernel<Tag, NW, 1, 4, ACCUM>, 4);
-      else go(expand_tok_kernel<Tag, NW, 1, 8, ACCUM>, 8);
-      break;
-    case 2:
-      if (nbs_env == 4) go(expand_tok_kernel<Tag, NW, 2, 4, ACCUM>, 4);
-      else go(expand_tok_kernel<Tag, NW, 2, 8, ACCUM>, 8);
-      break;
-    case 4:
-      if (nbs_env == 4) go(expand_tok_kernel<Tag, NW, 4, 4, ACCUM>, 4);
-      else go(expand_tok_kernel<Tag, NW, 4, 8, ACCUM>, 8);
-      break;
-    default:
-      go(expand_tok_kernel<Tag, NW, 8, 4, ACCUM>, 4);
-      break;
-  }
-  (void)WB;
-}
 
 // (rank blocks, token blocks) with rb * bmb <= 8
 template <template <int, int> class L, class... A>
@@ -1390,101 +994,45 @@ static void dispatch8(int rb, int bmb, A&&... args) {
     default: L<8, 1>::run(args...); break;  // rb 8 (bmb 1 only)
   }
 }
-// (rank blocks, token blocks) with rb * bmb <= 16
-template <template <int, int> class L, class... A>
-static void dispatch16(int rb, int bmb, A&&... args) {
-  switch (rb * 10 + bmb) {
-    case 11: L<1, 1>::run(args...); break;
-    case 12: L<1, 2>::run(args...); break;
-    case 14: L<1, 4>::run(args...); break;
-    case 21: L<2, 1>::run(args...); break;
-    case 22: L<2, 2>::run(args...); break;
-    case 24: L<2, 4>::run(args...); break;
-    case 41: L<4, 1>::run(args...); break;
-    case 42: L<4, 2>::run(args...); break;
-    case 44: L<4, 4>::run(args...); break;
-    case 81: L<8, 1>::run(args...); break;
-    default: L<8, 2>::run(args...); break;  // rb 8, bmb 2
-  }
-}
 
-template <class Tag, int NW, bool ACCUM, bool EMIT_G>
+template <class Tag, bool ACCUM, bool EMIT_G>
 struct FusedNW {
   template <int RB, int BMB>
-  using L = FusedLaunch<Tag, NW, RB, BMB, ACCUM, EMIT_G>;
+  using L = FusedLaunch<Tag, 4, RB, BMB, ACCUM, EMIT_G>;
 };
-template <class Tag, int NW, bool EMIT_G, bool EMIT_F>
-struct ShrinkNW {
+template <class Tag, bool ACCUM>
+struct ExpandColsRB {
   template <int RB, int BMB>
-  using L = ShrinkLaunch<Tag, NW, RB, BMB, EMIT_G, EMIT_F>;
-};
-template <class Tag, int NW, bool ACCUM>
-struct ExpandColsNW {
-  template <int RB, int BMB>
-  using L = ExpandColsLaunch<Tag, NW, RB, BMB, ACCUM>;
-};
-template <class Tag, int NW, bool ACCUM>
-struct ExpandNW {
-  template <int RB, int BMB>
-  using L = ExpandLaunch<Tag, NW, RB, BMB, ACCUM>;
+  using L = ExpandColsLaunch<Tag, RB, BMB, ACCUM>;
 };
 
-template <class Tag, bool ACCUM, bool EMIT_G>
-static void launch_fused(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  if (pick_nw("LORA_FUSED_NW", rb, bmb, 0) == 8)
-    dispatch8<FusedNW<Tag, 8, ACCUM, EMIT_G>::template L>(rb, bmb, a, st);
-  else
-    dispatch8<FusedNW<Tag, 4, ACCUM, EMIT_G>::template L>(rb, bmb, a, st);
-}
 template <class Tag, bool EMIT_G, bool EMIT_F>
 static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  if (pick_nw("LORA_SHRINK_NW", rb, bmb) == 8)
-    dispatch16<ShrinkNW<Tag, 8, EMIT_G, EMIT_F>::template L>(rb, bmb, a, st);
-  else
-    dispatch16<ShrinkNW<Tag, 4, EMIT_G, EMIT_F>::template L>(rb, bmb, a, st);
-}
-template <class Tag, bool ACCUM>
-static void launch_expand(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  if (pick_nw("LORA_EXPAND_NW", rb, bmb) == 8)
-    dispatch8<ExpandNW<Tag, 8, ACCUM>::template L>(rb, bmb, a, st);
-  else
-    dispatch8<ExpandNW<Tag, 4, ACCUM>::template L>(rb, bmb, a, st);
-}
-
-template <class Tag, bool ACCUM>
-static void launch_expand_cols(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  if (env_int("LORA_EXPAND_NW", 4) == 8 && rb * bmb <= 4)
-    dispatch8<ExpandColsNW<Tag, 8, ACCUM>::template L>(rb, bmb, a, st);
-  else
-    dispatch8<ExpandColsNW<Tag, 4, ACCUM>::template L>(rb, bmb, a, st);
+  // the pairs bmb_shrink() returns; 8 waves while the cross-wave partial-sum
+  // buffer (NW * rb * bmb KB) stays <= 32 KB, else 4
+  switch (rb * 10 + bmb) {
+    case 11: ShrinkLaunch<Tag, 8, 1, 1, EMIT_G, EMIT_F>::run(a, st); break;
+    case 21: ShrinkLaunch<Tag, 8, 2, 1, EMIT_G, EMIT_F>::run(a, st); break;
+    case 22: ShrinkLaunch<Tag, 8, 2, 2, EMIT_G, EMIT_F>::run(a, st); break;
+    case 24: ShrinkLaunch<Tag, 4, 2, 4, EMIT_G, EMIT_F>::run(a, st); break;
+    case 41: ShrinkLaunch<Tag, 8, 4, 1, EMIT_G, EMIT_F>::run(a, st); break;
+    case 42: ShrinkLaunch<Tag, 4, 4, 2, EMIT_G, EMIT_F>::run(a, st); break;
+    case 44: ShrinkLaunch<Tag, 4, 4, 4, EMIT_G, EMIT_F>::run(a, st); break;
+    case 81: ShrinkLaunch<Tag, 4, 8, 1, EMIT_G, EMIT_F>::run(a, st); break;
+    default: ShrinkLaunch<Tag, 4, 8, 2, EMIT_G, EMIT_F>::run(a, st); break;  // rb 8, bmb 2
+  }
 }
 
-// Shrink Z against W1 and expand into the output, fused or split (see
-// pick_schedule); with EMIT_G also writes the planes for the gradient kernels.
+// Shrink Z against W1 and expand into the output as the plan says; with
+// EMIT_G also writes the planes for the gradient kernels.
 template <class Tag, bool ACCUM, bool EMIT_G>
-static void run_shrink_expand(FusedArgs a, int rb, hipStream_t st) {
-  const int mode = pick_schedule(a.Nout, a.Kin);
-  if (mode == 4) {
-    launch_shrink_tok<Tag, EMIT_G, true>(a, rb, st);
-    launch_expand_tok<Tag, ACCUM>(a, rb, st);
+static void run_shrink_expand(FusedArgs a, const SinglePlan& pl, int rb, hipStream_t st) {
+  if (pl.fused) {
+    dispatch8<FusedNW<Tag, ACCUM, EMIT_G>::template L>(rb, pl.bmb, a, st);
     return;
   }
-  if (mode == 3) {
-    launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
-    launch_expand_cols<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, 8), st);
-    return;
-  }
-  if (mode == 2) {
-    launch_shrink<Tag, EMIT_G, true>(a, rb, pick_bmb_shrink(a.M, rb), st);
-    a.nsplit = pick_split(a.Nout);
-    launch_expand<Tag, ACCUM>(a, rb, pick_bmb_expand("LORA_EXPAND_BMB", a.M, rb, a.nsplit), st);
-  } else {
-    a.nsplit = 1;
-    a.rot = env_int("LORA_FUSED_ROT", 1);
-    a.rows_out = env_int("LORA_FUSED_ROWS", 1);
-    const int bmb = ACCUM ? pick_bmb_expand("LORA_FUSED_BMB", a.M, rb, 1) : pick_bmb_dx(a.M, rb);
-    launch_fused<Tag, ACCUM, EMIT_G>(a, rb, bmb, st);
-  }
+  launch_shrink<Tag, EMIT_G, true>(a, rb, pl.bmb_shrink, st);
+  dispatch8<ExpandColsRB<Tag, ACCUM>::template L>(rb, pl.bmb, a, st);
 }
 
 template <class Tag>
@@ -1573,14 +1121,14 @@ static SingleLayout layout_for(int op, int64_t M, int64_t K, int64_t L, int r, i
     s.w2 = static_cast<size_t>(K * rp) * es;  // A as K x r
     s.ldg = round_up(M > 0 ? M : 1, 64);
     s.g = static_cast<size_t>(4 * rp * s.ldg);
-    s.P = tn_chunks_max(M, K);
+    s.P = tn_chunks_for(M, K, 512);
     s.part = static_cast<size_t>(s.P * K * rp) * 4;
     s.frag = frag;
   } else {
     s.w1 = static_cast<size_t>(rp * K) * es;  // A as r x K
     s.ldg = round_up(M > 0 ? M : 1, 64);
     s.g = static_cast<size_t>(4 * rp * s.ldg);
-    s.P = tn_chunks_max(M, L);
+    s.P = tn_chunks_for(M, L, 512);
     s.part = static_cast<size_t>(s.P * L * rp) * 4;
   }
   return s;
@@ -1726,7 +1274,8 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   const SingleLayout lay = layout_for(LORA_OP_FWD, M, K, L, static_cast<int>(r), x->dtype);
   // Weights read in place and the fused schedule use no workspace: the
   // caller may then pass none.
-  const bool needs_ws = !a_direct || !b_direct || pick_schedule(L, K) != 1;
+  const SinglePlan plan = plan_single(true, M, K, rb);
+  const bool needs_ws = !a_direct || !b_direct || !plan.fused;
   if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total()))
     return LORA_ERR_WORKSPACE;
   Carver cv(needs_ws ? workspace : nullptr);
@@ -1769,9 +1318,9 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   a.scale = scale;
   a.frag = frag;
   if (x->dtype == LORA_BF16)
-    run_shrink_expand<BF16, true, false>(a, rb, st);
+    run_shrink_expand<BF16, true, false>(a, plan, rb, st);
   else
-    run_shrink_expand<F32, true, false>(a, rb, st);
+    run_shrink_expand<F32, true, false>(a, plan, rb, st);
   return launch_status();
 }
 
@@ -1857,17 +1406,18 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   t.rp = static_cast<int>(rp);
   t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
+  const SinglePlan plan = plan_single(false, M, L, rb);
   if (xt->dtype == LORA_BF16) {
     if (accumulate)
-      run_shrink_expand<BF16, true, true>(a, rb, st);
+      run_shrink_expand<BF16, true, true>(a, plan, rb, st);
     else
-      run_shrink_expand<BF16, false, true>(a, rb, st);
+      run_shrink_expand<BF16, false, true>(a, plan, rb, st);
     launch_tn<BF16>(t, rb, st);
   } else {
     if (accumulate)
-      run_shrink_expand<F32, true, true>(a, rb, st);
+      run_shrink_expand<F32, true, true>(a, plan, rb, st);
     else
-      run_shrink_expand<F32, false, true>(a, rb, st);
+      run_shrink_expand<F32, false, true>(a, plan, rb, st);
     launch_tn<F32>(t, rb, st);
   }
   launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dA->ptr), dA->stride_row,
@@ -1947,8 +1497,7 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   a.r = static_cast<int>(r);
   a.rp = static_cast<int>(rp);
   a.scale = scale;
-  a.nsplit = 1;
-  const int bmb = pick_bmb_shrink(M, rb);
+  const int bmb = bmb_shrink(M, rb);
   TnArgs t{};
   t.z = dy->ptr;
   t.ldz = dy->stride_row;

@@ -42,3 +42,23 @@ def same_bits(a: np.ndarray, b: np.ndarray) -> bool:
     a = np.ascontiguousarray(a, dtype=np.float32)
     b = np.ascontiguousarray(b, dtype=np.float32)
     return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _max_nnz(a, axis):
+    return int((a != 0).sum(axis=axis).max())
+
+
+def exactness_bounds(c):
+    """Largest magnitude any partial sum of a single-adapter case can reach,
+    from nonzero counts, when every input value is 0 or +-1 and Y0 lies in
+    {-2..2} (the sparse integer-exact inputs of synth.single_adapter); a rank
+    intermediate must also be exact as a bf16 hi + lo pair (at most 16
+    significant bits). Keys: h = |X A|, dyb = |dY B^T|, and the outputs."""
+    s = abs(c.scale)
+    h = min(_max_nnz(c.X, 1), _max_nnz(c.A, 0))
+    dyb = min(_max_nnz(c.dY, 1), _max_nnz(c.B, 1))
+    return {"h": h, "dyb": dyb,
+            "y": 2 + s * h * _max_nnz(c.B, 0),
+            "dx": 8 + 2 * s * dyb * _max_nnz(c.A, 1),   # also covers dx added twice / onto dx0 in [-8, 8]
+            "dA": s * dyb * _max_nnz(c.X, 0),
+            "dB": s * h * _max_nnz(c.dY, 0)}

@@ -27,7 +27,7 @@ import lora_rank_adapter_amd as L
 from lora_rank_adapter_amd import _lib
 import oracle
 import synth
-from tests.gpu_util import dev, f32, host, note, same_bits
+from tests.gpu_util import dev, exactness_bounds, f32, host, note, same_bits
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -49,31 +49,13 @@ def _upload(c):
     return X, A_w, B_w, dY
 
 
-def _max_nnz(a, axis):
-    return int((a != 0).sum(axis=axis).max())
-
-
-def _exactness_bounds(c):
-    """Largest magnitude any partial sum can reach, from nonzero counts (every
-    input value is 0 or +-1, Y0 in {-2..2}); each rank intermediate must also
-    be exact as a bf16 hi + lo pair (at most 16 significant bits)."""
-    s = abs(c.scale)
-    h = min(_max_nnz(c.X, 1), _max_nnz(c.A, 0))          # |(X A)[m, j]|
-    dyb = min(_max_nnz(c.dY, 1), _max_nnz(c.B, 1))       # |(dY B^T)[m, j]|
-    y = 2 + s * h * _max_nnz(c.B, 0)                     # |Y0 + s (X A) B|
-    dx = 8 + s * dyb * _max_nnz(c.A, 1)                  # |dx0 + s dYB A^T| (accumulate case)
-    dA = s * dyb * _max_nnz(c.X, 0)                      # |s X^T dYB|
-    dB = s * h * _max_nnz(c.dY, 0)                       # |s (X A)^T dY|
-    return {"h": h, "dyb": dyb, "y": y, "dx": dx, "dA": dA, "dB": dB}
-
-
 @pytest.mark.parametrize("shape", sorted(SHAPES))
 def test_full_size_integer_exact_bitwise(shape):
     M, K, L_, r, s, seed = SHAPES[shape]
     note(f"full-size integer-exact {shape}: drawing inputs")
     c = synth.single_adapter(M, K, L_, r, seed=100 + seed, dtype="bf16", scale=s, y0="normal",
                              int_exact=True, density=DENSITY)
-    b = _exactness_bounds(c)
+    b = exactness_bounds(c)
     # |h|, |dYB| < 2^15 (hi + lo exact, scale a power of two); outputs < 2^22
     assert b["h"] < 2 ** 15 and b["dyb"] < 2 ** 15, b
     assert max(b["y"], b["dx"], b["dA"], b["dB"]) < 2 ** 22, b

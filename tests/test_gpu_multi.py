@@ -26,13 +26,26 @@ CASES = [
     ("prefill-like", 1500, 1024, (512, 128, 128), 12, 128, (8, 16, 32, 64, 128), 0.0, "bf16"),
     ("fp32", 77, 64, (32, 16), 5, 16, (0, 4, 16), 0.2, "f32"),
     ("one-token", 1, 8, (4,), 1, 1, (1,), 0.0, "bf16"),
+    ("prefill-long", 0, 512, (384, 128, 64), 12, 64, (8, 16, 32, 64), 0.0, "bf16"),
+    ("fp32-prefill", 0, 256, (128, 64), 10, 32, (4, 16, 32), 0.0, "f32"),
 ]
+# Which kernel each case reaches (the library picks by shape):
+#   shrink: row-split (bf16, >= 1024 tokens): prefill-like, prefill-long;
+#           pipelined, 16-token tiles (< 1024 tokens): decode-small, ragged-ranks, fp32, one-token;
+#           pipelined, 64-token tiles (f32, >= 1024 tokens): fp32-prefill;
+#           general (no buffer descriptors): test_shrink_general_kernel.
+#   expand: column owner (>= 2048 tokens): prefill-long;
+#           streaming (fewer): the others;
+#           general (rows of h not 16-byte aligned): test_expand_general_kernel.
 
 
 def _case(name, T, K, out_slices, S, r_max, choices, zero_p, dtype, seed=0, int_exact=False, wild_slots=True):
     rng = np.random.default_rng(1000 + seed + T)
-    if name == "prefill-like":
+    if name in ("prefill-like", "fp32-prefill"):
         ts, ranks, _ = synth.prefill_routing(12, S, choices, rng, median=120.0, sigma=0.6, cap=400)
+        T = ts.shape[0]
+    elif name == "prefill-long":
+        ts, ranks, _ = synth.prefill_routing(20, S, choices, rng, median=150.0, sigma=0.5, cap=400)
         T = ts.shape[0]
     else:
         ts, ranks = synth.decode_routing(T, S, r_max, choices, zero_p, rng) if S > 1 else (
@@ -97,17 +110,16 @@ def _grouping_inputs(kind, rng):
     return ts, ranks
 
 
-@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("kind", ["chunk-multiple", "bursty", "many-slots", "max-chunked", "all-inactive",
                                   "beyond-chunked"])
-def test_grouping_schedules_bitwise(kind, mode, monkeypatch):
-    """Both grouping kernels (one workgroup; one workgroup per 1024-token
-    chunk) against the stable sort of the oracle."""
-    monkeypatch.setenv("LORA_GROUP", str(mode))
+def test_grouping_schedules_bitwise(kind):
+    """Both grouping kernels against the stable sort of the oracle: one
+    workgroup per 1024-token chunk up to 32768 tokens (max-chunked is the
+    largest), one workgroup beyond (beyond-chunked)."""
     rng = np.random.default_rng(77)
     ts, ranks = _grouping_inputs(kind, rng)
     S = ranks.shape[0]
-    note(f"grouping schedule {mode} {kind} T={ts.shape[0]} S={S}")
+    note(f"grouping {kind} T={ts.shape[0]} S={S}")
     addr = L.lora_addressing_build(L.Addressing(torch.from_numpy(ts).to(DEV), S), torch.from_numpy(ranks).to(DEV), 64)
     torch.cuda.synchronize()
     counts, offsets, sorted_tokens, n = oracle.group_tokens(ts, ranks, 64)
@@ -133,32 +145,55 @@ def test_shrink(case):
     assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
 
 
-# LORA_MULTI_SHRINK: 1 GEMM form, 2 general, 3 pipelined general, 4-7 row-split
-# (x tile staged in LDS: 128-token tiles with stages of 64 or 128 features, then 64-token tiles)
-SHRINK_MODES = [1, 2, 3, 4, 5, 6, 7]
-
-
-@pytest.mark.parametrize("mode", SHRINK_MODES)
-@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
-def test_shrink_every_schedule(case, mode, monkeypatch):
-    """Every shrink kernel (GEMM form with the adapter staged in LDS, general,
-    pipelined general, row-split) on the same cases, including a feature count
-    that is not a multiple of the 32- and 64-feature steps, ranks that are not
-    multiples of 16 and a slot with more than 16 (slice, rank block) pairs."""
-    monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
-    test_shrink(case)
-
-
-@pytest.mark.parametrize("mode", SHRINK_MODES)
-def test_shrink_schedules_integer_exact(mode, monkeypatch):
-    monkeypatch.setenv("LORA_MULTI_SHRINK", str(mode))
-    note(f"shrink integer-exact schedule {mode}")
-    m = _case("prefill-like", 0, 200, (64, 32), 12, 48, (8, 16, 48), 0.0, "bf16", int_exact=True)
+@pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-long"])
+def test_shrink_integer_exact(name):
+    """Each shrink kernel (pipelined with 16- and 64-token tiles, row-split,
+    bf16 and f32) bit for bit on integer inputs; unspecified entries of h
+    untouched."""
+    case = next(c for c in CASES if c[0] == name)
+    m = _case(*case, int_exact=True)
+    dtype = case[-1]
+    note(f"shrink integer-exact {name} T={m.T}")
     addr, ranks = _addr(m)
     act, spec = _spec_mask(m)
     h = torch.full((m.T, m.num_slices, m.r_max), SENTINEL, dtype=torch.float32, device=DEV)
-    L.lora_shrink(dev(m.x, "bf16"), dev(m.a, "bf16"), addr, ranks, m.num_slices, m.r_max, h=h)
+    L.lora_shrink(dev(m.x, dtype), dev(m.a, dtype), addr, ranks, m.num_slices, m.r_max, h=h)
     torch.cuda.synchronize()
+    want = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max)
+    got = host(h)
+    assert np.all(got[~spec] == SENTINEL)
+    assert same_bits(got[spec], want[spec].astype(np.float32))
+
+
+def _wide_stride_adapter(m, dtype):
+    """The adapter as a view whose rank rows lie 2^27 (bf16) or 2^26 (f32)
+    elements apart, so one slot's rows span more than a 2 GiB buffer
+    descriptor; the memory between rows holds NaN."""
+    es = 2 if dtype == "bf16" else 4
+    s1 = ((1 << 31) // (es * m.num_slices * m.r_max) + 16) // 8 * 8   # 16-byte aligned rows
+    s0 = m.K
+    n_rows = m.num_slices * m.r_max
+    size = (n_rows - 1) * s1 + (m.S - 1) * s0 + m.K
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    store = torch.full((size,), float("nan"), dtype=tdt, device=DEV)
+    a_dev = store.as_strided((m.S, n_rows, m.K), (s0, s1, 1))
+    a_dev.copy_(dev(m.a, dtype))
+    return store, a_dev
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shrink_general_kernel(dtype):
+    """One slot's adapter rows spanning more than 2 GiB (a strided view): the
+    shrink without buffer descriptors, bit for bit on integer inputs."""
+    note(f"shrink general kernel {dtype}")
+    m = _case("ragged-ranks", 203, 64, (100, 28), 9, 40, (0, 3, 17, 40), 0.1, dtype, int_exact=True)
+    addr, ranks = _addr(m)
+    act, spec = _spec_mask(m)
+    store, a_dev = _wide_stride_adapter(m, dtype)
+    h = torch.full((m.T, m.num_slices, m.r_max), SENTINEL, dtype=torch.float32, device=DEV)
+    L.lora_shrink(dev(m.x, dtype), a_dev, addr, ranks, m.num_slices, m.r_max, h=h)
+    torch.cuda.synchronize()
+    del store, a_dev
     want = oracle.shrink(m.x, m.a, m.token_slot, m.ranks, m.num_slices, m.r_max)
     got = host(h)
     assert np.all(got[~spec] == SENTINEL)
@@ -185,52 +220,46 @@ def test_expand_fused(case):
     assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3])
-@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
-def test_expand_every_schedule(case, mode, monkeypatch):
-    """Each expand_fused kernel (streaming, column owner, general) on the same
-    cases: parity, inactive rows untouched, NaN padding never read."""
-    monkeypatch.setenv("LORA_MULTI_EXPAND", str(mode))
-    test_expand_fused(case)
-
-
-@pytest.mark.parametrize("mode", [1, 2, 3])
-def test_expand_schedules_integer_exact(mode, monkeypatch):
-    monkeypatch.setenv("LORA_MULTI_EXPAND", str(mode))
-    note(f"expand integer-exact schedule {mode}")
-    m = _case("prefill-like", 0, 96, (64, 32), 12, 32, (8, 16, 32), 0.0, "bf16", int_exact=True)
+def _expand_exact(m, dtype, h_view=None):
     addr, ranks = _addr(m)
     act, spec = _spec_mask(m)
     rng = np.random.default_rng(9)
     hin = rng.integers(-2, 3, size=(m.T, m.num_slices, m.r_max)).astype(np.float32)
     hin[~spec] = np.nan
+    h = f32(hin) if h_view is None else h_view(hin)
     y = f32(m.y0)
-    L.lora_expand_fused(f32(hin), dev(m.b, "bf16"), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
+    L.lora_expand_fused(h, dev(m.b, dtype), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
     torch.cuda.synchronize()
     want = oracle.expand_fused(hin, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max)
     assert same_bits(host(y), want.astype(np.float32))
 
 
-@pytest.mark.parametrize("group", [1, 3, 4, 16])
-def test_expand_owner_xcd_groups_integer_exact(group, monkeypatch):
-    """The column-owner expand maps workgroups to (token piece, column chunk)
-    items in XCD groups of any size; the grid is padded to a multiple of 8
-    groups and the padding exits. Every group size must give the exact
-    result (14 pieces x 5 chunks: no size here divides the item count)."""
-    monkeypatch.setenv("LORA_MULTI_EXPAND", "2")
-    monkeypatch.setenv("LORA_OWNER_GROUP", str(group))
-    note(f"owner expand, XCD group {group}")
-    m = _case("prefill-like", 0, 96, (384, 128, 64), 12, 32, (8, 16, 32), 0.0, "bf16", seed=4, int_exact=True)
-    addr, ranks = _addr(m)
-    act, spec = _spec_mask(m)
-    rng = np.random.default_rng(10)
-    hin = rng.integers(-2, 3, size=(m.T, m.num_slices, m.r_max)).astype(np.float32)
-    hin[~spec] = np.nan
-    y = f32(m.y0)
-    L.lora_expand_fused(f32(hin), dev(m.b, "bf16"), addr, ranks, f32(m.scalings), y, m.out_slices, m.r_max)
-    torch.cuda.synchronize()
-    want = oracle.expand_fused(hin, m.b, m.token_slot, m.ranks, m.scalings, m.y0, m.out_slices, m.r_max)
-    assert same_bits(host(y), want.astype(np.float32))
+@pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-long"])
+def test_expand_integer_exact(name):
+    """The streaming and column-owner expand kernels (bf16 and f32 weights)
+    bit for bit on integer inputs, NaN in every entry of h they must not read;
+    the owner case (20 requests, about 3000 tokens) has a work-item count that
+    is not a multiple of its XCD grouping."""
+    case = next(c for c in CASES if c[0] == name)
+    m = _case(*case, int_exact=True)
+    note(f"expand integer-exact {name} T={m.T}")
+    _expand_exact(m, case[-1])
+
+
+@pytest.mark.parametrize("name", ["decode-small", "prefill-like"])
+def test_expand_general_kernel(name):
+    """Rows of h whose stride is not a multiple of 4 floats: the general
+    expand kernel (element loads), 16- and 64-token tiles, bit for bit."""
+    case = next(c for c in CASES if c[0] == name)
+    m = _case(*case, int_exact=True)
+    note(f"expand general kernel {name} T={m.T}")
+
+    def odd_view(hin):
+        buf = torch.full((m.T, m.num_slices, m.r_max + 1), float("nan"), device=DEV)
+        view = buf[:, :, :m.r_max]
+        view.copy_(f32(hin))
+        return view
+    _expand_exact(m, case[-1], odd_view)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])

@@ -12,7 +12,7 @@ import torch
 import lora_rank_adapter_amd as L
 import oracle
 import synth
-from tests.gpu_util import dev, f32, host, note, same_bits, tol
+from tests.gpu_util import dev, exactness_bounds, f32, host, note, same_bits, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -305,53 +305,65 @@ def test_fp32_workload():
     assert oracle.rel_frobenius(host(dB), odB) <= tol(dtype)
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3, 4])
-def test_every_schedule_matches_oracle(mode, monkeypatch):
-    """Each forward / dX schedule the library can pick (fused, column split,
-    column owner, token split) gives oracle parity on ragged shapes."""
-    monkeypatch.setenv("LORA_EXPAND_MODE", str(mode))
-    for (M, K, L_, r, dtype, s) in [(200, 264, 1000, 16, "bf16", 2.0), (129, 1032, 520, 33, "bf16", 0.5),
-                                    (70, 132, 300, 19, "f32", 0.5), (300, 512, 2056, 128, "bf16", 1.0)]:
-        note(f"schedule {mode} {(M, K, L_, r, dtype)}")
-        c = synth.single_adapter(M, K, L_, r, seed=300 + M + mode, dtype=dtype, scale=s, y0="normal")
-        X, A_w, B_w, dY = _upload(c, dtype)
-        y = f32(c.Y0)
-        L.lora_fwd(X, A_w.t(), B_w.t(), y, s)
-        dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s)
-        torch.cuda.synchronize()
-        want = oracle.lora_fwd(c.X, c.A, c.B, c.Y0, s)
-        assert oracle.rel_frobenius(host(y) - c.Y0, want - c.Y0) <= tol(dtype)
-        odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
-        assert oracle.rel_frobenius(host(dx), odx) <= tol(dtype)
-        assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
-        # the accumulating dX through the same schedule, added onto the result above
-        base = host(dx)
-        L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dx)
-        torch.cuda.synchronize()
-        assert oracle.rel_frobenius(host(dx) - base, odx) <= tol(dtype)
+# Shapes that reach every branch of the library's schedule plan (chosen by
+# shape alone): fused forward with 64-, 32- and 16-token tiles, fused dX with
+# 32- and 16-token tiles, shrink tiles of 16, 32 and 64 tokens with 8 or 4
+# waves, and the split schedule (contraction over more than 8192 features:
+# shrink kernel + column-owner expand) with 64-, 32- and 16-token expand tiles,
+# including token groups that walk one and two tiles (ragged tails in every
+# dimension), in bf16 and f32.
+PLAN_CASES = [
+    (32768, 256, 264, 16, "bf16", 2.0),    # fused fwd 64-token tiles, fused dX 32-token tiles
+    (16400, 512, 264, 40, "bf16", 0.5),    # fused fwd 32-token tiles, shrink 64-token tiles (4 waves)
+    (9000, 264, 512, 100, "bf16", 1.0),    # rank 100 (8 rank blocks): shrink 32-token tiles, 4 waves
+    (9000, 264, 512, 20, "bf16", 2.0),     # shrink 32-token tiles, 8 waves
+    (1500, 8200, 2056, 128, "bf16", 0.5),  # split forward, expand groups walking 1-2 tiles
+    (1500, 2056, 8200, 128, "bf16", 2.0),  # split dX, same
+    (4100, 8200, 1000, 16, "bf16", 1.0),   # split forward, 64-token expand tiles
+    (2100, 264, 8200, 64, "bf16", 0.5),    # split dX, 32-token expand tiles
+    (3000, 8196, 300, 19, "f32", 0.5),     # split forward, f32
+    (70, 132, 8196, 19, "f32", 2.0),       # split dX, f32
+]
+EXACT_DENSITY = (1.0 / 8, 1.0 / 4, 1.0 / 4, 1.0 / 8)
 
 
-@pytest.mark.parametrize("bmb", [1, 2, 4])
-def test_dx_kernel_token_tiles(bmb, monkeypatch):
-    """The fused dX kernel with 16-, 32- and 64-token tiles on ragged shapes
-    (dX, and dA from the planes it writes) against the oracle, plus an
-    integer-exact case that must match bit for bit."""
-    monkeypatch.setenv("LORA_DX_BMB", str(bmb))
-    for (M, K, L_, r, dtype, s) in [(200, 264, 1000, 16, "bf16", 2.0), (129, 1032, 520, 33, "bf16", 0.5),
-                                    (70, 132, 300, 19, "f32", 0.5), (517, 2048, 1536, 8, "bf16", 1.0)]:
-        note(f"dx tiles {bmb} {(M, K, L_, r, dtype)}")
-        c = synth.single_adapter(M, K, L_, r, seed=500 + M + bmb, dtype=dtype, scale=s)
-        X, A_w, B_w, dY = _upload(c, dtype)
-        dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s)
-        torch.cuda.synchronize()
-        odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
-        assert oracle.rel_frobenius(host(dx), odx) <= tol(dtype)
-        assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
-    M, K, L_, r = 96, 256, 200, 16
-    c = synth.single_adapter(M, K, L_, r, seed=43, dtype="bf16", scale=2.0, int_exact=True)
-    X, A_w, B_w, dY = _upload(c, "bf16")
-    dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, 2.0)
+@pytest.mark.parametrize("case", PLAN_CASES, ids=_ids)
+@pytest.mark.parametrize("kind", ["normal", "exact"])
+def test_every_schedule_matches_oracle(case, kind):
+    """Each branch of the schedule plan against the oracle: within tolerance
+    for normal inputs, bit for bit for sparse signed inputs whose every
+    partial sum is exact (checked before the GPU runs). Forward, dX (also
+    accumulated), dA, dB."""
+    M, K, L_, r, dtype, s = case
+    note(f"schedule {kind} {case}")
+    if kind == "exact":
+        c = synth.single_adapter(M, K, L_, r, seed=600 + M, dtype=dtype, scale=s, y0="normal", int_exact=True,
+                                 density=EXACT_DENSITY)
+        b = exactness_bounds(c)
+        assert b["h"] < 2 ** 15 and b["dyb"] < 2 ** 15, b
+        assert max(b["y"], b["dx"], b["dA"], b["dB"]) < 2 ** 22, b
+    else:
+        c = synth.single_adapter(M, K, L_, r, seed=600 + M, dtype=dtype, scale=s, y0="normal")
+    X, A_w, B_w, dY = _upload(c, dtype)
+    y = f32(c.Y0)
+    L.lora_fwd(X, A_w.t(), B_w.t(), y, s)
+    dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s)
+    dB = L.lora_bwd_db(A_w, X.t(), dY, s)
+    dxa = dx.clone()
+    L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dxa)
     torch.cuda.synchronize()
-    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, 2.0)
-    assert same_bits(host(dx), odx.astype(np.float32))
-    assert same_bits(host(dA), odA.astype(np.float32))
+    want = oracle.lora_fwd(c.X, c.A, c.B, c.Y0, s)
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    odB = oracle.lora_bwd_db(c.A.T, c.X.T, c.dY, s)
+    if kind == "exact":
+        assert same_bits(host(y), want.astype(np.float32)), "Y"
+        assert same_bits(host(dx), odx.astype(np.float32)), "dX"
+        assert same_bits(host(dxa), (2.0 * odx).astype(np.float32)), "dX accumulated"
+        assert same_bits(host(dA), odA.astype(np.float32)), "dA"
+        assert same_bits(host(dB), odB.astype(np.float32)), "dB"
+        return
+    assert oracle.rel_frobenius(host(y) - c.Y0, want - c.Y0) <= tol(dtype)
+    assert oracle.rel_frobenius(host(dx), odx) <= tol(dtype)
+    assert oracle.rel_frobenius(host(dxa) - host(dx), odx) <= tol(dtype)
+    assert oracle.rel_frobenius(host(dA), odA) <= tol(dtype)
+    assert oracle.rel_frobenius(host(dB), odB) <= tol(dtype)
