@@ -53,20 +53,33 @@ DEFAULT_WORKLOAD = "single-bf16-M16384-K4096-L14336-r64"
 
 # The kernels the roofline entry is about, per workload: what lora_fwd
 # launches at that shape (weights used in place, so no packing launch): the
-# one fused shrink+expand kernel.
+# fused shrink+expand kernel for the 134 MB output; for the 940 MB output the
+# split schedule's shrink kernel and column-band expand (both are the
+# forward's dominant work, timed together).
 ROOFLINE_KERNEL = {
     "single-bf16-M8192-K4096-L4096-r16": ["fused_kernel"],
-    "single-bf16-M16384-K4096-L14336-r64": ["fused_kernel"],
+    "single-bf16-M16384-K4096-L14336-r64": ["shrink_kernel", "expand_band_kernel"],
 }
 # How those launches are told apart from the same templates' backward
 # instances in a profile: the forward ones accumulate into Y (ACCUM = true,
-# EMIT_G = false in fused_kernel, followed by its output-layout flag, and in
-# expand_kernel; EMIT_G = false, EMIT_F = true in shrink_kernel).
+# EMIT_G = false in fused_kernel; ACCUM = true in expand_band_kernel, whose
+# accumulating-dX instance is the same template but has another grid) or
+# write only fragments (EMIT_G = false, EMIT_F = true in shrink_kernel).
 ROOFLINE_PATTERN = {
-    "fused_kernel": r"\bfused_kernel<.*, true, false, (true|false)>",
+    "fused_kernel": r"\bfused_kernel<.*, true, false>",
     "shrink_kernel": r"\bshrink_kernel<.*, false, true>",
-    "expand_kernel": r"\bexpand_kernel<.*, true>",
+    "expand_band_kernel": r"\bexpand_band_kernel<.*, true>",
 }
+
+
+def roofline_grid(kernel, workload):
+    """Work-items of the forward's launch of `kernel` (None: any): the band
+    expand runs 256 threads per (256-column band, group of four 32-token
+    tiles)."""
+    if kernel != "expand_band_kernel":
+        return None
+    M, _K, Lc, _r, _s, _seed = WORKLOADS[workload]
+    return -(-Lc // 256) * -(-(-(-M // 32)) // 4) * 256
 COPY_PROBE_BYTES = 1 << 30
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -113,21 +126,24 @@ def traffic_from_profile(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _counter_per_dispatch(path, counter, pattern):
+def _counter_per_dispatch(path, counter, pattern, grid=None):
     """{dispatch id: counter value} (KiB for the byte counters) over the
-    dispatches whose kernel name matches the regex `pattern`."""
+    dispatches whose kernel name matches the regex `pattern` (and whose grid
+    has `grid` work-items, if given)."""
     per = {}
     rx = re.compile(pattern)
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
+            if grid is not None and int(row["Grid_Size"]) != grid:
+                continue
             if row["Counter_Name"] == counter and rx.search(row["Kernel_Name"]):
                 d = int(row["Dispatch_Id"])
                 per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
     return per
 
 
-def _kernel_mean(path, counter, pattern):
-    per = _counter_per_dispatch(path, counter, pattern)
+def _kernel_mean(path, counter, pattern, grid=None):
+    per = _counter_per_dispatch(path, counter, pattern, grid)
     if not per:
         raise SystemExit(f"no dispatch of {pattern!r} with {counter} in {path}")
     return statistics.mean(per.values()), len(per)
@@ -151,8 +167,8 @@ def traffic_summary(fetch_csv, write_csv, workload, command):
     f_copy = _copy_probe_kib(fetch_csv, "FETCH_SIZE") * 1024
     w_copy = _copy_probe_kib(write_csv, "WRITE_SIZE") * 1024
     f_scale, w_scale = COPY_PROBE_BYTES / f_copy, COPY_PROBE_BYTES / w_copy
-    fetch = [_kernel_mean(fetch_csv, "FETCH_SIZE", ROOFLINE_PATTERN[k]) for k in kern]
-    write = [_kernel_mean(write_csv, "WRITE_SIZE", ROOFLINE_PATTERN[k]) for k in kern]
+    fetch = [_kernel_mean(fetch_csv, "FETCH_SIZE", ROOFLINE_PATTERN[k], roofline_grid(k, workload)) for k in kern]
+    write = [_kernel_mean(write_csv, "WRITE_SIZE", ROOFLINE_PATTERN[k], roofline_grid(k, workload)) for k in kern]
     f_k = sum(v for v, _ in fetch)
     w_k = sum(v for v, _ in write)
     n_f = [n for _, n in fetch]

@@ -25,9 +25,10 @@
 //                 are loaded and stored with the non-temporal cache policy.
 //   shrink_kernel the same shrink alone, writing s*H as gradient planes and/or
 //                 MFMA fragments for the column-owner expand below.
-//   expand_cols_kernel  column-owner expand (contractions longer than 8192
-//                 features): a workgroup stages its W2 column slice in LDS
-//                 once and walks token tiles.
+//   expand_band_kernel  column-band expand (the split schedule): a workgroup
+//                 owns a 256-column band, keeps its W2 fragments in
+//                 registers and walks token tiles, writing whole 1 KB row
+//                 segments.
 //   tn_kernel     weight-gradient partial sums over a chunk of tokens:
 //                 part[p][n][j] = sum_m Z[m][n] * G[j][m]. Z tiles are staged
 //                 in LDS (XOR-swizzled rows) and read transposed.
@@ -379,36 +380,67 @@ __device__ __forceinline__ void emit_planes(const FusedArgs& p, int64_t m0, cons
 // block; wave w takes NBU consecutive blocks per stage (the NW waves cover
 // NW*NBU adjacent blocks together), two stages in flight, and the stage walk
 // starts at stage `rot` (mod the stage count) so that tiles in flight at the
-// same time do not walk the same column offsets in lockstep. The output is
-// read and written one row segment at a time: each stage's MFMA products (16
-// columns x 16 tokens per tile, in MFMA layout) go to this wave's LDS tile,
-// and lanes then take 16-byte pieces of whole rows (CW/4 lanes per row of the
-// stage's CW columns), add the output row-linearly (ACCUM) and store it. Row
-// segments of 512 bytes per instruction pair reach HBM as whole lines, which
-// streams markedly faster than the 64-byte-per-row pieces of the MFMA layout
-// when one workgroup owns a token tile's full rows. The LDS tile is private to
-// the wave (LDS instructions of one wave complete in order), so no barrier is
-// needed. Output rows past M lie outside the output descriptor (loads read 0,
-// stores are dropped).
+// same time do not walk the same column offsets in lockstep.
+//
+// The output is read and written one row segment at a time: each stage's
+// MFMA products (16 columns x 16 tokens per tile, in MFMA layout) go to an
+// LDS tile, and lanes then take 16-byte pieces of whole rows, add the output
+// row-linearly (ACCUM) and store it. How long those row segments are decides
+// how fast the output streams: 2 rows x 512 bytes per instruction stream at
+// the speed of a plain elementwise add over the same tensor, 8 rows x 128
+// bytes up to 40% slower (measured on a 16384 x 4096 float32 output). So:
+//  - SH = false (a wave's own columns span >= 256 bytes): each wave's LDS tile
+//    is private (LDS instructions of one wave complete in order, no barrier)
+//    and the wave writes its own columns of all 16*BMB rows;
+//  - SH = true (128 bytes: rank >= 64 leaves room for two column blocks per
+//    wave; 16384 x 4096, rank 64: 152 -> 133 us; with 256-byte segments the
+//    barrier costs more than it gains, 62 -> 66 us for the 8192 x 4096 dX):
+//    the NW waves write their products into one LDS tile of the stage's
+//    NW*16*NBU columns, wait at a barrier, and wave w then reads, adds and
+//    writes rows [w*16*BMB/NW, (w+1)*16*BMB/NW) over all of them. Two tiles
+//    alternate between stages, so one barrier per stage suffices: a wave
+//    writes tile k%2 only after every wave has passed the barrier of stage
+//    k-1, i.e. finished reading tile (k-2)%2.
+// Output rows past M lie outside the output descriptor (loads read 0, stores
+// are dropped); columns past the output use kOOB.
+template <int NW, int BMB, int NBU>
+struct ExpandRows {
+  static constexpr int CW = 16 * NBU;                  // columns of a wave per stage
+  static constexpr bool SH = CW <= 32 && NW * CW <= 256 && (16 * BMB) % NW == 0;
+  static constexpr int TW = SH ? NW * CW : CW;         // columns of an LDS tile
+  static constexpr int LDW = TW + 4;                   // LDS row pitch (floats)
+  static constexpr int LPR = TW / 4;                   // lanes per row (16 bytes each)
+  static constexpr int RPI = 64 / LPR;                 // rows per instruction
+  static constexpr int ROWS = SH ? 16 * BMB / NW : 16 * BMB;  // rows a wave writes
+  static constexpr int NI = ROWS / RPI;                // row instructions per stage
+  static constexpr int TILE = 16 * BMB * LDW;          // floats per LDS tile
+  // floats of LDS: SH, two shared tiles; else one private tile per wave
+  static constexpr int FLOATS = SH ? 2 * TILE : NW * TILE;
+  static_assert(64 % LPR == 0 && ROWS % RPI == 0 && NI >= 1, "stage shape");
+};
+
 template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
 __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0, int64_t rot,
-                                                 const uint4 (&hf)[BMB][RB], float* obuf) {
+                                                 const uint4 (&hf)[BMB][RB], float* lds) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
-  constexpr int CW = 16 * NBU;        // columns per wave per stage
-  constexpr int LDW = CW + 4;         // LDS row pitch (floats)
-  constexpr int LPR = CW / 4;         // lanes per row (16 bytes each)
-  constexpr int RPI = 64 / LPR;       // rows per instruction
-  constexpr int NI = 16 * BMB / RPI;  // row instructions per stage
-  static_assert(64 % LPR == 0 && (16 * BMB) % RPI == 0, "stage shape");
+  using X = ExpandRows<NW, BMB, NBU>;
+  constexpr int LDW = X::LDW;
+  constexpr int RPI = X::RPI;
+  constexpr int NI = X::NI;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int lr = lane / LPR;          // row within an instruction
-  const int lc = (lane % LPR) * 4;    // column within the stage
+  const int lr = lane / X::LPR;       // row within an instruction
+  const int lc = (lane % X::LPR) * 4; // column within the tile
+  // where this wave's products go in a tile, and the first row it writes out
+  const int pcol = X::SH ? wave * X::CW : 0;
+  const int row0 = X::SH ? wave * X::ROWS : 0;
+  float* tile0 = X::SH ? lds : lds + wave * X::TILE;
+  float* tile1 = X::SH ? lds + X::TILE : tile0;
   const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
   const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
   const int64_t nb_end = (p.Nout + 15) / 16;
@@ -417,22 +449,25 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
   // in vector registers and turn the selects below into branches)
   const int nst = uniform_int((nb_end + gstep - 1) / gstep);
   const int r0 = nst > 0 ? uniform_int(rot % nst) : 0;
-  auto stage_nb = [&](int k) -> int64_t {  // first column block of this wave in stage k
+  // first column block of stage k (of the whole workgroup); nb_end past the end
+  auto stage_nb = [&](int k) -> int64_t {
     const int kk = k + r0;
-    const int v = (kk - (kk >= nst ? nst : 0)) * gstep + wave * NBU;
+    const int v = (kk - (kk >= nst ? nst : 0)) * gstep;
     return k < nst ? v : nb_end;
   };
+  // first column block of the tile this lane writes out, for stage block nb0
+  auto tile_nb = [&](int64_t nb0) -> int64_t { return X::SH ? nb0 : nb0 + wave * NBU; };
   // output offset of this lane's piece in row instruction i of the stage at nb0
   auto ooff = [&](int i, int64_t nb0) -> uint32_t {
-    const int64_t n = nb0 * 16 + lc;
-    const int row = RPI * i + lr;
+    const int64_t n = tile_nb(nb0) * 16 + lc;
+    const int row = row0 + RPI * i + lr;
     return (nb0 < nb_end && n < p.Nout) ? static_cast<uint32_t>(((int64_t)row * p.ldo + n) * 4) : kOOB;
   };
   auto load2 = [&](wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0) {
 #pragma unroll
     for (int u = 0; u < NBU; ++u) {
-      const int64_t nb = nb0 + u;
-      const int64_t nrow = (nb < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
+      const int64_t nb = nb0 + wave * NBU + u;
+      const int64_t nrow = (nb0 < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
 #pragma unroll
       for (int q = 0; q < RB; ++q) {
         const int j0 = 16 * q + 4 * grp;
@@ -447,7 +482,7 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
         cv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto comp2 = [&](const wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0) {
+  auto comp2 = [&](const wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0, float* tile) {
 #pragma unroll
     for (int u = 0; u < NBU; ++u) {
 #pragma unroll
@@ -455,13 +490,14 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
         f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < RB; ++q) mma_rank16<Tag>(pr, WF::operand(wv[u][q]), hf[b][q]);
-        // lane holds columns 16u + 4grp .. +3 of token 16b + col
-        *reinterpret_cast<f32x4_t*>(obuf + (16 * b + col) * LDW + 16 * u + 4 * grp) = pr;
+        // lane holds columns 16u + 4grp .. +3 (of this wave's blocks) of token 16b + col
+        *reinterpret_cast<f32x4_t*>(tile + (16 * b + col) * LDW + pcol + 16 * u + 4 * grp) = pr;
       }
     }
+    if constexpr (X::SH) __syncthreads();
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(obuf + (RPI * i + lr) * LDW + lc);
+      const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(tile + (row0 + RPI * i + lr) * LDW + lc);
       sstore16(ro, ooff(i, nb0), __builtin_bit_cast(uint4, cv[i] + pr));
     }
   };
@@ -473,11 +509,11 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
     for (int k = 0; k < nst; k += 2) {
       load2(wvB, cvB, stage_nb(k + 1));
       sched_fence();
-      comp2(wvA, cvA, stage_nb(k));
+      comp2(wvA, cvA, stage_nb(k), tile0);
       sched_fence();
       load2(wvA, cvA, stage_nb(k + 2));
       sched_fence();
-      comp2(wvB, cvB, stage_nb(k + 1));
+      comp2(wvB, cvB, stage_nb(k + 1), tile1);
       sched_fence();
     }
   }
@@ -486,11 +522,14 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 // Fused shrink -> expand: one workgroup per token tile, the rank intermediate
 // never leaves registers and LDS (optionally also written as planes for the
 // gradient kernels).
+// The expand's LDS tiles reuse the shrink's LDS (staging tiles
+// and partial sums) once every wave has read its reduced sums.
 template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G>
 __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
-  __shared__ __attribute__((aligned(16))) char shr[SS::TOTAL];
-  __shared__ float obuf[NW][16 * BMB * (16 * NBU + 4)];
+  constexpr int XB = ExpandRows<NW, BMB, NBU>::FLOATS * 4;
+  constexpr int LDS = SS::TOTAL > XB ? SS::TOTAL : XB;
+  __shared__ __attribute__((aligned(16))) char shr[LDS];
   auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   const int64_t tile = blockIdx.x;
   const int64_t m0 = tile * (16 * BMB);
@@ -500,7 +539,8 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   if constexpr (EMIT_G) {
     if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
-  expand_tile_rows<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, tile, hf, obuf[wave_id()]);
+  __syncthreads();  // every wave has read the partial sums
+  expand_tile_rows<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, tile, hf, reinterpret_cast<float*>(shr));
 }
 
 // Shrink only: s*H of each token tile, written as gradient-kernel planes
@@ -529,50 +569,68 @@ __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
   }
 }
 
-// Column-owner expand. Workgroup (c, g) owns the 16-column blocks
-// [c*nbs, (c+1)*nbs) and walks the token tiles g, g+G, g+2G, ...; its slice of
-// W2 is staged once in LDS in MFMA operand order, so the loop holds only the
-// output tiles in registers and can keep many loads in flight. Workgroups with
-// the same g start on the same tile: at any time the chip updates the full
-// rows of a few adjacent tiles. Output tiles of the next token tile are
-// prefetched while the current one is computed. nbs = NW * NBU.
-template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
-__global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
+// Column-band expand (the split schedule's second kernel). Workgroup (c, g)
+// owns the output columns [c*BW, (c+1)*BW), BW = NW*NBW*16 = 256, and walks
+// the token tiles g, g+G, g+2G, ... (G = gridDim.y) of 16*BMB tokens each.
+// Workgroup ids run over the bands first, so the workgroups resident at any
+// time cover the same few token tiles: the chip streams a narrow window of
+// output rows, which keeps a large output (thousands of rows of tens of KB)
+// streaming at the speed of a plain elementwise pass, where one workgroup per
+// token tile walking whole rows (all rows in flight at once) loses 10-20%.
+// Wave w keeps the W2 fragments of its NBW column blocks in registers for the
+// whole walk. Per tile: the s*H fragments (the same for every wave), the MFMA
+// products into a shared LDS tile, a barrier, then wave w reads, adds
+// (ACCUM) and writes rows [w*R, (w+1)*R), R = 16*BMB/NW, of the tile over the
+// band, one whole 1 KB row segment per instruction. The next tile's
+// fragments and output rows load while the current one is computed; two LDS
+// tiles alternate, so one barrier per tile suffices (a wave writes tile k%2
+// only after every wave has passed the barrier of tile k-1, i.e. finished
+// reading tile (k-2)%2). Tiles past the last read zeros and store nothing
+// (empty output descriptor).
+template <class Tag, int NW, int RB, int BMB, int NBW, bool ACCUM>
+__global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
-  constexpr int NBS = NW * NBU;             // column blocks of this workgroup
-  __shared__ wf_t w2s[NBS * RB * 64];       // [block][rank block][lane]
+  constexpr int BW = NW * NBW * 16;     // band columns
+  constexpr int LDW = BW + 4;           // LDS row pitch (floats)
+  constexpr int LPR = BW / 4;           // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;         // rows per instruction
+  constexpr int R = 16 * BMB / NW;      // rows a wave writes per tile
+  constexpr int NI = R / RPI;           // row instructions per tile
+  static_assert(LPR <= 64 && 64 % LPR == 0 && R % RPI == 0 && NI >= 1, "band shape");
+  constexpr int TILE = 16 * BMB * LDW;  // floats per LDS tile
+  __shared__ __attribute__((aligned(16))) float lds[2 * TILE];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int64_t nnb = (p.Nout + 15) / 16;
-  const int64_t nb_base = (int64_t)blockIdx.x * NBS;
+  const int lr = lane / LPR;
+  const int lc = (lane % LPR) * 4;
+  const int64_t c0 = (int64_t)blockIdx.x * BW;  // first column of the band
+  const int64_t nb0 = c0 / 16 + wave * NBW;     // first column block of this wave
 
-  // stage the W2 slice (rows past Nout and columns past r become zero)
+  // this wave's W2 fragments (rows past Nout and ranks past r read as zero)
+  wf_t w[NBW][RB];
   {
     const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
-    for (int i = threadIdx.x; i < NBS * RB * 64; i += 64 * NW) {
-      const int l = i & 63;
-      const int q = (i >> 6) % RB;
-      const int nbl = (i >> 6) / RB;
-      const int64_t nb = nb_base + nbl;
-      const int64_t n = nb * 16 + (l & 15);
-      const int j0 = 16 * q + 4 * (l >> 4);
-      const int64_t nrow = (nb < nnb && n < p.Nout) ? n : p.Nout;  // p.Nout: outside rw2
-      w2s[i] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+#pragma unroll
+    for (int u = 0; u < NBW; ++u) {
+      const int64_t n = (nb0 + u) * 16 + col;
+      const int64_t nrow = n < p.Nout ? n : p.Nout;  // p.Nout: outside rw2
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int j0 = 16 * q + 4 * grp;
+        w[u][q] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+      }
     }
   }
-  __syncthreads();
-
   const int64_t gstride = gridDim.y;
-  auto tile_m0 = [&](int64_t t) -> int64_t { return t * (16 * BMB); };
-  // per-tile loads: fragments of s*H and (ACCUM) the output tiles
-  auto load_tile = [&](uint4 (&hf)[BMB][RB], f32x4_t (&cv)[NBU][BMB], int64_t t) {
+  const int64_t ncol = c0 + lc;  // this lane's output column in the row-linear pass
+  auto load_tile = [&](uint4 (&hf)[BMB][RB], f32x4_t (&cv)[NI], int64_t t) {
     const bool tok = t < p.tiles;
-    const int64_t m0 = tok ? tile_m0(t) : 0;
+    const int64_t m0 = tok ? t * (16 * BMB) : 0;
 #pragma unroll
     for (int b = 0; b < BMB; ++b)
 #pragma unroll
@@ -580,59 +638,50 @@ __global__ __launch_bounds__(64 * NW) void expand_cols_kernel(FusedArgs p) {
     if constexpr (ACCUM) {
       const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, tok ? (p.M - m0) * p.ldo * 4 : 0);
 #pragma unroll
-      for (int u = 0; u < NBU; ++u) {
-        const int64_t nb = nb_base + wave * NBU + u;
-        const int64_t ncol = nb * 16 + 4 * grp;
-#pragma unroll
-        for (int b = 0; b < BMB; ++b) {
-          const uint32_t off = (nb < nnb && ncol < p.Nout)
-                                   ? static_cast<uint32_t>(((16 * b + col) * p.ldo + ncol) * 4)
-                                   : kOOB;
-          cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ro, off));
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int row = wave * R + RPI * i + lr;
+        cv[i] = __builtin_bit_cast(
+            f32x4_t, sload16(ro, ncol < p.Nout ? static_cast<uint32_t>((row * p.ldo + ncol) * 4) : kOOB));
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < NBU; ++u)
-#pragma unroll
-        for (int b = 0; b < BMB; ++b) cv[u][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NI; ++i) cv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto comp_tile = [&](const uint4 (&hf)[BMB][RB], f32x4_t (&cv)[NBU][BMB], int64_t t) {
-    const int64_t m0 = tile_m0(t);
-    const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
+  auto comp_tile = [&](const uint4 (&hf)[BMB][RB], const f32x4_t (&cv)[NI], int64_t t, float* tile) {
 #pragma unroll
-    for (int u = 0; u < NBU; ++u) {
-      const int nbl = wave * NBU + u;
-      const int64_t nb = nb_base + nbl;
-      const int64_t ncol = nb * 16 + 4 * grp;
-      wf_t w[RB];
-#pragma unroll
-      for (int q = 0; q < RB; ++q) w[q] = w2s[(nbl * RB + q) * 64 + lane];
+    for (int u = 0; u < NBW; ++u)
 #pragma unroll
       for (int b = 0; b < BMB; ++b) {
+        f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < RB; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(w[q]), hf[b][q]);
-        const uint32_t off =
-            (nb < nnb && ncol < p.Nout) ? static_cast<uint32_t>(((16 * b + col) * p.ldo + ncol) * 4) : kOOB;
-        sstore16(ro, off, __builtin_bit_cast(uint4, cv[u][b]));
+        for (int q = 0; q < RB; ++q) mma_rank16<Tag>(pr, WF::operand(w[u][q]), hf[b][q]);
+        // lane holds columns 16u + 4grp .. +3 of this wave's blocks, token 16b + col
+        *reinterpret_cast<f32x4_t*>(tile + (16 * b + col) * LDW + 16 * (wave * NBW + u) + 4 * grp) = pr;
       }
+    __syncthreads();
+    const int64_t m0 = t * (16 * BMB);
+    const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, t < p.tiles ? (p.M - m0) * p.ldo * 4 : 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = wave * R + RPI * i + lr;
+      const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(tile + row * LDW + lc);
+      sstore16(ro, ncol < p.Nout ? static_cast<uint32_t>((row * p.ldo + ncol) * 4) : kOOB,
+               __builtin_bit_cast(uint4, cv[i] + pr));
     }
   };
   uint4 hfA[BMB][RB], hfB[BMB][RB];
-  f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
-  // two tiles in flight; a tile past the last reads zeros and stores nothing
-  // (empty output descriptor), so the loop body has no exit in the middle
+  f32x4_t cvA[NI], cvB[NI];
   if (blockIdx.y < p.tiles) {
     load_tile(hfA, cvA, blockIdx.y);
     for (int64_t t = blockIdx.y; t < p.tiles; t += 2 * gstride) {
       load_tile(hfB, cvB, t + gstride);
       sched_fence();
-      comp_tile(hfA, cvA, t);
+      comp_tile(hfA, cvA, t, lds);
       sched_fence();
       load_tile(hfA, cvA, t + 2 * gstride);
       sched_fence();
-      comp_tile(hfB, cvB, t + gstride);
+      comp_tile(hfB, cvB, t + gstride, lds + TILE);
       sched_fence();
     }
   }
@@ -665,7 +714,11 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   constexpr int VPR = NS / VEC;       // 128-bit vectors per Z row
   constexpr int ZV = TS * VPR / 256;  // Z vectors per thread per stage
   constexpr int GPL = (ES == 2) ? 2 : 1;  // G planes (bf16 hi/lo)
-  constexpr int GROWB = TS * ES;          // LDS bytes per G row and plane
+  constexpr int GROWB = TS * ES;          // bytes per G row and plane
+#ifndef LORA_GPAD
+#define LORA_GPAD 0
+#endif
+  constexpr int GPITCH = GROWB + LORA_GPAD;  // LDS row pitch of G
   constexpr int GVR = TS / VEC;           // vectors per G row
   constexpr int GTOT = GPL * 16 * RB * GVR;
   constexpr int GV = (GTOT + 255) / 256;
@@ -675,7 +728,7 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   constexpr int SWZ_UNIT = (ES == 2) ? 32 : 64;
 
   __shared__ __attribute__((aligned(16))) char zt[TS * ROWB];
-  __shared__ __attribute__((aligned(16))) char gs[GPL * 16 * RB * GROWB];
+  __shared__ __attribute__((aligned(16))) char gs[GPL * 16 * RB * GPITCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -743,7 +796,7 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
       const int v = tid + 256 * i;
-      if (v < GTOT) *reinterpret_cast<uint4*>(gs + v * 16) = gr[i];
+      if (v < GTOT) *reinterpret_cast<uint4*>(gs + (v / GVR) * GPITCH + (v % GVR) * 16) = gr[i];
     }
   };
 
@@ -768,8 +821,8 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
         uint4 ghi[RB], glo[RB];
 #pragma unroll
         for (int q = 0; q < RB; ++q) {
-          ghi[q] = *reinterpret_cast<const uint4*>(gs + (16 * q + col) * GROWB + u * 64 + grp * 16);
-          glo[q] = *reinterpret_cast<const uint4*>(gs + (16 * RB + 16 * q + col) * GROWB + u * 64 + grp * 16);
+          ghi[q] = *reinterpret_cast<const uint4*>(gs + (16 * q + col) * GPITCH + u * 64 + grp * 16);
+          glo[q] = *reinterpret_cast<const uint4*>(gs + (16 * RB + 16 * q + col) * GPITCH + u * 64 + grp * 16);
         }
 #pragma unroll
         for (int nb = 0; nb < NSB; ++nb) {
@@ -799,7 +852,7 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
         uint4 gf[RB];
 #pragma unroll
         for (int q = 0; q < RB; ++q)
-          gf[q] = *reinterpret_cast<const uint4*>(gs + (16 * q + col) * GROWB + (u * 16 + 4 * grp) * 4);
+          gf[q] = *reinterpret_cast<const uint4*>(gs + (16 * q + col) * GPITCH + (u * 16 + 4 * grp) * 4);
 #pragma unroll
         for (int nb = 0; nb < NSB; ++nb) {
           const int nl = (wave * NSB + nb) * 16 + col;
@@ -842,10 +895,21 @@ constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 
 #ifndef LORA_EXPAND_VB
 #define LORA_EXPAND_VB 48
 #endif
+// At rank > 32 the register rule alone leaves one 32-feature step per
+// stage, and the shrink loops are latency-bound with about one wave per SIMD
+// (16384 x 14336 dY shrink: 3.6 resident waves per CU, 156 us); two steps
+// per stage there measured 156 -> 95 us for that shrink and 441 -> 421 us
+// for the forward at 16384 x 4096 x 14336, rank 64 (four steps: no further
+// gain).
 template <int RB, int BMB>
 struct FusedShape {
-  static constexpr int U = (LORA_SHRINK_VB / (BMB + RB)) > 0 ? pow2_floor(LORA_SHRINK_VB / (BMB + RB)) : 1;
-  static constexpr int NBU = pow2_floor(LORA_EXPAND_VB / (2 * RB + 4 * BMB));
+  static constexpr int U0 = (LORA_SHRINK_VB / (BMB + RB)) > 0 ? pow2_floor(LORA_SHRINK_VB / (BMB + RB)) : 1;
+  static constexpr int U = (RB >= 4 && U0 < 2) ? 2 : U0;
+  static constexpr int NBU0 = pow2_floor(LORA_EXPAND_VB / (2 * RB + 4 * BMB));
+#ifndef LORA_NBU4
+#define LORA_NBU4 0
+#endif
+  static constexpr int NBU = (RB >= 4 && LORA_NBU4 > 0) ? LORA_NBU4 : NBU0;
 };
 
 // ---------------------------------------------------------------------------
@@ -859,32 +923,38 @@ struct FusedShape {
 //    workgroups, else 1; dX (no output loads) 2 at rank <= 16 while >= 256
 //    workgroups, else 1 (8192 x 4096, rank 16: 63.6 against 67.0 us).
 //  - contraction > 8192 features (the dX of an MLP-up layer contracts over
-//    its 14336 outputs): shrink_kernel writes s*H as MFMA fragments, then
-//    expand_cols_kernel (column owner, W2 slice staged in LDS once) updates
-//    the output; measured faster there than the fused kernel.
+//    its 14336 outputs), or an output larger than 256 MB (the Infinity
+//    Cache): shrink_kernel writes s*H as MFMA fragments, then
+//    expand_band_kernel updates the output band by band. In the fused kernel
+//    every workgroup owns whole output rows, so all rows stream at once; at
+//    16384 x 14336 (940 MB) that pattern tops out near 5.2 TB/s even as a
+//    plain add, while the band order streams at 5.8 TB/s (forward 410 ->
+//    352 us); at 8192 x 4096 (134 MB) the fused kernel stays faster (58.5
+//    against 62.1 us).
 //  - shrink tiles: 16*bmb tokens with bmb 4 or 2 while rb*bmb <= 16 and
 //    >= 256 workgroups; 1 at rank <= 16 (twice the workgroups measure faster
 //    there: 34.8 against 36.7 us for the X*A shrink at 8192 x 4096, rank 16);
 //    8 waves while the cross-wave partial-sum buffer stays <= 32 KB, else 4.
-//  - column-owner expand: token blocks as the fused forward with 8
-//    workgroups per tile counted; token groups >= 64 and enough to fill the
-//    chip twice for narrow outputs, at most one per tile.
+//  - column-band expand: 32-token tiles (16 at rank > 64, where the
+//    fragments of two token blocks would not fit the registers), about four
+//    tiles per workgroup.
 //  - weight-gradient token chunks: about 512 workgroups in all, at most one
 //    chunk per 64 tokens (P = 32 at 8192 x 4096 measured best: 16 chunks
 //    16.5, 64 chunks 16.7 us against 15.1 us).
 // ---------------------------------------------------------------------------
 
 constexpr int64_t kFusedMaxContraction = 8192;
+constexpr int64_t kFusedMaxOutputBytes = int64_t(256) << 20;  // the Infinity Cache's size
 
 struct SinglePlan {
-  bool fused;        // fused_kernel, else shrink_kernel + expand_cols_kernel
-  int bmb;           // token blocks per fused tile, or per expand_cols tile
+  bool fused;        // fused_kernel, else shrink_kernel + expand_band_kernel
+  int bmb;           // token blocks per fused tile, or per expand_band tile
   int bmb_shrink;    // token blocks per shrink_kernel tile (its waves: launch_shrink)
 };
 
-static int bmb_expand(int64_t M, int rb, int64_t wgs_per_tile) {
+static int bmb_expand(int64_t M, int rb) {
   for (int c : {4, 2}) {
-    if (c * rb <= 8 && ceil_div(M, 16 * c) * wgs_per_tile >= 512) return c;
+    if (c * rb <= 8 && ceil_div(M, 16 * c) >= 512) return c;
   }
   return 1;
 }
@@ -897,35 +967,25 @@ static int bmb_shrink(int64_t M, int rb) {
   return 1;
 }
 
-// Column blocks per expand_cols workgroup: NW * NBU with the W2 slice in at
-// most 64 KB of LDS (bf16 fragments take 8 bytes per lane, f32 16).
-template <class Tag, int RB>
-struct ColsShape {
-  static constexpr int NW = 4;
-  static constexpr int WBYTES = (sizeof(typename Tag::elem) == 2) ? 8 : 16;
-  static constexpr int NBU0 = 65536 / (NW * RB * 64 * WBYTES);
-  static constexpr int NBU = NBU0 >= 8 ? 8 : (NBU0 >= 4 ? 4 : (NBU0 >= 2 ? 2 : 1));
-};
-
 // forward (expand accumulates into its output) or dX (no output loads);
 // kin = contraction of the shrink, nout = width of the expand.
-static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int rb) {
+static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int64_t nout, int rb) {
   SinglePlan p{};
-  p.fused = kin <= kFusedMaxContraction;
+  p.fused = kin <= kFusedMaxContraction && M * nout * 4 <= kFusedMaxOutputBytes;
   p.bmb_shrink = bmb_shrink(M, rb);
   if (p.fused)
-    p.bmb = forward ? bmb_expand(M, rb, 1) : ((rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1);
+    p.bmb = forward ? bmb_expand(M, rb) : ((rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1);
   else
-    p.bmb = bmb_expand(M, rb, 8);
+    p.bmb = rb <= 4 ? 2 : 1;
   return p;
 }
 
-// Token groups of the column-owner expand: >= 64 and enough workgroups to
-// fill the chip twice for narrow outputs, at most one per tile.
-static int64_t cols_groups(int64_t cols, int64_t tiles) {
-  int64_t groups = ceil_div(512, cols) > 64 ? ceil_div(512, cols) : 64;
-  if (groups > tiles) groups = tiles;
-  return groups < 1 ? 1 : groups;
+// Token groups of the column-band expand: about four token tiles per
+// workgroup (measured on a 16384 x 14336 float32 output: 32-token tiles and
+// 1 KB bands stream at 5.8 TB/s with 64-128 groups, 4.9 TB/s with 16).
+static int64_t band_groups(int64_t tiles) {
+  const int64_t g = ceil_div(tiles, 4);
+  return g < 1 ? 1 : g;
 }
 
 // Token chunks of the weight-gradient kernels: about `wgs` workgroups in all,
@@ -968,14 +1028,13 @@ struct ShrinkLaunch {
 };
 
 template <class Tag, int RB, int BMB, bool ACCUM>
-struct ExpandColsLaunch {
+struct ExpandBandLaunch {
   static void run(FusedArgs a, hipStream_t st) {
-    using C = ColsShape<Tag, RB>;
+    constexpr int NW = 4, NBW = 4;  // 256-column bands
     a.tiles = ceil_div(a.M, 16 * BMB);
-    const int64_t cols = ceil_div(ceil_div(a.Nout, 16), (int64_t)C::NW * C::NBU);
-    launch((expand_cols_kernel<Tag, C::NW, RB, BMB, C::NBU, ACCUM>),
-           dim3(static_cast<unsigned>(cols), static_cast<unsigned>(cols_groups(cols, a.tiles))), dim3(64 * C::NW), 0,
-           st, a);
+    const int64_t bands = ceil_div(a.Nout, (int64_t)NW * NBW * 16);
+    launch((expand_band_kernel<Tag, NW, RB, BMB, NBW, ACCUM>),
+           dim3(static_cast<unsigned>(bands), static_cast<unsigned>(band_groups(a.tiles))), dim3(64 * NW), 0, st, a);
   }
 };
 
@@ -1001,9 +1060,9 @@ struct FusedNW {
   using L = FusedLaunch<Tag, 4, RB, BMB, ACCUM, EMIT_G>;
 };
 template <class Tag, bool ACCUM>
-struct ExpandColsRB {
+struct ExpandBandRB {
   template <int RB, int BMB>
-  using L = ExpandColsLaunch<Tag, RB, BMB, ACCUM>;
+  using L = ExpandBandLaunch<Tag, RB, BMB, ACCUM>;
 };
 
 template <class Tag, bool EMIT_G, bool EMIT_F>
@@ -1032,7 +1091,7 @@ static void run_shrink_expand(FusedArgs a, const SinglePlan& pl, int rb, hipStre
     return;
   }
   launch_shrink<Tag, EMIT_G, true>(a, rb, pl.bmb_shrink, st);
-  dispatch8<ExpandColsRB<Tag, ACCUM>::template L>(rb, pl.bmb, a, st);
+  dispatch8<ExpandBandRB<Tag, ACCUM>::template L>(rb, pl.bmb, a, st);
 }
 
 template <class Tag>
@@ -1274,7 +1333,7 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   const SingleLayout lay = layout_for(LORA_OP_FWD, M, K, L, static_cast<int>(r), x->dtype);
   // Weights read in place and the fused schedule use no workspace: the
   // caller may then pass none.
-  const SinglePlan plan = plan_single(true, M, K, rb);
+  const SinglePlan plan = plan_single(true, M, K, L, rb);
   const bool needs_ws = !a_direct || !b_direct || !plan.fused;
   if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total()))
     return LORA_ERR_WORKSPACE;
@@ -1406,7 +1465,7 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   t.rp = static_cast<int>(rp);
   t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
-  const SinglePlan plan = plan_single(false, M, L, rb);
+  const SinglePlan plan = plan_single(false, M, L, K, rb);
   if (xt->dtype == LORA_BF16) {
     if (accumulate)
       run_shrink_expand<BF16, true, true>(a, plan, rb, st);
