@@ -97,14 +97,8 @@ __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, uint4 v) {
 // with default stores lose most of the gain), and the system-scope bit (sc1)
 // on the stores adds about 1% more. Weights and intermediates keep the default
 // policy. Cache-policy operand bits on gfx950: 1 sc0, 2 nt, 16 sc1.
-#ifndef LORA_STREAM_LOAD_POLICY
-#define LORA_STREAM_LOAD_POLICY 2
-#endif
-#ifndef LORA_STREAM_STORE_POLICY
-#define LORA_STREAM_STORE_POLICY 18
-#endif
-constexpr int kStreamLoadPolicy = LORA_STREAM_LOAD_POLICY;    // nt
-constexpr int kStreamStorePolicy = LORA_STREAM_STORE_POLICY;  // nt | sc1
+constexpr int kStreamLoadPolicy = 2;    // nt
+constexpr int kStreamStorePolicy = 18;  // nt | sc1
 
 __device__ __forceinline__ uint4 sload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStreamLoadPolicy));

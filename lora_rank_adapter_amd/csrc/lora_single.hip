@@ -715,10 +715,10 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   constexpr int ZV = TS * VPR / 256;  // Z vectors per thread per stage
   constexpr int GPL = (ES == 2) ? 2 : 1;  // G planes (bf16 hi/lo)
   constexpr int GROWB = TS * ES;          // bytes per G row and plane
-#ifndef LORA_GPAD
-#define LORA_GPAD 0
-#endif
-  constexpr int GPITCH = GROWB + LORA_GPAD;  // LDS row pitch of G
+  // LDS row pitch of G, padded by 16 bytes: the 16 rows one fragment read
+  // touches then fall in distinct banks (unpadded, 128-byte rows put them on
+  // two bank groups; 16384 x 14336, rank 64: lora_bwd_db 164 -> 156 us)
+  constexpr int GPITCH = GROWB + 16;
   constexpr int GVR = TS / VEC;           // vectors per G row
   constexpr int GTOT = GPL * 16 * RB * GVR;
   constexpr int GV = (GTOT + 255) / 256;
@@ -747,28 +747,32 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
 #pragma unroll
     for (int q = 0; q < RB; ++q) acc[nb][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 zr[ZV];
-  uint4 gr[GV];
+  // stages of loads in flight: one (two or three measured slower: the
+  // registers then allow one wave per SIMD; 16384 x 14336, rank 64:
+  // lora_bwd_db 169 -> 185 / 199 us)
+  constexpr int DEPTH = 1;
+  uint4 zr[DEPTH][ZV];
+  uint4 gr[DEPTH][GV];
 
   // Z rows past the chunk end and G columns past M read 0 (the G buffer holds
   // zeros for tokens in [M, ldg)); Z columns past N use kOOB.
   const rsrc_t rz = make_rsrc(z + m_begin * p.ldz, (m_end - m_begin) * p.ldz * ES);
   const rsrc_t rg = make_rsrc(g, (int64_t)GPL * p.rp * p.ldg * ES);
-  auto load_stage = [&](int64_t m0) {
+  auto load_stage = [&](int d, int64_t m0) {
 #pragma unroll
     for (int i = 0; i < ZV; ++i) {
       const int v = tid + 256 * i;
       const int row = v / VPR;
       const int vc = v - row * VPR;
       const int64_t n = n_base + (int64_t)vc * VEC;
-      zr[i] = sload16(rz, n < p.N ? static_cast<uint32_t>(((m0 - m_begin + row) * p.ldz + n) * ES) : kOOB);
+      zr[d][i] = sload16(rz, n < p.N ? static_cast<uint32_t>(((m0 - m_begin + row) * p.ldz + n) * ES) : kOOB);
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
       const int v = tid + 256 * i;
       const int grow = v / GVR;  // plane * 16*RB + j
       const int vc = v - grow * GVR;
-      gr[i] = bload16(rg, v < GTOT ? static_cast<uint32_t>(((int64_t)grow * p.ldg + m0 + vc * VEC) * ES) : kOOB);
+      gr[d][i] = bload16(rg, v < GTOT ? static_cast<uint32_t>(((int64_t)grow * p.ldg + m0 + vc * VEC) * ES) : kOOB);
     }
   };
 
@@ -785,36 +789,25 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
     }
   };
 
-  auto store_stage = [&]() {
+  auto store_stage = [&](int d) {
 #pragma unroll
     for (int i = 0; i < ZV; ++i) {
       const int v = tid + 256 * i;
       const int row = v / VPR;
       const int vc = v - row * VPR;
-      *reinterpret_cast<uint4*>(zt + zoff(row, vc * 16)) = zr[i];
+      *reinterpret_cast<uint4*>(zt + zoff(row, vc * 16)) = zr[d][i];
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
       const int v = tid + 256 * i;
-      if (v < GTOT) *reinterpret_cast<uint4*>(gs + (v / GVR) * GPITCH + (v % GVR) * 16) = gr[i];
+      if (v < GTOT) *reinterpret_cast<uint4*>(gs + (v / GVR) * GPITCH + (v % GVR) * 16) = gr[d][i];
     }
   };
 
   // f32 operand element (bf16 operands use transposed reads instead)
   auto zval = [&](int m, int nl) -> uint32_t { return *reinterpret_cast<const uint32_t*>(zt + zoff(m, nl * ES)); };
 
-  const int64_t nstage = (m_end - m_begin + TS - 1) / TS;
-  if (nstage > 0) load_stage(m_begin);
-  for (int64_t s = 0; s < nstage; ++s) {
-    __syncthreads();
-    store_stage();
-    __syncthreads();
-    // the next stage's loads stay in flight during this stage's products;
-    // past the last stage they read zeros (Z rows past the chunk) and are
-    // never stored
-    load_stage(m_begin + (s + 1) * TS);
-    sched_fence();
-
+  auto compute = [&]() {
     if constexpr (ES == 2) {
 #pragma unroll
       for (int u = 0; u < TS / 32; ++u) {
@@ -863,6 +856,27 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
         }
       }
     }
+  };
+
+  // DEPTH stages of loads in flight: stage s + DEPTH loads while stage s is
+  // multiplied. Stages past the chunk read zeros (Z rows past the chunk end)
+  // and add nothing, so the loop body needs no exit in the middle.
+  const int64_t nstage = (m_end - m_begin + TS - 1) / TS;
+  if (nstage > 0) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_stage(d, m_begin + d * TS);
+    for (int64_t s = 0; s < nstage; s += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        __syncthreads();
+        store_stage(d);
+        __syncthreads();
+        load_stage(d, m_begin + (s + d + DEPTH) * TS);
+        sched_fence();
+        compute();
+        sched_fence();
+      }
+    }
   }
 
   float* part = p.part + (int64_t)blockIdx.y * p.N * p.rp;
@@ -889,12 +903,6 @@ constexpr int kTnCols = 256;  // columns per tn_kernel workgroup
 // (2 VGPRs) and BMB output tiles (4 VGPRs) per column block; keep a stage
 // near 48 VGPRs. A shrink stage holds U*(BMB+RB) 16-byte vectors.
 constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
-#ifndef LORA_SHRINK_VB
-#define LORA_SHRINK_VB 8
-#endif
-#ifndef LORA_EXPAND_VB
-#define LORA_EXPAND_VB 48
-#endif
 // At rank > 32 the register rule alone leaves one 32-feature step per
 // stage, and the shrink loops are latency-bound with about one wave per SIMD
 // (16384 x 14336 dY shrink: 3.6 resident waves per CU, 156 us); two steps
@@ -903,13 +911,11 @@ constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 
 // gain).
 template <int RB, int BMB>
 struct FusedShape {
-  static constexpr int U0 = (LORA_SHRINK_VB / (BMB + RB)) > 0 ? pow2_floor(LORA_SHRINK_VB / (BMB + RB)) : 1;
+  static constexpr int U0 = (8 / (BMB + RB)) > 0 ? pow2_floor(8 / (BMB + RB)) : 1;
   static constexpr int U = (RB >= 4 && U0 < 2) ? 2 : U0;
-  static constexpr int NBU0 = pow2_floor(LORA_EXPAND_VB / (2 * RB + 4 * BMB));
-#ifndef LORA_NBU4
-#define LORA_NBU4 0
-#endif
-  static constexpr int NBU = (RB >= 4 && LORA_NBU4 > 0) ? LORA_NBU4 : NBU0;
+  // (four column blocks per stage at rank 64 measured no faster: 416 against
+  // 417 us, with one wave per SIMD)
+  static constexpr int NBU = pow2_floor(48 / (2 * RB + 4 * BMB));
 };
 
 // ---------------------------------------------------------------------------
