@@ -303,6 +303,26 @@ int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora_t3* b, con
                       int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream);
 
 /*
+ * lora_apply_linear without a caller workspace, for callers that cannot
+ * allocate (code under HIP graph capture, serving loops that must not call
+ * hipMalloc, harnesses that forbid allocation). The rank intermediate h lives
+ * in a device array of the library (32 MiB per GPU, allocated when the library's
+ * code object loads on that GPU and held until the process ends), laid out
+ * T x num_slices x r_max float32; the call allocates and frees nothing.
+ *   Arguments as for lora_apply_linear, without h; results are bit for bit
+ *   those of lora_apply_linear (the same kernels).
+ *   T * num_slices * r_max * 4 bytes must not exceed 32 MiB: LORA_ERR_LIMIT
+ *   (before anything is launched) otherwise.
+ *   Every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (on different streams, or
+ *   from different threads without ordering) race and give wrong results;
+ *   calls ordered on one stream do not.
+ */
+int lora_apply_linear_noalloc(const lora_mat* x, const lora_t3* a, const lora_t3* b, const lora_addressing* addr,
+                              const int32_t* ranks, const float* scalings, const lora_mat* y,
+                              const int64_t* out_slices, int32_t num_slices, int32_t r_max, void* stream);
+
+/*
  * Multi-adapter embedding gather (LoraOpsBackend.gather_shrink:
  * h[t] = a[slot(t)][:, ids[t]], i.e. column ids[t] of the token's adapter):
  *   ids  int32[T] device.

@@ -4,7 +4,7 @@ The computation lives in the HIP library ``liblora_mi355x.so`` (C ABI in
 include/lora.h); this package is its Python binding. See ``ops`` for the
 functions: lora_fwd, lora_bwd_dx_da, lora_bwd_dx_da_accumulate, lora_bwd_db,
 lora_addressing_build, lora_shrink, lora_expand_fused, lora_apply_linear,
-lora_gather_shrink, lora_workspace_bytes, and the kernel-timing calls
+lora_apply_linear_noalloc, lora_gather_shrink, lora_workspace_bytes, and the kernel-timing calls
 lora_timing_begin/pause/resume/read/reserve. Importing
 ``lora_rank_adapter_amd.torch_ops`` registers the same operations as torch
 custom ops (namespace ``lora_amd``) with fake implementations for tracing and
@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     lora_shrink,
     lora_expand_fused,
     lora_apply_linear,
+    lora_apply_linear_noalloc,
     lora_gather_shrink,
     lora_workspace_bytes,
     lora_timing_begin,

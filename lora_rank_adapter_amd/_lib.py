@@ -94,6 +94,9 @@ SIGNATURES = {
     "lora_apply_linear": (ctypes.c_int, [_P(LoraMat), _P(LoraT3), _P(LoraT3), _P(LoraAddressing), ctypes.c_void_p,
                                          ctypes.c_void_p, _P(LoraMat), _P(ctypes.c_int64), ctypes.c_int32,
                                          ctypes.c_int32, _P(LoraT3), ctypes.c_void_p]),
+    "lora_apply_linear_noalloc": (ctypes.c_int, [_P(LoraMat), _P(LoraT3), _P(LoraT3), _P(LoraAddressing),
+                                                 ctypes.c_void_p, ctypes.c_void_p, _P(LoraMat), _P(ctypes.c_int64),
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "lora_gather_shrink": (ctypes.c_int, [ctypes.c_void_p, _P(LoraT3), _P(LoraAddressing), ctypes.c_void_p,
                                           ctypes.c_int32, _P(LoraT3), ctypes.c_void_p]),
     "lora_timing_begin": (ctypes.c_int, []),

@@ -31,6 +31,7 @@
 //                              beyond 2 GiB)
 //   gather_kernel              exact column gather, one wave per token
 
+#include <mutex>
 #include <type_traits>
 
 #include "lora_device.hpp"
@@ -40,6 +41,14 @@ namespace lora {
 
 constexpr int kMaxSlots = 1024;
 constexpr int kMaxSlices = 16;
+
+// Device-resident rank intermediate of lora_apply_linear_noalloc: every GPU
+// the library runs on holds its own copy (allocated with the code object when
+// it loads on that device, kept until the process ends). Host code never uses
+// the array's name as an address: its device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 __device__ __forceinline__ int clamp_rank(int v, int r_max) { return v < 0 ? 0 : (v > r_max ? r_max : v); }
 
@@ -1476,6 +1485,25 @@ static void launch_expand(const ExpandArgs& a, int bmb, int rbm, int64_t tiles, 
     launch_expand_b<Tag, 1>(a, rbm, grid, st);
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call from each device and kept (each device's copy has its own address).
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LORA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LORA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LORA_OK;
+}
+
 }  // namespace lora
 
 using namespace lora;
@@ -1727,6 +1755,34 @@ extern "C" int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora
   rc = lora_shrink(x, a, addr, ranks, num_slices, r_max, h, stream);
   if (rc != LORA_OK) return rc;
   return lora_expand_fused(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, stream);
+}
+
+// lora_apply_linear with the rank intermediate in the library's per-device
+// scratch instead of a caller workspace: for callers that cannot allocate.
+// The kernels and their order are those of lora_apply_linear (bit for bit the
+// same results); h needs no clearing, since entries past a slot's rank and of
+// inactive tokens are never read.
+extern "C" int lora_apply_linear_noalloc(const lora_mat* x, const lora_t3* a, const lora_t3* b,
+                                         const lora_addressing* addr, const int32_t* ranks, const float* scalings,
+                                         const lora_mat* y, const int64_t* out_slices, int32_t num_slices,
+                                         int32_t r_max, void* stream) {
+  if (!addr) return LORA_ERR_NULL;
+  if (addr->T < 0 || num_slices < 1 || num_slices > kMaxSlices) return LORA_ERR_SHAPE;
+  if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
+  if ((int64_t)addr->T * num_slices * r_max * 4 > kScratchBytes) return LORA_ERR_LIMIT;
+  void* sp = nullptr;
+  const int rc = scratch_address(&sp);
+  if (rc != LORA_OK) return rc;
+  lora_t3 h{};
+  h.ptr = sp;
+  h.dtype = LORA_F32;
+  h.d0 = addr->T;
+  h.d1 = num_slices;
+  h.d2 = r_max;
+  h.s0 = (int64_t)num_slices * r_max;
+  h.s1 = r_max;
+  h.s2 = 1;
+  return lora_apply_linear(x, a, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, &h, stream);
 }
 
 extern "C" int lora_gather_shrink(const int32_t* ids, const lora_t3* a, const lora_addressing* addr,

@@ -216,6 +216,19 @@ def lora_apply_linear(x: torch.Tensor, y: torch.Tensor, a: torch.Tensor, b: torc
     return y
 
 
+def lora_apply_linear_noalloc(x: torch.Tensor, y: torch.Tensor, a: torch.Tensor, b: torch.Tensor, addr: Addressing,
+                              ranks: torch.Tensor, scalings: torch.Tensor, out_slices, r_max: int) -> torch.Tensor:
+    """lora_apply_linear with the rank intermediate in the library's per-GPU
+    scratch (no allocation in the library or here). Returns y."""
+    lib = _lib.load()
+    n = len(out_slices)
+    sl = (ctypes.c_int64 * n)(*[int(v) for v in out_slices])
+    check("lora_apply_linear_noalloc", lib.lora_apply_linear_noalloc(
+        ctypes.byref(mat(x)), ctypes.byref(t3(a)), ctypes.byref(t3(b)), ctypes.byref(addr.struct()), _ptr(ranks),
+        _ptr(scalings), ctypes.byref(mat(y)), sl, n, int(r_max), _stream(x.device)))
+    return y
+
+
 def lora_gather_shrink(ids: torch.Tensor, a: torch.Tensor, addr: Addressing, ranks: torch.Tensor, r_max: int,
                        h: torch.Tensor | None = None) -> torch.Tensor:
     """h[t, 0, j] = a[slot(t), j, ids[t]] for j < rank (+0.0 for ids outside [0, V)). Returns h [T x 1 x r_max]."""
