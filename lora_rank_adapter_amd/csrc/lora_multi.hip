@@ -20,8 +20,8 @@
 //   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
 //                              descriptor loads and two register stages
 //   slot_shrink_rows_kernel    shrink for many tokens: a 128-token tile x up to
-//                              256 adapter rows (all slices) per workgroup, x
-//                              staged once in LDS, waves split the rows
+//                              128 adapter rows per workgroup, x staged once in
+//                              LDS, waves split the rows
 //   slot_expand_owner_kernel   expand for many tokens: a token piece x column
 //                              chunk per workgroup, weights staged once in LDS,
 //                              a piece's chunks grouped per XCD
@@ -349,7 +349,7 @@ struct ShrinkArgs {
   const int32_t* ranks;
   int64_t K;
   int S, r_max, n_slices, row_chunks;
-  int row_groups;   // row-split kernel: workgroups per token tile (16 rank-block pairs each)
+  int row_groups;   // row-split kernel: workgroups per token tile (4 * PPW rank-block pairs each)
   int64_t x_bytes;  // bytes of x a descriptor may span (GEMM kernel)
   bool h_vec;  // h rows 16-byte aligned (strides multiples of 4)
 };
@@ -687,10 +687,10 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
 
 // Row-split shrink for bf16 inputs (x and one slot's a within 2 GiB
 // descriptors). A workgroup owns a tile of up to 128 grouped tokens of one
-// slot against up to 16 (slice, 16-row rank block) pairs: 256 adapter rows
-// over every slice at once (a slot with more pairs gets further row-group
-// workgroups). Wave w takes pairs w, w+4, w+8 and w+12 of its row group over
-// the whole feature axis, so no partial sums are exchanged between waves.
+// slot against up to 4*PPW (slice, 16-row rank block) pairs of its slices (a
+// slot with more pairs gets further row-group workgroups). Wave w takes pairs
+// w, w+4, ... of its row group over the whole feature axis, so no partial
+// sums are exchanged between waves.
 // The tile's x rows are fetched once per stage of 32*U features by the whole
 // workgroup, row-linearly (each load instruction covers whole row segments),
 // into a double-buffered LDS tile with padded rows (every fragment read is
@@ -841,13 +841,14 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
   }
 }
 
-template <int TT, int U>
+template <int TT, int U, int PPW>
 __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
-  static_assert(TT * U >= 4 && (U & (U - 1)) == 0, "stage shape");
+  static_assert(TT * U >= 4 && (U & (U - 1)) == 0 && PPW >= 1 && PPW <= 4, "stage shape");
   constexpr int TB = 16 * TT;
   constexpr int XV = TT * U / 4;
+  constexpr int GP = 4 * PPW;  // (slice, rank block) pairs per workgroup
   __shared__ __attribute__((aligned(16))) char lds[2 * 16 * TT * (64 * U + 16)];
-  __shared__ __attribute__((aligned(16))) char alds[4][64 * (64 * U + 16)];  // per wave: 4 pairs x 16 rows
+  __shared__ __attribute__((aligned(16))) char alds[4][16 * PPW * (64 * U + 16)];  // per wave: PPW pairs x 16 rows
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
   const int tid = threadIdx.x;
@@ -870,14 +871,14 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
   const int nq = (rho + 15) >> 4;
   const int npairs = p.n_slices * nq;
-  const int pbeg = 16 * rg;
+  const int pbeg = GP * rg;
   if (pbeg >= npairs) return;  // uniform over the workgroup
   if (tid < TB) sh_tok[tid] = (tid < tl.len) ? p.sorted[tl.start + tid] : 0;
   __syncthreads();
   // this wave's pairs: pbeg + wave + 4i for i < npw (waves without pairs still
   // load their share of x and take part in every barrier)
   const int avail = npairs - pbeg - wave;
-  const int npw = uniform_int(avail <= 0 ? 0 : (((avail + 3) >> 2) < 4 ? ((avail + 3) >> 2) : 4));
+  const int npw = uniform_int(avail <= 0 ? 0 : (((avail + 3) >> 2) < PPW ? ((avail + 3) >> 2) : PPW));
 
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
   const rsrc_t ra = make_rsrc(static_cast<const uint16_t*>(p.a) + (int64_t)tl.slot * p.as0,
@@ -906,9 +907,15 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   switch (npw) {
     case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
     case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
-    case 2: shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
-    case 3: shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
-    default: shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 2:
+      if constexpr (PPW >= 2) shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
+      break;
+    case 3:
+      if constexpr (PPW >= 3) shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
+      break;
+    default:
+      if constexpr (PPW >= 4) shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
+      break;
   }
 }
 
@@ -1588,11 +1595,17 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
                        (int64_t)num_slices * r_max * a->s1 * (int64_t)es <= kMaxBufferBytes && K < (int64_t(1) << 30);
   p.x_bytes = T * x->stride_row * (int64_t)es;
   if (desc_ok && x->dtype == LORA_BF16 && T >= 1024) {
-    constexpr int tt = 8;  // 16-token blocks per row-split tile
-    p.row_groups = static_cast<int>(ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 16));
+    // 128-token tiles; two (slice, rank block) pairs per wave, i.e. 8 per
+    // workgroup: the prefill batch (16731 tokens, 46 slots, ranks 8-128) has
+    // only 153 token tiles, and with 16 pairs per workgroup most of a tile's
+    // work sat on one CU (224 us); 8 pairs: 191 us, 4: 206 us; 64-token tiles
+    // 206-230 us; 128-feature stages 307 us
+    constexpr int tt = 8;
+    constexpr int ppw = 2;
+    p.row_groups = static_cast<int>(ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 4 * ppw));
     const int64_t rtiles = ceil_div(T, 16 * tt) + S;
     const dim3 grid(static_cast<unsigned>(round_up(rtiles, 8 * kRowsGroup) * p.row_groups));
-    launch((slot_shrink_rows_kernel<tt, 2>), grid, dim3(256), 0, st, p);
+    launch((slot_shrink_rows_kernel<tt, 2, ppw>), grid, dim3(256), 0, st, p);
     return launch_status();
   }
   const bool pipe = desc_ok;
