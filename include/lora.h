@@ -290,13 +290,19 @@ int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing*
  *   b, scalings, y, out_slices
  *              as for lora_expand_fused (num_slices = number of out_slices).
  *   h          T x num_slices x r_max float32 WORKSPACE owned by the caller,
- *              with the layout rules of both calls; it receives the rank
- *              intermediate (entries of inactive tokens and past a slot's
- *              rank are left as they were).
+ *              with the layout rules of both calls; its contents after the
+ *              call are unspecified.
  *   y[t, slice i] += scalings[slot(t)] * (x[t] @ a[s, slice i]^T) @ b[s, slice i]^T
- *   for active t on slot s (ranks as in the two calls). Runs the shrink and
- *   the expand back to back on the stream. The arguments of both are checked
- *   before either launches: a failing call launches nothing.
+ *   for active t on slot s (ranks as in the two calls). Batches of 512 tokens
+ *   or more whose token tiles and 1024- or 2048-column chunks fit one round
+ *   of the GPU's 256 CUs (tiles estimated as if the tokens spread evenly over
+ *   the S slots), with x, a and b of one dtype, run as ONE launch that keeps
+ *   the rank intermediate on chip and leaves h unwritten; the others run the
+ *   shrink into h and the expand back to back on the stream. Both forms give
+ *   the same bits where the shrink takes the pipelined kernel (batches below
+ *   1024 tokens, and larger ones with few slots). The arguments of both
+ *   operations are checked before anything launches: a failing call launches
+ *   nothing.
  */
 int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora_t3* b, const lora_addressing* addr,
                       const int32_t* ranks, const float* scalings, const lora_mat* y, const int64_t* out_slices,

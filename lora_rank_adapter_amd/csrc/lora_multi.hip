@@ -466,34 +466,164 @@ __global__ __launch_bounds__(256) void slot_shrink_kernel(ShrinkArgs p) {
   }
 }
 
+// Per-wave feature loop of the pipelined shrink. The calling wave contracts
+// the feature chunks [cbeg, cend) (CH = 4*VEC features each) of a tile's x
+// rows (token block b < BMB: tokens tok[16b + lane%16], those at or past
+// `len` masked) with the adapter rows j0 + 16q + (lane%16) (q < RB; rows at
+// or past rho masked) of one slice of one slot. acc[b][q] gets the chunks
+// added in increasing order; lane (col, grp) holds rows 4*grp..4*grp+3 of
+// rank block q for token col, i.e. h[token][j0 + 16q + 4grp + i].
+// bf16: each stage's x rows and adapter rows are loaded row-linearly (whole
+// row segments per instruction) into the wave's LDS tile `stage` (rows padded
+// by 16 bytes, SBYTES bytes) and read back as conflict-free fragments; f32:
+// the fragments are loaded directly. Loads go through buffer descriptors
+// (masked lanes use kOOB, no branches), and U chunks of the next stage are in
+// flight while the current one is multiplied. Needs x and the slot's adapter
+// rows within 2 GiB descriptors (the host checks).
+template <class Tag, int BMB, int RB, int U>
+struct PipeShrink {
+  using E = typename Tag::elem;
+  static constexpr int VEC = Tag::VEC;
+  static constexpr int ES = sizeof(E);
+  static constexpr int CH = 4 * VEC;  // features per MFMA step
+  static constexpr bool LIN = ES == 2;
+  static constexpr int SROW = U * CH * ES;
+  static constexpr int PITCH = SROW + 16;
+  static constexpr int LPR = SROW / 16;
+  static constexpr int RPI = LIN ? 64 / LPR : 16;
+  static constexpr int ZN = LIN ? 16 * BMB / RPI : BMB;
+  static constexpr int WN = LIN ? 16 * RB / RPI : RB;
+  static constexpr int SBYTES = LIN ? 16 * (BMB + RB) * PITCH : 0;
+
+  static __device__ __forceinline__ void run(f32x4_t (&acc)[BMB][RB], const ShrinkArgs& p, const int* tok, int len,
+                                             int slot, int slice, int j0, int rho, int cbeg, int cend, char* stage) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+    const rsrc_t ra = make_rsrc(static_cast<const E*>(p.a) + (int64_t)slot * p.as0,
+                                (int64_t)p.n_slices * p.r_max * p.as1 * ES);
+    uint32_t xoff[BMB];
+    bool bany[BMB];
+#pragma unroll
+    for (int b = 0; b < BMB; ++b) {
+      const bool ok = 16 * b + col < len;
+      xoff[b] = ok ? static_cast<uint32_t>(((int64_t)tok[16 * b + col] * p.ldx + grp * VEC) * ES) : kOOB;
+      bany[b] = 16 * b < len;
+    }
+    uint32_t aoff[RB];
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int j = j0 + 16 * q + col;
+      aoff[q] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + grp * VEC) * ES) : kOOB;
+    }
+
+    const int lpiece = lane % LPR;
+    const int lstep = lpiece >> 2;
+    const int lgrp = lpiece & 3;
+    uint32_t lx[LIN ? ZN : 1], la[LIN ? WN : 1];
+    if constexpr (LIN) {
+#pragma unroll
+      for (int i = 0; i < ZN; ++i) {
+        const int row = i * RPI + lane / LPR;
+        lx[i] = row < len ? static_cast<uint32_t>(((int64_t)tok[row] * p.ldx + lgrp * VEC) * ES) : kOOB;
+      }
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const int j = j0 + i * RPI + lane / LPR;
+        la[i] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + lgrp * VEC) * ES) : kOOB;
+      }
+    }
+
+    const int K = static_cast<int>(p.K);
+    // LIN: xf[0] holds the stage's ZN row-linear x vectors, af[0] its WN
+    // adapter vectors; else [u][b] and [u][q] MFMA fragments
+    auto load = [&](uint4 (&xf)[U][ZN], uint4 (&af)[U][WN], int c) {
+      if constexpr (LIN) {
+        const int cc = c + lstep;
+        const bool kok = cc < cend && cc * CH + lgrp * VEC < K;
+        const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);
+#pragma unroll
+        for (int i = 0; i < ZN; ++i) xf[0][i] = sload16(rx, (kok && lx[i] != kOOB) ? lx[i] + kb : kOOB);
+#pragma unroll
+        for (int i = 0; i < WN; ++i) af[0][i] = bload16(ra, (kok && la[i] != kOOB) ? la[i] + kb : kOOB);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int cc = c + u;
+          const bool kok = cc < cend && cc * CH + grp * VEC < K;
+          const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);  // < x row bytes when kok
+#pragma unroll
+          for (int b = 0; b < BMB; ++b) xf[u][b] = sload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
+#pragma unroll
+          for (int q = 0; q < RB; ++q) af[u][q] = bload16(ra, (kok && aoff[q] != kOOB) ? aoff[q] + kb : kOOB);
+        }
+      }
+    };
+    auto mma = [&](const uint4 (&xf)[U][ZN], const uint4 (&af)[U][WN]) {
+      if constexpr (LIN) {
+#pragma unroll
+        for (int i = 0; i < ZN; ++i)
+          *reinterpret_cast<uint4*>(stage + (i * RPI + lane / LPR) * PITCH + lpiece * 16) = xf[0][i];
+#pragma unroll
+        for (int i = 0; i < WN; ++i)
+          *reinterpret_cast<uint4*>(stage + (16 * BMB + i * RPI + lane / LPR) * PITCH + lpiece * 16) = af[0][i];
+        uint4 w[U][RB];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < RB; ++q)
+            w[u][q] = *reinterpret_cast<const uint4*>(stage + (16 * (BMB + q) + col) * PITCH + (u * 4 + grp) * 16);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int b = 0; b < BMB; ++b)
+            if (bany[b]) {
+              const uint4 z = *reinterpret_cast<const uint4*>(stage + (16 * b + col) * PITCH + (u * 4 + grp) * 16);
+#pragma unroll
+              for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], w[u][q], z);
+            }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int b = 0; b < BMB; ++b)
+            if (bany[b]) {
+#pragma unroll
+              for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], af[u][q], xf[u][b]);
+            }
+      }
+    };
+    // two register stages; the loop body has no exit in the middle (an odd
+    // stage count ends with a stage of zeros)
+    uint4 xA[U][ZN], aA[U][WN], xB[U][ZN], aB[U][WN];
+    if (cbeg < cend) {
+      load(xA, aA, cbeg);
+      for (int c = cbeg; c < cend; c += 2 * U) {
+        load(xB, aB, c + U);
+        sched_fence();
+        mma(xA, aA);
+        sched_fence();
+        load(xA, aA, c + 2 * U);
+        sched_fence();
+        mma(xB, aB);
+        sched_fence();
+      }
+    }
+  }
+};
+
 constexpr int kShrinkGroup = 4;  // token tiles per XCD group (pipelined shrink)
 
 // Pipelined form of slot_shrink_kernel (same grid and reduction): every wave
-// contracts one contiguous range of the feature axis, the loads go through
-// buffer descriptors (masked lanes use kOOB, no branches), and U chunks of the
-// next stage are in flight while the current stage is multiplied. Needs x and
-// one slot's adapter rows within 2 GiB descriptors (the host checks).
+// contracts one contiguous quarter of the feature axis with PipeShrink.
 template <class Tag, int BMB, int RB, int U>
 __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
-  using E = typename Tag::elem;
-  constexpr int VEC = Tag::VEC;
-  constexpr int ES = sizeof(E);
-  constexpr int CH = 4 * VEC;  // features per MFMA step
+  using PS = PipeShrink<Tag, BMB, RB, U>;
   constexpr int TB = 16 * BMB;
-  // bf16: x rows and adapter rows loaded row-linearly (whole row segments of
-  // the stage per instruction) into a per-wave LDS tile (rows padded by 16
-  // bytes), fragments read back conflict-free; the tiles share their memory
-  // with the partial sums (one barrier after the feature loop)
-  constexpr bool LIN = ES == 2;
-  constexpr int SROW = U * CH * ES;
-  constexpr int PITCH = SROW + 16;
-  constexpr int LPR = SROW / 16;
-  constexpr int RPI = LIN ? 64 / LPR : 16;
-  constexpr int ZN = LIN ? 16 * BMB / RPI : BMB;
-  constexpr int WN = LIN ? 16 * RB / RPI : RB;
-  constexpr int SBYTES = LIN ? 16 * (BMB + RB) * PITCH : 0;
   constexpr int RBYTES = 4 * BMB * RB * 64 * 16;
-  __shared__ __attribute__((aligned(16))) char shr[4 * SBYTES > RBYTES ? 4 * SBYTES : RBYTES];
+  // the staging tiles share their memory with the partial sums
+  __shared__ __attribute__((aligned(16))) char shr[4 * PS::SBYTES > RBYTES ? 4 * PS::SBYTES : RBYTES];
   auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
@@ -530,130 +660,17 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
   if (threadIdx.x < TB) sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? p.sorted[tl.start + threadIdx.x] : 0;
   __syncthreads();
 
-  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
-  const rsrc_t ra = make_rsrc(static_cast<const E*>(p.a) + (int64_t)tl.slot * p.as0,
-                              (int64_t)p.n_slices * p.r_max * p.as1 * ES);
-  uint32_t xoff[BMB];
-  bool bany[BMB];
-#pragma unroll
-  for (int b = 0; b < BMB; ++b) {
-    const bool ok = 16 * b + col < tl.len;
-    xoff[b] = ok ? static_cast<uint32_t>(((int64_t)sh_tok[16 * b + col] * p.ldx + grp * VEC) * ES) : kOOB;
-    bany[b] = 16 * b < tl.len;
-  }
-  uint32_t aoff[RB];
-#pragma unroll
-  for (int q = 0; q < RB; ++q) {
-    const int j = j0 + 16 * q + col;
-    aoff[q] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + grp * VEC) * ES) : kOOB;
-  }
-
-  const int lpiece = lane % LPR;
-  const int lstep = lpiece >> 2;
-  const int lgrp = lpiece & 3;
-  uint32_t lx[LIN ? ZN : 1], la[LIN ? WN : 1];
-  if constexpr (LIN) {
-#pragma unroll
-    for (int i = 0; i < ZN; ++i) {
-      const int row = i * RPI + lane / LPR;
-      lx[i] = row < tl.len ? static_cast<uint32_t>(((int64_t)sh_tok[row] * p.ldx + lgrp * VEC) * ES) : kOOB;
-    }
-#pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      const int j = j0 + i * RPI + lane / LPR;
-      la[i] = j < rho ? static_cast<uint32_t>(((int64_t)(slice * p.r_max + j) * p.as1 + lgrp * VEC) * ES) : kOOB;
-    }
-  }
-  char* stage = shr + wave * SBYTES;
-
   f32x4_t acc[BMB][RB];
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
 #pragma unroll
     for (int q = 0; q < RB; ++q) acc[b][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nch = static_cast<int>((p.K + CH - 1) / CH);
+  const int nch = static_cast<int>((p.K + PS::CH - 1) / PS::CH);
   const int per = (nch + 3) / 4;
   const int cbeg = wave * per;
   const int cend = (cbeg + per < nch) ? cbeg + per : nch;
-  const int K = static_cast<int>(p.K);
-  // LIN: xf[0] holds the stage's ZN row-linear x vectors, af[0] its WN
-  // adapter vectors; else [u][b] and [u][q] MFMA fragments
-  auto load = [&](uint4 (&xf)[U][ZN], uint4 (&af)[U][WN], int c) {
-    if constexpr (LIN) {
-      const int cc = c + lstep;
-      const bool kok = cc < cend && cc * CH + lgrp * VEC < K;
-      const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);
-#pragma unroll
-      for (int i = 0; i < ZN; ++i) xf[0][i] = sload16(rx, (kok && lx[i] != kOOB) ? lx[i] + kb : kOOB);
-#pragma unroll
-      for (int i = 0; i < WN; ++i) af[0][i] = bload16(ra, (kok && la[i] != kOOB) ? la[i] + kb : kOOB);
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int cc = c + u;
-        const bool kok = cc < cend && cc * CH + grp * VEC < K;
-        const uint32_t kb = static_cast<uint32_t>(cc) * static_cast<uint32_t>(CH * ES);  // < x row bytes when kok
-#pragma unroll
-        for (int b = 0; b < BMB; ++b) xf[u][b] = sload16(rx, (kok && xoff[b] != kOOB) ? xoff[b] + kb : kOOB);
-#pragma unroll
-        for (int q = 0; q < RB; ++q) af[u][q] = bload16(ra, (kok && aoff[q] != kOOB) ? aoff[q] + kb : kOOB);
-      }
-    }
-  };
-  auto mma = [&](const uint4 (&xf)[U][ZN], const uint4 (&af)[U][WN]) {
-    if constexpr (LIN) {
-#pragma unroll
-      for (int i = 0; i < ZN; ++i)
-        *reinterpret_cast<uint4*>(stage + (i * RPI + lane / LPR) * PITCH + lpiece * 16) = xf[0][i];
-#pragma unroll
-      for (int i = 0; i < WN; ++i)
-        *reinterpret_cast<uint4*>(stage + (16 * BMB + i * RPI + lane / LPR) * PITCH + lpiece * 16) = af[0][i];
-      uint4 w[U][RB];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int q = 0; q < RB; ++q)
-          w[u][q] = *reinterpret_cast<const uint4*>(stage + (16 * (BMB + q) + col) * PITCH + (u * 4 + grp) * 16);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int b = 0; b < BMB; ++b)
-          if (bany[b]) {
-            const uint4 z = *reinterpret_cast<const uint4*>(stage + (16 * b + col) * PITCH + (u * 4 + grp) * 16);
-#pragma unroll
-            for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], w[u][q], z);
-          }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int b = 0; b < BMB; ++b)
-          if (bany[b]) {
-#pragma unroll
-            for (int q = 0; q < RB; ++q) mma_vec<Tag>(acc[b][q], af[u][q], xf[u][b]);
-          }
-    }
-  };
-  // two register stages; the loop body has no exit in the middle (an odd
-  // stage count ends with a stage of zeros)
-  {
-    uint4 xA[U][ZN], aA[U][WN], xB[U][ZN], aB[U][WN];
-    if (cbeg < cend) {
-      load(xA, aA, cbeg);
-      for (int c = cbeg; c < cend; c += 2 * U) {
-        load(xB, aB, c + U);
-        sched_fence();
-        mma(xA, aA);
-        sched_fence();
-        load(xA, aA, c + 2 * U);
-        sched_fence();
-        mma(xB, aB);
-        sched_fence();
-      }
-    }
-  }
-  if constexpr (LIN) __syncthreads();  // the staging tiles share their memory with the partial sums
+  PS::run(acc, p, sh_tok, tl.len, tl.slot, slice, j0, rho, cbeg, cend, shr + wave * PS::SBYTES);
+  if constexpr (PS::LIN) __syncthreads();
 
 #pragma unroll
   for (int b = 0; b < BMB; ++b)
@@ -1043,6 +1060,100 @@ __global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
   }
 }
 
+// Column walk of the streaming expand. The workgroup's NW waves update the
+// output columns [cb, ce) of one slice for a tile's tokens, 16*NBU columns per
+// wave per stage, with the next stage's weight and output loads in flight
+// while the current stage is multiplied. hf[b][q]: (sc*h)^T operand fragments
+// of token block b (rank block q < NQ, ranks >= rho zero); yrow[b]: byte
+// offset in y of this lane's token row at the slice start (used only when
+// tok_ok[b]); rb: descriptor over the slot's weight rows of the slice (ldb
+// elements apart). Masked lanes (tokens past the tile, columns past ce) use
+// kOOB, so the loop has no branch around its memory operations.
+template <class Tag, int BMB, int RBM, int NQ, int NBU, int NW>
+__device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], const uint32_t (&yrow)[BMB],
+                                                   const bool (&tok_ok)[BMB], rsrc_t ry, rsrc_t rb, int ldb, int cb,
+                                                   int ce, int rho) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  using WF = WFrag<Tag>;
+  using wf_t = typename WF::type;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  constexpr int kStage = NW * NBU * 16;
+  const int nst = (ce - cb + kStage - 1) / kStage;
+  auto yoff = [&](int b, int n) -> uint32_t {
+    return (tok_ok[b] && n < ce) ? yrow[b] + static_cast<uint32_t>(n) * 4u : kOOB;
+  };
+  auto load2 = [&](wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+      const int nb = cb + k * kStage + (wave * NBU + u) * 16;
+      const int nrow = nb + col;
+      const bool rok = k < nst && nrow < ce;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int j0 = 16 * q + 4 * grp;
+        wv[u][q] = WF::bload(rb, rok ? static_cast<uint32_t>((nrow * ldb + j0) * ES) : kOOB, j0, rho);
+      }
+#pragma unroll
+      for (int b = 0; b < BMB; ++b)
+        cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB));
+    }
+  };
+  auto comp2 = [&](const wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+      const int nb = cb + k * kStage + (wave * NBU + u) * 16;
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
+        sstore16(ry, yoff(b, nb + 4 * grp), __builtin_bit_cast(uint4, cv[u][b]));
+      }
+    }
+  };
+  wf_t wvA[NBU][NQ], wvB[NBU][NQ];
+  f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
+  // two stages in flight; a stage past the last loads nothing and its
+  // columns (>= ce) store nothing, so the loop body has no exit in the middle
+  if (nst > 0) {
+    load2(wvA, cvA, 0);
+    for (int k = 0; k < nst; k += 2) {
+      load2(wvB, cvB, k + 1);
+      sched_fence();
+      comp2(wvA, cvA, k);
+      sched_fence();
+      load2(wvA, cvA, k + 2);
+      sched_fence();
+      comp2(wvB, cvB, k + 1);
+      sched_fence();
+    }
+  }
+}
+
+// expand_stream_walk for the slot's rank-block count nq (a wave-uniform
+// value), so each tile runs exactly the MFMAs its rank needs.
+template <class Tag, int BMB, int RBM, int NBU, int NW>
+__device__ __forceinline__ void expand_stream_cols(int nq, const uint4 (&hf)[BMB][RBM], const uint32_t (&yrow)[BMB],
+                                                   const bool (&tok_ok)[BMB], rsrc_t ry, rsrc_t rb, int ldb, int cb,
+                                                   int ce, int rho) {
+#define LORA_WALK(NQ) expand_stream_walk<Tag, BMB, RBM, NQ, NBU, NW>(hf, yrow, tok_ok, ry, rb, ldb, cb, ce, rho)
+  switch (nq) {
+    case 0: break;
+    case 1: LORA_WALK(1); break;
+    case 2: if constexpr (RBM >= 2) LORA_WALK(2); break;
+    case 3: if constexpr (RBM >= 4) LORA_WALK(3); break;
+    case 4: if constexpr (RBM >= 4) LORA_WALK(4); break;
+    case 5: if constexpr (RBM >= 8) LORA_WALK(5); break;
+    case 6: if constexpr (RBM >= 8) LORA_WALK(6); break;
+    case 7: if constexpr (RBM >= 8) LORA_WALK(7); break;
+    default: if constexpr (RBM >= 8) LORA_WALK(8); break;
+  }
+#undef LORA_WALK
+}
+
 // Streaming form of expand_fused (bf16/f32 b rows 4-element aligned, h rows
 // 16-byte aligned, y below 2 GiB). A workgroup owns one tile (16*BMB tokens
 // of one slot) and a chunk of one output slice (chunk_cols columns, walked
@@ -1056,9 +1167,6 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
   constexpr int TB = 16 * BMB;
-  constexpr int NW = 4;
-  using WF = WFrag<Tag>;
-  using wf_t = typename WF::type;
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
 
@@ -1120,75 +1228,97 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
   const rsrc_t rb = make_rsrc(static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0 + off * p.bs1,
                               width * p.bs1 * ES);
   // column indices fit 32 bits (the host checks the descriptors' spans)
-  constexpr int kStage = NW * NBU * 16;
-  const int cb = static_cast<int>(c_begin);
-  const int ce = static_cast<int>(c_end);
-  const int nst = (ce - cb + kStage - 1) / kStage;
-  const int ldb = static_cast<int>(p.bs1);
-  auto yoff = [&](int b, int n) -> uint32_t {
-    return (tok_ok[b] && n < ce) ? yrow[b] + static_cast<uint32_t>(n) * 4u : kOOB;
-  };
-  // The column walk for NQ rank blocks (NQ = the slot's rank blocks, a
-  // wave-uniform value, so each tile runs exactly the MFMAs its rank needs).
-  auto walk = [&](auto nq_tag) {
-    constexpr int NQ = decltype(nq_tag)::value;
-    auto load2 = [&](wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
-#pragma unroll
-      for (int u = 0; u < NBU; ++u) {
-        const int nb = cb + k * kStage + (wave * NBU + u) * 16;
-        const int nrow = nb + col;
-        const bool rok = k < nst && nrow < ce;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int j0 = 16 * q + 4 * grp;
-          wv[u][q] = WF::bload(rb, rok ? static_cast<uint32_t>((nrow * ldb + j0) * ES) : kOOB, j0, rho);
-        }
-#pragma unroll
-        for (int b = 0; b < BMB; ++b)
-          cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB));
-      }
-    };
-    auto comp2 = [&](const wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
-#pragma unroll
-      for (int u = 0; u < NBU; ++u) {
-        const int nb = cb + k * kStage + (wave * NBU + u) * 16;
-#pragma unroll
-        for (int b = 0; b < BMB; ++b) {
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
-          sstore16(ry, yoff(b, nb + 4 * grp), __builtin_bit_cast(uint4, cv[u][b]));
-        }
-      }
-    };
-    wf_t wvA[NBU][NQ], wvB[NBU][NQ];
-    f32x4_t cvA[NBU][BMB], cvB[NBU][BMB];
-    // two stages in flight; a stage past the last loads nothing and its
-    // columns (>= ce) store nothing, so the loop body has no exit in the middle
-    if (nst > 0) {
-      load2(wvA, cvA, 0);
-      for (int k = 0; k < nst; k += 2) {
-        load2(wvB, cvB, k + 1);
-        sched_fence();
-        comp2(wvA, cvA, k);
-        sched_fence();
-        load2(wvA, cvA, k + 2);
-        sched_fence();
-        comp2(wvB, cvB, k + 1);
-        sched_fence();
-      }
-    }
-  };
-  switch (nq) {
-    case 0: break;
-    case 1: walk(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (RBM >= 2) walk(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (RBM >= 4) walk(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr (RBM >= 4) walk(std::integral_constant<int, 4>{}); break;
-    case 5: if constexpr (RBM >= 8) walk(std::integral_constant<int, 5>{}); break;
-    case 6: if constexpr (RBM >= 8) walk(std::integral_constant<int, 6>{}); break;
-    case 7: if constexpr (RBM >= 8) walk(std::integral_constant<int, 7>{}); break;
-    default: if constexpr (RBM >= 8) walk(std::integral_constant<int, 8>{}); break;
+  expand_stream_cols<Tag, BMB, RBM, NBU, 4>(nq, hf, yrow, tok_ok, ry, rb, static_cast<int>(p.bs1),
+                                            static_cast<int>(c_begin), static_cast<int>(c_end), rho);
+}
+
+// One-launch apply_linear for small batches: the rank intermediate never
+// leaves the chip. A workgroup owns a tile of up to 16 grouped tokens of one
+// slot and a chunk of chunk_cols columns of one output slice. Its NW waves
+// first contract the slice's adapter rows (the slot's whole rank) with the
+// tile's x rows, each wave over one contiguous range of the feature axis
+// (PipeShrink); the partial sums meet in LDS, and every wave adds them up in
+// wave order, scales them by the slot's scaling and keeps them as (sc*h)^T
+// operand fragments. The waves then walk the chunk's columns as the streaming
+// expand does. Every chunk of a tile recomputes its slice's h; the x and
+// adapter rows it re-reads come from L2, because the work items of one tile
+// go to one XCD (workgroup ids are dealt round-robin to the 8 XCDs; item
+// (tile, chunk) has id 8 * (chunk + total_chunks * (tile / 8)) + tile % 8).
+// With NW = 4 the feature ranges and the summation order are those of the
+// pipelined shrink, so y gets the bits of the two-launch path. Needs the
+// descriptors of both the pipelined shrink and the streaming expand.
+template <class Tag, int RBM, int NW, int U, int NBU>
+__global__ __launch_bounds__(64 * NW) void slot_apply_kernel(ShrinkArgs ps, ExpandArgs pe) {
+  using E = typename Tag::elem;
+  constexpr int ES = sizeof(E);
+  using PS = PipeShrink<Tag, 1, RBM, U>;
+  constexpr int RBYTES = NW * RBM * 64 * 16;
+  // the staging tiles share their memory with the partial sums
+  __shared__ __attribute__((aligned(16))) char shr[NW * PS::SBYTES > RBYTES ? NW * PS::SBYTES : RBYTES];
+  auto red = reinterpret_cast<f32x4_t(*)[RBM][64]>(shr);
+  __shared__ Tile sh_tile;
+  __shared__ int sh_tok[16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int col = lane & 15;
+  const int tc = pe.total_chunks;
+  const int kx = static_cast<int>(blockIdx.x >> 3);
+  const int ti = (kx / tc) * 8 + static_cast<int>(blockIdx.x & 7);
+  const int ch = kx - (kx / tc) * tc;
+  int slice = 0;
+  while (slice + 1 < pe.n_slices && ch >= pe.chunk_begin[slice + 1]) ++slice;
+  const int64_t width = pe.slice_w[slice];
+  const int64_t off = pe.slice_off[slice];
+  const int64_t c_begin = (int64_t)(ch - pe.chunk_begin[slice]) * pe.chunk_cols;
+  const int64_t c_end = (c_begin + pe.chunk_cols < width) ? c_begin + pe.chunk_cols : width;
+
+  if (wave == 0) {
+    const Tile tl = find_tile(ti, 16, ps.counts, ps.offsets, ps.S);
+    if (lane == 0) sh_tile = tl;
   }
+  __syncthreads();
+  const Tile tl = sh_tile;
+  if (tl.slot < 0) return;
+  const int rho = clamp_rank(ps.ranks[tl.slot], ps.r_max);
+  if (rho == 0) return;  // the slot adds nothing
+  if (threadIdx.x < 16) sh_tok[threadIdx.x] = (static_cast<int>(threadIdx.x) < tl.len) ? ps.sorted[tl.start + threadIdx.x] : 0;
+  __syncthreads();
+
+  // shrink: rows >= rho and tokens past the tile load as zero, so every
+  // partial sum past the slot's rank or the tile is +0
+  f32x4_t acc[1][RBM];
+#pragma unroll
+  for (int q = 0; q < RBM; ++q) acc[0][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nch = static_cast<int>((ps.K + PS::CH - 1) / PS::CH);
+  const int per = (nch + NW - 1) / NW;
+  const int cbeg = wave * per;
+  const int cend = (cbeg + per < nch) ? cbeg + per : nch;
+  PS::run(acc, ps, sh_tok, tl.len, tl.slot, slice, 0, rho, cbeg, cend, shr + wave * PS::SBYTES);
+  if constexpr (PS::LIN) __syncthreads();
+#pragma unroll
+  for (int q = 0; q < RBM; ++q) red[wave][q][lane] = acc[0][q];
+  __syncthreads();
+
+  // lane (col, grp) now finds h[token col][16q + 4grp + i] in red[.][q][lane]:
+  // exactly the operand fragment the expand needs
+  const float sc = pe.scalings[tl.slot];
+  uint4 hf[1][RBM];
+#pragma unroll
+  for (int q = 0; q < RBM; ++q) {
+    f32x4_t v = red[0][q][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][q][lane];
+    v *= sc;
+    hf[0][q] = split_frag<Tag>(v);
+  }
+  const bool tok_ok[1] = {col < tl.len};
+  const uint32_t yrow[1] = {static_cast<uint32_t>((int64_t)sh_tok[col] * pe.ldy * 4 + off * 4)};
+  const rsrc_t ry = make_rsrc(pe.y, pe.y_bytes);
+  const rsrc_t rb = make_rsrc(static_cast<const E*>(pe.b) + (int64_t)tl.slot * pe.bs0 + off * pe.bs1,
+                              width * pe.bs1 * ES);
+  expand_stream_cols<Tag, 1, RBM, NBU, NW>((rho + 15) / 16, hf, yrow, tok_ok, ry, rb, static_cast<int>(pe.bs1),
+                                           static_cast<int>(c_begin), static_cast<int>(c_end), rho);
 }
 
 // Column-owner form of expand_fused (same preconditions as the streaming
@@ -1492,6 +1622,46 @@ static void launch_expand(const ExpandArgs& a, int bmb, int rbm, int64_t tiles, 
     launch_expand_b<Tag, 1>(a, rbm, grid, st);
 }
 
+// One-launch apply_linear: 4 waves per workgroup (the feature ranges of the
+// pipelined shrink, hence its bits), U feature chunks per stage in the shrink
+// (one at rank 128, to stay within the register budget), 2 column blocks per
+// wave and stage in the expand.
+template <class Tag>
+static void launch_apply(const ShrinkArgs& ps, const ExpandArgs& pe, int rbm, int64_t tiles, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(round_up(tiles, 8) * pe.total_chunks));
+  const dim3 block(256);
+  switch (rbm) {
+    case 1: launch((slot_apply_kernel<Tag, 1, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
+    case 2: launch((slot_apply_kernel<Tag, 2, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
+    case 4: launch((slot_apply_kernel<Tag, 4, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
+    default: launch((slot_apply_kernel<Tag, 8, 4, 1, 2>), grid, block, 0, st, ps, pe); break;
+  }
+}
+
+// Column chunk of the one-launch apply_linear for a batch, or 0 where the two
+// launches are faster. A one-launch workgroup streams its slice's whole
+// adapter rows through one CU, so the form only pays while every workgroup
+// gets a CU of its own: at least kApplyMinTokens tokens, and token tiles times
+// column chunks within the CU count, the tiles estimated as if the tokens
+// spread evenly over the S slots; the narrowest chunk that fits is taken.
+// Measured (bf16, K 4096, slices 4096 + 1024 + 1024, ranks 0-64; two launches
+// against one): 32 slots at 256 tokens 25.9 / 26.9 us (1024 columns), 512:
+// 33.6 / 29.9 (1024), 768: 40.1 / 38.8 (2048), 1024: 46.5 / 39.9 (2048);
+// 1536 and more tokens, or 128 slots at 512 to 2048 tokens, are a tie or
+// slower whatever the chunk (1024, 1536, 2048 or 4096 columns).
+constexpr int64_t kApplyMinTokens = 512;
+constexpr int64_t kApplyMaxWorkgroups = 256;
+static int64_t apply_one_launch_cols(int64_t T, int64_t S, const int64_t* out_slices, int32_t num_slices) {
+  if (T < kApplyMinTokens || S < 1) return 0;
+  const int64_t tiles = S * ceil_div(T, 16 * S);
+  for (int64_t cols : {int64_t(1024), int64_t(2048)}) {
+    int64_t chunks = 0;
+    for (int i = 0; i < num_slices; ++i) chunks += ceil_div(out_slices[i], cols);
+    if (tiles * chunks <= kApplyMaxWorkgroups) return cols;
+  }
+  return 0;
+}
+
 // Device address of `scratch` on the current device, looked up on the first
 // call from each device and kept (each device's copy has its own address).
 constexpr int kMaxDevices = 64;
@@ -1557,53 +1727,78 @@ static int shrink_checks(const lora_mat* x, const lora_t3* a, const lora_address
   return LORA_OK;
 }
 
-extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
-                           int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream) {
-  const int rc = shrink_checks(x, a, addr, ranks, num_slices, r_max, h);
-  if (rc != LORA_OK) return rc;
-  const int64_t T = addr->T, S = addr->S, K = x->cols;
+// Kernel arguments of the shrink (after shrink_checks); h may be null (the
+// one-launch apply_linear keeps h on chip).
+static ShrinkArgs shrink_args(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
+                              int32_t num_slices, int32_t r_max, const lora_t3* h) {
   const size_t es = elem_size(x->dtype);
-  if (T == 0 || S == 0) return LORA_OK;
-  const int bmb = tile_bmb(static_cast<int>(T));
-  const int rb = (T >= 1024) ? 4 : 1;
-  const int64_t tiles = ceil_div(T, 16 * bmb) + S;
   ShrinkArgs p{};
   p.x = x->ptr;
   p.ldx = x->stride_row;
   p.a = a->ptr;
   p.as0 = a->s0;
   p.as1 = a->s1;
-  p.h = static_cast<float*>(h->ptr);
-  p.hs0 = h->s0;
-  p.hs1 = h->s1;
+  if (h) {
+    p.h = static_cast<float*>(h->ptr);
+    p.hs0 = h->s0;
+    p.hs1 = h->s1;
+    p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
+  }
   p.counts = addr->counts;
   p.offsets = addr->offsets;
   p.sorted = addr->sorted_tokens;
   p.ranks = ranks;
-  p.K = K;
-  p.S = static_cast<int>(S);
+  p.K = x->cols;
+  p.S = static_cast<int>(addr->S);
   p.r_max = r_max;
   p.n_slices = num_slices;
+  p.x_bytes = addr->T * x->stride_row * (int64_t)es;
+  return p;
+}
+
+// x and one slot's adapter rows fit 2 GiB buffer descriptors (pipelined and
+// row-split shrinks, one-launch apply_linear).
+static bool shrink_desc_ok(const lora_mat* x, const lora_t3* a, int64_t T, int32_t num_slices, int32_t r_max) {
+  const int64_t es = static_cast<int64_t>(elem_size(x->dtype));
+  return T * x->stride_row * es <= kMaxBufferBytes && (int64_t)num_slices * r_max * a->s1 * es <= kMaxBufferBytes &&
+         x->cols < (int64_t(1) << 30);
+}
+
+extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addressing* addr, const int32_t* ranks,
+                           int32_t num_slices, int32_t r_max, const lora_t3* h, void* stream) {
+  const int rc = shrink_checks(x, a, addr, ranks, num_slices, r_max, h);
+  if (rc != LORA_OK) return rc;
+  const int64_t T = addr->T, S = addr->S;
+  if (T == 0 || S == 0) return LORA_OK;
+  const int bmb = tile_bmb(static_cast<int>(T));
+  const int rb = (T >= 1024) ? 4 : 1;
+  const int64_t tiles = ceil_div(T, 16 * bmb) + S;
+  ShrinkArgs p = shrink_args(x, a, addr, ranks, num_slices, r_max, h);
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
-  p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Schedule, from the shapes: the row-split kernel for bf16 batches of 1024
-  // tokens or more; the pipelined kernel for fewer tokens or f32; the general
-  // kernel (no buffer descriptors) where x or one slot's adapter spans more
-  // than a 2 GiB descriptor.
-  const bool desc_ok = T * x->stride_row * (int64_t)es <= kMaxBufferBytes &&
-                       (int64_t)num_slices * r_max * a->s1 * (int64_t)es <= kMaxBufferBytes && K < (int64_t(1) << 30);
-  p.x_bytes = T * x->stride_row * (int64_t)es;
-  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024) {
-    // 128-token tiles; two (slice, rank block) pairs per wave, i.e. 8 per
-    // workgroup: the prefill batch (16731 tokens, 46 slots, ranks 8-128) has
-    // only 153 token tiles, and with 16 pairs per workgroup most of a tile's
-    // work sat on one CU (224 us); 8 pairs: 191 us, 4: 206 us; 64-token tiles
-    // 206-230 us; 128-feature stages 307 us
-    constexpr int tt = 8;
-    constexpr int ppw = 2;
-    p.row_groups = static_cast<int>(ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 4 * ppw));
-    const int64_t rtiles = ceil_div(T, 16 * tt) + S;
+  // tokens or more whose grid fills the chip twice (at least 512 workgroups,
+  // counting every slot of the table as used); the pipelined kernel for the
+  // others; the general kernel (no buffer descriptors) where x or one slot's
+  // adapter spans more than a 2 GiB descriptor.
+  // Measured with bf16 inputs, K 4096, slices 4096 + 1024 + 1024, ranks up
+  // to 64, tokens spread evenly over the slots: 32 slots at 1024 / 2048 /
+  // 4096 / 8192 tokens take 23 / 27 / 27 / 48 us pipelined against 54 / 62 /
+  // 76 / 77 us row-split (grids of 128 to 192 workgroups); 128 slots at 8192
+  // tokens 53 against 66 us. The prefill batch (16731 tokens in 46 requests,
+  // K 8192, ranks up to 128, a grid of 864) takes 188 us row-split against
+  // 236 us pipelined.
+  constexpr int tt = 8;    // row-split: 128-token tiles
+  constexpr int ppw = 2;   // row-split: (slice, rank block) pairs per wave
+  const bool desc_ok = shrink_desc_ok(x, a, T, num_slices, r_max);
+  const int64_t row_groups = ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 4 * ppw);
+  const int64_t rtiles = ceil_div(T, 16 * tt) + S;
+  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024 && rtiles * row_groups >= 512) {
+    // two (slice, rank block) pairs per wave, i.e. 8 per workgroup: the
+    // prefill batch has only 153 token tiles, and with 16 pairs per
+    // workgroup most of a tile's work sat on one CU (224 us); 8 pairs:
+    // 191 us, 4: 206 us; 64-token tiles 206-230 us; 128-feature stages 307 us
+    p.row_groups = static_cast<int>(row_groups);
     const dim3 grid(static_cast<unsigned>(round_up(rtiles, 8 * kRowsGroup) * p.row_groups));
     launch((slot_shrink_rows_kernel<tt, 2, ppw>), grid, dim3(256), 0, st, p);
     return launch_status();
@@ -1644,6 +1839,64 @@ static int expand_checks(const lora_t3* h, const lora_t3* b, const lora_addressi
   return LORA_OK;
 }
 
+// Kernel arguments of the expand (after expand_checks), without the column
+// chunks; h may be null (the one-launch apply_linear keeps h on chip).
+static ExpandArgs expand_args(const lora_t3* h, const lora_t3* b, const lora_addressing* addr, const int32_t* ranks,
+                              const float* scalings, const lora_mat* y, int32_t num_slices, int32_t r_max) {
+  const size_t es = elem_size(b->dtype);
+  ExpandArgs p{};
+  if (h) {
+    p.h = static_cast<const float*>(h->ptr);
+    p.hs0 = h->s0;
+    p.hs1 = h->s1;
+    p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
+    p.h_bytes = addr->T * h->s0 * 4;
+  }
+  p.b = b->ptr;
+  p.bs0 = b->s0;
+  p.bs1 = b->s1;
+  p.y = static_cast<float*>(y->ptr);
+  p.ldy = y->stride_row;
+  p.scalings = scalings;
+  p.b_vec = b->s1 % 4 == 0 && b->s0 % 4 == 0 && aligned(b->ptr, 4 * es);
+  p.counts = addr->counts;
+  p.offsets = addr->offsets;
+  p.sorted = addr->sorted_tokens;
+  p.ranks = ranks;
+  p.S = static_cast<int>(addr->S);
+  p.r_max = r_max;
+  p.n_slices = num_slices;
+  p.y_bytes = addr->T * y->stride_row * 4;
+  return p;
+}
+
+// Cuts every output slice into chunks of `cols` columns (the last one of a
+// slice shorter); returns the number of chunks.
+static int set_chunks(ExpandArgs& p, const int64_t* out_slices, int32_t num_slices, int64_t cols) {
+  p.chunk_cols = cols;
+  int64_t off = 0;
+  int chunks = 0;
+  for (int i = 0; i < num_slices; ++i) {
+    p.slice_off[i] = off;
+    p.slice_w[i] = out_slices[i];
+    p.chunk_begin[i] = chunks;
+    chunks += static_cast<int>(ceil_div(out_slices[i], cols));
+    off += out_slices[i];
+  }
+  p.chunk_begin[num_slices] = chunks;
+  p.total_chunks = chunks;
+  return chunks;
+}
+
+// y, the slice's weight rows of one slot and their row stride fit the
+// streaming expand's 32-bit descriptor offsets, and b rows allow vector loads
+// (streaming and column-owner expands, one-launch apply_linear).
+static bool expand_desc_ok(const ExpandArgs& p, const lora_t3* b, const lora_mat* y, int64_t T, int64_t O) {
+  const int64_t es = static_cast<int64_t>(elem_size(b->dtype));
+  return p.b_vec && T * y->stride_row * 4 <= kMaxBufferBytes && O * b->s1 * es <= kMaxBufferBytes &&
+         y->stride_row < (int64_t(1) << 30);
+}
+
 extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing* addr,
                                  const int32_t* ranks, const float* scalings, const lora_mat* y,
                                  const int64_t* out_slices, int32_t num_slices, int32_t r_max, void* stream) {
@@ -1651,53 +1904,19 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   const int rc = expand_checks(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, &O);
   if (rc != LORA_OK) return rc;
   const int64_t T = addr->T, S = addr->S;
-  const size_t es = elem_size(b->dtype);
   if (T == 0 || S == 0 || O == 0) return LORA_OK;
-  ExpandArgs p{};
-  p.h = static_cast<const float*>(h->ptr);
-  p.hs0 = h->s0;
-  p.hs1 = h->s1;
-  p.b = b->ptr;
-  p.bs0 = b->s0;
-  p.bs1 = b->s1;
-  p.y = static_cast<float*>(y->ptr);
-  p.ldy = y->stride_row;
-  p.scalings = scalings;
-  p.h_vec = h->s1 % 4 == 0 && h->s0 % 4 == 0 && aligned(h->ptr, 16);
-  p.b_vec = b->s1 % 4 == 0 && b->s0 % 4 == 0 && aligned(b->ptr, 4 * es);
-  p.counts = addr->counts;
-  p.offsets = addr->offsets;
-  p.sorted = addr->sorted_tokens;
-  p.ranks = ranks;
-  p.S = static_cast<int>(S);
-  p.r_max = r_max;
-  p.n_slices = num_slices;
+  ExpandArgs p = expand_args(h, b, addr, ranks, scalings, y, num_slices, r_max);
   const int rbm = rank_blocks(r_max);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Schedule, from the shapes: the column-owner kernel for 2048 tokens or
   // more, the streaming kernel for fewer, both when their descriptors can
   // span y, h and one slot's b with 32-bit offsets and the rows of h and b
   // allow vector loads; else the general kernel.
-  const bool stream_ok = p.h_vec && p.b_vec && (T * y->stride_row * 4 <= kMaxBufferBytes) &&
-                         (O * b->s1 * (int64_t)es <= kMaxBufferBytes) && y->stride_row < (int64_t(1) << 30);
-  const bool owner_ok = stream_ok && T * h->s0 * 4 <= kMaxBufferBytes;
+  const bool stream_ok = p.h_vec && expand_desc_ok(p, b, y, T, O);
+  const bool owner_ok = stream_ok && p.h_bytes <= kMaxBufferBytes;
   if (owner_ok && T >= 2048) {
     // many tokens: column owners, weights read once per token piece
-    p.chunk_cols = kOwnerCols;
-    int64_t off = 0;
-    int chunks = 0;
-    for (int i = 0; i < num_slices; ++i) {
-      p.slice_off[i] = off;
-      p.slice_w[i] = out_slices[i];
-      p.chunk_begin[i] = chunks;
-      chunks += static_cast<int>(ceil_div(out_slices[i], kOwnerCols));
-      off += out_slices[i];
-    }
-    p.chunk_begin[num_slices] = chunks;
-    p.total_chunks = chunks;
-    if (chunks == 0) return LORA_OK;
-    p.y_bytes = T * y->stride_row * 4;
-    p.h_bytes = T * h->s0 * 4;
+    if (set_chunks(p, out_slices, num_slices, kOwnerCols) == 0) return LORA_OK;
     const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
     if (b->dtype == LORA_BF16)
       launch_expand_owner<BF16>(p, rbm, pieces, st);
@@ -1709,20 +1928,7 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
     const int bmb = (T >= 1024 && rbm <= 4) ? 2 : 1;
     const int64_t tiles = ceil_div(T, 16 * bmb) + S;
     // about 1024 columns per workgroup, fewer when there are few tiles
-    p.chunk_cols = tiles >= 256 ? 1024 : 256;
-    int64_t off = 0;
-    int chunks = 0;
-    for (int i = 0; i < num_slices; ++i) {
-      p.slice_off[i] = off;
-      p.slice_w[i] = out_slices[i];
-      p.chunk_begin[i] = chunks;
-      chunks += static_cast<int>(ceil_div(out_slices[i], p.chunk_cols));
-      off += out_slices[i];
-    }
-    p.chunk_begin[num_slices] = chunks;
-    p.total_chunks = chunks;
-    if (chunks == 0) return LORA_OK;
-    p.y_bytes = T * y->stride_row * 4;
+    if (set_chunks(p, out_slices, num_slices, tiles >= 256 ? 1024 : 256) == 0) return LORA_OK;
     if (b->dtype == LORA_BF16) {
       if (bmb == 2) launch_expand_stream<BF16, 2>(p, rbm, tiles, st);
       else launch_expand_stream<BF16, 1>(p, rbm, tiles, st);
@@ -1732,18 +1938,7 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
     }
     return launch_status();
   }
-  int64_t off = 0;
-  int chunks = 0;
-  for (int i = 0; i < num_slices; ++i) {
-    p.slice_off[i] = off;
-    p.slice_w[i] = out_slices[i];
-    p.chunk_begin[i] = chunks;
-    chunks += static_cast<int>(ceil_div(out_slices[i], kExpandCols));
-    off += out_slices[i];
-  }
-  p.chunk_begin[num_slices] = chunks;
-  p.total_chunks = chunks;
-  if (chunks == 0) return LORA_OK;
+  if (set_chunks(p, out_slices, num_slices, kExpandCols) == 0) return LORA_OK;
   const int bmb = tile_bmb(static_cast<int>(T));
   const int64_t tiles = ceil_div(T, 16 * bmb) + S;
   if (b->dtype == LORA_BF16)
@@ -1753,9 +1948,12 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   return launch_status();
 }
 
-// LoraOpsBackend.apply_linear_: the shrink into the caller's h, then the
-// expand into y, on one stream. Both operations' arguments are checked
-// before either launches.
+// LoraOpsBackend.apply_linear_ (shrink then expand into y; the page lets a
+// backend fuse the two). Batches that apply_one_launch_cols accepts run as
+// one launch with h kept on chip (slot_apply_kernel), when x, a and b share a
+// dtype and the descriptors of both kernels fit; the others as the shrink
+// into the caller's h, then the expand, on one stream. Both operations'
+// arguments are checked before anything launches.
 extern "C" int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora_t3* b, const lora_addressing* addr,
                                  const int32_t* ranks, const float* scalings, const lora_mat* y,
                                  const int64_t* out_slices, int32_t num_slices, int32_t r_max, const lora_t3* h,
@@ -1765,6 +1963,23 @@ extern "C" int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora
   int64_t O = 0;
   rc = expand_checks(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, &O);
   if (rc != LORA_OK) return rc;
+  const int64_t T = addr->T, S = addr->S;
+  if (T == 0 || S == 0 || O == 0) return LORA_OK;
+  const int64_t cols = apply_one_launch_cols(T, S, out_slices, num_slices);
+  if (cols > 0 && b->dtype == x->dtype && shrink_desc_ok(x, a, T, num_slices, r_max)) {
+    ShrinkArgs ps = shrink_args(x, a, addr, ranks, num_slices, r_max, nullptr);
+    ExpandArgs pe = expand_args(nullptr, b, addr, ranks, scalings, y, num_slices, r_max);
+    if (expand_desc_ok(pe, b, y, T, O)) {
+      set_chunks(pe, out_slices, num_slices, cols);
+      const int64_t tiles = ceil_div(T, 16) + S;
+      hipStream_t st = static_cast<hipStream_t>(stream);
+      if (x->dtype == LORA_BF16)
+        launch_apply<BF16>(ps, pe, rank_blocks(r_max), tiles, st);
+      else
+        launch_apply<F32>(ps, pe, rank_blocks(r_max), tiles, st);
+      return launch_status();
+    }
+  }
   rc = lora_shrink(x, a, addr, ranks, num_slices, r_max, h, stream);
   if (rc != LORA_OK) return rc;
   return lora_expand_fused(h, b, addr, ranks, scalings, y, out_slices, num_slices, r_max, stream);

@@ -204,7 +204,8 @@ def lora_apply_linear(x: torch.Tensor, y: torch.Tensor, a: torch.Tensor, b: torc
                       ranks: torch.Tensor, scalings: torch.Tensor, out_slices, r_max: int,
                       h: torch.Tensor | None = None) -> torch.Tensor:
     """y[t, slice i] += scalings[slot(t)] * (x[t] @ a[slot(t), slice i]^T) @ b[slot(t), slice i]^T, in place
-    (shrink then expand; h [T x num_slices x r_max] float32 is the rank intermediate's workspace). Returns y."""
+    (one launch with the rank intermediate on chip, or shrink then expand through h [T x num_slices x r_max]
+    float32, the library's choice by shape; h's contents afterwards are unspecified). Returns y."""
     lib = _lib.load()
     n = len(out_slices)
     if h is None:

@@ -28,24 +28,33 @@ CASES = [
     ("one-token", 1, 8, (4,), 1, 1, (1,), 0.0, "bf16"),
     ("prefill-long", 0, 512, (384, 128, 64), 12, 64, (8, 16, 32, 64), 0.0, "bf16"),
     ("fp32-prefill", 0, 256, (128, 64), 10, 32, (4, 16, 32), 0.0, "f32"),
+    ("prefill-many-slots", 0, 256, (256, 64, 64), 176, 128, (8, 16, 64, 128), 0.0, "bf16"),
+    ("decode-mid", 640, 512, (1536, 256, 256), 16, 128, (0, 8, 100, 128), 0.1, "bf16"),
+    ("decode-wide", 1000, 256, (3000, 500, 500), 16, 64, (0, 16, 40, 64), 0.1, "bf16"),
+    ("decode-1k", 1100, 256, (1024, 256), 8, 32, (0, 8, 32), 0.1, "bf16"),
+    ("fp32-mid", 600, 64, (32, 16), 8, 16, (0, 4, 16), 0.2, "f32"),
 ]
 # Which kernel each case reaches (the library picks by shape):
-#   shrink: row-split (bf16, >= 1024 tokens): prefill-like, prefill-long;
-#           pipelined, 16-token tiles (< 1024 tokens): decode-small, ragged-ranks, fp32, one-token;
-#           pipelined, 64-token tiles (f32, >= 1024 tokens): fp32-prefill;
+#   shrink: row-split (bf16, >= 1024 tokens, a grid of >= 512 workgroups): prefill-many-slots;
+#           pipelined, 64-token tiles (>= 1024 tokens otherwise): prefill-like, prefill-long,
+#             fp32-prefill, decode-1k;
+#           pipelined, 16-token tiles (< 1024 tokens): the others;
 #           general (no buffer descriptors): test_shrink_general_kernel.
 #   expand: column owner (>= 2048 tokens): prefill-long;
 #           streaming (fewer): the others;
 #           general (rows of h not 16-byte aligned): test_expand_general_kernel.
+#   apply_linear: one launch, 1024-column chunks: decode-mid (rank 128, two slots' ranks
+#             outside [0, r_max]), decode-1k, fp32-mid; 2048-column chunks: decode-wide;
+#           shrink then expand: the others.
+ONE_LAUNCH = ("decode-mid", "decode-wide", "decode-1k", "fp32-mid")
+REQUESTS = {"prefill-like": 12, "fp32-prefill": 12, "prefill-long": 20, "prefill-many-slots": 16}
 
 
 def _case(name, T, K, out_slices, S, r_max, choices, zero_p, dtype, seed=0, int_exact=False, wild_slots=True):
     rng = np.random.default_rng(1000 + seed + T)
-    if name in ("prefill-like", "fp32-prefill"):
-        ts, ranks, _ = synth.prefill_routing(12, S, choices, rng, median=120.0, sigma=0.6, cap=400)
-        T = ts.shape[0]
-    elif name == "prefill-long":
-        ts, ranks, _ = synth.prefill_routing(20, S, choices, rng, median=150.0, sigma=0.5, cap=400)
+    if name in REQUESTS:
+        median, sigma = (150.0, 0.5) if name in ("prefill-long", "prefill-many-slots") else (120.0, 0.6)
+        ts, ranks, _ = synth.prefill_routing(REQUESTS[name], S, choices, rng, median=median, sigma=sigma, cap=400)
         T = ts.shape[0]
     else:
         ts, ranks = synth.decode_routing(T, S, r_max, choices, zero_p, rng) if S > 1 else (
@@ -54,6 +63,8 @@ def _case(name, T, K, out_slices, S, r_max, choices, zero_p, dtype, seed=0, int_
             ts[3] = -1          # slot ids outside [0, S): inactive
             ts[5] = S
             ts[7] = 999
+        if name == "decode-mid":
+            ranks[1], ranks[2] = -3, r_max + 5     # clamped to 0 and r_max
     # bf16-rounded values are exact in fp32 too, so the fp32 cases reuse the same draws
     return synth.multi_lora(ts, ranks, K, out_slices, r_max, rng=rng, int_exact=int_exact, name=name)
 
@@ -145,7 +156,7 @@ def test_shrink(case):
     assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
 
 
-@pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-long"])
+@pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-many-slots"])
 def test_shrink_integer_exact(name):
     """Each shrink kernel (pipelined with 16- and 64-token tiles, row-split,
     bf16 and f32) bit for bit on integer inputs; unspecified entries of h
@@ -281,9 +292,10 @@ def test_shrink_then_expand(case):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_apply_linear(case):
-    """lora_apply_linear (shrink then expand in one call, h as the caller's
-    workspace) gives the bits of the two separate calls and the oracle's
-    apply_linear within tolerance; inactive rows stay bitwise untouched."""
+    """lora_apply_linear gives the bits of the two separate calls, as one
+    launch (its shrink takes the pipelined shrink's feature ranges and
+    summation order) or as two, and the oracle's apply_linear within
+    tolerance; inactive rows stay bitwise untouched."""
     m = _case(*case)
     dtype = case[-1]
     note(f"apply_linear {case[0]}")
@@ -301,6 +313,42 @@ def test_apply_linear(case):
     act, _ = _spec_mask(m)
     assert same_bits(got[~act], m.y0[~act])
     assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
+
+
+@pytest.mark.parametrize("name", list(ONE_LAUNCH) + ["decode-small", "prefill-like"])
+def test_apply_linear_integer_exact(name):
+    """lora_apply_linear bit for bit against the oracle on integer inputs:
+    the one-launch kernel (1024- and 2048-column chunks, ranks up to 128 and
+    clamped ones, bf16 and f32, fewer and more than 1024 tokens) and the
+    shrink-then-expand path; rows of inactive tokens untouched."""
+    case = next(c for c in CASES if c[0] == name)
+    m = _case(*case, int_exact=True)
+    dtype = case[-1]
+    note(f"apply_linear integer-exact {name} T={m.T}")
+    addr, ranks = _addr(m)
+    y = f32(m.y0)
+    L.lora_apply_linear(dev(m.x, dtype), y, dev(m.a, dtype), dev(m.b, dtype), addr, ranks, f32(m.scalings),
+                        m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    want = oracle.apply_linear(m.x, m.y0, m.a, m.b, m.token_slot, m.ranks, m.scalings, m.out_slices, m.r_max)
+    assert same_bits(host(y), want.astype(np.float32))
+
+
+def test_apply_linear_mixed_weight_dtype():
+    """bf16 activations and adapter with f32 expand weights at a shape that
+    would run as one launch: the shrink-then-expand path, the bits of the two
+    separate calls."""
+    m = _case(*next(c for c in CASES if c[0] == "decode-mid"))
+    note(f"apply_linear mixed dtypes T={m.T}")
+    addr, ranks = _addr(m)
+    x, a, b, sc = dev(m.x, "bf16"), dev(m.a, "bf16"), dev(m.b, "f32"), f32(m.scalings)
+    h_ref = L.lora_shrink(x, a, addr, ranks, m.num_slices, m.r_max)
+    y_ref = f32(m.y0)
+    L.lora_expand_fused(h_ref, b, addr, ranks, sc, y_ref, m.out_slices, m.r_max)
+    y = f32(m.y0)
+    L.lora_apply_linear(x, y, a, b, addr, ranks, sc, m.out_slices, m.r_max)
+    torch.cuda.synchronize()
+    assert same_bits(host(y), host(y_ref))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
