@@ -344,9 +344,15 @@ def multi_lora_figures(dev, reps=20, graph=True):
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
 
-    def timed(f, n):
+    def timed(f, n, host=False):
+        """Time per call of n calls in a row. GPU time by default: the calls
+        queue behind a short GPU spin, so the GPU runs them back to back
+        whatever the host's submission cost (about 13 us per Python call,
+        more than a decode kernel takes); host=True times them as submitted."""
         f(0)
         torch.cuda.synchronize()
+        if not host:
+            torch.cuda._sleep(20_000_000)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(n):
@@ -358,9 +364,11 @@ def multi_lora_figures(dev, reps=20, graph=True):
     out = {}
     rng4 = np.random.default_rng(4)
     ts4, rk4 = synth.decode_routing(256, 32, 64, (0, 8, 16, 32, 64), 0.1, rng4)
+    ts4k, rk4k = synth.decode_routing(1024, 32, 64, (0, 8, 16, 32, 64), 0.1, np.random.default_rng(41))
     ts5, rk5, _lengths, _rng5 = synth.config5_routing()
     for name, ts_np, rk_np, K, slices, r_max in (
             ("decode-T256-K4096-qkv-S32-rmax64", ts4, rk4, 4096, (4096, 1024, 1024), 64),
+            ("decode-T1024-K4096-qkv-S32-rmax64", ts4k, rk4k, 4096, (4096, 1024, 1024), 64),
             ("prefill-K8192-qkv-S128-rmax128", ts5, rk5, 8192, (8192, 1024, 1024), 128)):
         T, S, n, SO = ts_np.shape[0], rk_np.shape[0], len(slices), sum(slices)
         set_bytes = 2 * T * K + 2 * S * n * r_max * K + 2 * S * SO * r_max + 4 * T * SO + 4 * T * n * r_max
@@ -380,6 +388,8 @@ def multi_lora_figures(dev, reps=20, graph=True):
                                                  h=hs[i % nsets]), reps)
         t_expand = timed(lambda i: L.lora_expand_fused(hs[i % nsets], bs[i % nsets], addr, rk, sc, ys[i % nsets],
                                                        slices, r_max), reps)
+        t_apply = timed(lambda i: L.lora_apply_linear(xs[i % nsets], ys[i % nsets], as_[i % nsets], bs[i % nsets],
+                                                      addr, rk, sc, slices, r_max, h=hs[i % nsets]), reps)
         rho = np.clip(rk_np, 0, r_max)
         act = (ts_np >= 0) & (ts_np < S) & (rho[np.clip(ts_np, 0, S - 1)] > 0)
         used = np.unique(ts_np[act])
@@ -394,16 +404,21 @@ def multi_lora_figures(dev, reps=20, graph=True):
             "shrink_us": t_shrink, "shrink_gbs": sh_bytes / t_shrink / 1e3,
             "expand_fused_us": t_expand, "expand_fused_gbs": ex_bytes / t_expand / 1e3,
             "expand_fused_frac": ex_bytes / t_expand / 1e3 / HBM_PEAK_GBS,
+            # one call; one launch with h on chip where the library takes that
+            # form (the 1024-token decode), else the shrink and the expand
+            "apply_linear_us": t_apply,
+            "apply_linear_gbs": (sh_bytes + ex_bytes - 8 * n * rho_sum) / t_apply / 1e3,
         }
         if T <= 4096 and graph:
-            # a decode step's three calls back to back, eagerly and as one
-            # captured HIP graph replayed per step (no host sync or
-            # data-dependent shape in them, so a serving loop can capture them)
+            # a serving step's calls (grouping, then apply_linear) back to
+            # back: as submitted eagerly, as one captured HIP graph replayed
+            # per step (no host sync or data-dependent shape in them, so a
+            # serving loop can capture them), and the GPU time of the eager
+            # step (queued behind a spin)
             def seq(i):
                 j = i % nsets
                 L.lora_addressing_build(addr, rk, r_max)
-                L.lora_shrink(xs[j], as_[j], addr, rk, n, r_max, h=hs[j])
-                L.lora_expand_fused(hs[j], bs[j], addr, rk, sc, ys[j], slices, r_max)
+                L.lora_apply_linear(xs[j], ys[j], as_[j], bs[j], addr, rk, sc, slices, r_max, h=hs[j])
 
             side = torch.cuda.Stream(device=dev)
             side.wait_stream(torch.cuda.current_stream(dev))
@@ -414,8 +429,9 @@ def multi_lora_figures(dev, reps=20, graph=True):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 seq(0)
-            out[name]["step_eager_us"] = timed(seq, reps)
-            out[name]["step_graph_us"] = timed(lambda i: graph.replay(), reps)
+            out[name]["step_eager_us"] = timed(seq, reps, host=True)
+            out[name]["step_graph_us"] = timed(lambda i: graph.replay(), reps, host=True)
+            out[name]["step_gpu_us"] = timed(seq, reps)
             del graph
         del xs, as_, bs, ys, hs
     # gather_shrink over the 128256-row embedding adapter table (4.2 GB, rank index contiguous)

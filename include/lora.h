@@ -166,24 +166,28 @@ size_t lora_workspace_bytes(int op, int64_t M, int64_t K, int64_t L, int32_t r, 
  *                   are packed into the workspace first).
  *   lora_B  r x L   any strides (a view of an L x r weight with stride_row 1
  *                   is read in place; others are packed).
- *   res     M x L   float32, accumulated in place (the page's `res`; pass a
- *                   zeroed buffer when there is none). stride_col 1, row
+ *   res     M x L   accumulated in place (the page's `res`; pass a zeroed
+ *                   buffer when there is none): float32, or bfloat16 when x,
+ *                   lora_A and lora_B are bfloat16 (the page's output dtype:
+ *                   the float32 sum of res and the update is rounded once to
+ *                   the nearest bfloat16, ties to even). stride_col 1, row
  *                   16-byte aligned, L a multiple of 4.
  *   1 <= r <= 128.
  *   The library picks one of two schedules from the shapes: fused (one
  *   workgroup per token tile computes the rank-r intermediate and expands it,
- *   the intermediate never leaves registers and LDS) or split (a shrink kernel
- *   writes the intermediate to the workspace as MFMA operand fragments, 1 KB
- *   per 16 tokens and 16 ranks, and several workgroups per token tile expand
- *   disjoint column ranges). Both give the same results up to float32
- *   summation order.
+ *   the intermediate never leaves registers and LDS) for K <= 8192 and an
+ *   output of at most 256 MB; else split (a shrink kernel writes the
+ *   intermediate to the workspace as MFMA operand fragments, 1 KB per 16
+ *   tokens and 16 ranks, and each workgroup of the expand owns a band of 256
+ *   output columns over a few token tiles). Both give the same results up to
+ *   float32 summation order.
  *   workspace: lora_workspace_bytes(LORA_OP_FWD, ...) bytes (an upper bound
- *   over all layouts). It is needed only when a weight must be packed (a
- *   layout other than the two read in place) or the split schedule runs
- *   (K > 8192); otherwise the call uses none and workspace may be NULL with
- *   workspace_bytes 0, as for the page's lora_forward_wrapper, which takes
- *   only x, lora_A, lora_B, res and scale. LORA_ERR_WORKSPACE when one is
- *   needed and missing or too small.
+ *   over all layouts and output dtypes). It is needed only when a weight must
+ *   be packed (a layout other than the two read in place) or the split
+ *   schedule runs; otherwise the call uses none and workspace may be NULL
+ *   with workspace_bytes 0, as for the page's lora_forward_wrapper, which
+ *   takes only x, lora_A, lora_B, res and scale. LORA_ERR_WORKSPACE when one
+ *   is needed and missing or too small.
  */
 int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_mat* lora_B, const lora_mat* res,
              float scale, void* workspace, size_t workspace_bytes, void* stream);
@@ -271,8 +275,10 @@ int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addressing* addr
  *              of 4, ptr 16-byte aligned.
  *   b          S x sum(out_slices) x r_max, bf16 or f32; s2 must be 1.
  *   scalings   float32[S], device.
- *   y          T x sum(out_slices) float32, updated in place; stride_col 1,
- *              16-byte aligned rows.
+ *   y          T x sum(out_slices), updated in place: float32, or bfloat16
+ *              when b is bfloat16 (the float32 sum of y and the update is
+ *              rounded once to the nearest bfloat16, ties to even);
+ *              stride_col 1, 16-byte aligned rows.
  *   out_slices int64[num_slices], HOST memory: widths of the output slices
  *              (each a multiple of 4), concatenated along y's columns and b's
  *              rows.

@@ -106,6 +106,12 @@ __device__ __forceinline__ uint4 sload16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void sstore16(rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, kStreamStorePolicy);
 }
+__device__ __forceinline__ uint2 sload8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kStreamLoadPolicy));
+}
+__device__ __forceinline__ void sstore8(rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (int)off, 0, kStreamStorePolicy);
+}
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -123,6 +129,49 @@ __device__ __forceinline__ uint32_t bf16_bits(float v) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
 }
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// An output the kernels add into in place, 4 consecutive columns per lane
+// (the offset is in bytes, kOOB for masked lanes). float32: one 16-byte
+// access. bfloat16: one 8-byte access; the float32 sum of the old value and
+// the update is rounded once, to nearest even (NaN stays NaN, beyond the
+// largest bfloat16 it becomes infinite).
+template <class O>
+struct Out;
+template <>
+struct Out<float> {
+  static constexpr int ES = 4;
+  static __device__ __forceinline__ f32x4_t load4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4_t, sload16(r, off));
+  }
+  static __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, f32x4_t v) {
+    sstore16(r, off, __builtin_bit_cast(uint4, v));
+  }
+  // plain-pointer forms (p: 16-byte aligned)
+  static __device__ __forceinline__ f32x4_t ld4(const void* p) {
+    return __builtin_bit_cast(f32x4_t, *reinterpret_cast<const uint4*>(p));
+  }
+  static __device__ __forceinline__ void st4(void* p, f32x4_t v) {
+    *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+  }
+};
+template <>
+struct Out<uint16_t> {
+  static constexpr int ES = 2;
+  static __device__ __forceinline__ f32x4_t load4(rsrc_t r, uint32_t off) { return unpack(sload8(r, off)); }
+  static __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, f32x4_t v) {
+    sstore8(r, off, pack(v));
+  }
+  // plain-pointer forms (p: 8-byte aligned)
+  static __device__ __forceinline__ f32x4_t ld4(const void* p) { return unpack(*reinterpret_cast<const uint2*>(p)); }
+  static __device__ __forceinline__ void st4(void* p, f32x4_t v) { *reinterpret_cast<uint2*>(p) = pack(v); }
+  static __device__ __forceinline__ uint2 pack(f32x4_t v) {
+    return make_uint2(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16));
+  }
+  static __device__ __forceinline__ f32x4_t unpack(uint2 w) {
+    return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                   __uint_as_float(w.y & 0xFFFF0000u)};
+  }
+};
 
 // ---------------------------------------------------------------------------
 // contraction step over one 128-bit vector per lane:  acc += A * B

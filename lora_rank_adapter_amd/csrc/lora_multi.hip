@@ -945,7 +945,7 @@ struct ExpandArgs {
   int64_t hs0, hs1;
   const void* b;
   int64_t bs0, bs1;  // slot and row strides; j contiguous
-  float* y;
+  void* y;  // float32, or bfloat16 (weights in bfloat16): updated in place
   int64_t ldy;
   const float* scalings;
   const int32_t* counts;
@@ -967,9 +967,11 @@ struct ExpandArgs {
 constexpr int kExpandNBU = 4;                  // 16-column blocks per wave
 constexpr int kExpandCols = 64 * kExpandNBU;   // columns per workgroup
 
-template <class Tag, int BMB, int RBM>
+template <class Tag, class YT, int BMB, int RBM>
 __global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
+  using O = Out<YT>;
+  YT* const yp = static_cast<YT*>(p.y);
   constexpr int TB = 16 * BMB;
   constexpr int NBU = kExpandNBU;
   __shared__ Tile sh_tile;
@@ -1042,7 +1044,7 @@ __global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
 #pragma unroll
     for (int b = 0; b < BMB; ++b) {
       const bool ok = tok_ok[b] && ncol < width;
-      cv[u][b] = ok ? ld16f(p.y + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      cv[u][b] = ok ? O::ld4(yp + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll
@@ -1055,7 +1057,7 @@ __global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
 #pragma unroll
       for (int q = 0; q < RBM; ++q)
         if (q < nq) mma_rank16<Tag>(cv[u][b], wv[u][q], hf[b][q]);
-      if (tok_ok[b] && ncol < width) st16f(p.y + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol, cv[u][b]);
+      if (tok_ok[b] && ncol < width) O::st4(yp + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol, cv[u][b]);
     }
   }
 }
@@ -1065,11 +1067,12 @@ __global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
 // wave per stage, with the next stage's weight and output loads in flight
 // while the current stage is multiplied. hf[b][q]: (sc*h)^T operand fragments
 // of token block b (rank block q < NQ, ranks >= rho zero); yrow[b]: byte
-// offset in y of this lane's token row at the slice start (used only when
-// tok_ok[b]); rb: descriptor over the slot's weight rows of the slice (ldb
-// elements apart). Masked lanes (tokens past the tile, columns past ce) use
-// kOOB, so the loop has no branch around its memory operations.
-template <class Tag, int BMB, int RBM, int NQ, int NBU, int NW>
+// offset in y (elements of type YT) of this lane's token row at the slice
+// start (used only when tok_ok[b]); rb: descriptor over the slot's weight rows
+// of the slice (ldb elements apart). Masked lanes (tokens past the tile,
+// columns past ce) use kOOB, so the loop has no branch around its memory
+// operations.
+template <class Tag, class YT, int BMB, int RBM, int NQ, int NBU, int NW>
 __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], const uint32_t (&yrow)[BMB],
                                                    const bool (&tok_ok)[BMB], rsrc_t ry, rsrc_t rb, int ldb, int cb,
                                                    int ce, int rho) {
@@ -1077,6 +1080,7 @@ __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], 
   constexpr int ES = sizeof(E);
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
+  using O = Out<YT>;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int col = lane & 15;
@@ -1084,7 +1088,7 @@ __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], 
   constexpr int kStage = NW * NBU * 16;
   const int nst = (ce - cb + kStage - 1) / kStage;
   auto yoff = [&](int b, int n) -> uint32_t {
-    return (tok_ok[b] && n < ce) ? yrow[b] + static_cast<uint32_t>(n) * 4u : kOOB;
+    return (tok_ok[b] && n < ce) ? yrow[b] + static_cast<uint32_t>(n) * static_cast<uint32_t>(O::ES) : kOOB;
   };
   auto load2 = [&](wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
 #pragma unroll
@@ -1099,7 +1103,7 @@ __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], 
       }
 #pragma unroll
       for (int b = 0; b < BMB; ++b)
-        cv[u][b] = __builtin_bit_cast(f32x4_t, sload16(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB));
+        cv[u][b] = O::load4(ry, k < nst ? yoff(b, nb + 4 * grp) : kOOB);
     }
   };
   auto comp2 = [&](const wf_t (&wv)[NBU][NQ], f32x4_t (&cv)[NBU][BMB], int k) {
@@ -1110,7 +1114,7 @@ __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], 
       for (int b = 0; b < BMB; ++b) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
-        sstore16(ry, yoff(b, nb + 4 * grp), __builtin_bit_cast(uint4, cv[u][b]));
+        O::store4(ry, yoff(b, nb + 4 * grp), cv[u][b]);
       }
     }
   };
@@ -1135,11 +1139,11 @@ __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], 
 
 // expand_stream_walk for the slot's rank-block count nq (a wave-uniform
 // value), so each tile runs exactly the MFMAs its rank needs.
-template <class Tag, int BMB, int RBM, int NBU, int NW>
+template <class Tag, class YT, int BMB, int RBM, int NBU, int NW>
 __device__ __forceinline__ void expand_stream_cols(int nq, const uint4 (&hf)[BMB][RBM], const uint32_t (&yrow)[BMB],
                                                    const bool (&tok_ok)[BMB], rsrc_t ry, rsrc_t rb, int ldb, int cb,
                                                    int ce, int rho) {
-#define LORA_WALK(NQ) expand_stream_walk<Tag, BMB, RBM, NQ, NBU, NW>(hf, yrow, tok_ok, ry, rb, ldb, cb, ce, rho)
+#define LORA_WALK(NQ) expand_stream_walk<Tag, YT, BMB, RBM, NQ, NBU, NW>(hf, yrow, tok_ok, ry, rb, ldb, cb, ce, rho)
   switch (nq) {
     case 0: break;
     case 1: LORA_WALK(1); break;
@@ -1162,10 +1166,11 @@ __device__ __forceinline__ void expand_stream_cols(int nq, const uint4 (&hf)[BMB
 // one tile, so the rows being updated at any time are few. Loads and stores
 // go through buffer descriptors: masked lanes (tokens past the tile, columns
 // past the slice) use an out-of-range offset.
-template <class Tag, int BMB, int RBM, int NBU>
+template <class Tag, class YT, int BMB, int RBM, int NBU>
 __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
+  constexpr int64_t YES = sizeof(YT);
   constexpr int TB = 16 * BMB;
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
@@ -1204,7 +1209,7 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
   for (int b = 0; b < BMB; ++b) {
     tok_ok[b] = 16 * b + col < tl.len;
     const int t = sh_tok[16 * b + col];
-    yrow[b] = static_cast<uint32_t>((int64_t)t * p.ldy * 4 + off * 4);
+    yrow[b] = static_cast<uint32_t>(((int64_t)t * p.ldy + off) * YES);
     const float* hrow = p.h + (int64_t)t * p.hs0 + (int64_t)slice * p.hs1;
 #pragma unroll
     for (int q = 0; q < RBM; ++q) {
@@ -1228,7 +1233,7 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
   const rsrc_t rb = make_rsrc(static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0 + off * p.bs1,
                               width * p.bs1 * ES);
   // column indices fit 32 bits (the host checks the descriptors' spans)
-  expand_stream_cols<Tag, BMB, RBM, NBU, 4>(nq, hf, yrow, tok_ok, ry, rb, static_cast<int>(p.bs1),
+  expand_stream_cols<Tag, YT, BMB, RBM, NBU, 4>(nq, hf, yrow, tok_ok, ry, rb, static_cast<int>(p.bs1),
                                             static_cast<int>(c_begin), static_cast<int>(c_end), rho);
 }
 
@@ -1247,10 +1252,11 @@ __global__ __launch_bounds__(256) void slot_expand_stream_kernel(ExpandArgs p) {
 // With NW = 4 the feature ranges and the summation order are those of the
 // pipelined shrink, so y gets the bits of the two-launch path. Needs the
 // descriptors of both the pipelined shrink and the streaming expand.
-template <class Tag, int RBM, int NW, int U, int NBU>
+template <class Tag, class YT, int RBM, int NW, int U, int NBU>
 __global__ __launch_bounds__(64 * NW) void slot_apply_kernel(ShrinkArgs ps, ExpandArgs pe) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
+  constexpr int64_t YES = sizeof(YT);
   using PS = PipeShrink<Tag, 1, RBM, U>;
   constexpr int RBYTES = NW * RBM * 64 * 16;
   // the staging tiles share their memory with the partial sums
@@ -1313,11 +1319,11 @@ __global__ __launch_bounds__(64 * NW) void slot_apply_kernel(ShrinkArgs ps, Expa
     hf[0][q] = split_frag<Tag>(v);
   }
   const bool tok_ok[1] = {col < tl.len};
-  const uint32_t yrow[1] = {static_cast<uint32_t>((int64_t)sh_tok[col] * pe.ldy * 4 + off * 4)};
+  const uint32_t yrow[1] = {static_cast<uint32_t>(((int64_t)sh_tok[col] * pe.ldy + off) * YES)};
   const rsrc_t ry = make_rsrc(pe.y, pe.y_bytes);
   const rsrc_t rb = make_rsrc(static_cast<const E*>(pe.b) + (int64_t)tl.slot * pe.bs0 + off * pe.bs1,
                               width * pe.bs1 * ES);
-  expand_stream_cols<Tag, 1, RBM, NBU, NW>((rho + 15) / 16, hf, yrow, tok_ok, ry, rb, static_cast<int>(pe.bs1),
+  expand_stream_cols<Tag, YT, 1, RBM, NBU, NW>((rho + 15) / 16, hf, yrow, tok_ok, ry, rb, static_cast<int>(pe.bs1),
                                            static_cast<int>(c_begin), static_cast<int>(c_end), rho);
 }
 
@@ -1335,10 +1341,11 @@ constexpr int kOwnerTokens = 1024;
 constexpr int kOwnerCols = 128;
 constexpr int kOwnerGroup = 4;  // consecutive work items per XCD group
 
-template <class Tag, int RBM>
+template <class Tag, class YT, int RBM>
 __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
+  using O = Out<YT>;
   constexpr int NW = 4;
   constexpr int NCT = kOwnerCols / 16;  // column tiles of the chunk
   using WF = WFrag<Tag>;
@@ -1402,8 +1409,9 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   const int nblk = (tl.len + 15) / 16;
 
   // Row-linear output: a block's 16 rows x 128 columns are read and written
-  // as 512-byte row segments (32 lanes per row, 2 rows per instruction); the
-  // MFMA products reach that layout through the wave's LDS tile.
+  // as row segments of 128 values (512 bytes in float32, 256 in bfloat16;
+  // 32 lanes per row, 2 rows per instruction); the MFMA products reach that
+  // layout through the wave's LDS tile.
   constexpr int LPR = NCT * 16 / 4;  // lanes per row
   constexpr int RPI = 64 / LPR;      // rows per instruction
   constexpr int NI = 16 / RPI;       // row instructions per block
@@ -1428,8 +1436,8 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
         const int tix = 16 * blk + RPI * i + lr;
         const bool ok = blk < nblk && tix < tl.len && col_ok;
         const int t = sh_tok[ok ? tix : 0];
-        B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * 4) : kOOB;
-        B.cv[i] = __builtin_bit_cast(f32x4_t, sload16(ry, B.yo[i]));
+        B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * O::ES) : kOOB;
+        B.cv[i] = O::load4(ry, B.yo[i]);
       }
       const int tix = 16 * blk + col;
       const bool tok_ok = blk < nblk && tix < tl.len;
@@ -1469,7 +1477,7 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(ob + (RPI * i + lr) * LDW + lc);
-        sstore16(ry, B.yo[i], __builtin_bit_cast(uint4, B.cv[i] + pr));
+        O::store4(ry, B.yo[i], B.cv[i] + pr);
       }
     };
     Blk A, Bb;
@@ -1578,63 +1586,78 @@ static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, b
   }
 }
 
-template <class Tag, int BMB>
+template <class Tag, class YT, int BMB>
 static void launch_expand_b(const ExpandArgs& a, int rbm, dim3 grid, hipStream_t st) {
   switch (rbm) {
-    case 1: launch((slot_expand_kernel<Tag, BMB, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: launch((slot_expand_kernel<Tag, BMB, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: launch((slot_expand_kernel<Tag, BMB, 4>), grid, dim3(256), 0, st, a); break;
-    default: launch((slot_expand_kernel<Tag, BMB, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_kernel<Tag, YT, BMB, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_kernel<Tag, YT, BMB, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_kernel<Tag, YT, BMB, 4>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_kernel<Tag, YT, BMB, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
 // Streaming expand: (BMB, NBU) per rank-block count, chosen to keep the
 // weight and output fragments of two stages within the register budget.
-template <class Tag, int BMB>
+template <class Tag, class YT, int BMB>
 static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.total_chunks));
   switch (rbm) {
-    case 1: launch((slot_expand_stream_kernel<Tag, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
-    case 2: launch((slot_expand_stream_kernel<Tag, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
-    case 4: launch((slot_expand_stream_kernel<Tag, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
-    default: launch((slot_expand_stream_kernel<Tag, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_stream_kernel<Tag, YT, BMB, 1, 4>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_stream_kernel<Tag, YT, BMB, 2, 4>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_stream_kernel<Tag, YT, BMB, 4, 2>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_stream_kernel<Tag, YT, BMB, 8, 2>), grid, dim3(256), 0, st, a); break;
   }
 }
 
-template <class Tag>
+template <class Tag, class YT>
 static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
   a.n_work = static_cast<int>(pieces * a.total_chunks);
   const dim3 grid(static_cast<unsigned>(round_up(a.n_work, 8 * kOwnerGroup)));
   switch (rbm) {
-    case 1: launch((slot_expand_owner_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: launch((slot_expand_owner_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: launch((slot_expand_owner_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
-    default: launch((slot_expand_owner_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_owner_kernel<Tag, YT, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_owner_kernel<Tag, YT, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_owner_kernel<Tag, YT, 4>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_owner_kernel<Tag, YT, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
-template <class Tag>
+template <class Tag, class YT>
 static void launch_expand(const ExpandArgs& a, int bmb, int rbm, int64_t tiles, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.total_chunks));
   if (bmb == 4)
-    launch_expand_b<Tag, 4>(a, rbm, grid, st);
+    launch_expand_b<Tag, YT, 4>(a, rbm, grid, st);
   else
-    launch_expand_b<Tag, 1>(a, rbm, grid, st);
+    launch_expand_b<Tag, YT, 1>(a, rbm, grid, st);
+}
+
+// Calls f(Tag{}, YT{}) for the expand weights' dtype and the output's: bf16
+// or f32 weights into a float32 y, bf16 weights into a bfloat16 y (the host
+// checks refuse bfloat16 y with f32 weights).
+template <class F>
+static void with_expand_types(int32_t b_dtype, int32_t y_dtype, F&& f) {
+  if (b_dtype == LORA_BF16) {
+    if (y_dtype == LORA_BF16)
+      f(BF16{}, uint16_t{});
+    else
+      f(BF16{}, float{});
+  } else {
+    f(F32{}, float{});
+  }
 }
 
 // One-launch apply_linear: 4 waves per workgroup (the feature ranges of the
 // pipelined shrink, hence its bits), U feature chunks per stage in the shrink
 // (one at rank 128, to stay within the register budget), 2 column blocks per
 // wave and stage in the expand.
-template <class Tag>
+template <class Tag, class YT>
 static void launch_apply(const ShrinkArgs& ps, const ExpandArgs& pe, int rbm, int64_t tiles, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(round_up(tiles, 8) * pe.total_chunks));
   const dim3 block(256);
   switch (rbm) {
-    case 1: launch((slot_apply_kernel<Tag, 1, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
-    case 2: launch((slot_apply_kernel<Tag, 2, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
-    case 4: launch((slot_apply_kernel<Tag, 4, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
-    default: launch((slot_apply_kernel<Tag, 8, 4, 1, 2>), grid, block, 0, st, ps, pe); break;
+    case 1: launch((slot_apply_kernel<Tag, YT, 1, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
+    case 2: launch((slot_apply_kernel<Tag, YT, 2, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
+    case 4: launch((slot_apply_kernel<Tag, YT, 4, 4, 2, 2>), grid, block, 0, st, ps, pe); break;
+    default: launch((slot_apply_kernel<Tag, YT, 8, 4, 1, 2>), grid, block, 0, st, ps, pe); break;
   }
 }
 
@@ -1830,7 +1853,10 @@ static int expand_checks(const lora_t3* h, const lora_t3* b, const lora_addressi
   if (h->d0 != T || h->d1 != num_slices || h->d2 != r_max) return LORA_ERR_SHAPE;
   if (b->d0 != S || b->d1 != O || b->d2 != r_max) return LORA_ERR_SHAPE;
   if (y->rows != T || y->cols != O) return LORA_ERR_SHAPE;
-  if (h->dtype != LORA_F32 || !float_dtype_ok(b->dtype) || y->dtype != LORA_F32) return LORA_ERR_DTYPE;
+  // y float32, or bfloat16 (updated in place, one rounding) with bf16 weights
+  if (h->dtype != LORA_F32 || !float_dtype_ok(b->dtype) ||
+      !(y->dtype == LORA_F32 || (y->dtype == LORA_BF16 && b->dtype == LORA_BF16)))
+    return LORA_ERR_DTYPE;
   if ((T > 0 && !h->ptr) || (S * O > 0 && !b->ptr) || (T * O > 0 && !y->ptr) || (S > 0 && !scalings))
     return LORA_ERR_NULL;
   if (h->s2 != 1 || b->s2 != 1) return LORA_ERR_STRIDE;
@@ -1855,7 +1881,7 @@ static ExpandArgs expand_args(const lora_t3* h, const lora_t3* b, const lora_add
   p.b = b->ptr;
   p.bs0 = b->s0;
   p.bs1 = b->s1;
-  p.y = static_cast<float*>(y->ptr);
+  p.y = y->ptr;
   p.ldy = y->stride_row;
   p.scalings = scalings;
   p.b_vec = b->s1 % 4 == 0 && b->s0 % 4 == 0 && aligned(b->ptr, 4 * es);
@@ -1866,7 +1892,7 @@ static ExpandArgs expand_args(const lora_t3* h, const lora_t3* b, const lora_add
   p.S = static_cast<int>(addr->S);
   p.r_max = r_max;
   p.n_slices = num_slices;
-  p.y_bytes = addr->T * y->stride_row * 4;
+  p.y_bytes = addr->T * y->stride_row * static_cast<int64_t>(elem_size(y->dtype));
   return p;
 }
 
@@ -1891,9 +1917,9 @@ static int set_chunks(ExpandArgs& p, const int64_t* out_slices, int32_t num_slic
 // y, the slice's weight rows of one slot and their row stride fit the
 // streaming expand's 32-bit descriptor offsets, and b rows allow vector loads
 // (streaming and column-owner expands, one-launch apply_linear).
-static bool expand_desc_ok(const ExpandArgs& p, const lora_t3* b, const lora_mat* y, int64_t T, int64_t O) {
+static bool expand_desc_ok(const ExpandArgs& p, const lora_t3* b, const lora_mat* y, int64_t O) {
   const int64_t es = static_cast<int64_t>(elem_size(b->dtype));
-  return p.b_vec && T * y->stride_row * 4 <= kMaxBufferBytes && O * b->s1 * es <= kMaxBufferBytes &&
+  return p.b_vec && p.y_bytes <= kMaxBufferBytes && O * b->s1 * es <= kMaxBufferBytes &&
          y->stride_row < (int64_t(1) << 30);
 }
 
@@ -1912,16 +1938,15 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   // more, the streaming kernel for fewer, both when their descriptors can
   // span y, h and one slot's b with 32-bit offsets and the rows of h and b
   // allow vector loads; else the general kernel.
-  const bool stream_ok = p.h_vec && expand_desc_ok(p, b, y, T, O);
+  const bool stream_ok = p.h_vec && expand_desc_ok(p, b, y, O);
   const bool owner_ok = stream_ok && p.h_bytes <= kMaxBufferBytes;
   if (owner_ok && T >= 2048) {
     // many tokens: column owners, weights read once per token piece
     if (set_chunks(p, out_slices, num_slices, kOwnerCols) == 0) return LORA_OK;
     const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
-    if (b->dtype == LORA_BF16)
-      launch_expand_owner<BF16>(p, rbm, pieces, st);
-    else
-      launch_expand_owner<F32>(p, rbm, pieces, st);
+    with_expand_types(b->dtype, y->dtype, [&](auto tag, auto yt) {
+      launch_expand_owner<decltype(tag), decltype(yt)>(p, rbm, pieces, st);
+    });
     return launch_status();
   }
   if (stream_ok) {
@@ -1929,22 +1954,20 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
     const int64_t tiles = ceil_div(T, 16 * bmb) + S;
     // about 1024 columns per workgroup, fewer when there are few tiles
     if (set_chunks(p, out_slices, num_slices, tiles >= 256 ? 1024 : 256) == 0) return LORA_OK;
-    if (b->dtype == LORA_BF16) {
-      if (bmb == 2) launch_expand_stream<BF16, 2>(p, rbm, tiles, st);
-      else launch_expand_stream<BF16, 1>(p, rbm, tiles, st);
-    } else {
-      if (bmb == 2) launch_expand_stream<F32, 2>(p, rbm, tiles, st);
-      else launch_expand_stream<F32, 1>(p, rbm, tiles, st);
-    }
+    with_expand_types(b->dtype, y->dtype, [&](auto tag, auto yt) {
+      if (bmb == 2)
+        launch_expand_stream<decltype(tag), decltype(yt), 2>(p, rbm, tiles, st);
+      else
+        launch_expand_stream<decltype(tag), decltype(yt), 1>(p, rbm, tiles, st);
+    });
     return launch_status();
   }
   if (set_chunks(p, out_slices, num_slices, kExpandCols) == 0) return LORA_OK;
   const int bmb = tile_bmb(static_cast<int>(T));
   const int64_t tiles = ceil_div(T, 16 * bmb) + S;
-  if (b->dtype == LORA_BF16)
-    launch_expand<BF16>(p, bmb, rbm, tiles, st);
-  else
-    launch_expand<F32>(p, bmb, rbm, tiles, st);
+  with_expand_types(b->dtype, y->dtype, [&](auto tag, auto yt) {
+    launch_expand<decltype(tag), decltype(yt)>(p, bmb, rbm, tiles, st);
+  });
   return launch_status();
 }
 
@@ -1969,14 +1992,13 @@ extern "C" int lora_apply_linear(const lora_mat* x, const lora_t3* a, const lora
   if (cols > 0 && b->dtype == x->dtype && shrink_desc_ok(x, a, T, num_slices, r_max)) {
     ShrinkArgs ps = shrink_args(x, a, addr, ranks, num_slices, r_max, nullptr);
     ExpandArgs pe = expand_args(nullptr, b, addr, ranks, scalings, y, num_slices, r_max);
-    if (expand_desc_ok(pe, b, y, T, O)) {
+    if (expand_desc_ok(pe, b, y, O)) {
       set_chunks(pe, out_slices, num_slices, cols);
       const int64_t tiles = ceil_div(T, 16) + S;
       hipStream_t st = static_cast<hipStream_t>(stream);
-      if (x->dtype == LORA_BF16)
-        launch_apply<BF16>(ps, pe, rank_blocks(r_max), tiles, st);
-      else
-        launch_apply<F32>(ps, pe, rank_blocks(r_max), tiles, st);
+      with_expand_types(b->dtype, y->dtype, [&](auto tag, auto yt) {
+        launch_apply<decltype(tag), decltype(yt)>(ps, pe, rank_blocks(r_max), tiles, st);
+      });
       return launch_status();
     }
   }

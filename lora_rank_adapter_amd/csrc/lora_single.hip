@@ -140,10 +140,11 @@ struct FusedArgs {
   int64_t ldz;
   const void* w1;
   int64_t ldw1;
-  // expand: W2 (Nout rows of r values) into the fp32 output (M x Nout)
+  // expand: W2 (Nout rows of r values) into the output (M x Nout, float32
+  // or, for the forward, bfloat16)
   const void* w2;
   int64_t ldw2;
-  float* out;
+  void* out;
   int64_t ldo;
   // s*H written for other kernels: transposed hi/lo planes for the gradient
   // kernels (rp rows of ldg tokens) and MFMA operand fragments for the
@@ -375,6 +376,22 @@ __device__ __forceinline__ void emit_planes(const FusedArgs& p, int64_t m0, cons
   }
 }
 
+// What an expand does with its output: overwrite it in float32 (dX), add
+// into float32 (Y, an accumulated dX), or add into bfloat16 (Y), the float32
+// sum rounded once.
+struct OutSet {
+  using T = float;
+  static constexpr bool ACCUM = false;
+};
+struct OutAdd {
+  using T = float;
+  static constexpr bool ACCUM = true;
+};
+struct OutAddBF16 {
+  using T = uint16_t;
+  static constexpr bool ACCUM = true;
+};
+
 // ---- expand of one token tile over all output columns ----------------------
 // out^T tile (16 columns x 16 tokens) (+)= W2 * (s*H)^T for every 16-column
 // block; wave w takes NBU consecutive blocks per stage (the NW waves cover
@@ -385,7 +402,7 @@ __device__ __forceinline__ void emit_planes(const FusedArgs& p, int64_t m0, cons
 // The output is read and written one row segment at a time: each stage's
 // MFMA products (16 columns x 16 tokens per tile, in MFMA layout) go to an
 // LDS tile, and lanes then take 16-byte pieces of whole rows, add the output
-// row-linearly (ACCUM) and store it. How long those row segments are decides
+// row-linearly (when the expand accumulates) and store it. How long those row segments are decides
 // how fast the output streams: 2 rows x 512 bytes per instruction stream at
 // the speed of a plain elementwise add over the same tensor, 8 rows x 128
 // bytes up to 40% slower (measured on a 16384 x 4096 float32 output). So:
@@ -419,7 +436,7 @@ struct ExpandRows {
   static_assert(64 % LPR == 0 && ROWS % RPI == 0 && NI >= 1, "stage shape");
 };
 
-template <class Tag, int NW, int RB, int BMB, int NBU, bool ACCUM>
+template <class Tag, int NW, int RB, int BMB, int NBU, class OM>
 __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0, int64_t rot,
                                                  const uint4 (&hf)[BMB][RB], float* lds) {
   using E = typename Tag::elem;
@@ -442,7 +459,8 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
   float* tile0 = X::SH ? lds : lds + wave * X::TILE;
   float* tile1 = X::SH ? lds + X::TILE : tile0;
   const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
-  const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, (p.M - m0) * p.ldo * 4);
+  using O = Out<typename OM::T>;
+  const rsrc_t ro = make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * O::ES, (p.M - m0) * p.ldo * O::ES);
   const int64_t nb_end = (p.Nout + 15) / 16;
   constexpr int gstep = NW * NBU;
   // stage bookkeeping in scalar registers (a 64-bit division would leave it
@@ -461,7 +479,7 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
   auto ooff = [&](int i, int64_t nb0) -> uint32_t {
     const int64_t n = tile_nb(nb0) * 16 + lc;
     const int row = row0 + RPI * i + lr;
-    return (nb0 < nb_end && n < p.Nout) ? static_cast<uint32_t>(((int64_t)row * p.ldo + n) * 4) : kOOB;
+    return (nb0 < nb_end && n < p.Nout) ? static_cast<uint32_t>(((int64_t)row * p.ldo + n) * O::ES) : kOOB;
   };
   auto load2 = [&](wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0) {
 #pragma unroll
@@ -476,8 +494,8 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if constexpr (ACCUM)
-        cv[i] = __builtin_bit_cast(f32x4_t, sload16(ro, ooff(i, nb0)));
+      if constexpr (OM::ACCUM)
+        cv[i] = O::load4(ro, ooff(i, nb0));
       else
         cv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -498,7 +516,7 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(tile + (row0 + RPI * i + lr) * LDW + lc);
-      sstore16(ro, ooff(i, nb0), __builtin_bit_cast(uint4, cv[i] + pr));
+      O::store4(ro, ooff(i, nb0), cv[i] + pr);
     }
   };
   // two stages in flight; stages past the end read zeros and store nothing
@@ -524,7 +542,7 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 // gradient kernels).
 // The expand's LDS tiles reuse the shrink's LDS (staging tiles
 // and partial sums) once every wave has read its reduced sums.
-template <class Tag, int NW, int RB, int BMB, int U, int NBU, bool ACCUM, bool EMIT_G>
+template <class Tag, int NW, int RB, int BMB, int U, int NBU, class OM, bool EMIT_G>
 __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
   using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
   constexpr int XB = ExpandRows<NW, BMB, NBU>::FLOATS * 4;
@@ -540,7 +558,7 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
     if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
   __syncthreads();  // every wave has read the partial sums
-  expand_tile_rows<Tag, NW, RB, BMB, NBU, ACCUM>(p, m0, tile, hf, reinterpret_cast<float*>(shr));
+  expand_tile_rows<Tag, NW, RB, BMB, NBU, OM>(p, m0, tile, hf, reinterpret_cast<float*>(shr));
 }
 
 // Shrink only: s*H of each token tile, written as gradient-kernel planes
@@ -580,16 +598,17 @@ __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
 // Wave w keeps the W2 fragments of its NBW column blocks in registers for the
 // whole walk. Per tile: the s*H fragments (the same for every wave), the MFMA
 // products into a shared LDS tile, a barrier, then wave w reads, adds
-// (ACCUM) and writes rows [w*R, (w+1)*R), R = 16*BMB/NW, of the tile over the
+// (when accumulating) and writes rows [w*R, (w+1)*R), R = 16*BMB/NW, of the tile over the
 // band, one whole 1 KB row segment per instruction. The next tile's
 // fragments and output rows load while the current one is computed; two LDS
 // tiles alternate, so one barrier per tile suffices (a wave writes tile k%2
 // only after every wave has passed the barrier of tile k-1, i.e. finished
 // reading tile (k-2)%2). Tiles past the last read zeros and store nothing
 // (empty output descriptor).
-template <class Tag, int NW, int RB, int BMB, int NBW, bool ACCUM>
+template <class Tag, int NW, int RB, int BMB, int NBW, class OM>
 __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
   using E = typename Tag::elem;
+  using O = Out<typename OM::T>;
   constexpr int ES = sizeof(E);
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
@@ -635,13 +654,12 @@ __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
     for (int b = 0; b < BMB; ++b)
 #pragma unroll
       for (int q = 0; q < RB; ++q) hf[b][q] = tok ? p.frag[((m0 / 16 + b) * RB + q) * 64 + lane] : zero4();
-    if constexpr (ACCUM) {
-      const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, tok ? (p.M - m0) * p.ldo * 4 : 0);
+    if constexpr (OM::ACCUM) {
+      const rsrc_t ro = make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * O::ES, tok ? (p.M - m0) * p.ldo * O::ES : 0);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int row = wave * R + RPI * i + lr;
-        cv[i] = __builtin_bit_cast(
-            f32x4_t, sload16(ro, ncol < p.Nout ? static_cast<uint32_t>((row * p.ldo + ncol) * 4) : kOOB));
+        cv[i] = O::load4(ro, ncol < p.Nout ? static_cast<uint32_t>((row * p.ldo + ncol) * O::ES) : kOOB);
       }
     } else {
 #pragma unroll
@@ -661,13 +679,12 @@ __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
       }
     __syncthreads();
     const int64_t m0 = t * (16 * BMB);
-    const rsrc_t ro = make_rsrc(p.out + m0 * p.ldo, t < p.tiles ? (p.M - m0) * p.ldo * 4 : 0);
+    const rsrc_t ro = make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * O::ES, t < p.tiles ? (p.M - m0) * p.ldo * O::ES : 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = wave * R + RPI * i + lr;
       const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(tile + row * LDW + lc);
-      sstore16(ro, ncol < p.Nout ? static_cast<uint32_t>((row * p.ldo + ncol) * 4) : kOOB,
-               __builtin_bit_cast(uint4, cv[i] + pr));
+      O::store4(ro, ncol < p.Nout ? static_cast<uint32_t>((row * p.ldo + ncol) * O::ES) : kOOB, cv[i] + pr);
     }
   };
   uint4 hfA[BMB][RB], hfB[BMB][RB];
@@ -974,10 +991,11 @@ static int bmb_shrink(int64_t M, int rb) {
 }
 
 // forward (expand accumulates into its output) or dX (no output loads);
-// kin = contraction of the shrink, nout = width of the expand.
-static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int64_t nout, int rb) {
+// kin = contraction of the shrink, nout = width of the expand, oes = bytes
+// per output element.
+static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int64_t nout, int rb, int64_t oes) {
   SinglePlan p{};
-  p.fused = kin <= kFusedMaxContraction && M * nout * 4 <= kFusedMaxOutputBytes;
+  p.fused = kin <= kFusedMaxContraction && M * nout * oes <= kFusedMaxOutputBytes;
   p.bmb_shrink = bmb_shrink(M, rb);
   if (p.fused)
     p.bmb = forward ? bmb_expand(M, rb) : ((rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1);
@@ -1010,14 +1028,14 @@ static int64_t tn_chunk_tokens(int64_t M, int64_t N) { return round_up(ceil_div(
 // kernel dispatch
 // ---------------------------------------------------------------------------
 
-template <class Tag, int NW, int RB, int BMB, bool ACCUM, bool EMIT_G>
+template <class Tag, int NW, int RB, int BMB, class OM, bool EMIT_G>
 struct FusedLaunch {
   static void run(FusedArgs a, hipStream_t st) {
     using S = FusedShape<RB, BMB>;
     // kernels that write planes cover every token row below ldg (zeros past M)
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, ACCUM, EMIT_G>), dim3((unsigned)a.tiles), dim3(64 * NW), 0,
+    launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, OM, EMIT_G>), dim3((unsigned)a.tiles), dim3(64 * NW), 0,
            st, a);
   }
 };
@@ -1033,13 +1051,13 @@ struct ShrinkLaunch {
   }
 };
 
-template <class Tag, int RB, int BMB, bool ACCUM>
+template <class Tag, int RB, int BMB, class OM>
 struct ExpandBandLaunch {
   static void run(FusedArgs a, hipStream_t st) {
     constexpr int NW = 4, NBW = 4;  // 256-column bands
     a.tiles = ceil_div(a.M, 16 * BMB);
     const int64_t bands = ceil_div(a.Nout, (int64_t)NW * NBW * 16);
-    launch((expand_band_kernel<Tag, NW, RB, BMB, NBW, ACCUM>),
+    launch((expand_band_kernel<Tag, NW, RB, BMB, NBW, OM>),
            dim3(static_cast<unsigned>(bands), static_cast<unsigned>(band_groups(a.tiles))), dim3(64 * NW), 0, st, a);
   }
 };
@@ -1060,15 +1078,15 @@ static void dispatch8(int rb, int bmb, A&&... args) {
   }
 }
 
-template <class Tag, bool ACCUM, bool EMIT_G>
+template <class Tag, class OM, bool EMIT_G>
 struct FusedNW {
   template <int RB, int BMB>
-  using L = FusedLaunch<Tag, 4, RB, BMB, ACCUM, EMIT_G>;
+  using L = FusedLaunch<Tag, 4, RB, BMB, OM, EMIT_G>;
 };
-template <class Tag, bool ACCUM>
+template <class Tag, class OM>
 struct ExpandBandRB {
   template <int RB, int BMB>
-  using L = ExpandBandLaunch<Tag, RB, BMB, ACCUM>;
+  using L = ExpandBandLaunch<Tag, RB, BMB, OM>;
 };
 
 template <class Tag, bool EMIT_G, bool EMIT_F>
@@ -1090,14 +1108,14 @@ static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
 
 // Shrink Z against W1 and expand into the output as the plan says; with
 // EMIT_G also writes the planes for the gradient kernels.
-template <class Tag, bool ACCUM, bool EMIT_G>
+template <class Tag, class OM, bool EMIT_G>
 static void run_shrink_expand(FusedArgs a, const SinglePlan& pl, int rb, hipStream_t st) {
   if (pl.fused) {
-    dispatch8<FusedNW<Tag, ACCUM, EMIT_G>::template L>(rb, pl.bmb, a, st);
+    dispatch8<FusedNW<Tag, OM, EMIT_G>::template L>(rb, pl.bmb, a, st);
     return;
   }
   launch_shrink<Tag, EMIT_G, true>(a, rb, pl.bmb_shrink, st);
-  dispatch8<ExpandBandRB<Tag, ACCUM>::template L>(rb, pl.bmb, a, st);
+  dispatch8<ExpandBandRB<Tag, OM>::template L>(rb, pl.bmb, a, st);
 }
 
 template <class Tag>
@@ -1154,10 +1172,11 @@ static bool fits32(int64_t bytes) { return bytes >= 0 && bytes <= kMaxBufferByte
 
 // Offsets the shrink/expand kernels form: one 64-token tile of the stream
 // and of the output, and the whole of each weight.
-static bool fused_fits(int64_t ldz, size_t es, int64_t r, int64_t ldw1, int64_t nout, int64_t ldw2, int64_t ldo) {
+static bool fused_fits(int64_t ldz, size_t es, int64_t r, int64_t ldw1, int64_t nout, int64_t ldw2, int64_t ldo,
+                       size_t oes = 4) {
   const int64_t rp = padded_rank(static_cast<int>(r));
   return fits32(64 * ldz * (int64_t)es) && fits32(rp * ldw1 * (int64_t)es) && fits32((nout + 16) * ldw2 * (int64_t)es) &&
-         fits32(64 * ldo * 4);
+         fits32(64 * ldo * (int64_t)oes);
 }
 
 // Workspace pieces of each operation (the same function sizes and carves).
@@ -1313,7 +1332,10 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   if (!valid_dims(x) || !valid_dims(lora_A) || !valid_dims(lora_B) || !valid_dims(res)) return LORA_ERR_SHAPE;
   const int64_t M = x->rows, K = x->cols, r = lora_A->cols, L = lora_B->cols;
   if (lora_A->rows != K || lora_B->rows != r || res->rows != M || res->cols != L) return LORA_ERR_SHAPE;
-  if (!float_dtype_ok(x->dtype) || lora_A->dtype != x->dtype || lora_B->dtype != x->dtype || res->dtype != LORA_F32)
+  // float32 output for any inputs; bfloat16 output (updated in place, one
+  // rounding) for bfloat16 inputs
+  if (!float_dtype_ok(x->dtype) || lora_A->dtype != x->dtype || lora_B->dtype != x->dtype ||
+      !(res->dtype == LORA_F32 || (res->dtype == LORA_BF16 && x->dtype == LORA_BF16)))
     return LORA_ERR_DTYPE;
   if (r < 1 || r > 128) return LORA_ERR_RANK;
   if ((M * K > 0 && !x->ptr) || (K * r > 0 && !lora_A->ptr) || (r * L > 0 && !lora_B->ptr) ||
@@ -1339,7 +1361,8 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   const SingleLayout lay = layout_for(LORA_OP_FWD, M, K, L, static_cast<int>(r), x->dtype);
   // Weights read in place and the fused schedule use no workspace: the
   // caller may then pass none.
-  const SinglePlan plan = plan_single(true, M, K, L, rb);
+  const size_t oes = elem_size(res->dtype);
+  const SinglePlan plan = plan_single(true, M, K, L, rb, static_cast<int64_t>(oes));
   const bool needs_ws = !a_direct || !b_direct || !plan.fused;
   if (needs_ws && (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total()))
     return LORA_ERR_WORKSPACE;
@@ -1348,7 +1371,7 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   void* w2p = cv.take(lay.w2);
   uint4* frag = static_cast<uint4*>(cv.take(lay.frag));
   if (!fused_fits(x->stride_row, es, r, a_direct ? lora_A->stride_col : K, L, b_direct ? lora_B->stride_col : rp,
-                  res->stride_row))
+                  res->stride_row, oes))
     return LORA_ERR_LIMIT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   FusedArgs a{};
@@ -1373,7 +1396,7 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
     a.ldw2 = rp;
   }
   if (njobs > 0) launch_pack(x->dtype, jobs[0], njobs > 1 ? &jobs[1] : nullptr, st);
-  a.out = static_cast<float*>(res->ptr);
+  a.out = res->ptr;
   a.ldo = res->stride_row;
   a.M = M;
   a.Kin = K;
@@ -1382,10 +1405,12 @@ extern "C" int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_ma
   a.rp = static_cast<int>(rp);
   a.scale = scale;
   a.frag = frag;
-  if (x->dtype == LORA_BF16)
-    run_shrink_expand<BF16, true, false>(a, plan, rb, st);
+  if (res->dtype == LORA_BF16)
+    run_shrink_expand<BF16, OutAddBF16, false>(a, plan, rb, st);
+  else if (x->dtype == LORA_BF16)
+    run_shrink_expand<BF16, OutAdd, false>(a, plan, rb, st);
   else
-    run_shrink_expand<F32, true, false>(a, plan, rb, st);
+    run_shrink_expand<F32, OutAdd, false>(a, plan, rb, st);
   return launch_status();
 }
 
@@ -1449,7 +1474,7 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   a.ldw1 = L;
   a.w2 = w2p;
   a.ldw2 = rp;
-  a.out = static_cast<float*>(dx->ptr);
+  a.out = dx->ptr;
   a.ldo = dx->stride_row;
   a.g = gbuf;
   a.ldg = lay.ldg;
@@ -1471,18 +1496,18 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   t.rp = static_cast<int>(rp);
   t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
-  const SinglePlan plan = plan_single(false, M, L, K, rb);
+  const SinglePlan plan = plan_single(false, M, L, K, rb, 4);
   if (xt->dtype == LORA_BF16) {
     if (accumulate)
-      run_shrink_expand<BF16, true, true>(a, plan, rb, st);
+      run_shrink_expand<BF16, OutAdd, true>(a, plan, rb, st);
     else
-      run_shrink_expand<BF16, false, true>(a, plan, rb, st);
+      run_shrink_expand<BF16, OutSet, true>(a, plan, rb, st);
     launch_tn<BF16>(t, rb, st);
   } else {
     if (accumulate)
-      run_shrink_expand<F32, true, true>(a, plan, rb, st);
+      run_shrink_expand<F32, OutAdd, true>(a, plan, rb, st);
     else
-      run_shrink_expand<F32, false, true>(a, plan, rb, st);
+      run_shrink_expand<F32, OutSet, true>(a, plan, rb, st);
     launch_tn<F32>(t, rb, st);
   }
   launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dA->ptr), dA->stride_row,

@@ -71,7 +71,8 @@ def _workspace(op, M, K, L, r, dtype, device, workspace):
 def lora_fwd(x: torch.Tensor, lora_A: torch.Tensor, lora_B: torch.Tensor, res: torch.Tensor, scale: float,
              workspace: torch.Tensor | None = None) -> torch.Tensor:
     """res += scale * (x @ lora_A) @ lora_B, in place; returns res.
-    x: M x K, lora_A: K x r, lora_B: r x L (views with any strides), res: M x L float32."""
+    x: M x K, lora_A: K x r, lora_B: r x L (views with any strides), res: M x L float32, or bfloat16 with
+    bfloat16 inputs (the float32 sum rounded once)."""
     lib = _lib.load()
     M, K = x.shape
     r, L = lora_B.shape

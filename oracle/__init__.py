@@ -31,4 +31,5 @@ from .lora_oracle import (  # noqa: F401
     apply_linear,
     rel_frobenius,
     bf16_bits_to_f64,
+    round_to_bf16,
 )

@@ -36,6 +36,28 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(v) -> np.ndarray:
+    """float64 values -> the nearest bfloat16 values (ties to the even
+    significand), returned as float64. bfloat16 keeps float32's exponent
+    range with 8 significant bits: in the binade [2^e, 2^(e+1)) the values
+    are spaced 2^(e-7), and below 2^-126 (subnormals) 2^-133. A result at or
+    beyond 2^128 is infinite; NaN stays NaN, zeros keep their sign. This is
+    the single rounding a bfloat16 output in place stores: the exact value
+    rounded once."""
+    v = _f64(v)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0.0)
+    a = np.abs(v[fin])
+    _, ex = np.frexp(a)                      # a = m * 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -126)             # binade exponent, floored at the normal range
+    spacing = np.ldexp(1.0, e - 7)
+    n = np.rint(a / spacing)                 # round half to even (a / spacing is exact)
+    r = n * spacing
+    r[r >= 2.0 ** 128] = np.inf
+    out[fin] = np.copysign(r, v[fin])
+    return out
+
+
 def rel_frobenius(got, want) -> float:
     """||got - want||_F / ||want||_F in float64; if ||want||_F == 0 the error is
     0 when got equals want exactly and +inf otherwise."""

@@ -62,3 +62,41 @@ def exactness_bounds(c):
             "dx": 8 + 2 * s * dyb * _max_nnz(c.A, 1),   # also covers dx added twice / onto dx0 in [-8, 8]
             "dA": s * dyb * _max_nnz(c.X, 0),
             "dB": s * h * _max_nnz(c.dY, 0)}
+
+
+def host_bf16(t: torch.Tensor) -> np.ndarray:
+    """A bfloat16 device tensor -> its values as float64 (exact widening)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bf16_spacing(v: np.ndarray) -> np.ndarray:
+    """Spacing of the bfloat16 grid at |v|: 2^(e-7) in the binade [2^e,
+    2^(e+1)), 2^-133 below 2^-126."""
+    a = np.abs(np.asarray(v, np.float64))
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(ex - 1, -126)
+    return np.ldexp(1.0, e - 7)
+
+
+def check_bf16_output(got: np.ndarray, exact: np.ndarray, rounded: np.ndarray, mag: np.ndarray, what: str,
+                      max_mismatch: float = 2.0 ** -7) -> None:
+    """A bfloat16 output updated in place against the exact result. The
+    device adds a float32 sum (rank intermediates as bf16 hi + lo pairs, each
+    within 2^-18 of its value) and rounds once, so every element must be
+    finite and within one bfloat16 spacing of the exact value plus the float32
+    path's own error, bounded here by 2^-16 * mag (mag: the elementwise sum of
+    the magnitudes added, |y0| + |s| |X| |A| |B|); and it must equal the exact
+    value rounded once to nearest even (``rounded``) except for at most a
+    fraction ``max_mismatch``: where the float32 sum lands on the other side
+    of a rounding midpoint than the exact value. Midpoints lie 2^-8 of a
+    value apart and the path's error is within 2^-16 of it, so at most about
+    2 * 2^-16 / 2^-8 = 2^-7 of the elements can cross one (measured: 1.6e-3
+    with the bf16 hi + lo rank intermediate, 1.5e-4 for plain float32)."""
+    got = np.asarray(got, np.float64)
+    exact = np.asarray(exact, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    bound = bf16_spacing(exact) + 2.0 ** -16 * np.asarray(mag, np.float64)
+    err = np.abs(got - exact)
+    assert (err <= bound).all(), (what, float((err / bound).max()))
+    mism = float((got != np.asarray(rounded, np.float64)).mean()) if got.size else 0.0
+    assert mism <= max_mismatch, (what, mism)

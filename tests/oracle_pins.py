@@ -449,6 +449,57 @@ def pin_bf16_closed_form(conv):
         assert v == (-mag if sgn else mag) and math.copysign(1.0, v) == (-1.0 if sgn else 1.0), hex(b)
 
 
+def pin_golden_bf16_round(rnd):
+    """Rounding to bfloat16 on the hand-worked golden cases (ties, just off
+    ties, overflow, subnormals, signed zero, NaN)."""
+    g = _load("bf16_round.json")
+    got = np.asarray(rnd(np.asarray([float(c["value"]) for c in g["cases"]])), np.float64)
+    for c, v in zip(g["cases"], got.tolist()):
+        want = float(c["rounded"])
+        if math.isnan(want):
+            assert math.isnan(v), (c["value"], v)
+        else:
+            assert v == want and math.copysign(1.0, v) == math.copysign(1.0, want), (c["value"], v, want)
+
+
+def pin_bf16_round_grid(rnd, conv):
+    """On the grid of every finite bfloat16 value (consecutive bit patterns
+    widened by the pinned conv): each value rounds to itself, the midpoint of
+    two neighbours to the one whose pattern is even, the float64 numbers next
+    to a midpoint to the nearer neighbour, and past the largest finite value
+    the midpoint to 2^128 and above gives infinity. Both signs."""
+    pos = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)      # +0 .. largest finite
+    vals = np.asarray(conv(pos), np.float64)
+    top = np.append(vals, 2.0 ** 128)                                   # the next grid point
+    even = (np.arange(top.shape[0] - 1) % 2) == 0                        # pattern parity of the lower one
+    lo, hi = top[:-1], top[1:]
+    mid = (lo + hi) / 2.0
+    tie = np.where(even, lo, hi)
+    tie[-1] = np.inf                                                     # 2^128 is infinity
+    hi_or_inf = hi.copy()
+    hi_or_inf[-1] = np.inf
+    for sgn in (1.0, -1.0):
+        _bitwise(np.asarray(rnd(sgn * vals), np.float64), sgn * vals, "grid values round to themselves")
+        _bitwise(np.asarray(rnd(sgn * mid), np.float64), sgn * tie, "midpoints round to the even pattern")
+        _bitwise(np.asarray(rnd(sgn * np.nextafter(mid, np.inf)), np.float64), sgn * hi_or_inf, "above a midpoint")
+        _bitwise(np.asarray(rnd(sgn * np.nextafter(mid, -np.inf)), np.float64), sgn * lo, "below a midpoint")
+
+
+def pin_bf16_round_f32(rnd):
+    """For float32 inputs the rounding is the one float32 -> bfloat16
+    conversion of torch (round to nearest even, a library routine): random
+    float32 bit patterns over the whole range, subnormals and the edge of
+    overflow included."""
+    import torch
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    bits[:4] = [0x7F7FFFFF, 0x7F7F8000, 0x007FFFFF, 0x00008000]          # overflow edge, subnormals
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    _bitwise(np.asarray(rnd(f.astype(np.float64)), np.float64), want, "float32 -> bfloat16 by torch")
+
+
 def pin_golden_apply(apply):
     """apply_linear on the hand-worked multi-adapter example gives its y."""
     g = _load("multi_tiny.json")
@@ -493,7 +544,8 @@ ALL_SINGLE = ("pin_golden_single", "pin_fwd_dense_identity", "pin_fwd_special_ca
 ALL_MULTI = ("pin_golden_multi", "pin_golden_gather", "pin_golden_grouping", "pin_multi_brute_force",
              "pin_multi_reduces_to_single", "pin_gather_is_onehot_shrink", "pin_grouping_is_stable_sort",
              "pin_golden_active", "pin_active_mask", "pin_golden_apply", "pin_apply_linear_brute")
-ALL_FORMAT = ("pin_golden_bf16", "pin_bf16_closed_form")
+ALL_FORMAT = ("pin_golden_bf16", "pin_bf16_closed_form", "pin_golden_bf16_round", "pin_bf16_round_grid",
+              "pin_bf16_round_f32")
 
 
 def run_all(o):
@@ -519,6 +571,9 @@ def run_all(o):
     pin_apply_linear_brute(o.apply_linear)
     pin_golden_bf16(o.bf16_bits_to_f64)
     pin_bf16_closed_form(o.bf16_bits_to_f64)
+    pin_golden_bf16_round(o.round_to_bf16)
+    pin_bf16_round_grid(o.round_to_bf16, o.bf16_bits_to_f64)
+    pin_bf16_round_f32(o.round_to_bf16)
 
 
 def pin_calls(o):
@@ -545,6 +600,9 @@ def pin_calls(o):
         ("apply_linear_brute", lambda: pin_apply_linear_brute(o.apply_linear)),
         ("golden_bf16", lambda: pin_golden_bf16(o.bf16_bits_to_f64)),
         ("bf16_closed_form", lambda: pin_bf16_closed_form(o.bf16_bits_to_f64)),
+        ("golden_bf16_round", lambda: pin_golden_bf16_round(o.round_to_bf16)),
+        ("bf16_round_grid", lambda: pin_bf16_round_grid(o.round_to_bf16, o.bf16_bits_to_f64)),
+        ("bf16_round_f32", lambda: pin_bf16_round_f32(o.round_to_bf16)),
     ]
 
 

@@ -93,7 +93,8 @@ def test_fwd_validation(lib):
     assert fwd(lib, m(M, K, ptr=None), A, B, res) == -1
     assert fwd(lib, x, A, B, m(M, L_ + 4, dtype=0)) == -2                 # res shape
     assert fwd(lib, x, m(K + 8, r, sr=1, sc=K + 8), B, res) == -2          # A rows != K
-    assert fwd(lib, x, A, B, m(M, L_, dtype=1)) == -3                      # res must be fp32
+    assert fwd(lib, m(M, K, dtype=0), m(K, r, 0, sr=1, sc=K), m(r, L_, 0, sr=1, sc=r),
+               m(M, L_, dtype=1)) == -3                                    # bf16 res needs bf16 inputs
     assert fwd(lib, m(M, K, dtype=0), A, B, res) == -3                     # mixed input dtypes
     assert fwd(lib, m(M, K, dtype=7), m(K, r, 7), m(r, L_, 7), res) == -3
     assert fwd(lib, x, m(K, 0, sr=1, sc=K), m(0, L_, sr=1, sc=1), res) == -5
@@ -185,18 +186,20 @@ def test_multi_validation(lib):
     assert expand(sc=0) == -1
     assert expand(slices=(ctypes.c_int64 * 2)(30, 18)) == -2      # widths must be multiples of 4
     assert expand(slices=(ctypes.c_int64 * 2)(32, 20)) == -2      # must sum to y's width
-    assert expand(y_=m(T, 48, dtype=1)) == -3
+    b32 = LoraT3(FAKE, 0, 0, S, 48, r_max, 48 * r_max, r_max, 1)
+    assert expand(b_=b32, y_=m(T, 48, dtype=1)) == -3                 # bf16 y needs bf16 weights
+    assert expand(y_=m(T, 48, dtype=7)) == -3
     assert expand(h_=LoraT3(FAKE, 0, 0, T, 2, r_max, 2 * r_max, 1, 2)) == -4      # rank index not contiguous
 
-    def apply(x_=x, y_=y, h_=h, slices=sl, n=2):
-        return lib.lora_apply_linear(ctypes.byref(x_), ctypes.byref(a), ctypes.byref(b), ctypes.byref(addr),
+    def apply(x_=x, y_=y, h_=h, slices=sl, n=2, b_=b):
+        return lib.lora_apply_linear(ctypes.byref(x_), ctypes.byref(a), ctypes.byref(b_), ctypes.byref(addr),
                                      ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.byref(y_), slices, n, r_max,
                                      ctypes.byref(h_), None)
 
     # the shrink's and the expand's checks both run before any launch
     assert apply(h_=LoraT3(FAKE, 1, 0, T, 2, r_max, 2 * r_max, r_max, 1)) == -3       # h must be float32
     assert apply(slices=(ctypes.c_int64 * 2)(32, 20)) == -2                            # expand: widths vs y
-    assert apply(y_=m(T, 48, dtype=1)) == -3                                           # expand: y float32
+    assert apply(b_=b32, y_=m(T, 48, dtype=1)) == -3                                   # expand: bf16 y, f32 b
     assert apply(x_=m(T, K + 8)) == -2                                                 # shrink: x vs a
 
     ah = LoraT3(FAKE, 1, 0, S, r_max, 1000, r_max * 1000, 1000, 1)

@@ -13,7 +13,7 @@ from tests import oracle_pins as P
 def _ns(**over):
     base = {k: getattr(O, k) for k in ("lora_fwd", "lora_bwd_dx_da", "lora_bwd_db", "group_tokens",
                                        "shrink", "expand_fused", "gather_shrink", "token_ranks",
-                                       "active_mask", "apply_linear", "bf16_bits_to_f64")}
+                                       "active_mask", "apply_linear", "bf16_bits_to_f64", "round_to_bf16")}
     base.update(over)
     return types.SimpleNamespace(**base)
 
@@ -193,6 +193,46 @@ def bf16_drops_sign(bits):
     return np.abs(O.bf16_bits_to_f64(bits))
 
 
+def _round_with(v, rule, floor_exp=True, overflow=True):
+    """round_to_bf16 with one step replaced (for the mutants below)."""
+    v = _f(v)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0.0)
+    a = np.abs(v[fin])
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, -126) if floor_exp else ex - 1
+    spacing = np.ldexp(1.0, e - 7)
+    r = rule(a / spacing) * spacing
+    if overflow:
+        r[r >= 2.0 ** 128] = np.inf
+    else:
+        r = np.minimum(r, 255 * 2.0 ** 120)
+    out[fin] = np.copysign(r, v[fin])
+    return out
+
+
+def round_truncates(v):
+    return _round_with(v, np.floor)
+
+
+def round_ties_away(v):
+    return _round_with(v, lambda n: np.floor(n + 0.5))
+
+
+def round_saturates(v):
+    return _round_with(v, np.rint, overflow=False)
+
+
+def round_no_subnormals(v):
+    return _round_with(v, np.rint, floor_exp=False)
+
+
+def round_twice_via_f32(v):
+    with np.errstate(over="ignore"):
+        f = _f(v).astype(np.float32)
+    return O.round_to_bf16(f.astype(np.float64))
+
+
 MUTANTS = {
     "ranks_slot_le_S": dict(token_ranks=ranks_slot_le_S, active_mask=active_mask_of(ranks_slot_le_S)),
     "ranks_negative_slot_wraps": dict(token_ranks=ranks_negative_slot_wraps,
@@ -206,6 +246,11 @@ MUTANTS = {
     "bf16_shift15": dict(bf16_bits_to_f64=bf16_shift15),
     "bf16_as_fp16": dict(bf16_bits_to_f64=bf16_as_fp16),
     "bf16_drops_sign": dict(bf16_bits_to_f64=bf16_drops_sign),
+    "round_truncates": dict(round_to_bf16=round_truncates),
+    "round_ties_away": dict(round_to_bf16=round_ties_away),
+    "round_saturates": dict(round_to_bf16=round_saturates),
+    "round_no_subnormals": dict(round_to_bf16=round_no_subnormals),
+    "round_twice_via_f32": dict(round_to_bf16=round_twice_via_f32),
     "fwd_no_scale": dict(lora_fwd=fwd_no_scale),
     "fwd_overwrites": dict(lora_fwd=fwd_overwrites),
     "fwd_squared_scale": dict(lora_fwd=fwd_squared_scale),

@@ -89,6 +89,18 @@ def test_bf16_widening_closed_form():
     P.pin_bf16_closed_form(oracle.bf16_bits_to_f64)
 
 
+def test_golden_bf16_rounding():
+    P.pin_golden_bf16_round(oracle.round_to_bf16)
+
+
+def test_bf16_rounding_grid():
+    P.pin_bf16_round_grid(oracle.round_to_bf16, oracle.bf16_bits_to_f64)
+
+
+def test_bf16_rounding_matches_torch_on_float32():
+    P.pin_bf16_round_f32(oracle.round_to_bf16)
+
+
 def test_apply_linear_is_shrink_then_expand():
     import numpy as np
     rng = np.random.default_rng(31)
