@@ -426,13 +426,13 @@ def multi_lora_figures(dev, reps=20, graph=True):
                 seq(0)
             torch.cuda.current_stream(dev).wait_stream(side)
             torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
+            step_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(step_graph):
                 seq(0)
             out[name]["step_eager_us"] = timed(seq, reps, host=True)
-            out[name]["step_graph_us"] = timed(lambda i: graph.replay(), reps, host=True)
+            out[name]["step_graph_us"] = timed(lambda i: step_graph.replay(), reps, host=True)
             out[name]["step_gpu_us"] = timed(seq, reps)
-            del graph
+            del step_graph
         del xs, as_, bs, ys, hs
     # gather_shrink over the 128256-row embedding adapter table (4.2 GB, rank index contiguous)
     T, S, r_max, V = ts5.shape[0], 128, 128, 128256
