@@ -149,6 +149,17 @@ def _kernel_mean(path, counter, pattern, grid=None):
     return statistics.mean(per.values()), len(per)
 
 
+def copy_probe(dev):
+    """Three plain copies of COPY_PROBE_BYTES (the byte counters' calibration)."""
+    import torch
+    src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst_t = torch.empty_like(src_t)
+    for _ in range(3):
+        dst_t.copy_(src_t)
+    torch.cuda.synchronize()
+    del src_t, dst_t
+
+
 def _copy_probe_kib(path, counter):
     """The counter for the 1 GiB copies of --copy-probe: the last three copy
     dispatches of the run (the input clones before them are smaller)."""
@@ -502,6 +513,8 @@ def main():
     if args.multi_only:
         print(json.dumps({"multi_lora": multi_lora_figures(dev, reps=args.multi_reps, graph=not args.no_graph)}),
               flush=True)
+        if args.copy_probe:
+            copy_probe(dev)
         return
     M, K, Lc, r, scale, seed = WORKLOADS[args.workload]
     case = synth.single_adapter(M, K, Lc, r, seed=seed, dtype="bf16", scale=scale, name=args.workload)
@@ -594,12 +607,7 @@ def main():
     dxda_acc_ms = statistics.median(e[0].elapsed_time(e[1]) for e in eva)
 
     if args.copy_probe:
-        src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
-        dst_t = torch.empty_like(src_t)
-        for _ in range(3):
-            dst_t.copy_(src_t)
-        torch.cuda.synchronize()
-        del src_t, dst_t
+        copy_probe(dev)
 
     ab = algorithmic_bytes(M, K, Lc, r)
     step_bytes = ab["fwd"] + ab["dx_da"] + ab["db"]
