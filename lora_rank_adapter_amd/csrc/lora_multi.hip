@@ -22,13 +22,18 @@
 //   slot_shrink_rows_kernel    shrink for many tokens: a 128-token tile x up to
 //                              128 adapter rows per workgroup, x staged once in
 //                              LDS, waves split the rows
-//   slot_expand_owner_kernel   expand for many tokens: a token piece x column
-//                              chunk per workgroup, weights staged once in LDS,
-//                              a piece's chunks grouped per XCD
-//   slot_expand_stream_kernel  expand for few tokens: tile x column chunk,
+//   slot_expand_band_kernel    expand for 512 tokens or more: a token piece x
+//                              256-column band per workgroup, weights in
+//                              registers, h fragments shared through LDS,
+//                              1 KB row segments of y
+//   slot_expand_stream_kernel  expand for fewer tokens: tile x column chunk,
 //                              weights from L2, two stages of outputs in flight
 //   slot_expand_kernel         expand for any layout (unaligned rows, y or b
 //                              beyond 2 GiB)
+//   slot_apply_kernel          apply_linear in one launch (h kept on chip)
+// Every expand forms the update of an output element as an MFMA chain over
+// its rank blocks starting from zero and then adds it to y, so all of them
+// (and both forms of apply_linear) give the same bits.
 //   gather_kernel              exact column gather, one wave per token
 
 #include <mutex>
@@ -954,9 +959,9 @@ struct ExpandArgs {
   const int32_t* ranks;
   int S, r_max, n_slices, total_chunks;
   int64_t chunk_cols;  // columns per chunk (streaming kernel)
-  int64_t y_bytes;     // bytes of y a descriptor may span (streaming and owner kernels)
-  int64_t h_bytes;     // bytes of h a descriptor may span (owner kernel)
-  int n_work;          // owner kernel: pieces x total_chunks work items
+  int64_t y_bytes;     // bytes of y a descriptor may span (streaming and band kernels)
+  int64_t h_bytes;     // bytes of h a descriptor may span (band kernel)
+  int n_work;          // band kernel: pieces x total_chunks work items
   bool h_vec;  // h rows 16-byte aligned
   bool b_vec;  // b rows aligned for 4-element loads
   int64_t slice_off[kMaxSlices];
@@ -1054,10 +1059,11 @@ __global__ __launch_bounds__(256) void slot_expand_kernel(ExpandArgs p) {
 #pragma unroll
     for (int b = 0; b < BMB; ++b) {
       if (16 * b >= tl.len) continue;
+      f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q = 0; q < RBM; ++q)
-        if (q < nq) mma_rank16<Tag>(cv[u][b], wv[u][q], hf[b][q]);
-      if (tok_ok[b] && ncol < width) O::st4(yp + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol, cv[u][b]);
+        if (q < nq) mma_rank16<Tag>(pr, wv[u][q], hf[b][q]);
+      if (tok_ok[b] && ncol < width) O::st4(yp + (int64_t)sh_tok[16 * b + col] * p.ldy + off + ncol, cv[u][b] + pr);
     }
   }
 }
@@ -1112,9 +1118,10 @@ __device__ __forceinline__ void expand_stream_walk(const uint4 (&hf)[BMB][RBM], 
       const int nb = cb + k * kStage + (wave * NBU + u) * 16;
 #pragma unroll
       for (int b = 0; b < BMB; ++b) {
+        f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(cv[u][b], WF::operand(wv[u][q]), hf[b][q]);
-        O::store4(ry, yoff(b, nb + 4 * grp), cv[u][b]);
+        for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(pr, WF::operand(wv[u][q]), hf[b][q]);
+        O::store4(ry, yoff(b, nb + 4 * grp), cv[u][b] + pr);
       }
     }
   };
@@ -1327,44 +1334,52 @@ __global__ __launch_bounds__(64 * NW) void slot_apply_kernel(ShrinkArgs ps, Expa
                                            static_cast<int>(c_begin), static_cast<int>(c_end), rho);
 }
 
-// Column-owner form of expand_fused (same preconditions as the streaming
-// form). A workgroup owns a piece of one slot's grouped tokens (at most
-// kOwnerTokens) and a chunk of kOwnerCols columns of one output slice. It
-// stages that slot's weight columns for the chunk in LDS once (MFMA operand
-// order, ranks >= rho zero), then each wave walks token blocks blk = wave,
-// wave + 4, ... of the piece: the block's h fragments go to registers, and the
-// block's output rows are updated across the chunk, 16 columns per MFMA tile,
-// with the next stage of output tiles loaded while the current one is
-// multiplied. The weights are read once per piece instead of once per token
-// block.
-constexpr int kOwnerTokens = 1024;
-constexpr int kOwnerCols = 128;
-constexpr int kOwnerGroup = 4;  // consecutive work items per XCD group
+// Column-band form of expand_fused (many tokens). A workgroup owns a piece
+// of one slot's grouped tokens (at most kBandTokens) and a band of
+// kBandCols = 256 columns of one output slice; wave w keeps the weight
+// fragments of the band's columns [64w, 64w + 64) in registers. Per 16-token
+// tile: the tile's (sc * h)^T operand fragments are built once per workgroup
+// (wave w loads and converts rank blocks w, w + 4, ... one tile ahead) and
+// shared through LDS; every wave multiplies them with its weight fragments
+// into a shared LDS output tile; after one barrier wave w reads, adds and
+// writes rows [4w, 4w + 4) of the tile over the band, one whole row segment
+// (1 KB in float32) per instruction. Fragment and output tiles are double
+// buffered, so one barrier per tile orders every LDS access: a buffer is
+// written for tile k + 2 only after every wave has passed the barrier of
+// tile k + 1, i.e. finished with tile k. Tiles past the piece load nothing
+// and store nothing (masked offsets), and every wave runs the same number of
+// barriers. Work items (piece, band) go to the XCDs in groups of kBandGroup
+// consecutive items (mostly bands of one piece, which read the same h rows
+// and weights), so those are re-read from one XCD's L2.
+constexpr int kBandCols = 256;
+constexpr int kBandGroup = 4;  // consecutive work items per XCD group
 
 template <class Tag, class YT, int RBM>
-__global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
+__global__ __launch_bounds__(256) void slot_expand_band_kernel(ExpandArgs p) {
+  constexpr int kBandTokens = RBM >= 8 ? 256 : 64;
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
-  using O = Out<YT>;
-  constexpr int NW = 4;
-  constexpr int NCT = kOwnerCols / 16;  // column tiles of the chunk
+  constexpr int64_t YES = sizeof(YT);
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
-  __shared__ wf_t wls[NCT * RBM * 64];
-  __shared__ float obuf[NW][16 * (NCT * 16 + 4)];
+  using O = Out<YT>;
+  constexpr int NW = 4;
+  constexpr int NBW = kBandCols / (16 * NW);  // column blocks per wave
+  constexpr int LDW = kBandCols + 4;          // LDS row pitch (floats)
+  constexpr int R = 16 / NW;                  // rows a wave writes per tile
+  constexpr int TILE = 16 * LDW;
+  constexpr int QW = (RBM + NW - 1) / NW;     // rank blocks a wave converts per tile
+  static_assert(kBandCols == 64 * 4, "one 16-byte piece per lane and row");
+  __shared__ __attribute__((aligned(16))) float lds[2 * TILE];
+  __shared__ uint4 hfs[2][RBM][64];           // fragment tiles
   __shared__ Tile sh_tile;
-  __shared__ int sh_tok[kOwnerTokens];
+  __shared__ int sh_tok[kBandTokens];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
-  // workgroup -> work item (piece, chunk): ids go round-robin over the 8
-  // XCDs; the k-th workgroup of XCD x takes item ((k / G) * 8 + x) * G + k % G,
-  // so G consecutive chunks of a piece (which read the same h rows) share an
-  // XCD's L2. A bijection onto [0, gridDim.x); the grid is padded to a
-  // multiple of 8 G and the items past n_work exit.
-  constexpr int G = kOwnerGroup;
+  constexpr int G = kBandGroup;
   const int kx = static_cast<int>(blockIdx.x >> 3);
   const int item = ((kx / G) * 8 + static_cast<int>(blockIdx.x & 7)) * G + kx % G;
   if (item >= p.n_work) return;
@@ -1374,11 +1389,10 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   while (slice + 1 < p.n_slices && ch >= p.chunk_begin[slice + 1]) ++slice;
   const int64_t width = p.slice_w[slice];
   const int64_t off = p.slice_off[slice];
-  const int c0 = (ch - p.chunk_begin[slice]) * kOwnerCols;
-  const int ce = (c0 + kOwnerCols < width) ? c0 + kOwnerCols : static_cast<int>(width);
+  const int c0 = (ch - p.chunk_begin[slice]) * kBandCols;
 
   if (wave == 0) {
-    const Tile tl = find_tile(pi, kOwnerTokens, p.counts, p.offsets, p.S);
+    const Tile tl = find_tile(pi, kBandTokens, p.counts, p.offsets, p.S);
     if (lane == 0) sh_tile = tl;
   }
   __syncthreads();
@@ -1387,109 +1401,106 @@ __global__ __launch_bounds__(256) void slot_expand_owner_kernel(ExpandArgs p) {
   const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
   const int nq = (rho + 15) / 16;
   if (nq == 0) return;
-  for (int i = threadIdx.x; i < kOwnerTokens; i += 256) sh_tok[i] = (i < tl.len) ? p.sorted[tl.start + i] : 0;
-
-  // weight columns of the chunk, in operand order [column tile][rank block][lane]
-  const rsrc_t rb = make_rsrc(static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0 + off * p.bs1,
-                              width * p.bs1 * ES);
-  const int ldb = static_cast<int>(p.bs1);
-  for (int i = threadIdx.x; i < NCT * nq * 64; i += 256) {
-    const int l = i & 63;
-    const int q = (i >> 6) % nq;
-    const int ct = (i >> 6) / nq;
-    const int n = c0 + ct * 16 + (l & 15);
-    const int j0 = 16 * q + 4 * (l >> 4);
-    wls[(ct * RBM + q) * 64 + l] =
-        WF::bload(rb, n < ce ? static_cast<uint32_t>((n * ldb + j0) * ES) : kOOB, j0, rho);
-  }
+  for (int i = threadIdx.x; i < kBandTokens; i += 256) sh_tok[i] = (i < tl.len) ? p.sorted[tl.start + i] : 0;
   __syncthreads();
 
   const float sc = p.scalings[tl.slot];
+  const rsrc_t rb = make_rsrc(static_cast<const E*>(p.b) + (int64_t)tl.slot * p.bs0 + off * p.bs1,
+                              width * p.bs1 * ES);
+  const int ldb = static_cast<int>(p.bs1);
   const rsrc_t ry = make_rsrc(p.y, p.y_bytes);
-  const int nblk = (tl.len + 15) / 16;
-
-  // Row-linear output: a block's 16 rows x 128 columns are read and written
-  // as row segments of 128 values (512 bytes in float32, 256 in bfloat16;
-  // 32 lanes per row, 2 rows per instruction); the MFMA products reach that
-  // layout through the wave's LDS tile.
-  constexpr int LPR = NCT * 16 / 4;  // lanes per row
-  constexpr int RPI = 64 / LPR;      // rows per instruction
-  constexpr int NI = 16 / RPI;       // row instructions per block
-  constexpr int LDW = NCT * 16 + 4;  // LDS row pitch (floats)
-  float* ob = obuf[wave];
-  const int lr = lane / LPR;
-  const int lc = (lane % LPR) * 4;
-  const bool col_ok = c0 + lc < ce;
   const rsrc_t rh = make_rsrc(p.h, p.h_bytes);
+  const int ntiles = (tl.len + 15) / 16;
+  const int lc = lane * 4;  // this lane's column of the band in the row-linear pass
+  const bool col_ok = c0 + lc < width;
+
   auto walk = [&](auto nq_tag) {
     constexpr int NQ = decltype(nq_tag)::value;
-    struct Blk {
-      f32x4_t cv[NI];   // output rows (row-linear pieces)
-      uint32_t yo[NI];  // their offsets (kOOB when masked)
-      f32x4_t hv[NQ];   // the block's h values (MFMA operand rows)
-    };
-    // a block's output rows and its h values are loaded one block ahead of
-    // their use (h from L2: its latency would otherwise stall every block)
-    auto load_blk = [&](Blk& B, int blk) {
+    wf_t w[NBW][NQ];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int tix = 16 * blk + RPI * i + lr;
-        const bool ok = blk < nblk && tix < tl.len && col_ok;
-        const int t = sh_tok[ok ? tix : 0];
-        B.yo[i] = ok ? static_cast<uint32_t>(((int64_t)t * p.ldy + off + c0 + lc) * O::ES) : kOOB;
-        B.cv[i] = O::load4(ry, B.yo[i]);
-      }
-      const int tix = 16 * blk + col;
-      const bool tok_ok = blk < nblk && tix < tl.len;
-      const int t = sh_tok[tok_ok ? tix : 0];
-      const uint32_t hbase = static_cast<uint32_t>(((int64_t)t * p.hs0 + (int64_t)slice * p.hs1) * 4);
+    for (int u = 0; u < NBW; ++u) {
+      const int n = c0 + (wave * NBW + u) * 16 + col;
+      const bool ok = n < width;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
+        const int j0 = 16 * q + 4 * grp;
+        w[u][q] = WF::bload(rb, ok ? static_cast<uint32_t>((n * ldb + j0) * ES) : kOOB, j0, rho);
+      }
+    }
+    struct Tl {
+      f32x4_t hv[QW];  // this wave's rank blocks q = wave + NW*i of the tile's h
+      f32x4_t cv[R];   // this wave's output rows (row-linear pieces)
+      uint32_t yo[R];  // their offsets (kOOB when masked)
+    };
+    auto load_tile = [&](Tl& T, int t) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int tix = 16 * t + wave * R + i;
+        const bool ok = t < ntiles && tix < tl.len && col_ok;
+        const int tok = sh_tok[ok ? tix : 0];
+        T.yo[i] = ok ? static_cast<uint32_t>(((int64_t)tok * p.ldy + off + c0 + lc) * YES) : kOOB;
+        T.cv[i] = O::load4(ry, T.yo[i]);
+      }
+      const int tix = 16 * t + col;
+      const bool tok_ok = t < ntiles && tix < tl.len;
+      const int tok = sh_tok[tok_ok ? tix : 0];
+      const uint32_t hbase = static_cast<uint32_t>(((int64_t)tok * p.hs0 + (int64_t)slice * p.hs1) * 4);
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const int q = wave + NW * i;
         const int j = 16 * q + 4 * grp;
-        B.hv[q] = __builtin_bit_cast(f32x4_t, bload16(rh, (tok_ok && j < rho) ? hbase + j * 4 : kOOB));
+        T.hv[i] = __builtin_bit_cast(f32x4_t, bload16(rh, (q < NQ && tok_ok && j < rho) ? hbase + j * 4 : kOOB));
       }
     };
-    // a block past the last loads nothing and stores nothing (every offset
-    // is masked), so it needs no branch around it
-    auto comp_blk = [&](Blk& B, int blk) {
-      // an opaque zero keeps the weight reads below inside the block loop
-      // (read from LDS per block instead of held in registers across blocks)
-      int lz;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
-      const wf_t* wl = wls + lz;
+    // this wave's rank blocks of the tile's h -> operand fragments in LDS
+    auto put_frags = [&](const Tl& T, int buf) {
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const int q = wave + NW * i;
+        if (q < NQ) {
+          const int j = 16 * q + 4 * grp;
+          f32x4_t v = T.hv[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (j + e < rho) ? v[e] : 0.f;  // padding may hold NaN
+          v *= sc;
+          hfs[buf][q][lane] = split_frag<Tag>(v);
+        }
+      }
+    };
+    auto comp_tile = [&](const Tl& T, int buf, const Tl& Tn) {
       uint4 hf[NQ];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int j = 16 * q + 4 * grp;
-        f32x4_t v = B.hv[q];
+      for (int q = 0; q < NQ; ++q) hf[q] = hfs[buf][q][lane];
+      float* tile = lds + buf * TILE;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (j + e < rho) ? v[e] : 0.f;  // padding may hold NaN
-        v *= sc;
-        hf[q] = split_frag<Tag>(v);
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+      for (int u = 0; u < NBW; ++u) {
         f32x4_t pr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(pr, WF::operand(wl[(ct * RBM + q) * 64 + lane]), hf[q]);
-        *reinterpret_cast<f32x4_t*>(ob + col * LDW + ct * 16 + 4 * grp) = pr;
+        for (int q = 0; q < NQ; ++q) mma_rank16<Tag>(pr, WF::operand(w[u][q]), hf[q]);
+        // lane holds columns 16u + 4grp .. +3 (of this wave's 64) of token col
+        *reinterpret_cast<f32x4_t*>(tile + col * LDW + (wave * NBW + u) * 16 + 4 * grp) = pr;
       }
+      put_frags(Tn, buf ^ 1);  // the next tile's fragments
+      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(ob + (RPI * i + lr) * LDW + lc);
-        O::store4(ry, B.yo[i], B.cv[i] + pr);
+      for (int i = 0; i < R; ++i) {
+        const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(tile + (wave * R + i) * LDW + lc);
+        O::store4(ry, T.yo[i], T.cv[i] + pr);
       }
     };
-    Blk A, Bb;
-    load_blk(A, wave);
-    for (int blk = wave; blk < nblk; blk += 2 * NW) {
-      load_blk(Bb, blk + NW);  // masked past the last block
+    Tl A, B;
+    load_tile(A, 0);
+    put_frags(A, 0);
+    load_tile(B, 1);
+    __syncthreads();  // tile 0's fragments
+    for (int t = 0; t < ntiles; t += 2) {
+      comp_tile(A, 0, B);
       sched_fence();
-      comp_blk(A, blk);
+      load_tile(A, t + 2);
       sched_fence();
-      load_blk(A, blk + 2 * NW);
+      comp_tile(B, 1, A);
       sched_fence();
-      comp_blk(Bb, blk + NW);
+      load_tile(B, t + 3);
       sched_fence();
     }
   };
@@ -1609,15 +1620,20 @@ static void launch_expand_stream(ExpandArgs a, int rbm, int64_t tiles, hipStream
   }
 }
 
+// Column-band expand: pieces of 256 tokens for slots with more than 64 rank
+// columns (the workgroup's weight fragments span 8 rank blocks), 64 tokens
+// otherwise (kernel-side: kBandTokens).
+static int64_t band_piece_tokens(int rbm) { return rbm >= 8 ? 256 : 64; }
+
 template <class Tag, class YT>
-static void launch_expand_owner(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
+static void launch_expand_band(ExpandArgs a, int rbm, int64_t pieces, hipStream_t st) {
   a.n_work = static_cast<int>(pieces * a.total_chunks);
-  const dim3 grid(static_cast<unsigned>(round_up(a.n_work, 8 * kOwnerGroup)));
+  const dim3 grid(static_cast<unsigned>(round_up(a.n_work, 8 * kBandGroup)));
   switch (rbm) {
-    case 1: launch((slot_expand_owner_kernel<Tag, YT, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: launch((slot_expand_owner_kernel<Tag, YT, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: launch((slot_expand_owner_kernel<Tag, YT, 4>), grid, dim3(256), 0, st, a); break;
-    default: launch((slot_expand_owner_kernel<Tag, YT, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch((slot_expand_band_kernel<Tag, YT, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch((slot_expand_band_kernel<Tag, YT, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch((slot_expand_band_kernel<Tag, YT, 4>), grid, dim3(256), 0, st, a); break;
+    default: launch((slot_expand_band_kernel<Tag, YT, 8>), grid, dim3(256), 0, st, a); break;
   }
 }
 
@@ -1916,7 +1932,7 @@ static int set_chunks(ExpandArgs& p, const int64_t* out_slices, int32_t num_slic
 
 // y, the slice's weight rows of one slot and their row stride fit the
 // streaming expand's 32-bit descriptor offsets, and b rows allow vector loads
-// (streaming and column-owner expands, one-launch apply_linear).
+// (streaming and column-band expands, one-launch apply_linear).
 static bool expand_desc_ok(const ExpandArgs& p, const lora_t3* b, const lora_mat* y, int64_t O) {
   const int64_t es = static_cast<int64_t>(elem_size(b->dtype));
   return p.b_vec && p.y_bytes <= kMaxBufferBytes && O * b->s1 * es <= kMaxBufferBytes &&
@@ -1934,18 +1950,22 @@ extern "C" int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_
   ExpandArgs p = expand_args(h, b, addr, ranks, scalings, y, num_slices, r_max);
   const int rbm = rank_blocks(r_max);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Schedule, from the shapes: the column-owner kernel for 2048 tokens or
-  // more, the streaming kernel for fewer, both when their descriptors can
-  // span y, h and one slot's b with 32-bit offsets and the rows of h and b
-  // allow vector loads; else the general kernel.
+  // Schedule, from the shapes: the column-band kernel for 512 tokens or more,
+  // the streaming kernel for fewer, both when their descriptors can span y,
+  // h and one slot's b with 32-bit offsets and the rows of h and b allow
+  // vector loads; else the general kernel. Measured (bf16, float32 y): the
+  // prefill batch (16731 tokens, 46 slots, r_max 128 / 64 / 32) 268 / 263 /
+  // 247 us band against 285 / 277 / 283 us for a column-owner form with
+  // 1024-token pieces and 128-column chunks; 32 slots, ranks up to 64, at
+  // 512 / 1024 / 1536 / 2048 tokens 15 / 19 / 22 / 28 us band against 17 / 25
+  // / 33 / 37 us for the streaming kernel or the owner form.
   const bool stream_ok = p.h_vec && expand_desc_ok(p, b, y, O);
-  const bool owner_ok = stream_ok && p.h_bytes <= kMaxBufferBytes;
-  if (owner_ok && T >= 2048) {
-    // many tokens: column owners, weights read once per token piece
-    if (set_chunks(p, out_slices, num_slices, kOwnerCols) == 0) return LORA_OK;
-    const int64_t pieces = ceil_div(T, kOwnerTokens) + S;
+  const bool band_ok = stream_ok && p.h_bytes <= kMaxBufferBytes;
+  if (band_ok && T >= 512) {
+    if (set_chunks(p, out_slices, num_slices, kBandCols) == 0) return LORA_OK;
+    const int64_t pieces = ceil_div(T, band_piece_tokens(rbm)) + S;
     with_expand_types(b->dtype, y->dtype, [&](auto tag, auto yt) {
-      launch_expand_owner<decltype(tag), decltype(yt)>(p, rbm, pieces, st);
+      launch_expand_band<decltype(tag), decltype(yt)>(p, rbm, pieces, st);
     });
     return launch_status();
   }

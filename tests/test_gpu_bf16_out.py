@@ -98,7 +98,7 @@ def test_fwd_bf16_output_refuses_f32_inputs():
 # the expand and apply_linear schedule each reaches
 MULTI = {
     "decode-stream": (200, 256, (128, 64, 64), 9, 40, (0, 3, 17, 40), 0.1),       # streaming expand
-    "owner": (0, 256, (256, 64, 64), 12, 64, (8, 16, 32, 64), 0.0),             # column-owner expand (> 2048 tokens)
+    "band": (0, 256, (256, 64, 64), 12, 64, (8, 16, 32, 64), 0.0),              # column-band expand (>= 512 tokens)
     "one-launch-r128": (640, 512, (1536, 256, 256), 16, 128, (0, 8, 100, 128), 0.1),   # one-launch apply_linear
     "one-launch-2048": (1000, 256, (3000, 500, 500), 16, 64, (0, 16, 40, 64), 0.1),   # one launch, 2048-column chunks
 }

@@ -15,7 +15,7 @@ rank 16; 16384 x 4096 x 14336, rank 64):
 These are the defaults being exercised: at 8192 tokens the fused dX kernel
 with 32-token tiles and 32 token chunks in the weight-gradient kernels; at
 16384 x 14336 the split dX schedule (the contraction over 14336 features is
-longer than 8192) and the column-owner expand.
+longer than 8192) and the column-band expand.
 """
 import ctypes
 

@@ -40,9 +40,12 @@ CASES = [
 #             fp32-prefill, decode-1k;
 #           pipelined, 16-token tiles (< 1024 tokens): the others;
 #           general (no buffer descriptors): test_shrink_general_kernel.
-#   expand: column owner (>= 2048 tokens): prefill-long;
-#           streaming (fewer): the others;
+#   expand: column band (>= 512 tokens; 256-token pieces at r_max 128, 64 below): prefill-like,
+#             prefill-long, fp32-prefill, prefill-many-slots, decode-mid, decode-wide, decode-1k, fp32-mid;
+#           streaming (fewer): decode-small, ragged-ranks, fp32, one-token;
 #           general (rows of h not 16-byte aligned): test_expand_general_kernel.
+#   Every expand adds the MFMA chain of an element's rank blocks to y the same way, so all of them,
+#   and both forms of apply_linear, give the same bits.
 #   apply_linear: one launch, 1024-column chunks: decode-mid (rank 128, two slots' ranks
 #             outside [0, r_max]), decode-1k, fp32-mid; 2048-column chunks: decode-wide;
 #           shrink then expand: the others.
@@ -247,10 +250,10 @@ def _expand_exact(m, dtype, h_view=None):
 
 @pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-long"])
 def test_expand_integer_exact(name):
-    """The streaming and column-owner expand kernels (bf16 and f32 weights)
-    bit for bit on integer inputs, NaN in every entry of h they must not read;
-    the owner case (20 requests, about 3000 tokens) has a work-item count that
-    is not a multiple of its XCD grouping."""
+    """The streaming and column-band expand kernels (bf16 and f32 weights,
+    rank blocks 1 to 8) bit for bit on integer inputs, NaN in every entry of h
+    they must not read; the band cases have work-item counts that are not
+    multiples of their XCD grouping."""
     case = next(c for c in CASES if c[0] == name)
     m = _case(*case, int_exact=True)
     note(f"expand integer-exact {name} T={m.T}")
