@@ -66,9 +66,9 @@ ROOFLINE_KERNEL = {
 # accumulating-dX instance is the same template but has another grid) or
 # write only fragments (EMIT_G = false, EMIT_F = true in shrink_kernel).
 ROOFLINE_PATTERN = {
-    "fused_kernel": r"\bfused_kernel<.*, true, false>",
+    "fused_kernel": r"\bfused_kernel<.*, lora::OutAdd, false>",
     "shrink_kernel": r"\bshrink_kernel<.*, false, true>",
-    "expand_band_kernel": r"\bexpand_band_kernel<.*, true>",
+    "expand_band_kernel": r"\bexpand_band_kernel<.*, lora::OutAdd>",
 }
 
 
@@ -204,6 +204,73 @@ def traffic_summary(fetch_csv, write_csv, workload, command):
     print(json.dumps(rec))
 
 
+def multi_traffic_summary(fetch_csv, write_csv, command):
+    """HBM bytes per dispatch of the multi-adapter kernels (a --multi-only run
+    with --copy-probe): FETCH_SIZE and WRITE_SIZE scaled like the forward's,
+    per (kernel, grid size); the prefill shrink and expand (the row-split
+    shrink, the band expand's largest grid) against their algorithmic bytes."""
+    import numpy as np
+
+    import synth
+    f_scale = COPY_PROBE_BYTES / (_copy_probe_kib(fetch_csv, "FETCH_SIZE") * 1024)
+    w_scale = COPY_PROBE_BYTES / (_copy_probe_kib(write_csv, "WRITE_SIZE") * 1024)
+
+    def per_kernel(path, counter):
+        out = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter or "lora::" not in row["Kernel_Name"]:
+                    continue
+                name = re.sub(r"^void ", "", row["Kernel_Name"]).split("(")[0]
+                key = (name, int(row["Grid_Size"]), int(row["Dispatch_Id"]))
+                out[key] = out.get(key, 0.0) + float(row["Counter_Value"])
+        agg = {}
+        for (name, grid, _), v in out.items():
+            agg.setdefault((name, grid), []).append(v)
+        return agg
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    # algorithmic bytes of the prefill calls, as multi_lora_figures counts them
+    ts, rk, _, _ = synth.config5_routing()
+    K, slices, r_max = 8192, (8192, 1024, 1024), 128
+    S, n, SO = rk.shape[0], len(slices), sum(slices)
+    rho = np.clip(rk, 0, r_max)
+    act = (ts >= 0) & (ts < S) & (rho[np.clip(ts, 0, S - 1)] > 0)
+    live = int(rho[np.unique(ts[act])].sum())
+    na, rho_sum = int(act.sum()), int(rho[ts[act]].sum())
+    sh_bytes = na * 2 * K + 2 * K * n * live + 4 * n * rho_sum
+    ex_bytes = 4 * n * rho_sum + 2 * SO * live + 8 * SO * na
+    lines = ["# Multi-adapter kernels: HBM bytes per dispatch (rocprofv3 byte counters)", "",
+             "Commands (from the repository root; one counter per run):", "", "```", command, "```", "",
+             f"FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}: the bytes a plain 1 GiB copy "
+             "moves per counter unit in the same run (`--copy-probe`). The run covers the decode workloads (256 and "
+             "1024 tokens) and the prefill workload (16731 tokens); kernels are told apart by grid size.", "",
+             "| kernel | grid | dispatches | MB fetched | MB written |", "|---|---|---|---|---|"]
+    rows = []
+    for key in sorted(set(fetch) | set(write)):
+        fv, wv = fetch.get(key, [0.0]), write.get(key, [0.0])
+        fmb = statistics.mean(fv) * 1024 * f_scale / 1e6
+        wmb = statistics.mean(wv) * 1024 * w_scale / 1e6
+        rows.append((key, len(fv), fmb, wmb))
+        lines.append(f"| `{key[0]}` | {key[1]} | {len(fv)} | {fmb:.1f} | {wmb:.1f} |")
+
+    def largest(name):
+        cand = [r for r in rows if re.search(name, r[0][0])]
+        return max(cand, key=lambda r: r[0][1]) if cand else None
+    lines += ["", "Prefill (46 slots, r_max 128):"]
+    for label, pat, alg in (("shrink (row-split)", r"slot_shrink_rows_kernel", sh_bytes),
+                            ("expand_fused (column band)", r"slot_expand_band_kernel", ex_bytes)):
+        r = largest(pat)
+        if r:
+            tot = (r[2] + r[3]) * 1e6
+            lines.append(f"- {label}: {r[2]:.1f} MB fetched + {r[3]:.1f} MB written = {tot / 1e6:.1f} MB against "
+                         f"{alg / 1e6:.1f} MB algorithmic ({tot / alg:.3f}x)")
+    path = os.path.join(ROOT, "profiles", "traffic_multi-adapter_decode-T256-T1024_prefill-T16731.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -290,6 +357,25 @@ def stats_summary(csv_path, name, command):
         kname = re.sub(r"\((lora::)?\w+Args\)$", "", kname)
         lines.append(f"| `{kname[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    # rocprofv3's statistics merge a kernel's launches of every shape; the
+    # trace beside them gives the mean per grid size (one kernel serves
+    # several calls, e.g. the column-band expand of the forward and of dX)
+    trace = os.path.join(os.path.dirname(csv_path), "run_kernel_trace.csv")
+    if os.path.exists(trace):
+        per = {}
+        with open(trace, newline="") as f:
+            for r in csv.DictReader(f):
+                if "lora::" not in r["Kernel_Name"]:
+                    continue
+                kname = re.sub(r"^void ", "", r["Kernel_Name"])
+                kname = re.sub(r"\((lora::)?\w+Args\)$", "", kname)
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                per.setdefault((kname, grid), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "Per launch shape (kernel trace in the same directory):", "",
+                  "| kernel | grid (threads) | launches | avg µs | median µs |", "|---|---|---|---|---|"]
+        for (kname, grid), ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| `{kname[:100]}` | {grid} | {len(ds)} | {statistics.mean(ds):.2f} | "
+                         f"{statistics.median(ds):.2f} |")
     path = os.path.join(ROOT, "profiles", f"kernel_stats_{name}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -480,6 +566,8 @@ def main():
     ap.add_argument("--stats-summary", metavar="CSV",
                     help="summarise a rocprofv3 --kernel-trace --stats kernel_stats.csv into profiles/")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--multi-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="byte counters of a --multi-only --copy-probe run -> profiles/")
     ap.add_argument("--command", default="", help="the profiled command, recorded with --traffic-summary")
     args = ap.parse_args()
     if args.traffic_summary:
@@ -490,6 +578,9 @@ def main():
         return
     if args.stats_summary:
         stats_summary(args.stats_summary, args.summary_name, args.command)
+        return
+    if args.multi_traffic_summary:
+        multi_traffic_summary(*args.multi_traffic_summary, args.command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

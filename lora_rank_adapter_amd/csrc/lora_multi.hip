@@ -1352,7 +1352,9 @@ __global__ __launch_bounds__(64 * NW) void slot_apply_kernel(ShrinkArgs ps, Expa
 // consecutive items (mostly bands of one piece, which read the same h rows
 // and weights), so those are re-read from one XCD's L2.
 constexpr int kBandCols = 256;
-constexpr int kBandGroup = 4;  // consecutive work items per XCD group
+// consecutive work items per XCD group (prefill, r_max 128 / 64: groups of
+// 2, 4, 8 -> 267.2 / 258.9, 267.4 / 262.6, 272.3 / 265.5 us)
+constexpr int kBandGroup = 2;
 
 template <class Tag, class YT, int RBM>
 __global__ __launch_bounds__(256) void slot_expand_band_kernel(ExpandArgs p) {
