@@ -202,7 +202,11 @@ int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_mat* lora_B, 
  *   dy      M x L   output gradient; stride_col 1, 16-byte aligned rows, L a
  *                   multiple of 8 (bf16) or 4 (f32).
  *   lora_B  L x r   any strides.
- *   lora_A  r x K   any strides.
+ *   lora_A  r x K   any strides. bf16 weights in the nn.Linear layouts
+ *                   (stride_col 1 for both, rows of a multiple of 8 elements
+ *                   starting 16-byte aligned, r a multiple of 8) are read in
+ *                   place; other layouts are packed into the workspace first
+ *                   (one more kernel launch, same results bit for bit).
  *   dx      M x K   float32 out (overwritten): dx = scale * (dy @ lora_B) @ lora_A.
  *                   stride_col 1, 16-byte aligned rows.
  *   dA      K x r   float32 out (overwritten), any strides:

@@ -108,29 +108,38 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ out,
 }
 
 // out(n, j) = sum over p = 0..P-1 (in that order) of part[p][n][j], j < r.
-// Loads are issued 16 partials at a time; the adds keep the p order.
+// A thread takes V adjacent j of one n (V = 4: 16-byte loads; rp is a
+// multiple of 16 and the partials are 256-byte aligned). Loads are issued 16
+// partials at a time; the adds keep the p order, so both widths give the
+// same bits.
+template <int V>
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int P, int64_t N, int rp, int r,
                                                      float* __restrict__ out, int64_t os_n, int64_t os_j) {
+  typedef float vec_t __attribute__((ext_vector_type(V)));
+  const int per_n = rp / V;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= N * r) return;
-  const int64_t n = idx / r;
-  const int j = static_cast<int>(idx - n * r);
-  const float* src = part + n * rp + j;
-  const int64_t step = N * rp;
+  if (idx >= N * per_n) return;
+  const int64_t n = idx / per_n;
+  const int j = static_cast<int>(idx - n * per_n) * V;
+  if (j >= r) return;  // rank padding
+  const vec_t* src = reinterpret_cast<const vec_t*>(part + n * rp + j);
+  const int64_t step = N * rp / V;
   // the partials are added in chunk order p = 0, 1, ..., P-1; each group of
   // 16 loads is issued before any of it is added (predicated past P), so the
   // loads of a group are in flight together rather than one per add
   // (16384 x 14336 dB, 9 chunks: 13.6 -> 8 us)
-  float s = 0.0f;
+  vec_t s = vec_t(0.f);
   for (int pp = 0; pp < P; pp += 16) {
-    float v[16];
+    vec_t v[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = (pp + e < P) ? src[(pp + e) * step] : 0.0f;
+    for (int e = 0; e < 16; ++e) v[e] = (pp + e < P) ? src[(pp + e) * step] : vec_t(0.f);
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if (pp + e < P) s = (pp + e == 0) ? v[e] : s + v[e];
   }
-  out[n * os_n + j * os_j] = s;
+#pragma unroll
+  for (int e = 0; e < V; ++e)
+    if (j + e < r) out[n * os_n + (j + e) * os_j] = s[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -174,18 +183,27 @@ struct FusedArgs {
 // only: the wave's 16*BMB stream rows and 16*RB weight rows of one stage,
 // rows padded by 16 bytes so that the 16 rows one fragment read touches fall
 // in distinct banks).
-template <class Tag, int NW, int RB, int BMB, int U>
+// WT: W1 is stored feature-major (Kin rows of ldw1 elements, the r ranks of
+// a feature contiguous, as lora_B's L x r weight is for the dY shrink). The
+// stage then holds its 32*U feature rows of rp ranks each (rows padded by 16
+// bytes) after the stream rows, and the weight fragments are read from them
+// with transposed LDS reads.
+template <class Tag, int NW, int RB, int BMB, int U, bool WT = false>
 struct ShrinkStage {
   static constexpr int ES = sizeof(typename Tag::elem);
   static constexpr bool LIN = ES == 2;
+  static_assert(!WT || LIN, "feature-major weights are read as bf16 only");
   static constexpr int SROW = U * 4 * Tag::VEC * ES;  // bytes of a row per stage
   static constexpr int PITCH = SROW + 16;
-  static constexpr int BYTES = LIN ? 16 * (BMB + RB) * PITCH : 0;  // per wave: stream rows, then weight rows
+  static constexpr int WOFF = 16 * BMB * PITCH;       // first weight byte of a wave's tile
+  static constexpr int WPITCH = 32 * RB + 16;         // WT: bytes per staged feature row
+  // per wave: stream rows, then weight rows
+  static constexpr int BYTES = !LIN ? 0 : WT ? WOFF + 32 * U * WPITCH : 16 * (BMB + RB) * PITCH;
   static constexpr int RED = NW * BMB * RB * 64 * 16;
   static constexpr int TOTAL = (NW * BYTES > RED) ? NW * BYTES : RED;
 };
 
-template <class Tag, int NW, int RB, int BMB, int U>
+template <class Tag, int NW, int RB, int BMB, int U, bool WT>
 __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x4_t (*red)[BMB * RB][64],
                                             f32x4_t (&acc)[BMB][RB], uint4 (&hf)[BMB][RB], char* stage) {
   using E = typename Tag::elem;
@@ -200,7 +218,7 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   // segments of the stage: SROW bytes of 64/LPR rows) into this wave's LDS
   // tile and read back in MFMA operand order; in MFMA order every instruction
   // would touch 16 rows x 64 bytes, half of each 128-byte line.
-  using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
+  using SS = ShrinkStage<Tag, NW, RB, BMB, U, WT>;
   constexpr bool LIN = SS::LIN;
   constexpr int LPR = SS::SROW / 16;                 // lanes per row
   constexpr int RPI = LIN ? 64 / LPR : 16;           // rows per row-linear load
@@ -210,7 +228,7 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
                 "stage shape");
 
   const rsrc_t rz = make_rsrc(static_cast<const E*>(p.z) + m0 * p.ldz, (p.M - m0) * p.ldz * ES);
-  const rsrc_t rw1 = make_rsrc(p.w1, (int64_t)p.r * p.ldw1 * ES);
+  const rsrc_t rw1 = make_rsrc(p.w1, (WT ? p.Kin : (int64_t)p.r) * p.ldw1 * ES);
   uint32_t zoff[BMB];
 #pragma unroll
   for (int b = 0; b < BMB; ++b) zoff[b] = static_cast<uint32_t>(((16 * b + col) * p.ldz + grp * VEC) * ES);
@@ -230,7 +248,20 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
   for (int q = 0; q < RB; ++q) woff[q] = static_cast<uint32_t>(((int64_t)(16 * q + col) * p.ldw1 + grp * VEC) * ES);
   // weight rows past r lie outside rw1 and read as zero
   uint32_t lwrow[LIN ? WN : 1];
-  if constexpr (LIN) {
+  // WT: vector i of a lane is 16-byte piece wpc[i] (8 ranks) of the stage's
+  // feature row wl[i] (WN = U * RB vectors cover the 32*U rows of 2*RB
+  // pieces); pieces at ranks >= r read as zero (r is a multiple of 8)
+  int wl[WT ? WN : 1], wpc[WT ? WN : 1];
+  static_assert(!WT || WN == U * RB, "feature-major weight vectors per stage");
+  if constexpr (WT) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int v = i * 64 + lane;
+      wl[i] = v / (2 * RB);
+      wpc[i] = v % (2 * RB);
+      lwrow[i] = (wpc[i] * 8 < p.r) ? static_cast<uint32_t>(((int64_t)wl[i] * p.ldw1 + wpc[i] * 8) * ES) : kOOB;
+    }
+  } else if constexpr (LIN) {
 #pragma unroll
     for (int i = 0; i < WN; ++i)
       lwrow[i] = static_cast<uint32_t>(((int64_t)(i * RPI + lane / LPR) * p.ldw1 + lgrp * VEC) * ES);
@@ -257,8 +288,18 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
       const uint32_t kb = static_cast<uint32_t>(cc * CH * ES);
 #pragma unroll
       for (int i = 0; i < ZN; ++i) zf[0][i] = sload16(rz, kok ? lrow[i] + kb : kOOB);
+      if constexpr (WT) {
+        // the stage's feature rows c*CH .. c*CH + 32*U - 1
+        const uint32_t fb = static_cast<uint32_t>(c * CH * p.ldw1 * ES);
 #pragma unroll
-      for (int i = 0; i < WN; ++i) wf[0][i] = bload16(rw1, kok ? lwrow[i] + kb : kOOB);
+        for (int i = 0; i < WN; ++i) {
+          const bool ok = c + wl[i] / CH < cend && c * CH + wl[i] < p.Kin && lwrow[i] != kOOB;
+          wf[0][i] = bload16(rw1, ok ? lwrow[i] + fb : kOOB);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < WN; ++i) wf[0][i] = bload16(rw1, kok ? lwrow[i] + kb : kOOB);
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -279,15 +320,37 @@ __device__ __forceinline__ void shrink_tile(const FusedArgs& p, int64_t m0, f32x
 #pragma unroll
       for (int i = 0; i < ZN; ++i)
         *reinterpret_cast<uint4*>(stage + (i * RPI + lane / LPR) * SS::PITCH + lpiece * 16) = zf[0][i];
-#pragma unroll
-      for (int i = 0; i < WN; ++i)
-        *reinterpret_cast<uint4*>(stage + (16 * BMB + i * RPI + lane / LPR) * SS::PITCH + lpiece * 16) = wf[0][i];
       uint4 w[U][RB];
+      if constexpr (WT) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int i = 0; i < WN; ++i)
+          *reinterpret_cast<uint4*>(stage + SS::WOFF + wl[i] * SS::WPITCH + wpc[i] * 16) = wf[0][i];
+        // fragment (u, q): lane (col, grp) needs W1[16q + col][32u + 8grp + 0..7],
+        // i.e. rank 16q + col of feature rows 32u + 8grp + 0..7. A transposed
+        // read hands lane i of each 16-lane group element i%4 of the 8-byte
+        // pieces addressed by lanes 4e + i/4 (e < 4): lane c addresses feature
+        // row 32u + 8grp + 4h + c/4, ranks 16q + 4(c%4) .. +3.
 #pragma unroll
-        for (int q = 0; q < RB; ++q)
-          w[u][q] = *reinterpret_cast<const uint4*>(stage + (16 * (BMB + q) + col) * SS::PITCH + (u * 4 + grp) * 16);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            uint2 half[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              half[h] = lds_read_tr16(stage, SS::WOFF + (32 * u + 8 * grp + 4 * h + (col >> 2)) * SS::WPITCH +
+                                                 (16 * q + 4 * (col & 3)) * 2);
+            w[u][q] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < WN; ++i)
+          *reinterpret_cast<uint4*>(stage + (16 * BMB + i * RPI + lane / LPR) * SS::PITCH + lpiece * 16) = wf[0][i];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < RB; ++q)
+            w[u][q] = *reinterpret_cast<const uint4*>(stage + (16 * (BMB + q) + col) * SS::PITCH + (u * 4 + grp) * 16);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -439,9 +502,22 @@ struct ExpandRows {
   static_assert(64 % LPR == 0 && ROWS % RPI == 0 && NI >= 1, "stage shape");
 };
 
-template <class Tag, int NW, int RB, int BMB, int NBU, class OM>
+// WT: W2 is stored rank-major (r rows of ldw2 elements, output columns
+// contiguous, as lora_A's r x K weight is for dX). Each stage's rank rows
+// over the wave's 16*NBU columns are then loaded row-linearly, written to
+// the wave's own LDS tile `wlds` (WRows<NBU>::BYTES per rank block) and read
+// back as fragments with transposed reads; a wave's LDS instructions complete
+// in order, so the tile needs no barrier.
+template <int NBU>
+struct WRows {
+  static constexpr int PITCH = 32 * NBU + 16;  // bytes per staged rank row
+  static constexpr int VPR = 2 * NBU;          // 16-byte vectors per rank row
+  static constexpr int BYTES = 16 * PITCH;     // one rank block (16 rows)
+};
+
+template <class Tag, int NW, int RB, int BMB, int NBU, class OM, bool WT>
 __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0, int64_t rot,
-                                                 const uint4 (&hf)[BMB][RB], float* lds) {
+                                                 const uint4 (&hf)[BMB][RB], float* lds, char* wlds) {
   using E = typename Tag::elem;
   constexpr int ES = sizeof(E);
   using WF = WFrag<Tag>;
@@ -461,7 +537,18 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
   const int row0 = X::SH ? wave * X::ROWS : 0;
   float* tile0 = X::SH ? lds : lds + wave * X::TILE;
   float* tile1 = X::SH ? lds + X::TILE : tile0;
-  const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
+  const rsrc_t rw2 = make_rsrc(p.w2, (WT ? (int64_t)p.r : p.Nout) * p.ldw2 * ES);
+  // WT: raw vector i of a lane is piece wpc[i] (8 columns) of rank row wj[i]
+  // of the stage's 16*NBU columns
+  using WR = WRows<NBU>;
+  constexpr int NV = WT ? 16 * RB * WR::VPR / 64 : 1;
+  static_assert(!WT || (16 * RB * WR::VPR) % 64 == 0, "rank rows per stage");
+  int wj[NV], wpc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    wj[i] = (i * 64 + lane) / WR::VPR;
+    wpc[i] = (i * 64 + lane) % WR::VPR;
+  }
   using O = Out<typename OM::T>;
   const rsrc_t ro = make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * O::ES, (p.M - m0) * p.ldo * O::ES);
   const int64_t nb_end = (p.Nout + 15) / 16;
@@ -484,15 +571,25 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
     const int row = row0 + RPI * i + lr;
     return (nb0 < nb_end && n < p.Nout) ? static_cast<uint32_t>(((int64_t)row * p.ldo + n) * O::ES) : kOOB;
   };
-  auto load2 = [&](wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0) {
+  auto load2 = [&](wf_t (&wv)[NBU][RB], uint4 (&rv)[NV], f32x4_t (&cv)[NI], int64_t nb0) {
+    if constexpr (WT) {
+      const int64_t n0w = (nb0 + wave * NBU) * 16;
 #pragma unroll
-    for (int u = 0; u < NBU; ++u) {
-      const int64_t nb = nb0 + wave * NBU + u;
-      const int64_t nrow = (nb0 < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
+      for (int i = 0; i < NV; ++i) {
+        const int64_t n = n0w + wpc[i] * 8;
+        const bool ok = nb0 < nb_end && wj[i] < p.r && n < p.Nout;
+        rv[i] = bload16(rw2, ok ? static_cast<uint32_t>(((int64_t)wj[i] * p.ldw2 + n) * ES) : kOOB);
+      }
+    } else {
 #pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const int j0 = 16 * q + 4 * grp;
-        wv[u][q] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+      for (int u = 0; u < NBU; ++u) {
+        const int64_t nb = nb0 + wave * NBU + u;
+        const int64_t nrow = (nb0 < nb_end && nb * 16 + col < p.Nout) ? nb * 16 + col : p.Nout;  // p.Nout: outside rw2
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          const int j0 = 16 * q + 4 * grp;
+          wv[u][q] = WF::bload(rw2, static_cast<uint32_t>((nrow * p.ldw2 + j0) * ES), j0, p.r);
+        }
       }
     }
 #pragma unroll
@@ -503,7 +600,22 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
         cv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto comp2 = [&](const wf_t (&wv)[NBU][RB], f32x4_t (&cv)[NI], int64_t nb0, float* tile) {
+  auto comp2 = [&](wf_t (&wv)[NBU][RB], const uint4 (&rv)[NV], f32x4_t (&cv)[NI], int64_t nb0, float* tile) {
+    if constexpr (WT) {
+      // fragment (u, q): lane (col, grp) needs W2[n][16q + 4grp + 0..3] for
+      // column n = 16u + col of the wave's stage columns, i.e. column n of
+      // rank rows 16q + 4grp + 0..3: lane c of a 16-lane group addresses rank
+      // row 16q + 4grp + c/4, columns 16u + 4(c%4) .. +3 (the transposed read
+      // hands lane i element i%4 of the pieces of lanes 4e + i/4, e < 4)
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        *reinterpret_cast<uint4*>(wlds + wj[i] * WR::PITCH + wpc[i] * 16) = rv[i];
+#pragma unroll
+      for (int u = 0; u < NBU; ++u)
+#pragma unroll
+        for (int q = 0; q < RB; ++q)
+          wv[u][q] = lds_read_tr16(wlds, (16 * q + 4 * grp + (col >> 2)) * WR::PITCH + (16 * u + 4 * (col & 3)) * 2);
+    }
 #pragma unroll
     for (int u = 0; u < NBU; ++u) {
 #pragma unroll
@@ -523,18 +635,20 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
     }
   };
   // two stages in flight; stages past the end read zeros and store nothing
+  // (WT: the raw rank rows are in flight, the fragments are formed in comp2)
   wf_t wvA[NBU][RB], wvB[NBU][RB];
+  uint4 rvA[NV], rvB[NV];
   f32x4_t cvA[NI], cvB[NI];
   if (nst > 0) {
-    load2(wvA, cvA, stage_nb(0));
+    load2(wvA, rvA, cvA, stage_nb(0));
     for (int k = 0; k < nst; k += 2) {
-      load2(wvB, cvB, stage_nb(k + 1));
+      load2(wvB, rvB, cvB, stage_nb(k + 1));
       sched_fence();
-      comp2(wvA, cvA, stage_nb(k), tile0);
+      comp2(wvA, rvA, cvA, stage_nb(k), tile0);
       sched_fence();
-      load2(wvA, cvA, stage_nb(k + 2));
+      load2(wvA, rvA, cvA, stage_nb(k + 2));
       sched_fence();
-      comp2(wvB, cvB, stage_nb(k + 1), tile1);
+      comp2(wvB, rvB, cvB, stage_nb(k + 1), tile1);
       sched_fence();
     }
   }
@@ -545,36 +659,40 @@ __device__ __forceinline__ void expand_tile_rows(const FusedArgs& p, int64_t m0,
 // gradient kernels).
 // The expand's LDS tiles reuse the shrink's LDS (staging tiles
 // and partial sums) once every wave has read its reduced sums.
-template <class Tag, int NW, int RB, int BMB, int U, int NBU, class OM, bool EMIT_G>
+// WT: both weights in the transposed storage (W1 feature-major, W2
+// rank-major); the expand's per-wave weight tiles follow its output tiles.
+template <class Tag, int NW, int RB, int BMB, int U, int NBU, class OM, bool EMIT_G, bool WT>
 __global__ __launch_bounds__(64 * NW) void fused_kernel(FusedArgs p) {
-  using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
+  using SS = ShrinkStage<Tag, NW, RB, BMB, U, WT>;
   constexpr int XB = ExpandRows<NW, BMB, NBU>::FLOATS * 4;
-  constexpr int LDS = SS::TOTAL > XB ? SS::TOTAL : XB;
+  constexpr int XW = WT ? NW * RB * WRows<NBU>::BYTES : 0;
+  constexpr int LDS = SS::TOTAL > XB + XW ? SS::TOTAL : XB + XW;
   __shared__ __attribute__((aligned(16))) char shr[LDS];
   auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   const int64_t tile = blockIdx.x;
   const int64_t m0 = tile * (16 * BMB);
   f32x4_t acc[BMB][RB];
   uint4 hf[BMB][RB];
-  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf, shr + wave_id() * SS::BYTES);
+  shrink_tile<Tag, NW, RB, BMB, U, WT>(p, m0, red, acc, hf, shr + wave_id() * SS::BYTES);
   if constexpr (EMIT_G) {
     if (wave_id() == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
   }
   __syncthreads();  // every wave has read the partial sums
-  expand_tile_rows<Tag, NW, RB, BMB, NBU, OM>(p, m0, tile, hf, reinterpret_cast<float*>(shr));
+  expand_tile_rows<Tag, NW, RB, BMB, NBU, OM, WT>(p, m0, tile, hf, reinterpret_cast<float*>(shr),
+                                                  shr + XB + wave_id() * RB * WRows<NBU>::BYTES);
 }
 
 // Shrink only: s*H of each token tile, written as gradient-kernel planes
 // (EMIT_G) and/or expand fragments (EMIT_F).
-template <class Tag, int NW, int RB, int BMB, int U, bool EMIT_G, bool EMIT_F>
+template <class Tag, int NW, int RB, int BMB, int U, bool EMIT_G, bool EMIT_F, bool WT>
 __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
-  using SS = ShrinkStage<Tag, NW, RB, BMB, U>;
+  using SS = ShrinkStage<Tag, NW, RB, BMB, U, WT>;
   __shared__ __attribute__((aligned(16))) char shr[SS::TOTAL];
   auto red = reinterpret_cast<f32x4_t(*)[BMB * RB][64]>(shr);
   const int64_t m0 = (int64_t)blockIdx.x * (16 * BMB);
   f32x4_t acc[BMB][RB];
   uint4 hf[BMB][RB];
-  shrink_tile<Tag, NW, RB, BMB, U>(p, m0, red, acc, hf, shr + wave_id() * SS::BYTES);
+  shrink_tile<Tag, NW, RB, BMB, U, WT>(p, m0, red, acc, hf, shr + wave_id() * SS::BYTES);
   const int wave = wave_id();
   if constexpr (EMIT_G) {
     if (wave == 0) emit_planes<Tag, RB, BMB>(p, m0, acc, hf);
@@ -608,7 +726,10 @@ __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
 // only after every wave has passed the barrier of tile k-1, i.e. finished
 // reading tile (k-2)%2). Tiles past the last read zeros and store nothing
 // (empty output descriptor).
-template <class Tag, int NW, int RB, int BMB, int NBW, class OM>
+// WT: W2 stored rank-major (r rows of ldw2 elements); each wave stages the
+// rank rows of its 16*NBW columns one rank block at a time in its own LDS
+// tile and reads its fragments back with transposed reads, before the walk.
+template <class Tag, int NW, int RB, int BMB, int NBW, class OM, bool WT>
 __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
   using E = typename Tag::elem;
   using O = Out<typename OM::T>;
@@ -635,7 +756,40 @@ __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
 
   // this wave's W2 fragments (rows past Nout and ranks past r read as zero)
   wf_t w[NBW][RB];
-  {
+  if constexpr (WT) {
+    using WR = WRows<NBW>;
+    constexpr int NV = 16 * WR::VPR / 64;  // vectors per lane and rank block
+    static_assert(NV >= 1 && (16 * WR::VPR) % 64 == 0 && NW * WR::BYTES <= 2 * TILE * 4, "band weight tile");
+    char* wl = reinterpret_cast<char*>(lds) + wave * WR::BYTES;
+    const rsrc_t rw2 = make_rsrc(p.w2, (int64_t)p.r * p.ldw2 * ES);
+    uint4 rv[RB][NV];
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int v = i * 64 + lane;
+        const int j = 16 * q + v / WR::VPR;
+        const int64_t n = nb0 * 16 + (v % WR::VPR) * 8;
+        rv[q][i] = bload16(rw2, (j < p.r && n < p.Nout) ? static_cast<uint32_t>(((int64_t)j * p.ldw2 + n) * ES) : kOOB);
+      }
+    // rank block q: rows 16q .. 16q+15 into the wave's tile, then fragment u
+    // (lane (col, grp): column 16u + col of rank rows 16q + 4grp + 0..3) by a
+    // transposed read (lane c addresses row 4grp + c/4, columns 16u + 4(c%4)).
+    // The next block's writes follow this block's reads in the wave's LDS
+    // order.
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int v = i * 64 + lane;
+        *reinterpret_cast<uint4*>(wl + (v / WR::VPR) * WR::PITCH + (v % WR::VPR) * 16) = rv[q][i];
+      }
+#pragma unroll
+      for (int u = 0; u < NBW; ++u)
+        w[u][q] = lds_read_tr16(wl, (4 * grp + (col >> 2)) * WR::PITCH + (16 * u + 4 * (col & 3)) * 2);
+    }
+    __syncthreads();  // the tiles below reuse this LDS
+  } else {
     const rsrc_t rw2 = make_rsrc(p.w2, p.Nout * p.ldw2 * ES);
 #pragma unroll
     for (int u = 0; u < NBW; ++u) {
@@ -1047,36 +1201,36 @@ static int64_t tn_chunk_tokens(int64_t M, int64_t N) { return round_up(ceil_div(
 // kernel dispatch
 // ---------------------------------------------------------------------------
 
-template <class Tag, int NW, int RB, int BMB, class OM, bool EMIT_G>
+template <class Tag, int NW, int RB, int BMB, class OM, bool EMIT_G, bool WT>
 struct FusedLaunch {
   static void run(FusedArgs a, hipStream_t st) {
     using S = FusedShape<RB, BMB>;
     // kernels that write planes cover every token row below ldg (zeros past M)
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, OM, EMIT_G>), dim3((unsigned)a.tiles), dim3(64 * NW), 0,
-           st, a);
+    launch((fused_kernel<Tag, NW, RB, BMB, S::U, S::NBU, OM, EMIT_G, WT>), dim3((unsigned)a.tiles), dim3(64 * NW),
+           0, st, a);
   }
 };
 
-template <class Tag, int NW, int RB, int BMB, bool EMIT_G, bool EMIT_F>
+template <class Tag, int NW, int RB, int BMB, bool EMIT_G, bool EMIT_F, bool WT>
 struct ShrinkLaunch {
   static void run(FusedArgs a, hipStream_t st) {
     using S = FusedShape<RB, BMB>;
     const int64_t rows = (EMIT_G && a.ldg > a.M) ? a.ldg : a.M;
     a.tiles = ceil_div(rows, 16 * BMB);
-    launch((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F>), dim3((unsigned)a.tiles), dim3(64 * NW), 0, st,
-           a);
+    launch((shrink_kernel<Tag, NW, RB, BMB, S::U, EMIT_G, EMIT_F, WT>), dim3((unsigned)a.tiles), dim3(64 * NW), 0,
+           st, a);
   }
 };
 
-template <class Tag, int RB, int BMB, class OM>
+template <class Tag, int RB, int BMB, class OM, bool WT>
 struct ExpandBandLaunch {
   static void run(FusedArgs a, hipStream_t st) {
     constexpr int NW = 4, NBW = 4;  // 256-column bands
     a.tiles = ceil_div(a.M, 16 * BMB);
     const int64_t bands = ceil_div(a.Nout, (int64_t)NW * NBW * 16);
-    launch((expand_band_kernel<Tag, NW, RB, BMB, NBW, OM>),
+    launch((expand_band_kernel<Tag, NW, RB, BMB, NBW, OM, WT>),
            dim3(static_cast<unsigned>(bands), static_cast<unsigned>(band_groups(a.tiles))), dim3(64 * NW), 0, st, a);
   }
 };
@@ -1097,44 +1251,45 @@ static void dispatch8(int rb, int bmb, A&&... args) {
   }
 }
 
-template <class Tag, class OM, bool EMIT_G>
+template <class Tag, class OM, bool EMIT_G, bool WT>
 struct FusedNW {
   template <int RB, int BMB>
-  using L = FusedLaunch<Tag, 4, RB, BMB, OM, EMIT_G>;
+  using L = FusedLaunch<Tag, 4, RB, BMB, OM, EMIT_G, WT>;
 };
-template <class Tag, class OM>
+template <class Tag, class OM, bool WT>
 struct ExpandBandRB {
   template <int RB, int BMB>
-  using L = ExpandBandLaunch<Tag, RB, BMB, OM>;
+  using L = ExpandBandLaunch<Tag, RB, BMB, OM, WT>;
 };
 
-template <class Tag, bool EMIT_G, bool EMIT_F>
+template <class Tag, bool EMIT_G, bool EMIT_F, bool WT = false>
 static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
   // the pairs bmb_shrink() returns; 8 waves while the cross-wave partial-sum
   // buffer (NW * rb * bmb KB) stays <= 32 KB, else 4
   switch (rb * 10 + bmb) {
-    case 11: ShrinkLaunch<Tag, 8, 1, 1, EMIT_G, EMIT_F>::run(a, st); break;
-    case 21: ShrinkLaunch<Tag, 8, 2, 1, EMIT_G, EMIT_F>::run(a, st); break;
-    case 22: ShrinkLaunch<Tag, 8, 2, 2, EMIT_G, EMIT_F>::run(a, st); break;
-    case 24: ShrinkLaunch<Tag, 4, 2, 4, EMIT_G, EMIT_F>::run(a, st); break;
-    case 41: ShrinkLaunch<Tag, 8, 4, 1, EMIT_G, EMIT_F>::run(a, st); break;
-    case 42: ShrinkLaunch<Tag, 4, 4, 2, EMIT_G, EMIT_F>::run(a, st); break;
-    case 44: ShrinkLaunch<Tag, 4, 4, 4, EMIT_G, EMIT_F>::run(a, st); break;
-    case 81: ShrinkLaunch<Tag, 4, 8, 1, EMIT_G, EMIT_F>::run(a, st); break;
-    default: ShrinkLaunch<Tag, 4, 8, 2, EMIT_G, EMIT_F>::run(a, st); break;  // rb 8, bmb 2
+    case 11: ShrinkLaunch<Tag, 8, 1, 1, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 21: ShrinkLaunch<Tag, 8, 2, 1, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 22: ShrinkLaunch<Tag, 8, 2, 2, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 24: ShrinkLaunch<Tag, 4, 2, 4, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 41: ShrinkLaunch<Tag, 8, 4, 1, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 42: ShrinkLaunch<Tag, 4, 4, 2, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 44: ShrinkLaunch<Tag, 4, 4, 4, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 81: ShrinkLaunch<Tag, 4, 8, 1, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    default: ShrinkLaunch<Tag, 4, 8, 2, EMIT_G, EMIT_F, WT>::run(a, st); break;  // rb 8, bmb 2
   }
 }
 
 // Shrink Z against W1 and expand into the output as the plan says; with
-// EMIT_G also writes the planes for the gradient kernels.
-template <class Tag, class OM, bool EMIT_G>
+// EMIT_G also writes the planes for the gradient kernels; WT: weights in the
+// transposed storage (dX from nn.Linear-layout bf16 weights).
+template <class Tag, class OM, bool EMIT_G, bool WT = false>
 static void run_shrink_expand(FusedArgs a, const SinglePlan& pl, int rb, hipStream_t st) {
   if (pl.fused) {
-    dispatch8<FusedNW<Tag, OM, EMIT_G>::template L>(rb, pl.bmb, a, st);
+    dispatch8<FusedNW<Tag, OM, EMIT_G, WT>::template L>(rb, pl.bmb, a, st);
     return;
   }
-  launch_shrink<Tag, EMIT_G, true>(a, rb, pl.bmb_shrink, st);
-  dispatch8<ExpandBandRB<Tag, OM>::template L>(rb, pl.bmb, a, st);
+  launch_shrink<Tag, EMIT_G, true, WT>(a, rb, pl.bmb_shrink, st);
+  dispatch8<ExpandBandRB<Tag, OM, WT>::template L>(rb, pl.bmb, a, st);
 }
 
 template <class Tag>
@@ -1182,10 +1337,17 @@ static void launch_fill_zero(const lora_mat* m, hipStream_t st) {
 
 static void launch_reduce(const float* part, int P, int64_t N, int rp, int r, float* out, int64_t os_n, int64_t os_j,
                           hipStream_t st) {
-  const int64_t total = N * r;
-  if (total <= 0) return;
-  launch(reduce_kernel, dim3(static_cast<unsigned>(ceil_div(total, 256))), dim3(256), 0, st, part, P, N,
-                     rp, r, out, os_n, os_j);
+  if (N * r <= 0) return;
+  // 16-byte loads while that keeps >= 256 workgroups (the 16384 x 14336 dB
+  // call: 146 -> 140 us); fewer, longer threads measured slower at 8192 x
+  // 4096, rank 16 (64 workgroups: +1.5 us per call)
+  const int64_t wide = N * (rp / 4);
+  if (wide >= 256 * 256)
+    launch(reduce_kernel<4>, dim3(static_cast<unsigned>(ceil_div(wide, 256))), dim3(256), 0, st, part, P, N, rp, r,
+           out, os_n, os_j);
+  else
+    launch(reduce_kernel<1>, dim3(static_cast<unsigned>(ceil_div(N * rp, 256))), dim3(256), 0, st, part, P, N, rp,
+           r, out, os_n, os_j);
 }
 
 // Buffer descriptors address with 32-bit byte offsets: every range one
@@ -1484,18 +1646,33 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   if (!fused_fits(dy->stride_row, es, r, L, K, rp, dx->stride_row) || !fits32(chunk * xt->stride_col * (int64_t)es) ||
       !fits32((int64_t)lay.g))
     return LORA_ERR_LIMIT;
-  // W1 = B^T (r x L, L contiguous); W2 = A^T (K x r, r contiguous).
-  const PackJob jb = pack_job(lora_B->ptr, lora_B->stride_col, lora_B->stride_row, r, L, w1p, rp, L, L);
-  const PackJob ja = pack_job(lora_A->ptr, lora_A->stride_col, lora_A->stride_row, K, r, w2p, K, rp, rp);
-  launch_pack(xt->dtype, jb, &ja, st);
-
+  // The kernels take W1 = B^T (r rows over the L outputs) and W2 = A^T (K rows
+  // over the r ranks). bf16 weights in the nn.Linear layouts (lora_B L x r and
+  // lora_A r x K, rows contiguous, 16-byte aligned rows, r a multiple of 8)
+  // are read in place in that transposed storage; any other layout is first
+  // packed into the workspace.
+  const bool in_place = xt->dtype == LORA_BF16 && r % 8 == 0 && lora_B->stride_col == 1 &&
+                        lora_B->stride_row >= r && lora_B->stride_row % 8 == 0 && aligned(lora_B->ptr, 16) &&
+                        lora_A->stride_col == 1 && lora_A->stride_row >= K && lora_A->stride_row % 8 == 0 &&
+                        aligned(lora_A->ptr, 16) && fits32(L * lora_B->stride_row * (int64_t)es) &&
+                        fits32(r * lora_A->stride_row * (int64_t)es);
   FusedArgs a{};
+  if (in_place) {
+    a.w1 = lora_B->ptr;
+    a.ldw1 = lora_B->stride_row;
+    a.w2 = lora_A->ptr;
+    a.ldw2 = lora_A->stride_row;
+  } else {
+    const PackJob jb = pack_job(lora_B->ptr, lora_B->stride_col, lora_B->stride_row, r, L, w1p, rp, L, L);
+    const PackJob ja = pack_job(lora_A->ptr, lora_A->stride_col, lora_A->stride_row, K, r, w2p, K, rp, rp);
+    launch_pack(xt->dtype, jb, &ja, st);
+    a.w1 = w1p;
+    a.ldw1 = L;
+    a.w2 = w2p;
+    a.ldw2 = rp;
+  }
   a.z = dy->ptr;
   a.ldz = dy->stride_row;
-  a.w1 = w1p;
-  a.ldw1 = L;
-  a.w2 = w2p;
-  a.ldw2 = rp;
   a.out = dx->ptr;
   a.ldo = dx->stride_row;
   a.g = gbuf;
@@ -1520,10 +1697,17 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   const int P = static_cast<int>(ceil_div(M, t.chunk));
   const SinglePlan plan = plan_single(false, M, L, K, rb, 4);
   if (xt->dtype == LORA_BF16) {
-    if (accumulate)
-      run_shrink_expand<BF16, OutAdd, true>(a, plan, rb, st);
-    else
-      run_shrink_expand<BF16, OutSet, true>(a, plan, rb, st);
+    if (in_place) {
+      if (accumulate)
+        run_shrink_expand<BF16, OutAdd, true, true>(a, plan, rb, st);
+      else
+        run_shrink_expand<BF16, OutSet, true, true>(a, plan, rb, st);
+    } else {
+      if (accumulate)
+        run_shrink_expand<BF16, OutAdd, true>(a, plan, rb, st);
+      else
+        run_shrink_expand<BF16, OutSet, true>(a, plan, rb, st);
+    }
     launch_tn<BF16>(t, rb, st);
   } else {
     if (accumulate)

@@ -125,6 +125,62 @@ def test_weight_layouts_and_output_strides():
     assert oracle.rel_frobenius(host(y1) - c.Y0, want - c.Y0) <= 2e-3
 
 
+# (M, K, L, r): the fused dX kernel at rank 16 and 64, the split schedule's
+# shrink + column-band expand at rank 64 and 128
+IN_PLACE_CASES = [(200, 264, 1000, 16), (130, 512, 296, 64), (2100, 264, 8200, 64), (700, 1032, 8200, 128)]
+
+
+@pytest.mark.parametrize("case", IN_PLACE_CASES, ids=lambda c: "M{}-K{}-L{}-r{}".format(*c))
+def test_bwd_weights_read_in_place(case):
+    """bf16 weights in the nn.Linear layouts are read in place by the dX/dA
+    call (lora_B's feature rows and lora_A's rank rows staged and read
+    transposed); weights in padded rows, and weights whose rows do not start
+    16-byte aligned (packed by the library instead), give the same bits."""
+    M, K, L_, r = case
+    note(f"weights in place {case}")
+    c = synth.single_adapter(M, K, L_, r, seed=70 + r, dtype="bf16", scale=0.5)
+    X, A_w, B_w, dY = _upload(c, "bf16")
+    dx1, dA1 = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, 0.5)
+    # rows padded to r + 8 and K + 8 elements (in place, other strides)
+    B_pad = torch.zeros((L_, r + 8), dtype=B_w.dtype, device=X.device)
+    B_pad[:, :r] = B_w
+    A_pad = torch.zeros((r, K + 8), dtype=A_w.dtype, device=X.device)
+    A_pad[:, :K] = A_w
+    dx2, dA2 = L.lora_bwd_dx_da(X.t(), dY, B_pad[:, :r], A_pad[:, :K], 0.5)
+    # rows starting 2 bytes past a 16-byte boundary: packed
+    B_off = torch.zeros((L_ * r + 1,), dtype=B_w.dtype, device=X.device)
+    B_off[1:] = B_w.reshape(-1)
+    dx3, dA3 = L.lora_bwd_dx_da(X.t(), dY, B_off[1:].view(L_, r), A_w, 0.5)
+    torch.cuda.synchronize()
+    for got in ((dx2, dA2), (dx3, dA3)):
+        assert same_bits(host(got[0]), host(dx1)), "dX"
+        assert same_bits(host(got[1]), host(dA1)), "dA"
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, 0.5)
+    assert oracle.rel_frobenius(host(dx1), odx) <= 2e-3
+    assert oracle.rel_frobenius(host(dA1), odA) <= 2e-3
+
+
+def test_bwd_in_place_weights_launch_no_pack():
+    """The dX/dA call on nn.Linear-layout bf16 weights launches three kernels
+    (fused shrink-expand, weight-gradient partials, reduce); weights that
+    must be packed first add the pack launch."""
+    note("in-place weights: launch count")
+    M, K, L_, r = 600, 1024, 768, 16
+    c = synth.single_adapter(M, K, L_, r, seed=62, dtype="bf16", scale=1.0)
+    X, A_w, B_w, dY = _upload(c, "bf16")
+    B_off = torch.zeros((L_ * r + 1,), dtype=B_w.dtype, device=X.device)
+    B_off[1:] = B_w.reshape(-1)
+    counts = []
+    for b in (B_w, B_off[1:].view(L_, r)):
+        torch.cuda.synchronize()
+        L.lora_timing_begin()
+        L.lora_bwd_dx_da(X.t(), dY, b, A_w, 1.0)
+        L.lora_timing_pause()
+        counts.append(L.lora_timing_read()[1])
+    torch.cuda.synchronize()
+    assert counts == [3, 4], counts
+
+
 def test_deterministic_reruns():
     note("determinism")
     c = synth.single_adapter(333, 1024, 640, 48, seed=51, dtype="bf16", scale=0.5)
