@@ -176,7 +176,7 @@ size_t lora_workspace_bytes(int op, int64_t M, int64_t K, int64_t L, int32_t r, 
  *   The library picks one of two schedules from the shapes: fused (one
  *   workgroup per token tile computes the rank-r intermediate and expands it,
  *   the intermediate never leaves registers and LDS) for K <= 8192 and an
- *   output of at most 256 MB; else split (a shrink kernel writes the
+ *   output below 256 MB; else split (a shrink kernel writes the
  *   intermediate to the workspace as MFMA operand fragments, 1 KB per 16
  *   tokens and 16 ranks, and each workgroup of the expand owns a band of 256
  *   output columns over a few token tiles). Both give the same results up to

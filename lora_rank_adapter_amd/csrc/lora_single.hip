@@ -729,29 +729,39 @@ __global__ __launch_bounds__(64 * NW) void shrink_kernel(FusedArgs p) {
 // WT: W2 stored rank-major (r rows of ldw2 elements); each wave stages the
 // rank rows of its 16*NBW columns one rank block at a time in its own LDS
 // tile and reads its fragments back with transposed reads, before the walk.
+template <int NW, int BMB, int NBW>
+struct BandShape {
+  static constexpr int BW = NW * NBW * 16;     // band columns
+  static constexpr int LDW = BW + 4;           // LDS row pitch (floats)
+  static constexpr int TILE = 16 * BMB * LDW;  // floats per LDS tile
+  static constexpr int LDS_BYTES = 2 * TILE * 4;
+};
+
+// Band `band`, token group `group` of `ngroups` (the workgroup's coordinates).
 template <class Tag, int NW, int RB, int BMB, int NBW, class OM, bool WT>
-__global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
+__device__ __forceinline__ void expand_band_body(const FusedArgs& p, int64_t band, int64_t group, int64_t ngroups,
+                                                 float* lds) {
   using E = typename Tag::elem;
   using O = Out<typename OM::T>;
   constexpr int ES = sizeof(E);
   using WF = WFrag<Tag>;
   using wf_t = typename WF::type;
-  constexpr int BW = NW * NBW * 16;     // band columns
-  constexpr int LDW = BW + 4;           // LDS row pitch (floats)
+  using BS = BandShape<NW, BMB, NBW>;
+  constexpr int BW = BS::BW;
+  constexpr int LDW = BS::LDW;
   constexpr int LPR = BW / 4;           // lanes per row (16 bytes each)
   constexpr int RPI = 64 / LPR;         // rows per instruction
   constexpr int R = 16 * BMB / NW;      // rows a wave writes per tile
   constexpr int NI = R / RPI;           // row instructions per tile
   static_assert(LPR <= 64 && 64 % LPR == 0 && R % RPI == 0 && NI >= 1, "band shape");
-  constexpr int TILE = 16 * BMB * LDW;  // floats per LDS tile
-  __shared__ __attribute__((aligned(16))) float lds[2 * TILE];
+  constexpr int TILE = BS::TILE;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int lr = lane / LPR;
   const int lc = (lane % LPR) * 4;
-  const int64_t c0 = (int64_t)blockIdx.x * BW;  // first column of the band
+  const int64_t c0 = band * BW;  // first column of the band
   const int64_t nb0 = c0 / 16 + wave * NBW;     // first column block of this wave
 
   // this wave's W2 fragments (rows past Nout and ranks past r read as zero)
@@ -802,7 +812,7 @@ __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
       }
     }
   }
-  const int64_t gstride = gridDim.y;
+  const int64_t gstride = ngroups;
   const int64_t ncol = c0 + lc;  // this lane's output column in the row-linear pass
   auto load_tile = [&](uint4 (&hf)[BMB][RB], f32x4_t (&cv)[NI], int64_t t) {
     const bool tok = t < p.tiles;
@@ -846,9 +856,9 @@ __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
   };
   uint4 hfA[BMB][RB], hfB[BMB][RB];
   f32x4_t cvA[NI], cvB[NI];
-  if (blockIdx.y < p.tiles) {
-    load_tile(hfA, cvA, blockIdx.y);
-    for (int64_t t = blockIdx.y; t < p.tiles; t += 2 * gstride) {
+  if (group < p.tiles) {
+    load_tile(hfA, cvA, group);
+    for (int64_t t = group; t < p.tiles; t += 2 * gstride) {
       load_tile(hfB, cvB, t + gstride);
       sched_fence();
       comp_tile(hfA, cvA, t, lds);
@@ -859,6 +869,12 @@ __global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
       sched_fence();
     }
   }
+}
+
+template <class Tag, int NW, int RB, int BMB, int NBW, class OM, bool WT>
+__global__ __launch_bounds__(64 * NW) void expand_band_kernel(FusedArgs p) {
+  __shared__ __attribute__((aligned(16))) float lds[BandShape<NW, BMB, NBW>::TILE * 2];
+  expand_band_body<Tag, NW, RB, BMB, NBW, OM, WT>(p, blockIdx.x, blockIdx.y, gridDim.y, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -879,22 +895,36 @@ struct TnArgs {
 };
 
 template <class Tag, int RB>
-__global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
+struct TnShape {
+  static constexpr int ES = sizeof(typename Tag::elem);
+  static constexpr int NS = 256;                      // columns per workgroup
+  static constexpr int TS = (ES == 2) ? 64 : 32;      // tokens per stage
+  static constexpr int GPL = (ES == 2) ? 2 : 1;       // G planes (bf16 hi/lo)
+  // LDS row pitch of G, padded by 16 bytes: the 16 rows one fragment read
+  // touches then fall in distinct banks (unpadded, 128-byte rows put them on
+  // two bank groups; 16384 x 14336, rank 64: lora_bwd_db 164 -> 156 us)
+  static constexpr int GPITCH = TS * ES + 16;
+  static constexpr int ZT_BYTES = TS * NS * ES;       // the staged Z tile
+  static constexpr int GS_BYTES = GPL * 16 * RB * GPITCH;
+};
+
+// The k-th work item of XCD `xcd` (the mapping below), with the Z tile and G
+// rows staged in `zt` and `gs`.
+template <class Tag, int RB>
+__device__ __forceinline__ void tn_body(const TnArgs& p, int xcd, int k, char* zt, char* gs) {
   using E = typename Tag::elem;
+  using TSh = TnShape<Tag, RB>;
   constexpr int VEC = Tag::VEC;
   constexpr int ES = sizeof(E);
   constexpr int NSB = 4;              // 16-column blocks per wave
   constexpr int NS = 64 * NSB;        // columns per workgroup
-  constexpr int TS = (ES == 2) ? 64 : 32;  // tokens per stage (bf16: two 32-token MFMA steps)
+  static_assert(NS == TSh::NS, "tn columns");
+  constexpr int TS = TSh::TS;         // tokens per stage (bf16: two 32-token MFMA steps)
   constexpr int ROWB = NS * ES;       // LDS bytes per staged Z row
   constexpr int VPR = NS / VEC;       // 128-bit vectors per Z row
   constexpr int ZV = TS * VPR / 256;  // Z vectors per thread per stage
-  constexpr int GPL = (ES == 2) ? 2 : 1;  // G planes (bf16 hi/lo)
-  constexpr int GROWB = TS * ES;          // bytes per G row and plane
-  // LDS row pitch of G, padded by 16 bytes: the 16 rows one fragment read
-  // touches then fall in distinct banks (unpadded, 128-byte rows put them on
-  // two bank groups; 16384 x 14336, rank 64: lora_bwd_db 164 -> 156 us)
-  constexpr int GPITCH = GROWB + 16;
+  constexpr int GPL = TSh::GPL;
+  constexpr int GPITCH = TSh::GPITCH;
   constexpr int GVR = TS / VEC;           // vectors per G row
   constexpr int GTOT = GPL * 16 * RB * GVR;
   constexpr int GV = (GTOT + 255) / 256;
@@ -902,9 +932,6 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   // XOR their 32/64-byte column windows apart to avoid LDS bank conflicts.
   constexpr int SWZ_SHIFT = (ES == 2) ? 3 : 2;
   constexpr int SWZ_UNIT = (ES == 2) ? 32 : 64;
-
-  __shared__ __attribute__((aligned(16))) char zt[TS * ROWB];
-  __shared__ __attribute__((aligned(16))) char gs[GPL * 16 * RB * GPITCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -919,8 +946,7 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
   // that XCD's L2 (16384 x 14336, rank 64: lora_bwd_db 158 -> 144 us); with
   // fewer chunks each XCD still gets its share of the columns. Items past the
   // last exit.
-  const int xcd = static_cast<int>(blockIdx.x & 7);
-  const int item = xcd * p.per + static_cast<int>(blockIdx.x >> 3);
+  const int item = xcd * p.per + k;
   if (item >= p.nblk * p.nchunk) return;
   const int chunk_id = item / p.nblk;
   const int64_t n_base = (int64_t)(item - chunk_id * p.nblk) * NS;
@@ -1080,6 +1106,52 @@ __global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
     }
 }
 
+template <class Tag, int RB>
+__global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
+  using TSh = TnShape<Tag, RB>;
+  __shared__ __attribute__((aligned(16))) char zt[TSh::ZT_BYTES];
+  __shared__ __attribute__((aligned(16))) char gs[TSh::GS_BYTES];
+  tn_body<Tag, RB>(p, static_cast<int>(blockIdx.x & 7), static_cast<int>(blockIdx.x >> 3), zt, gs);
+}
+
+// Where the workgroups of band_tn_kernel go: the first `tn_groups` groups of
+// 8 consecutive ids (one per XCD) are weight-gradient groups, the rest
+// column-band expand items.
+struct BandTnMap {
+  int64_t tn_groups;
+  int64_t band_items, bands, band_groups;  // items = bands x token groups
+};
+
+// dX's column-band expand and dA's weight-gradient partials in one launch.
+// Both read only what the shrink before them wrote (fragments and planes of
+// s*dYB) and the call's inputs, so they may run side by side: the expand
+// writes dX while the partial sums stream X, instead of a write-only pass
+// and then a read-only one, each with its own tail. The weight-gradient
+// workgroups (the longer ones) take the first ids, so they start first and
+// the band items fill the CUs as they finish (16384 x 4096 x 14336, rank 64:
+// lora_bwd_dx_da 181 us as two launches, 188 us with the two kinds
+// interleaved evenly, 173 us this way). Group g < T of 8 workgroups takes,
+// on XCD x, the weight-gradient item of XCD x's g-th workgroup in tn_kernel
+// (ids are dealt round-robin to the XCDs, so a group of 8 consecutive ids
+// covers each XCD once).
+template <class Tag, int RB, int BMB, class OM, bool WT>
+__global__ __launch_bounds__(256) void band_tn_kernel(FusedArgs a, TnArgs t, BandTnMap m) {
+  using TSh = TnShape<Tag, RB>;
+  constexpr int TN_LDS = TSh::ZT_BYTES + TSh::GS_BYTES;
+  constexpr int BAND_LDS = BandShape<4, BMB, 4>::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char shr[TN_LDS > BAND_LDS ? TN_LDS : BAND_LDS];
+  const int64_t g = blockIdx.x >> 3;
+  const int x = static_cast<int>(blockIdx.x & 7);
+  if (g < m.tn_groups) {
+    tn_body<Tag, RB>(t, x, static_cast<int>(g), shr, shr + TSh::ZT_BYTES);
+    return;
+  }
+  const int64_t i = (g - m.tn_groups) * 8 + x;
+  if (i >= m.band_items) return;
+  expand_band_body<Tag, 4, RB, BMB, 4, OM, WT>(a, i % m.bands, i / m.bands, m.band_groups,
+                                               reinterpret_cast<float*>(shr));
+}
+
 // ---------------------------------------------------------------------------
 // host-side schedule plan and launch helpers
 // ---------------------------------------------------------------------------
@@ -1117,14 +1189,18 @@ struct FusedShape {
 //    workgroups, else 1; dX (no output loads) 2 at rank <= 16 while >= 256
 //    workgroups, else 1 (8192 x 4096, rank 16: 63.6 against 67.0 us).
 //  - contraction > 8192 features (the dX of an MLP-up layer contracts over
-//    its 14336 outputs), or an output larger than 256 MB (the Infinity
-//    Cache): shrink_kernel writes s*H as MFMA fragments, then
+//    its 14336 outputs), or a forward output of 256 MB (the Infinity
+//    Cache) or more: shrink_kernel writes s*H as MFMA fragments, then
 //    expand_band_kernel updates the output band by band. In the fused kernel
 //    every workgroup owns whole output rows, so all rows stream at once; at
 //    16384 x 14336 (940 MB) that pattern tops out near 5.2 TB/s even as a
 //    plain add, while the band order streams at 5.8 TB/s (forward 410 ->
 //    352 us); at 8192 x 4096 (134 MB) the fused kernel stays faster (58.5
 //    against 62.1 us).
+//  - dX: the split schedule from a 128 MB output on, its band expand and
+//    dA's weight-gradient partials in one launch (band_tn_kernel): 16384 x
+//    4096 x 4096, rank 64 (268 MB): 170 -> 115 us for lora_bwd_dx_da; at
+//    8192 x 4096 x 4096, rank 16 (134 MB) 60.2 against 60.4 us fused.
 //  - shrink tiles: 16*bmb tokens with bmb 4 or 2 while rb*bmb <= 16 and
 //    >= 256 workgroups; 1 at rank <= 16 (twice the workgroups measure faster
 //    there: 34.8 against 36.7 us for the X*A shrink at 8192 x 4096, rank 16);
@@ -1138,7 +1214,8 @@ struct FusedShape {
 // ---------------------------------------------------------------------------
 
 constexpr int64_t kFusedMaxContraction = 8192;
-constexpr int64_t kFusedMaxOutputBytes = int64_t(256) << 20;  // the Infinity Cache's size
+constexpr int64_t kFusedMaxOutputBytes = int64_t(256) << 20;    // forward: below the Infinity Cache's size
+constexpr int64_t kFusedMaxDxOutputBytes = int64_t(128) << 20;  // dX: below half of it
 
 struct SinglePlan {
   bool fused;        // fused_kernel, else shrink_kernel + expand_band_kernel
@@ -1166,7 +1243,7 @@ static int bmb_shrink(int64_t M, int rb) {
 // per output element.
 static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int64_t nout, int rb, int64_t oes) {
   SinglePlan p{};
-  p.fused = kin <= kFusedMaxContraction && M * nout * oes <= kFusedMaxOutputBytes;
+  p.fused = kin <= kFusedMaxContraction && M * nout * oes < (forward ? kFusedMaxOutputBytes : kFusedMaxDxOutputBytes);
   p.bmb_shrink = bmb_shrink(M, rb);
   if (p.fused)
     p.bmb = forward ? bmb_expand(M, rb) : ((rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1);
@@ -1279,6 +1356,13 @@ static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
   }
 }
 
+// tn_kernel's work items: column blocks x token chunks, `per` per XCD
+static void tn_grid(TnArgs& a) {
+  a.nblk = static_cast<int>(ceil_div(a.N, kTnCols));
+  a.nchunk = static_cast<int>(ceil_div(a.M, a.chunk));
+  a.per = static_cast<int>(ceil_div((int64_t)a.nblk * a.nchunk, 8));
+}
+
 // Shrink Z against W1 and expand into the output as the plan says; with
 // EMIT_G also writes the planes for the gradient kernels; WT: weights in the
 // transposed storage (dX from nn.Linear-layout bf16 weights).
@@ -1292,11 +1376,44 @@ static void run_shrink_expand(FusedArgs a, const SinglePlan& pl, int rb, hipStre
   dispatch8<ExpandBandRB<Tag, OM, WT>::template L>(rb, pl.bmb, a, st);
 }
 
+template <class Tag, class OM, bool WT>
+struct BandTnRB {
+  template <int RB, int BMB>
+  struct L {
+    static void run(FusedArgs a, TnArgs t, hipStream_t st) {
+      a.tiles = ceil_div(a.M, 16 * BMB);
+      tn_grid(t);
+      BandTnMap m{};
+      m.bands = ceil_div(a.Nout, (int64_t)256);
+      m.band_groups = band_groups(a.tiles);
+      m.band_items = m.bands * m.band_groups;
+      m.tn_groups = t.per;
+      const int64_t groups = m.tn_groups + ceil_div(m.band_items, (int64_t)8);
+      launch((band_tn_kernel<Tag, RB, BMB, OM, WT>), dim3(static_cast<unsigned>(8 * groups)), dim3(256), 0, st, a, t,
+             m);
+    }
+  };
+};
+
+// The dX/dA call's kernels after the weights are in place: the fused
+// shrink-expand (writing the planes of s*dYB) and then the weight-gradient
+// partials; or, on the split schedule, the shrink and then dX's band expand
+// and dA's partials in one launch.
+template <class Tag, class OM, bool WT>
+static void run_dx_da(FusedArgs a, TnArgs t, const SinglePlan& pl, int rb, hipStream_t st) {
+  if (pl.fused) {
+    dispatch8<FusedNW<Tag, OM, true, WT>::template L>(rb, pl.bmb, a, st);
+    launch_tn<Tag>(t, rb, st);
+    return;
+  }
+  launch_shrink<Tag, true, true, WT>(a, rb, pl.bmb_shrink, st);
+  dispatch8<BandTnRB<Tag, OM, WT>::template L>(rb, pl.bmb, a, t, st);
+}
+
+
 template <class Tag>
 static void launch_tn(TnArgs a, int rb, hipStream_t st) {
-  a.nblk = static_cast<int>(ceil_div(a.N, kTnCols));
-  a.nchunk = static_cast<int>(ceil_div(a.M, a.chunk));
-  a.per = static_cast<int>(ceil_div((int64_t)a.nblk * a.nchunk, 8));
+  tn_grid(a);
   const dim3 grid(static_cast<unsigned>(8 * a.per));
   switch (rb) {
     case 1: launch((tn_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
@@ -1699,22 +1816,20 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   if (xt->dtype == LORA_BF16) {
     if (in_place) {
       if (accumulate)
-        run_shrink_expand<BF16, OutAdd, true, true>(a, plan, rb, st);
+        run_dx_da<BF16, OutAdd, true>(a, t, plan, rb, st);
       else
-        run_shrink_expand<BF16, OutSet, true, true>(a, plan, rb, st);
+        run_dx_da<BF16, OutSet, true>(a, t, plan, rb, st);
     } else {
       if (accumulate)
-        run_shrink_expand<BF16, OutAdd, true>(a, plan, rb, st);
+        run_dx_da<BF16, OutAdd, false>(a, t, plan, rb, st);
       else
-        run_shrink_expand<BF16, OutSet, true>(a, plan, rb, st);
+        run_dx_da<BF16, OutSet, false>(a, t, plan, rb, st);
     }
-    launch_tn<BF16>(t, rb, st);
   } else {
     if (accumulate)
-      run_shrink_expand<F32, OutAdd, true>(a, plan, rb, st);
+      run_dx_da<F32, OutAdd, false>(a, t, plan, rb, st);
     else
-      run_shrink_expand<F32, OutSet, true>(a, plan, rb, st);
-    launch_tn<F32>(t, rb, st);
+      run_dx_da<F32, OutSet, false>(a, t, plan, rb, st);
   }
   launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dA->ptr), dA->stride_row,
                 dA->stride_col, st);

@@ -12,10 +12,12 @@ rank 16; 16384 x 4096 x 14336, rank 64):
   whole output and for every 64-row tile of it, so one wrong tile cannot hide
   in the whole-matrix norm.
 
-These are the defaults being exercised: at 8192 tokens the fused dX kernel
-with 32-token tiles and 32 token chunks in the weight-gradient kernels; at
-16384 x 14336 the split dX schedule (the contraction over 14336 features is
-longer than 8192) and the column-band expand.
+These are the defaults being exercised: the split dX schedule at both
+shapes (a 134 MB dX at 8192 x 4096, a contraction over 14336 features at
+16384 x 14336), with dX's column-band expand and dA's weight-gradient
+partials in one launch, 32 token chunks in the weight-gradient kernels at
+8192 tokens; the fused forward at 8192 x 4096 and the split forward (a
+940 MB Y) at 16384 x 14336.
 """
 import ctypes
 
