@@ -894,10 +894,10 @@ struct TnArgs {
   int per;           // work items per XCD run: ceil(nblk * nchunk / 8)
 };
 
-template <class Tag, int RB>
+template <class Tag, int RB, int NW = 4>
 struct TnShape {
   static constexpr int ES = sizeof(typename Tag::elem);
-  static constexpr int NS = 256;                      // columns per workgroup
+  static constexpr int NS = 64 * NW;                  // columns per workgroup (64 per wave)
   static constexpr int TS = (ES == 2) ? 64 : 32;      // tokens per stage
   static constexpr int GPL = (ES == 2) ? 2 : 1;       // G planes (bf16 hi/lo)
   // LDS row pitch of G, padded by 16 bytes: the 16 rows one fragment read
@@ -910,24 +910,26 @@ struct TnShape {
 
 // The k-th work item of XCD `xcd` (the mapping below), with the Z tile and G
 // rows staged in `zt` and `gs`.
-template <class Tag, int RB>
+template <class Tag, int RB, int NW = 4>
 __device__ __forceinline__ void tn_body(const TnArgs& p, int xcd, int k, char* zt, char* gs) {
   using E = typename Tag::elem;
-  using TSh = TnShape<Tag, RB>;
+  using TSh = TnShape<Tag, RB, NW>;
   constexpr int VEC = Tag::VEC;
   constexpr int ES = sizeof(E);
+  constexpr int NT = 64 * NW;         // threads
   constexpr int NSB = 4;              // 16-column blocks per wave
-  constexpr int NS = 64 * NSB;        // columns per workgroup
-  static_assert(NS == TSh::NS, "tn columns");
+  constexpr int NS = TSh::NS;         // columns per workgroup
+  static_assert(NS == 16 * NSB * NW, "tn columns");
   constexpr int TS = TSh::TS;         // tokens per stage (bf16: two 32-token MFMA steps)
   constexpr int ROWB = NS * ES;       // LDS bytes per staged Z row
   constexpr int VPR = NS / VEC;       // 128-bit vectors per Z row
-  constexpr int ZV = TS * VPR / 256;  // Z vectors per thread per stage
+  constexpr int ZV = TS * VPR / NT;   // Z vectors per thread per stage
+  static_assert(ZV * NT == TS * VPR, "Z stage");
   constexpr int GPL = TSh::GPL;
   constexpr int GPITCH = TSh::GPITCH;
   constexpr int GVR = TS / VEC;           // vectors per G row
   constexpr int GTOT = GPL * 16 * RB * GVR;
-  constexpr int GV = (GTOT + 255) / 256;
+  constexpr int GV = (GTOT + NT - 1) / NT;
   // rows 8 (bf16) or 4 (f32) apart are read together by the four lane groups:
   // XOR their 32/64-byte column windows apart to avoid LDS bank conflicts.
   constexpr int SWZ_SHIFT = (ES == 2) ? 3 : 2;
@@ -975,7 +977,7 @@ __device__ __forceinline__ void tn_body(const TnArgs& p, int xcd, int k, char* z
   auto load_stage = [&](int d, int64_t m0) {
 #pragma unroll
     for (int i = 0; i < ZV; ++i) {
-      const int v = tid + 256 * i;
+      const int v = tid + NT * i;
       const int row = v / VPR;
       const int vc = v - row * VPR;
       const int64_t n = n_base + (int64_t)vc * VEC;
@@ -983,7 +985,7 @@ __device__ __forceinline__ void tn_body(const TnArgs& p, int xcd, int k, char* z
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
-      const int v = tid + 256 * i;
+      const int v = tid + NT * i;
       const int grow = v / GVR;  // plane * 16*RB + j
       const int vc = v - grow * GVR;
       gr[d][i] = bload16(rg, v < GTOT ? static_cast<uint32_t>(((int64_t)grow * p.ldg + m0 + vc * VEC) * ES) : kOOB);
@@ -1006,14 +1008,14 @@ __device__ __forceinline__ void tn_body(const TnArgs& p, int xcd, int k, char* z
   auto store_stage = [&](int d) {
 #pragma unroll
     for (int i = 0; i < ZV; ++i) {
-      const int v = tid + 256 * i;
+      const int v = tid + NT * i;
       const int row = v / VPR;
       const int vc = v - row * VPR;
       *reinterpret_cast<uint4*>(zt + zoff(row, vc * 16)) = zr[d][i];
     }
 #pragma unroll
     for (int i = 0; i < GV; ++i) {
-      const int v = tid + 256 * i;
+      const int v = tid + NT * i;
       if (v < GTOT) *reinterpret_cast<uint4*>(gs + (v / GVR) * GPITCH + (v % GVR) * 16) = gr[d][i];
     }
   };
@@ -1106,12 +1108,12 @@ __device__ __forceinline__ void tn_body(const TnArgs& p, int xcd, int k, char* z
     }
 }
 
-template <class Tag, int RB>
-__global__ __launch_bounds__(256) void tn_kernel(TnArgs p) {
-  using TSh = TnShape<Tag, RB>;
+template <class Tag, int RB, int NW>
+__global__ __launch_bounds__(64 * NW) void tn_kernel(TnArgs p) {
+  using TSh = TnShape<Tag, RB, NW>;
   __shared__ __attribute__((aligned(16))) char zt[TSh::ZT_BYTES];
   __shared__ __attribute__((aligned(16))) char gs[TSh::GS_BYTES];
-  tn_body<Tag, RB>(p, static_cast<int>(blockIdx.x & 7), static_cast<int>(blockIdx.x >> 3), zt, gs);
+  tn_body<Tag, RB, NW>(p, static_cast<int>(blockIdx.x & 7), static_cast<int>(blockIdx.x >> 3), zt, gs);
 }
 
 // Where the workgroups of band_tn_kernel go: the first `tn_groups` groups of
@@ -1156,7 +1158,7 @@ __global__ __launch_bounds__(256) void band_tn_kernel(FusedArgs a, TnArgs t, Ban
 // host-side schedule plan and launch helpers
 // ---------------------------------------------------------------------------
 
-constexpr int kTnCols = 256;  // columns per tn_kernel workgroup
+constexpr int kTnCols = 256;  // columns per 4-wave tn_kernel workgroup (64 per wave)
 
 // Stage sizes: U contraction chunks (shrink) and NBU column blocks (expand)
 // per pipeline stage. A bf16 expand stage holds RB weight fragments
@@ -1263,8 +1265,8 @@ static int64_t band_groups(int64_t tiles) {
 // Token chunks of the weight-gradient kernels: about `wgs` workgroups in all,
 // a multiple of 8 chunks from 8 on (one XCD per chunk, the same number per
 // XCD), at most one chunk per 64 tokens.
-static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs) {
-  const int64_t slices = ceil_div(N, kTnCols);
+static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs, int64_t cols) {
+  const int64_t slices = ceil_div(N, cols);
   int64_t P = ceil_div(wgs, slices);
   P = P < 8 ? P : (P + 4) / 8 * 8;
   const int64_t cap = ceil_div(M, 64);
@@ -1272,7 +1274,28 @@ static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs) {
   return P < 1 ? 1 : P;
 }
 
-static int64_t tn_chunk_tokens(int64_t M, int64_t N) { return round_up(ceil_div(M, tn_chunks_for(M, N, 512)), 64); }
+// Weight-gradient plan: waves per workgroup (64 columns each), the chunk
+// count the partials are sized for, tokens per chunk. dB over wide outputs
+// (wide_ok, N >= kTnWideMin) takes 8-wave, 512-column workgroups, about 224
+// of them: one stage of loads in flight per thread (more costs occupancy),
+// so a wider workgroup keeps twice the bytes in flight, and each G row it
+// stages serves twice the columns. Only one such workgroup fits a CU's LDS,
+// so the grid is kept to one round (lora_bwd_db, rank 64, L = 14336: 16384
+// tokens 142.6 -> 138.8 us, 8192 tokens 83.7 -> 80.9 us; 448 workgroups,
+// 1.75 rounds: 152.6 and 96.2 us).
+constexpr int64_t kTnWideMin = 8192;
+constexpr int64_t kTnWideWgs = 224;
+struct TnPlan {
+  int nw;
+  int64_t P, chunk;
+};
+static TnPlan tn_plan(int64_t M, int64_t N, bool wide_ok) {
+  TnPlan t;
+  t.nw = (wide_ok && N >= kTnWideMin) ? 8 : 4;
+  t.P = tn_chunks_for(M, N, t.nw == 8 ? kTnWideWgs : 512, 64 * t.nw);
+  t.chunk = round_up(ceil_div(M, t.P), 64);
+  return t;
+}
 
 // ---------------------------------------------------------------------------
 // kernel dispatch
@@ -1357,8 +1380,8 @@ static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
 }
 
 // tn_kernel's work items: column blocks x token chunks, `per` per XCD
-static void tn_grid(TnArgs& a) {
-  a.nblk = static_cast<int>(ceil_div(a.N, kTnCols));
+static void tn_grid(TnArgs& a, int cols) {
+  a.nblk = static_cast<int>(ceil_div(a.N, (int64_t)cols));
   a.nchunk = static_cast<int>(ceil_div(a.M, a.chunk));
   a.per = static_cast<int>(ceil_div((int64_t)a.nblk * a.nchunk, 8));
 }
@@ -1382,7 +1405,7 @@ struct BandTnRB {
   struct L {
     static void run(FusedArgs a, TnArgs t, hipStream_t st) {
       a.tiles = ceil_div(a.M, 16 * BMB);
-      tn_grid(t);
+      tn_grid(t, kTnCols);
       BandTnMap m{};
       m.bands = ceil_div(a.Nout, (int64_t)256);
       m.band_groups = band_groups(a.tiles);
@@ -1403,7 +1426,7 @@ template <class Tag, class OM, bool WT>
 static void run_dx_da(FusedArgs a, TnArgs t, const SinglePlan& pl, int rb, hipStream_t st) {
   if (pl.fused) {
     dispatch8<FusedNW<Tag, OM, true, WT>::template L>(rb, pl.bmb, a, st);
-    launch_tn<Tag>(t, rb, st);
+    launch_tn<Tag>(t, rb, 4, st);
     return;
   }
   launch_shrink<Tag, true, true, WT>(a, rb, pl.bmb_shrink, st);
@@ -1412,14 +1435,19 @@ static void run_dx_da(FusedArgs a, TnArgs t, const SinglePlan& pl, int rb, hipSt
 
 
 template <class Tag>
-static void launch_tn(TnArgs a, int rb, hipStream_t st) {
-  tn_grid(a);
+static void launch_tn(TnArgs a, int rb, int nw, hipStream_t st) {
+  tn_grid(a, 64 * nw);
   const dim3 grid(static_cast<unsigned>(8 * a.per));
-  switch (rb) {
-    case 1: launch((tn_kernel<Tag, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: launch((tn_kernel<Tag, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: launch((tn_kernel<Tag, 4>), grid, dim3(256), 0, st, a); break;
-    default: launch((tn_kernel<Tag, 8>), grid, dim3(256), 0, st, a); break;
+  const dim3 block(static_cast<unsigned>(64 * nw));
+  switch (rb * 10 + nw) {
+    case 14: launch((tn_kernel<Tag, 1, 4>), grid, block, 0, st, a); break;
+    case 24: launch((tn_kernel<Tag, 2, 4>), grid, block, 0, st, a); break;
+    case 44: launch((tn_kernel<Tag, 4, 4>), grid, block, 0, st, a); break;
+    case 84: launch((tn_kernel<Tag, 8, 4>), grid, block, 0, st, a); break;
+    case 18: launch((tn_kernel<Tag, 1, 8>), grid, block, 0, st, a); break;
+    case 28: launch((tn_kernel<Tag, 2, 8>), grid, block, 0, st, a); break;
+    case 48: launch((tn_kernel<Tag, 4, 8>), grid, block, 0, st, a); break;
+    default: launch((tn_kernel<Tag, 8, 8>), grid, block, 0, st, a); break;
   }
 }
 
@@ -1506,14 +1534,14 @@ static SingleLayout layout_for(int op, int64_t M, int64_t K, int64_t L, int r, i
     s.w2 = static_cast<size_t>(K * rp) * es;  // A as K x r
     s.ldg = round_up(M > 0 ? M : 1, 64);
     s.g = static_cast<size_t>(4 * rp * s.ldg);
-    s.P = tn_chunks_for(M, K, 512);
+    s.P = tn_plan(M, K, false).P;
     s.part = static_cast<size_t>(s.P * K * rp) * 4;
     s.frag = frag;
   } else {
     s.w1 = static_cast<size_t>(rp * K) * es;  // A as r x K
     s.ldg = round_up(M > 0 ? M : 1, 64);
     s.g = static_cast<size_t>(4 * rp * s.ldg);
-    s.P = tn_chunks_for(M, L, 512);
+    s.P = tn_plan(M, L, true).P;
     s.part = static_cast<size_t>(s.P * L * rp) * 4;
   }
   return s;
@@ -1759,7 +1787,7 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   const int rb = rank_blocks(static_cast<int>(r));
   const int64_t rp = 16 * rb;
   const size_t es = elem_size(xt->dtype);
-  const int64_t chunk = tn_chunk_tokens(M, K);
+  const int64_t chunk = tn_plan(M, K, false).chunk;
   if (!fused_fits(dy->stride_row, es, r, L, K, rp, dx->stride_row) || !fits32(chunk * xt->stride_col * (int64_t)es) ||
       !fits32((int64_t)lay.g))
     return LORA_ERR_LIMIT;
@@ -1885,7 +1913,8 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   FusedArgs a{};
   const bool a_direct = lora_A->stride_col == 1 && lora_A->stride_row >= K &&
                         (lora_A->stride_row * (int64_t)es) % 16 == 0 && aligned(lora_A->ptr, 16);
-  const int64_t chunk = tn_chunk_tokens(M, L);
+  const TnPlan tp = tn_plan(M, L, true);
+  const int64_t chunk = tp.chunk;
   if (!fused_fits(xt->stride_col, es, r, a_direct ? lora_A->stride_row : K, 0, 0, 0) ||
       !fits32(chunk * dy->stride_row * (int64_t)es) || !fits32((int64_t)lay.g))
     return LORA_ERR_LIMIT;
@@ -1922,10 +1951,10 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   const int P = static_cast<int>(ceil_div(M, t.chunk));
   if (xt->dtype == LORA_BF16) {
     launch_shrink<BF16, true, false>(a, rb, bmb, st);
-    launch_tn<BF16>(t, rb, st);
+    launch_tn<BF16>(t, rb, tp.nw, st);
   } else {
     launch_shrink<F32, true, false>(a, rb, bmb, st);
-    launch_tn<F32>(t, rb, st);
+    launch_tn<F32>(t, rb, tp.nw, st);
   }
   // dB is r x L: partial row n = l, column j.
   launch_reduce(part, P, L, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dB->ptr), dB->stride_col,

@@ -368,7 +368,8 @@ def test_fp32_workload():
 # the band expand and dA's partials in one launch) for contractions over more
 # than 8192 features, forward outputs of 256 MB or more and dX outputs of
 # 128 MB or more, with 32- and 16-token band tiles and token groups walking
-# several tiles (ragged tails in every dimension), in bf16 and f32.
+# several tiles (ragged tails in every dimension), and dB's 8-wave
+# weight-gradient workgroups (8192 or more outputs), in bf16 and f32.
 PLAN_CASES = [
     (32768, 256, 264, 16, "bf16", 2.0),    # fused fwd 64-token tiles, fused dX 32-token tiles
     (16400, 512, 264, 40, "bf16", 0.5),    # fused fwd 32-token tiles, shrink 64-token tiles (4 waves)
@@ -379,6 +380,7 @@ PLAN_CASES = [
     (4100, 8200, 1000, 16, "bf16", 1.0),   # split forward, 32-token band tiles
     (2100, 264, 8200, 64, "bf16", 0.5),    # split dX, 32-token band tiles
     (8200, 4096, 264, 16, "bf16", 2.0),    # split dX for a 134 MB dX (contraction 264)
+    (300, 264, 8312, 16, "bf16", 1.0),     # dB over 8312 outputs: 8-wave weight-gradient workgroups, rank 16
     (16400, 256, 4104, 16, "bf16", 2.0),   # split forward for a 269 MB output (contraction 256)
     (3000, 8196, 300, 19, "f32", 0.5),     # split forward, f32
     (70, 132, 8196, 19, "f32", 2.0),       # split dX, f32
