@@ -61,14 +61,16 @@ ROOFLINE_KERNEL = {
     "single-bf16-M16384-K4096-L14336-r64": ["shrink_kernel", "expand_band_kernel"],
 }
 # How those launches are told apart from the same templates' backward
-# instances in a profile: the forward ones accumulate into Y (ACCUM = true,
-# EMIT_G = false in fused_kernel; ACCUM = true in expand_band_kernel, whose
-# accumulating-dX instance is the same template but has another grid) or
-# write only fragments (EMIT_G = false, EMIT_F = true in shrink_kernel).
+# instances in a profile (the last template argument of each is WT, the
+# backward's transposed-weight flag, false in the forward): the forward ones
+# accumulate into Y (lora::OutAdd with EMIT_G = false in fused_kernel;
+# lora::OutAdd in expand_band_kernel, the backward's band expands running
+# inside band_tn_kernel) or write only fragments (EMIT_G = false,
+# EMIT_F = true in shrink_kernel).
 ROOFLINE_PATTERN = {
-    "fused_kernel": r"\bfused_kernel<.*, lora::OutAdd, false>",
-    "shrink_kernel": r"\bshrink_kernel<.*, false, true>",
-    "expand_band_kernel": r"\bexpand_band_kernel<.*, lora::OutAdd>",
+    "fused_kernel": r"\bfused_kernel<.*, lora::OutAdd, false, false>",
+    "shrink_kernel": r"\bshrink_kernel<.*, false, true, false>",
+    "expand_band_kernel": r"\bexpand_band_kernel<.*, lora::OutAdd, false>",
 }
 
 
