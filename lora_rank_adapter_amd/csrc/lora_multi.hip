@@ -15,6 +15,7 @@
 //
 // Kernels:
 //   group_kernel               stable counting sort (one 1024-thread workgroup)
+//   group_small_kernel         the same for up to 1024 tokens, one per thread
 //   group_chunk_kernel         the same with one workgroup per 1024-token chunk
 //   slot_shrink_kernel         shrink, one workgroup per (tile, slice, rank chunk)
 //   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
@@ -290,6 +291,75 @@ __global__ __launch_bounds__(1024) void group_chunk_kernel(const int32_t* __rest
     int pos = base[key] + rank_in_wave;
     for (int w = 0; w < wave; ++w) pos += wcnt[w][key];
     sorted_tokens[pos] = t;
+  }
+}
+
+// The same stable counting sort for T <= 1024 (a decode batch): one token
+// per thread of one workgroup. The tokens' slots and the ranks are loaded
+// together; one ballot pass gives each wave's count of every key and each
+// token's rank among the lanes of its wave with the same key before it; the
+// per-key totals are scanned (one key per thread); a token then lands at its
+// slot's offset plus the same-key tokens of earlier waves plus its rank in
+// its wave. Four barriers and one round of global loads, where the chunked
+// kernel's multi-chunk bookkeeping takes eight and three (GPU time per call:
+// 256 tokens 6.7 -> 3.1 us, 1024 tokens 7.3 -> 3.6 us).
+constexpr int kGroupSmallMaxT = 1024;
+__global__ __launch_bounds__(1024) void group_small_kernel(const int32_t* __restrict__ token_slot, int T, int S,
+                                                           const int32_t* __restrict__ ranks, int r_max,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_tokens) {
+  __shared__ int rho[kMaxSlots];
+  __shared__ int base[kMaxSlots + 1];
+  __shared__ int wcnt[16][kMaxSlots + 1];  // per-wave count of each key
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int slot = tid < T ? token_slot[tid] : -1;
+  const int rk = tid < S ? ranks[tid] : 0;
+  if (tid < S) rho[tid] = clamp_rank(rk, r_max);
+  for (int i = tid; i <= S; i += 1024) {
+#pragma unroll
+    for (int w = 0; w < 16; ++w) wcnt[w][i] = 0;
+  }
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) <= S) ++nbits;  // keys 0..S (S = inactive)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int key = (slot >= 0 && slot < S && rho[slot] > 0) ? slot : S;
+  const uint64_t peers = key_peers(key, nbits);
+  const int rank_in_wave = __popcll(peers & lt_mask);
+  if ((peers & lt_mask) == 0) wcnt[wave][key] = __popcll(peers);
+  __syncthreads();
+  // per-key totals and their exclusive scan (S <= 1024: one key per thread)
+  int c = 0;
+  if (tid < S) {
+#pragma unroll
+    for (int w = 0; w < 16; ++w) c += wcnt[w][tid];
+  }
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int excl = before + incl - c;
+  if (tid < S) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    base[tid] = excl;
+  }
+  if (tid == S - 1) offsets[S] = excl + c;
+  if (S == 0 && tid == 0) offsets[0] = 0;
+  __syncthreads();
+  if (key < S) {
+    int pos = base[key] + rank_in_wave;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][key];
+    sorted_tokens[pos] = tid;
   }
 }
 
@@ -1732,9 +1802,13 @@ extern "C" int lora_addressing_build(const lora_addressing* addr, const int32_t*
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
   if (addr->S > 0 && !addr->counts) return LORA_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // one workgroup per 1024-token chunk up to kGroupChunkMaxT tokens (each
-  // holds every token's key in registers), one workgroup beyond
-  if (addr->T <= kGroupChunkMaxT) {
+  // up to 1024 tokens one token per thread; one workgroup per 1024-token
+  // chunk up to kGroupChunkMaxT tokens (each holds every token's key in
+  // registers); one workgroup beyond
+  if (addr->T <= kGroupSmallMaxT) {
+    launch(group_small_kernel, dim3(1), dim3(1024), 0, st, addr->token_slot, addr->T, addr->S, ranks, r_max,
+           addr->counts, addr->offsets, addr->sorted_tokens);
+  } else if (addr->T <= kGroupChunkMaxT) {
     const int chunks = addr->T > 0 ? static_cast<int>(ceil_div(addr->T, 1024)) : 1;
     launch(group_chunk_kernel, dim3(static_cast<unsigned>(chunks)), dim3(1024), 0, st, addr->token_slot, addr->T,
            addr->S, ranks, r_max, addr->counts, addr->offsets, addr->sorted_tokens);

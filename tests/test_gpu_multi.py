@@ -35,6 +35,9 @@ CASES = [
     ("fp32-mid", 600, 64, (32, 16), 8, 16, (0, 4, 16), 0.2, "f32"),
 ]
 # Which kernel each case reaches (the library picks by shape):
+#   grouping: one token per thread (<= 1024 tokens): decode-small, ragged-ranks, fp32, one-token,
+#             decode-mid, decode-wide, fp32-mid; one workgroup per 1024-token chunk: the others
+#             (and test_grouping_schedules_bitwise for every grouping kernel);
 #   shrink: row-split (bf16, >= 1024 tokens, a grid of >= 512 workgroups): prefill-many-slots;
 #           pipelined, 64-token tiles (>= 1024 tokens otherwise): prefill-like, prefill-long,
 #             fp32-prefill, decode-1k;
@@ -102,7 +105,22 @@ def test_grouping_bitwise(case):
 
 
 def _grouping_inputs(kind, rng):
-    if kind == "chunk-multiple":
+    if kind == "small-max":
+        T, S = 1024, 40
+        ts = rng.integers(-1, S + 2, T).astype(np.int32)
+    elif kind == "small-many-slots":
+        T, S = 1000, 1000
+        ts = rng.integers(-5, S + 5, T).astype(np.int32)
+    elif kind == "small-one-token":
+        T, S = 1, 3
+        ts = np.asarray([2], np.int32)
+    elif kind == "small-one-slot":
+        T, S = 640, 8
+        ts = np.full(T, 2, np.int32)
+    elif kind == "small-all-inactive":
+        T, S = 300, 8
+        ts = np.full(T, -1, np.int32)
+    elif kind == "chunk-multiple":
         T, S = 4096, 40
         ts = rng.integers(0, S, T).astype(np.int32)
     elif kind == "bursty":
@@ -121,15 +139,19 @@ def _grouping_inputs(kind, rng):
         T, S = 70000, 64
         ts = rng.integers(0, S + 2, T).astype(np.int32)
     ranks = rng.choice(np.asarray([0, 4, 16, 64], np.int32), S).astype(np.int32)
+    if kind in ("small-one-token", "small-one-slot"):
+        ranks[2] = 16
     return ts, ranks
 
 
-@pytest.mark.parametrize("kind", ["chunk-multiple", "bursty", "many-slots", "max-chunked", "all-inactive",
-                                  "beyond-chunked"])
+@pytest.mark.parametrize("kind", ["small-max", "small-many-slots", "small-one-token", "small-one-slot",
+                                  "small-all-inactive", "chunk-multiple", "bursty", "many-slots", "max-chunked",
+                                  "all-inactive", "beyond-chunked"])
 def test_grouping_schedules_bitwise(kind):
-    """Both grouping kernels against the stable sort of the oracle: one
-    workgroup per 1024-token chunk up to 32768 tokens (max-chunked is the
-    largest), one workgroup beyond (beyond-chunked)."""
+    """The three grouping kernels against the stable sort of the oracle: one
+    token per thread up to 1024 tokens (the small-* kinds; small-max is the
+    largest), one workgroup per 1024-token chunk up to 32768 tokens
+    (max-chunked is the largest), one workgroup beyond (beyond-chunked)."""
     rng = np.random.default_rng(77)
     ts, ranks = _grouping_inputs(kind, rng)
     S = ranks.shape[0]
