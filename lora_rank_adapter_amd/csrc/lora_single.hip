@@ -1283,16 +1283,23 @@ static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs, int64_t cols) {
 // so the grid is kept to one round (lora_bwd_db, rank 64, L = 14336: 16384
 // tokens 142.6 -> 138.8 us, 8192 tokens 83.7 -> 80.9 us; 448 workgroups,
 // 1.75 rounds: 152.6 and 96.2 us).
+// dA's partial sums beside dX's band expand (band_tn_kernel) take about 256
+// workgroups: the band items fill the rest of the chip, and half as many
+// chunks halve the partials to write and add (lora_bwd_dx_da 172.0 -> 168.5
+// us at 16384 x 4096 x 14336, 59.6 -> 57.7 us at 8192 x 4096 x 4096, 114.0
+// -> 108.9 us at 8192 x 4096 x 14336; 128 workgroups: 179.7, 61.4, 112.5 us).
+// The workspace holds the partials of the 512-workgroup plan, the most.
 constexpr int64_t kTnWideMin = 8192;
 constexpr int64_t kTnWideWgs = 224;
+constexpr int64_t kTnBandWgs = 256;
 struct TnPlan {
   int nw;
   int64_t P, chunk;
 };
-static TnPlan tn_plan(int64_t M, int64_t N, bool wide_ok) {
+static TnPlan tn_plan(int64_t M, int64_t N, bool wide_ok, bool beside_band = false) {
   TnPlan t;
   t.nw = (wide_ok && N >= kTnWideMin) ? 8 : 4;
-  t.P = tn_chunks_for(M, N, t.nw == 8 ? kTnWideWgs : 512, 64 * t.nw);
+  t.P = tn_chunks_for(M, N, t.nw == 8 ? kTnWideWgs : (beside_band ? kTnBandWgs : 512), 64 * t.nw);
   t.chunk = round_up(ceil_div(M, t.P), 64);
   return t;
 }
@@ -1787,7 +1794,8 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   const int rb = rank_blocks(static_cast<int>(r));
   const int64_t rp = 16 * rb;
   const size_t es = elem_size(xt->dtype);
-  const int64_t chunk = tn_plan(M, K, false).chunk;
+  const SinglePlan plan = plan_single(false, M, L, K, rb, 4);
+  const int64_t chunk = tn_plan(M, K, false, !plan.fused).chunk;
   if (!fused_fits(dy->stride_row, es, r, L, K, rp, dx->stride_row) || !fits32(chunk * xt->stride_col * (int64_t)es) ||
       !fits32((int64_t)lay.g))
     return LORA_ERR_LIMIT;
@@ -1840,7 +1848,6 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   t.rp = static_cast<int>(rp);
   t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
-  const SinglePlan plan = plan_single(false, M, L, K, rb, 4);
   if (xt->dtype == LORA_BF16) {
     if (in_place) {
       if (accumulate)
