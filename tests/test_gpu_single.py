@@ -125,9 +125,11 @@ def test_weight_layouts_and_output_strides():
     assert oracle.rel_frobenius(host(y1) - c.Y0, want - c.Y0) <= 2e-3
 
 
-# (M, K, L, r): the fused dX kernel at rank 16 and 64, the split schedule's
-# shrink + column-band expand at rank 64 and 128
-IN_PLACE_CASES = [(200, 264, 1000, 16), (130, 512, 296, 64), (2100, 264, 8200, 64), (700, 1032, 8200, 128)]
+# (M, K, L, r): the fused dX kernel at rank 8 (half of one rank block), 16
+# and 64, the split schedule's shrink + band expand beside dA's partials at
+# rank 8, 64 and 128
+IN_PLACE_CASES = [(200, 264, 1000, 16), (130, 512, 296, 64), (2100, 264, 8200, 64), (700, 1032, 8200, 128),
+                  (96, 256, 200, 8), (400, 512, 8208, 8)]
 
 
 @pytest.mark.parametrize("case", IN_PLACE_CASES, ids=lambda c: "M{}-K{}-L{}-r{}".format(*c))
