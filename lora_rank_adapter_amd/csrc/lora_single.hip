@@ -1276,13 +1276,15 @@ static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs, int64_t cols) {
 
 // Weight-gradient plan: waves per workgroup (64 columns each), the chunk
 // count the partials are sized for, tokens per chunk. dB over wide outputs
-// (wide_ok, N >= kTnWideMin) takes 8-wave, 512-column workgroups, about 224
-// of them: one stage of loads in flight per thread (more costs occupancy),
-// so a wider workgroup keeps twice the bytes in flight, and each G row it
-// stages serves twice the columns. Only one such workgroup fits a CU's LDS,
-// so the grid is kept to one round (lora_bwd_db, rank 64, L = 14336: 16384
-// tokens 142.6 -> 138.8 us, 8192 tokens 83.7 -> 80.9 us; 448 workgroups,
-// 1.75 rounds: 152.6 and 96.2 us).
+// (wide_ok, N >= kTnWideMin) takes 8-wave, 512-column workgroups: one stage
+// of loads in flight per thread (more costs occupancy), so a wider workgroup
+// keeps twice the bytes in flight, and each G row it stages serves twice the
+// columns. Only one such workgroup fits a CU's LDS, so the grid is one round:
+// as many token chunks as keep the workgroups within the 256 CUs
+// (lora_bwd_db, rank 64, L = 14336: 16384 tokens 142.6 -> 138.8 us with 8
+// chunks (224 workgroups), 134 us with 9 (252; a chunk's column blocks then
+// no longer all share one XCD); 8192 tokens 83.7 -> 80.9 us; 448
+// workgroups, 1.75 rounds: 152.6 and 96.2 us).
 // dA's partial sums beside dX's band expand (band_tn_kernel) take about 256
 // workgroups: the band items fill the rest of the chip, and half as many
 // chunks halve the partials to write and add (lora_bwd_dx_da 172.0 -> 168.5
@@ -1290,7 +1292,6 @@ static int64_t tn_chunks_for(int64_t M, int64_t N, int64_t wgs, int64_t cols) {
 // -> 108.9 us at 8192 x 4096 x 14336; 128 workgroups: 179.7, 61.4, 112.5 us).
 // The workspace holds the partials of the 512-workgroup plan, the most.
 constexpr int64_t kTnWideMin = 8192;
-constexpr int64_t kTnWideWgs = 224;
 constexpr int64_t kTnBandWgs = 256;
 struct TnPlan {
   int nw;
@@ -1299,7 +1300,14 @@ struct TnPlan {
 static TnPlan tn_plan(int64_t M, int64_t N, bool wide_ok, bool beside_band = false) {
   TnPlan t;
   t.nw = (wide_ok && N >= kTnWideMin) ? 8 : 4;
-  t.P = tn_chunks_for(M, N, t.nw == 8 ? kTnWideWgs : (beside_band ? kTnBandWgs : 512), 64 * t.nw);
+  if (t.nw == 8) {
+    int64_t P = 256 / ceil_div(N, (int64_t)512);
+    const int64_t cap = ceil_div(M, 64);
+    if (P > cap) P = cap;
+    t.P = P < 1 ? 1 : P;
+  } else {
+    t.P = tn_chunks_for(M, N, beside_band ? kTnBandWgs : 512, 64 * t.nw);
+  }
   t.chunk = round_up(ceil_div(M, t.P), 64);
   return t;
 }
