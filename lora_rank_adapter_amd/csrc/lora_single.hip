@@ -1211,8 +1211,10 @@ struct FusedShape {
 //    fragments of two token blocks would not fit the registers), about four
 //    tiles per workgroup.
 //  - weight-gradient token chunks: about 512 workgroups in all, at most one
-//    chunk per 64 tokens (P = 32 at 8192 x 4096 measured best: 16 chunks
-//    16.5, 64 chunks 16.7 us against 15.1 us).
+//    chunk per 64 tokens (P = 32 at 8192 x 4096 measured best for a launch
+//    of its own: 16 chunks 16.5, 64 chunks 16.7 us against 15.1 us); about
+//    256 beside dX's band expand; dB over wide outputs: 8-wave, 512-column
+//    workgroups in one round (tn_plan).
 // ---------------------------------------------------------------------------
 
 constexpr int64_t kFusedMaxContraction = 8192;
