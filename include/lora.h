@@ -207,10 +207,14 @@ int lora_fwd(const lora_mat* x, const lora_mat* lora_A, const lora_mat* lora_B, 
  *                   starting 16-byte aligned, r a multiple of 8) are read in
  *                   place; other layouts are packed into the workspace first
  *                   (one more kernel launch, same results bit for bit).
- *   dx      M x K   float32 out (overwritten): dx = scale * (dy @ lora_B) @ lora_A.
+ *   dx      M x K   out (overwritten): dx = scale * (dy @ lora_B) @ lora_A.
  *                   stride_col 1, 16-byte aligned rows.
- *   dA      K x r   float32 out (overwritten), any strides:
+ *   dA      K x r   out (overwritten), any strides:
  *                   dA = scale * xt @ (dy @ lora_B).
+ *   dx and dA each float32, or bfloat16 with bfloat16 inputs (the page's
+ *   wrapper takes a dtype for its outputs): a bfloat16 element is the float32
+ *   result rounded once to the nearest bfloat16 (ties to even).
+ *   LORA_ERR_DTYPE for a bfloat16 output with float32 inputs.
  *   1 <= r <= 128; workspace of lora_workspace_bytes(LORA_OP_BWD_DX_DA, ...).
  */
 int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_B, const lora_mat* lora_A,
@@ -223,7 +227,8 @@ int lora_bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lora_
  * buffer; a training step usually adds the adapter's input gradient to the
  * base layer's, which this does without a separate add over M x K):
  *   dx += scale * (dy @ lora_B) @ lora_A, every element read once and written
- *   once (float32 add of the float32 product); dA is overwritten as in
+ *   once (float32 add of the float32 product; in a bfloat16 dx the float32
+ *   sum rounded once); dA is overwritten as in
  *   lora_bwd_dx_da. Same arguments, layouts, workspace and errors; with M or
  *   L zero dx is left unchanged and dA set to zero.
  */
@@ -237,8 +242,9 @@ int lora_bwd_dx_da_accumulate(const lora_mat* xt, const lora_mat* dy, const lora
  *   lora_A  r x K   any strides.
  *   xt      K x M   input transposed (stride_row 1, as for lora_bwd_dx_da).
  *   dy      M x L   output gradient (stride_col 1, as for lora_bwd_dx_da).
- *   dB      r x L   float32 out (overwritten), any strides:
- *                   dB = scale * (lora_A @ xt) @ dy.
+ *   dB      r x L   out (overwritten), any strides:
+ *                   dB = scale * (lora_A @ xt) @ dy. float32, or bfloat16
+ *                   with bfloat16 inputs (rounded once, as for dA).
  *   1 <= r <= 128; workspace of lora_workspace_bytes(LORA_OP_BWD_DB, ...).
  */
 int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lora_mat* dy, float scale, const lora_mat* dB,

@@ -98,12 +98,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ out, int64_t rows, int64_t cols,
-                                                        int64_t s_r, int64_t s_c) {
+// E: float (float32 zero) or uint16_t (bfloat16 zero: all bits clear)
+template <class E>
+__global__ __launch_bounds__(256) void fill_zero_kernel(E* __restrict__ out, int64_t rows, int64_t cols, int64_t s_r,
+                                                        int64_t s_c) {
   const int64_t total = rows * cols;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
     const int64_t i = idx / cols;
-    out[i * s_r + (idx - i * cols) * s_c] = 0.0f;
+    out[i * s_r + (idx - i * cols) * s_c] = E(0);
   }
 }
 
@@ -111,10 +113,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ out,
 // A thread takes V adjacent j of one n (V = 4: 16-byte loads; rp is a
 // multiple of 16 and the partials are 256-byte aligned). Loads are issued 16
 // partials at a time; the adds keep the p order, so both widths give the
-// same bits.
-template <int V>
+// same bits. OT: float, or uint16_t for a bfloat16 output (the float32 sum
+// rounded once, to nearest even).
+template <int V, class OT>
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int P, int64_t N, int rp, int r,
-                                                     float* __restrict__ out, int64_t os_n, int64_t os_j) {
+                                                     OT* __restrict__ out, int64_t os_n, int64_t os_j) {
   typedef float vec_t __attribute__((ext_vector_type(V)));
   const int per_n = rp / V;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -138,8 +141,14 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
       if (pp + e < P) s = (pp + e == 0) ? v[e] : s + v[e];
   }
 #pragma unroll
-  for (int e = 0; e < V; ++e)
-    if (j + e < r) out[n * os_n + (j + e) * os_j] = s[e];
+  for (int e = 0; e < V; ++e) {
+    if (j + e < r) {
+      if constexpr (sizeof(OT) == 2)
+        out[n * os_n + (j + e) * os_j] = static_cast<uint16_t>(bf16_bits(s[e]));
+      else
+        out[n * os_n + (j + e) * os_j] = s[e];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -456,6 +465,10 @@ struct OutAdd {
 struct OutAddBF16 {
   using T = uint16_t;
   static constexpr bool ACCUM = true;
+};
+struct OutSetBF16 {  // bfloat16 dX, overwritten (the float32 product rounded once)
+  using T = uint16_t;
+  static constexpr bool ACCUM = false;
 };
 
 // ---- expand of one token tile over all output columns ----------------------
@@ -1368,6 +1381,29 @@ static void dispatch8(int rb, int bmb, A&&... args) {
   }
 }
 
+// The (rank blocks, token blocks) pairs plan_single gives dX: fused
+// kernel (16-token tiles, 32 at one rank block) and column-band expand
+// (32-token tiles, 16 at eight rank blocks); only these are instantiated.
+template <template <int, int> class L, class... A>
+static void dispatch_dx_fused(int rb, int bmb, A&&... args) {
+  switch (rb * 10 + bmb) {
+    case 11: L<1, 1>::run(args...); break;
+    case 12: L<1, 2>::run(args...); break;
+    case 21: L<2, 1>::run(args...); break;
+    case 41: L<4, 1>::run(args...); break;
+    default: L<8, 1>::run(args...); break;  // rb 8
+  }
+}
+template <template <int, int> class L, class... A>
+static void dispatch_dx_band(int rb, A&&... args) {
+  switch (rb) {
+    case 1: L<1, 2>::run(args...); break;
+    case 2: L<2, 2>::run(args...); break;
+    case 4: L<4, 2>::run(args...); break;
+    default: L<8, 1>::run(args...); break;
+  }
+}
+
 template <class Tag, class OM, bool EMIT_G, bool WT>
 struct FusedNW {
   template <int RB, int BMB>
@@ -1442,12 +1478,12 @@ struct BandTnRB {
 template <class Tag, class OM, bool WT>
 static void run_dx_da(FusedArgs a, TnArgs t, const SinglePlan& pl, int rb, hipStream_t st) {
   if (pl.fused) {
-    dispatch8<FusedNW<Tag, OM, true, WT>::template L>(rb, pl.bmb, a, st);
+    dispatch_dx_fused<FusedNW<Tag, OM, true, WT>::template L>(rb, pl.bmb, a, st);
     launch_tn<Tag>(t, rb, 4, st);
     return;
   }
   launch_shrink<Tag, true, true, WT>(a, rb, pl.bmb_shrink, st);
-  dispatch8<BandTnRB<Tag, OM, WT>::template L>(rb, pl.bmb, a, t, st);
+  dispatch_dx_band<BandTnRB<Tag, OM, WT>::template L>(rb, a, t, st);
 }
 
 
@@ -1493,23 +1529,37 @@ static void launch_fill_zero(const lora_mat* m, hipStream_t st) {
   if (total <= 0) return;
   int64_t blocks = ceil_div(total, 256);
   if (blocks > 8192) blocks = 8192;
-  launch(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                     static_cast<float*>(m->ptr), m->rows, m->cols, m->stride_row, m->stride_col);
+  if (m->dtype == LORA_BF16)
+    launch(fill_zero_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+           static_cast<uint16_t*>(m->ptr), m->rows, m->cols, m->stride_row, m->stride_col);
+  else
+    launch(fill_zero_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, static_cast<float*>(m->ptr),
+           m->rows, m->cols, m->stride_row, m->stride_col);
 }
 
-static void launch_reduce(const float* part, int P, int64_t N, int rp, int r, float* out, int64_t os_n, int64_t os_j,
-                          hipStream_t st) {
-  if (N * r <= 0) return;
+template <class OT>
+static void launch_reduce_t(const float* part, int P, int64_t N, int rp, int r, OT* out, int64_t os_n, int64_t os_j,
+                            hipStream_t st) {
   // 16-byte loads while that keeps >= 256 workgroups (the 16384 x 14336 dB
   // call: 146 -> 140 us); fewer, longer threads measured slower at 8192 x
   // 4096, rank 16 (64 workgroups: +1.5 us per call)
   const int64_t wide = N * (rp / 4);
   if (wide >= 256 * 256)
-    launch(reduce_kernel<4>, dim3(static_cast<unsigned>(ceil_div(wide, 256))), dim3(256), 0, st, part, P, N, rp, r,
-           out, os_n, os_j);
-  else
-    launch(reduce_kernel<1>, dim3(static_cast<unsigned>(ceil_div(N * rp, 256))), dim3(256), 0, st, part, P, N, rp,
+    launch(reduce_kernel<4, OT>, dim3(static_cast<unsigned>(ceil_div(wide, 256))), dim3(256), 0, st, part, P, N, rp,
            r, out, os_n, os_j);
+  else
+    launch(reduce_kernel<1, OT>, dim3(static_cast<unsigned>(ceil_div(N * rp, 256))), dim3(256), 0, st, part, P, N,
+           rp, r, out, os_n, os_j);
+}
+
+// The fixed-order sum of the P partials into out (float32 or bfloat16).
+static void launch_reduce(const float* part, int P, int64_t N, int rp, int r, const lora_mat* out, int64_t os_n,
+                          int64_t os_j, hipStream_t st) {
+  if (N * r <= 0) return;
+  if (out->dtype == LORA_BF16)
+    launch_reduce_t(part, P, N, rp, r, static_cast<uint16_t*>(out->ptr), os_n, os_j, st);
+  else
+    launch_reduce_t(part, P, N, rp, r, static_cast<float*>(out->ptr), os_n, os_j, st);
 }
 
 // Buffer descriptors address with 32-bit byte offsets: every range one
@@ -1772,8 +1822,10 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   if (dy->rows != M || lora_B->rows != L || lora_A->rows != r || lora_A->cols != K || dx->rows != M ||
       dx->cols != K || dA->rows != K || dA->cols != r)
     return LORA_ERR_SHAPE;
+  // outputs in float32, or in bfloat16 with bfloat16 inputs
+  auto out_ok = [&](int32_t d) { return d == LORA_F32 || (d == LORA_BF16 && xt->dtype == LORA_BF16); };
   if (!float_dtype_ok(xt->dtype) || dy->dtype != xt->dtype || lora_B->dtype != xt->dtype ||
-      lora_A->dtype != xt->dtype || dx->dtype != LORA_F32 || dA->dtype != LORA_F32)
+      lora_A->dtype != xt->dtype || !out_ok(dx->dtype) || !out_ok(dA->dtype))
     return LORA_ERR_DTYPE;
   if (r < 1 || r > 128) return LORA_ERR_RANK;
   if ((K * M > 0 && !xt->ptr) || (M * L > 0 && !dy->ptr) || (L * r > 0 && !lora_B->ptr) ||
@@ -1804,10 +1856,11 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   const int rb = rank_blocks(static_cast<int>(r));
   const int64_t rp = 16 * rb;
   const size_t es = elem_size(xt->dtype);
-  const SinglePlan plan = plan_single(false, M, L, K, rb, 4);
+  const size_t oes = elem_size(dx->dtype);
+  const SinglePlan plan = plan_single(false, M, L, K, rb, static_cast<int64_t>(oes));
   const int64_t chunk = tn_plan(M, K, false, !plan.fused).chunk;
-  if (!fused_fits(dy->stride_row, es, r, L, K, rp, dx->stride_row) || !fits32(chunk * xt->stride_col * (int64_t)es) ||
-      !fits32((int64_t)lay.g))
+  if (!fused_fits(dy->stride_row, es, r, L, K, rp, dx->stride_row, oes) ||
+      !fits32(chunk * xt->stride_col * (int64_t)es) || !fits32((int64_t)lay.g))
     return LORA_ERR_LIMIT;
   // The kernels take W1 = B^T (r rows over the L outputs) and W2 = A^T (K rows
   // over the r ranks). bf16 weights in the nn.Linear layouts (lora_B L x r and
@@ -1858,7 +1911,19 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
   t.rp = static_cast<int>(rp);
   t.chunk = chunk;
   const int P = static_cast<int>(ceil_div(M, t.chunk));
-  if (xt->dtype == LORA_BF16) {
+  if (dx->dtype == LORA_BF16) {
+    if (in_place) {
+      if (accumulate)
+        run_dx_da<BF16, OutAddBF16, true>(a, t, plan, rb, st);
+      else
+        run_dx_da<BF16, OutSetBF16, true>(a, t, plan, rb, st);
+    } else {
+      if (accumulate)
+        run_dx_da<BF16, OutAddBF16, false>(a, t, plan, rb, st);
+      else
+        run_dx_da<BF16, OutSetBF16, false>(a, t, plan, rb, st);
+    }
+  } else if (xt->dtype == LORA_BF16) {
     if (in_place) {
       if (accumulate)
         run_dx_da<BF16, OutAdd, true>(a, t, plan, rb, st);
@@ -1876,7 +1941,7 @@ static int bwd_dx_da(const lora_mat* xt, const lora_mat* dy, const lora_mat* lor
     else
       run_dx_da<F32, OutSet, false>(a, t, plan, rb, st);
   }
-  launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dA->ptr), dA->stride_row,
+  launch_reduce(part, P, K, static_cast<int>(rp), static_cast<int>(r), dA, dA->stride_row,
                 dA->stride_col, st);
   return launch_status();
 }
@@ -1899,8 +1964,9 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
   if (!valid_dims(lora_A) || !valid_dims(xt) || !valid_dims(dy) || !valid_dims(dB)) return LORA_ERR_SHAPE;
   const int64_t r = lora_A->rows, K = lora_A->cols, M = xt->cols, L = dy->cols;
   if (xt->rows != K || dy->rows != M || dB->rows != r || dB->cols != L) return LORA_ERR_SHAPE;
+  // dB in float32, or in bfloat16 with bfloat16 inputs
   if (!float_dtype_ok(lora_A->dtype) || xt->dtype != lora_A->dtype || dy->dtype != lora_A->dtype ||
-      dB->dtype != LORA_F32)
+      !(dB->dtype == LORA_F32 || (dB->dtype == LORA_BF16 && xt->dtype == LORA_BF16)))
     return LORA_ERR_DTYPE;
   if (r < 1 || r > 128) return LORA_ERR_RANK;
   if ((r * K > 0 && !lora_A->ptr) || (K * M > 0 && !xt->ptr) || (M * L > 0 && !dy->ptr) || (r * L > 0 && !dB->ptr))
@@ -1974,7 +2040,7 @@ extern "C" int lora_bwd_db(const lora_mat* lora_A, const lora_mat* xt, const lor
     launch_tn<F32>(t, rb, tp.nw, st);
   }
   // dB is r x L: partial row n = l, column j.
-  launch_reduce(part, P, L, static_cast<int>(rp), static_cast<int>(r), static_cast<float*>(dB->ptr), dB->stride_col,
+  launch_reduce(part, P, L, static_cast<int>(rp), static_cast<int>(r), dB, dB->stride_col,
                 dB->stride_row, st);
   return launch_status();
 }

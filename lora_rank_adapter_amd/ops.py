@@ -84,18 +84,19 @@ def lora_fwd(x: torch.Tensor, lora_A: torch.Tensor, lora_B: torch.Tensor, res: t
 
 def lora_bwd_dx_da(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lora_A: torch.Tensor, scale: float,
                    dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
-                   workspace: torch.Tensor | None = None):
+                   workspace: torch.Tensor | None = None, dtype: torch.dtype = torch.float32):
     """dx = scale * (dy @ lora_B) @ lora_A; dA = scale * xt @ (dy @ lora_B).
     xt: K x M (transposed view of row-major x), dy: M x L, lora_B: L x r, lora_A: r x K.
-    Returns (dx [M x K], dA [K x r]), float32."""
+    Returns (dx [M x K], dA [K x r]): the given tensors, else new ones of `dtype` (float32, or bfloat16 with
+    bfloat16 inputs: the float32 result rounded once)."""
     lib = _lib.load()
     K, M = xt.shape
     L = dy.shape[1]
     r = lora_B.shape[1]
     if dx is None:
-        dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+        dx = torch.empty((M, K), dtype=dtype, device=dy.device)
     if dA is None:
-        dA = torch.empty((K, r), dtype=torch.float32, device=dy.device)
+        dA = torch.empty((K, r), dtype=dtype, device=dy.device)
     ws, nbytes = _workspace(_lib.LORA_OP_BWD_DX_DA, M, K, L, r, dy.dtype, dy.device, workspace)
     check("lora_bwd_dx_da", lib.lora_bwd_dx_da(
         ctypes.byref(mat(xt)), ctypes.byref(mat(dy)), ctypes.byref(mat(lora_B)), ctypes.byref(mat(lora_A)),
@@ -105,16 +106,16 @@ def lora_bwd_dx_da(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lor
 
 def lora_bwd_dx_da_accumulate(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.Tensor, lora_A: torch.Tensor,
                               scale: float, dx: torch.Tensor, dA: torch.Tensor | None = None,
-                              workspace: torch.Tensor | None = None):
-    """dx += scale * (dy @ lora_B) @ lora_A (dx: M x K float32, added to in
-    place); dA = scale * xt @ (dy @ lora_B) as in lora_bwd_dx_da.
+                              workspace: torch.Tensor | None = None, dtype: torch.dtype = torch.float32):
+    """dx += scale * (dy @ lora_B) @ lora_A (dx: M x K float32, or bfloat16 with bfloat16 inputs, added to
+    in place); dA = scale * xt @ (dy @ lora_B) as in lora_bwd_dx_da (new of `dtype` when not given).
     Returns (dx, dA)."""
     lib = _lib.load()
     K, M = xt.shape
     L = dy.shape[1]
     r = lora_B.shape[1]
     if dA is None:
-        dA = torch.empty((K, r), dtype=torch.float32, device=dy.device)
+        dA = torch.empty((K, r), dtype=dtype, device=dy.device)
     ws, nbytes = _workspace(_lib.LORA_OP_BWD_DX_DA, M, K, L, r, dy.dtype, dy.device, workspace)
     check("lora_bwd_dx_da_accumulate", lib.lora_bwd_dx_da_accumulate(
         ctypes.byref(mat(xt)), ctypes.byref(mat(dy)), ctypes.byref(mat(lora_B)), ctypes.byref(mat(lora_A)),
@@ -123,14 +124,16 @@ def lora_bwd_dx_da_accumulate(xt: torch.Tensor, dy: torch.Tensor, lora_B: torch.
 
 
 def lora_bwd_db(lora_A: torch.Tensor, xt: torch.Tensor, dy: torch.Tensor, scale: float,
-                dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """dB = scale * (lora_A @ xt) @ dy.  lora_A: r x K, xt: K x M, dy: M x L. Returns dB [r x L] float32."""
+                dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """dB = scale * (lora_A @ xt) @ dy.  lora_A: r x K, xt: K x M, dy: M x L. Returns dB [r x L]: the given
+    tensor, else a new one of `dtype` (float32, or bfloat16 with bfloat16 inputs)."""
     lib = _lib.load()
     r, K = lora_A.shape
     M = xt.shape[1]
     L = dy.shape[1]
     if dB is None:
-        dB = torch.empty((r, L), dtype=torch.float32, device=dy.device)
+        dB = torch.empty((r, L), dtype=dtype, device=dy.device)
     ws, nbytes = _workspace(_lib.LORA_OP_BWD_DB, M, K, L, r, dy.dtype, dy.device, workspace)
     check("lora_bwd_db", lib.lora_bwd_db(ctypes.byref(mat(lora_A)), ctypes.byref(mat(xt)), ctypes.byref(mat(dy)),
                                          float(scale), ctypes.byref(mat(dB)), _ptr(ws), nbytes, _stream(dy.device)))

@@ -139,8 +139,11 @@ def test_bwd_validation(lib):
         assert dxda(ws=FAKE + 64) == -6                       # workspace must be 256-byte aligned
         assert dxda(xt_=m(K, M)) == -4                        # xt must be a view of row-major x
         assert dxda(dy_=m(M, L_ + 8)) == -2
-        assert dxda(dA_=m(K, r, dtype=1)) == -3
-        assert dxda(dx_=m(M, K, dtype=1)) == -3               # dx is float32 (read and written when accumulating)
+        # bfloat16 outputs need bfloat16 inputs
+        xt32, dy32, B32, A32 = m(K, M, dtype=0, sr=1, sc=K), m(M, L_, dtype=0), m(L_, r, dtype=0), m(r, K, dtype=0)
+        assert dxda(xt_=xt32, dy_=dy32, B_=B32, A_=A32, dA_=m(K, r, dtype=1)) == -3
+        assert dxda(xt_=xt32, dy_=dy32, B_=B32, A_=A32, dx_=m(M, K, dtype=1)) == -3
+        assert dxda(dx_=m(M, K, dtype=7)) == -3
         assert dxda(B_=m(L_, 200), A_=m(200, K)) == -2         # dA shape disagrees with rank 200
         assert dxda(B_=m(L_, 0), A_=m(0, K), dA_=m(K, 0, dtype=0)) == -5
 
@@ -150,6 +153,9 @@ def test_bwd_validation(lib):
 
     assert db(ws=0) == -6
     assert db(dB_=m(r, L_ + 4, dtype=0)) == -2
+    assert db(A_=m(r, K, dtype=0), xt_=m(K, M, dtype=0, sr=1, sc=K), dy_=m(M, L_, dtype=0),
+              dB_=m(r, L_, dtype=1)) == -3                                 # bf16 dB needs bf16 inputs
+    assert db(dB_=m(r, L_, dtype=7)) == -3
     assert db(dy_=m(M, L_, sr=L_ + 1)) == -4
 
 

@@ -1,7 +1,9 @@
-"""bfloat16 outputs updated in place: the forward's Y (lora_fwd with a
-bfloat16 res, the dtype argument of the NeMo lora_forward_wrapper entry) and
-the multi-adapter y (lora_expand_fused and lora_apply_linear, the in-place y
-of the M* LoraOpsBackend.expand_fused entry).
+"""bfloat16 outputs: the forward's Y (lora_fwd with a bfloat16 res, the
+dtype argument of the NeMo lora_forward_wrapper entry) and the multi-adapter
+y (lora_expand_fused and lora_apply_linear, the in-place y of the M*
+LoraOpsBackend.expand_fused entry), updated in place; the backward's dX
+(overwritten or accumulated), dA and dB (the dtype of the NeMo
+lora_da_dx_update_wrapper and lora_db_update_wrapper outputs).
 
 The stored value is the exact result rounded once to the nearest bfloat16
 (oracle.round_to_bf16 of the float64 oracle). Integer inputs make the
@@ -20,7 +22,7 @@ import torch
 import lora_rank_adapter_amd as L
 import oracle
 import synth
-from tests.gpu_util import DEV, check_bf16_output, dev, f32, host_bf16, note
+from tests.gpu_util import DEV, check_bf16_output, dev, exactness_bounds, f32, host_bf16, note
 
 pytestmark = pytest.mark.gpu
 
@@ -204,3 +206,80 @@ def test_expand_bf16_y_refuses_f32_weights():
     assert e.value.status == -3
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16(y), m.y0.astype(np.float64))
+
+
+# ---- single-adapter backward ----------------------------------------------
+
+# M, K, L, r, scale: the fused dX kernel (rank 16, 64) and the split schedule
+# (a contraction over 8200 outputs: band expand beside dA's partials, dB's
+# 8-wave weight-gradient workgroups)
+BWD_SHAPES = {
+    "fused-r16": (96, 256, 264, 16, 2.0),
+    "fused-r64": (300, 512, 520, 64, 0.5),
+    "split-r64": (130, 264, 8200, 64, 0.5),
+    "split-r128": (200, 512, 8200, 128, 1.0),
+}
+BWD_DENSITY = (1.0 / 8, 1.0 / 4, 1.0 / 4, 1.0 / 8)
+
+
+@pytest.mark.parametrize("kind", ["normal", "exact"])
+@pytest.mark.parametrize("shape", sorted(BWD_SHAPES))
+def test_bwd_bf16_outputs(shape, kind):
+    """dX (overwritten and accumulated into a bfloat16 base), dA and dB in
+    bfloat16 (the dtype of the NeMo lora_da_dx_update_wrapper and
+    lora_db_update_wrapper outputs): each element the float32 result rounded
+    once."""
+    M, K, N, r, s = BWD_SHAPES[shape]
+    note(f"bf16 backward outputs {shape} {kind}")
+    c = synth.single_adapter(M, K, N, r, seed=60 + r, dtype="bf16", scale=s, int_exact=kind == "exact",
+                             density=BWD_DENSITY if kind == "exact" else None)
+    if kind == "exact":
+        # every float32 partial sum exact (checked before the GPU runs)
+        b = exactness_bounds(c)
+        assert b["dyb"] < 2 ** 15 and max(b["dx"], b["dA"], b["dB"]) < 2 ** 20, b
+    X = dev(c.X, "bf16")
+    dY = dev(c.dY, "bf16")
+    A_w = dev(np.ascontiguousarray(c.A.T), "bf16")   # lora_A weight, r x K
+    B_w = dev(np.ascontiguousarray(c.B.T), "bf16")   # lora_B weight, L x r
+    rng = np.random.default_rng(7)
+    base = synth.round_bf16(rng.integers(-3, 4, (M, K)).astype(np.float32) if kind == "exact"
+                            else rng.standard_normal((M, K)).astype(np.float32))
+    dx, dA = L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s, dtype=torch.bfloat16)
+    dB = L.lora_bwd_db(A_w, X.t(), dY, s, dtype=torch.bfloat16)
+    dxa = dev(base, "bf16")
+    L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dxa, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert dx.dtype == dA.dtype == dB.dtype == torch.bfloat16
+    odx, odA = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    odB = oracle.lora_bwd_db(c.A.T, c.X.T, c.dY, s)
+    cases = [("dX", host_bf16(dx), odx), ("dA", host_bf16(dA), odA), ("dB", host_bf16(dB), odB),
+             ("dX accumulated", host_bf16(dxa), base.astype(np.float64) + odx)]
+    if kind == "exact":
+        for name, got, exact in cases:
+            assert np.array_equal(got, oracle.round_to_bf16(exact)), f"{name}: one rounding of an exact float32 value"
+        return
+    aX, adY, aA, aB = np.abs(c.X), np.abs(c.dY), np.abs(c.A), np.abs(c.B)
+    mdx, mdA = oracle.lora_bwd_dx_da(aX.T, adY, aB.T, aA.T, abs(s))
+    mdB = oracle.lora_bwd_db(aA.T, aX.T, adY, abs(s))
+    mags = [mdx, mdA, mdB, np.abs(base).astype(np.float64) + mdx]
+    for (name, got, exact), mag in zip(cases, mags):
+        check_bf16_output(got, exact, oracle.round_to_bf16(exact), mag, name)
+        assert oracle.rel_frobenius(got, exact) <= 2e-3, name
+
+
+def test_bwd_bf16_outputs_refuse_f32_inputs():
+    """bfloat16 backward outputs need bfloat16 inputs: LORA_ERR_DTYPE."""
+    note("bf16 backward outputs with f32 inputs")
+    M, K, N, r = 32, 64, 64, 8
+    xt = torch.zeros((M, K), device=DEV).t()
+    dy = torch.zeros((M, N), device=DEV)
+    Bw = torch.zeros((N, r), device=DEV)
+    Aw = torch.zeros((r, K), device=DEV)
+    for kw in ({"dx": torch.zeros((M, K), device=DEV, dtype=torch.bfloat16)},
+               {"dA": torch.zeros((K, r), device=DEV, dtype=torch.bfloat16)}):
+        with pytest.raises(L.LoraError) as e:
+            L.lora_bwd_dx_da(xt, dy, Bw, Aw, 1.0, **kw)
+        assert e.value.status == -3
+    with pytest.raises(L.LoraError) as e:
+        L.lora_bwd_db(Aw, xt, dy, 1.0, dtype=torch.bfloat16)
+    assert e.value.status == -3
