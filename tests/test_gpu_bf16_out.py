@@ -214,6 +214,7 @@ def test_expand_bf16_y_refuses_f32_weights():
 # (a contraction over 8200 outputs: band expand beside dA's partials, dB's
 # 8-wave weight-gradient workgroups)
 BWD_SHAPES = {
+    "fused-r20-packed": (150, 256, 264, 20, 1.0),   # rank not a multiple of 8: weights packed first
     "fused-r16": (96, 256, 264, 16, 2.0),
     "fused-r64": (300, 512, 520, 64, 0.5),
     "split-r64": (130, 264, 8200, 64, 0.5),
@@ -283,3 +284,24 @@ def test_bwd_bf16_outputs_refuse_f32_inputs():
     with pytest.raises(L.LoraError) as e:
         L.lora_bwd_db(Aw, xt, dy, 1.0, dtype=torch.bfloat16)
     assert e.value.status == -3
+
+
+def test_bwd_bf16_dx_padded_rows():
+    """A bfloat16 dX with padded rows (row stride K + 8): the padding columns
+    keep their bits, overwritten and accumulated; integer inputs, exact."""
+    M, K, N, r, s = 130, 256, 264, 16, 2.0
+    note("bf16 dX with padded rows")
+    c = synth.single_adapter(M, K, N, r, seed=66, dtype="bf16", scale=s, int_exact=True, density=BWD_DENSITY)
+    X, dY = dev(c.X, "bf16"), dev(c.dY, "bf16")
+    A_w = dev(np.ascontiguousarray(c.A.T), "bf16")
+    B_w = dev(np.ascontiguousarray(c.B.T), "bf16")
+    store = dev(np.full((M, K + 8), 7.0, np.float32), "bf16")
+    dx = store[:, :K]
+    L.lora_bwd_dx_da(X.t(), dY, B_w, A_w, s, dx=dx, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    odx, _ = oracle.lora_bwd_dx_da(c.X.T, c.dY, c.B.T, c.A.T, s)
+    assert np.array_equal(host_bf16(dx), oracle.round_to_bf16(odx))
+    L.lora_bwd_dx_da_accumulate(X.t(), dY, B_w, A_w, s, dx, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(dx), oracle.round_to_bf16(oracle.round_to_bf16(odx) + odx))
+    assert (host_bf16(store)[:, K:] == 7.0).all(), "padding columns were written"
