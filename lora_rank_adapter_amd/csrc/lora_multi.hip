@@ -1638,35 +1638,48 @@ static int check_addressing(const lora_addressing* addr, const int32_t* ranks) {
 
 static int tile_bmb(int T) { return T >= 1024 ? 4 : 1; }
 
+// Token tiles of the per-tile shrinks (16 tokens: bmb 1, or 64: bmb 4). A
+// workgroup streams its tile's x rows and its rank block's adapter rows over
+// the whole feature axis, and a CU streams only so fast, so the time follows
+// the busiest CU: rounds of 256 workgroups times rows per workgroup, with the
+// tokens taken as spread evenly over the S slots. Ties go to 16-token tiles.
+// Measured (bf16, K 4096, slices 4096 + 1024 + 1024, ranks 0-64, four rank
+// blocks per workgroup, us for 16- / 64-token tiles): 16 slots at 512 / 768 /
+// 1024 tokens 14.8 / 22.5, 15.6 / 24.5, -; 32 slots at 1024 / 1152 / 1536
+// tokens 16.5 / 23.0, 26.3 / 23.1, 26.8 / 25.1; 64 slots at 2048 / 3072 29.8 /
+// 24.9, 36.8 / 29.3; 128 slots at 1024 / 2048 / 4096 / 5120 / 6144 30.4 /
+// 36.0, 32.4 / 37.5, 42.1 / 42.1, 48.2 / 44.9, 55.4 / 46.0 (4608 tokens, the
+// one miss: 42.3 / 43.2).
+static int shrink_tile_bmb(int64_t T, int64_t S, int n_slices, int64_t row_chunks, int64_t a_rows) {
+  if (T < 1024 || S < 1) return 1;
+  auto cost = [&](int64_t bmb) {
+    const int64_t wgs = S * ceil_div(T, 16 * bmb * S) * n_slices * row_chunks;
+    return ceil_div(wgs, 256) * (16 * bmb + a_rows);
+  };
+  return cost(4) < cost(1) ? 4 : 1;
+}
+
+// 64-token tiles (bmb 4) come only with four rank blocks (rb 4): both are
+// taken from 1024 tokens, rb 4 from 512.
 template <class Tag>
 static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, bool pipe, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
   if (pipe) {
     const dim3 pgrid(static_cast<unsigned>(round_up(tiles, 8 * kShrinkGroup) * a.n_slices * a.row_chunks));
-    if (bmb == 4) {
-      if (rb == 4)
-        launch((slot_shrink_pipe_kernel<Tag, 4, 4, 2>), pgrid, dim3(256), 0, st, a);
-      else
-        launch((slot_shrink_pipe_kernel<Tag, 4, 1, 2>), pgrid, dim3(256), 0, st, a);
-    } else {
-      if (rb == 4)
-        launch((slot_shrink_pipe_kernel<Tag, 1, 4, 2>), pgrid, dim3(256), 0, st, a);
-      else
-        launch((slot_shrink_pipe_kernel<Tag, 1, 1, 4>), pgrid, dim3(256), 0, st, a);
-    }
+    if (bmb == 4)
+      launch((slot_shrink_pipe_kernel<Tag, 4, 4, 2>), pgrid, dim3(256), 0, st, a);
+    else if (rb == 4)
+      launch((slot_shrink_pipe_kernel<Tag, 1, 4, 2>), pgrid, dim3(256), 0, st, a);
+    else
+      launch((slot_shrink_pipe_kernel<Tag, 1, 1, 4>), pgrid, dim3(256), 0, st, a);
     return;
   }
-  if (bmb == 4) {
-    if (rb == 4)
-      launch((slot_shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
-    else
-      launch((slot_shrink_kernel<Tag, 4, 1>), grid, dim3(256), 0, st, a);
-  } else {
-    if (rb == 4)
-      launch((slot_shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
-    else
-      launch((slot_shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
-  }
+  if (bmb == 4)
+    launch((slot_shrink_kernel<Tag, 4, 4>), grid, dim3(256), 0, st, a);
+  else if (rb == 4)
+    launch((slot_shrink_kernel<Tag, 1, 4>), grid, dim3(256), 0, st, a);
+  else
+    launch((slot_shrink_kernel<Tag, 1, 1>), grid, dim3(256), 0, st, a);
 }
 
 template <class Tag, class YT, int BMB>
@@ -1753,24 +1766,23 @@ static void launch_apply(const ShrinkArgs& ps, const ExpandArgs& pe, int rbm, in
 // launches are faster. A one-launch workgroup streams its slice's whole
 // adapter rows through one CU, so the form only pays while every workgroup
 // gets a CU of its own: at least kApplyMinTokens tokens, and token tiles times
-// column chunks within the CU count, the tiles estimated as if the tokens
-// spread evenly over the S slots; the narrowest chunk that fits is taken.
+// 1024-column chunks within the CU count, the tiles estimated as if the tokens
+// spread evenly over the S slots.
 // Measured (bf16, K 4096, slices 4096 + 1024 + 1024, ranks 0-64; two launches
-// against one): 32 slots at 256 tokens 25.9 / 26.9 us (1024 columns), 512:
-// 33.6 / 29.9 (1024), 768: 40.1 / 38.8 (2048), 1024: 46.5 / 39.9 (2048);
-// 1536 and more tokens, or 128 slots at 512 to 2048 tokens, are a tie or
-// slower whatever the chunk (1024, 1536, 2048 or 4096 columns).
+// against one): 32 slots at 256 tokens 25.9 / 26.9 us, 512: 31.3 / 29.4
+// (1024 columns); 640 / 768 / 896 / 1024 tokens, where only 2048-column
+// chunks fit: 32.7 / 39.3, 32.2 / 39.2, 34.0 / 40.3, 34.9 / 39.7 us; 1536 and
+// more tokens, or 128 slots at 512 to 2048 tokens, are a tie or slower
+// whatever the chunk (1024, 1536, 2048 or 4096 columns).
 constexpr int64_t kApplyMinTokens = 512;
 constexpr int64_t kApplyMaxWorkgroups = 256;
+constexpr int64_t kApplyCols = 1024;
 static int64_t apply_one_launch_cols(int64_t T, int64_t S, const int64_t* out_slices, int32_t num_slices) {
   if (T < kApplyMinTokens || S < 1) return 0;
   const int64_t tiles = S * ceil_div(T, 16 * S);
-  for (int64_t cols : {int64_t(1024), int64_t(2048)}) {
-    int64_t chunks = 0;
-    for (int i = 0; i < num_slices; ++i) chunks += ceil_div(out_slices[i], cols);
-    if (tiles * chunks <= kApplyMaxWorkgroups) return cols;
-  }
-  return 0;
+  int64_t chunks = 0;
+  for (int i = 0; i < num_slices; ++i) chunks += ceil_div(out_slices[i], kApplyCols);
+  return tiles * chunks <= kApplyMaxWorkgroups ? kApplyCols : 0;
 }
 
 // Device address of `scratch` on the current device, looked up on the first
@@ -1885,11 +1897,14 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   if (rc != LORA_OK) return rc;
   const int64_t T = addr->T, S = addr->S;
   if (T == 0 || S == 0) return LORA_OK;
-  const int bmb = tile_bmb(static_cast<int>(T));
-  const int rb = (T >= 1024) ? 4 : 1;
-  const int64_t tiles = ceil_div(T, 16 * bmb) + S;
+  // four 16-row rank blocks per workgroup from 512 tokens (32 slots at 512 /
+  // 1024 tokens: 16.9 / 16.5 us against 17.3 / 27.8 us with one; at 256
+  // tokens one block is faster, 12.3 against 15.9 us)
+  const int rb = (T >= 512) ? 4 : 1;
   ShrinkArgs p = shrink_args(x, a, addr, ranks, num_slices, r_max, h);
   p.row_chunks = static_cast<int>(ceil_div(r_max, 16 * rb));
+  const int bmb = shrink_tile_bmb(T, S, num_slices, p.row_chunks, std::min<int64_t>(16 * rb, round_up(r_max, 16)));
+  const int64_t tiles = ceil_div(T, 16 * bmb) + S;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Schedule, from the shapes: the row-split kernel for bf16 batches of 1024
   // tokens or more whose grid fills the chip twice (at least 512 workgroups,
@@ -1898,7 +1913,7 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   // adapter spans more than a 2 GiB descriptor.
   // Measured with bf16 inputs, K 4096, slices 4096 + 1024 + 1024, ranks up
   // to 64, tokens spread evenly over the slots: 32 slots at 1024 / 2048 /
-  // 4096 / 8192 tokens take 23 / 27 / 27 / 48 us pipelined against 54 / 62 /
+  // 4096 / 8192 tokens take 17 / 27 / 27 / 48 us pipelined against 54 / 62 /
   // 76 / 77 us row-split (grids of 128 to 192 workgroups); 128 slots at 8192
   // tokens 53 against 66 us. The prefill batch (16731 tokens in 46 requests,
   // K 8192, ranks up to 128, a grid of 864) takes 188 us row-split against

@@ -102,7 +102,7 @@ MULTI = {
     "decode-stream": (200, 256, (128, 64, 64), 9, 40, (0, 3, 17, 40), 0.1),       # streaming expand
     "band": (0, 256, (256, 64, 64), 12, 64, (8, 16, 32, 64), 0.0),              # column-band expand (>= 512 tokens)
     "one-launch-r128": (640, 512, (1536, 256, 256), 16, 128, (0, 8, 100, 128), 0.1),   # one-launch apply_linear
-    "one-launch-2048": (1000, 256, (3000, 500, 500), 16, 64, (0, 16, 40, 64), 0.1),   # one launch, 2048-column chunks
+    "wide-two-launch": (1000, 256, (3000, 500, 500), 16, 64, (0, 16, 40, 64), 0.1),   # too wide for one launch
 }
 
 

@@ -39,9 +39,11 @@ CASES = [
 #             decode-mid, decode-wide, fp32-mid; one workgroup per 1024-token chunk: the others
 #             (and test_grouping_schedules_bitwise for every grouping kernel);
 #   shrink: row-split (bf16, >= 1024 tokens, a grid of >= 512 workgroups): prefill-many-slots;
-#           pipelined, 64-token tiles (>= 1024 tokens otherwise): prefill-like, prefill-long,
-#             fp32-prefill, decode-1k;
-#           pipelined, 16-token tiles (< 1024 tokens): the others;
+#           pipelined, 64-token tiles, four rank blocks (>= 1024 tokens where the busiest CU streams
+#             fewer rows so): prefill-like, prefill-long;
+#           pipelined, 16-token tiles, four rank blocks (>= 512 tokens otherwise): fp32-prefill,
+#             decode-mid, decode-wide, decode-1k, fp32-mid;
+#           pipelined, 16-token tiles, one rank block (< 512 tokens): the others;
 #           general (no buffer descriptors): test_shrink_general_kernel.
 #   expand: column band (>= 512 tokens; 256-token pieces at r_max 128, 64 below): prefill-like,
 #             prefill-long, fp32-prefill, prefill-many-slots, decode-mid, decode-wide, decode-1k, fp32-mid;
@@ -49,10 +51,10 @@ CASES = [
 #           general (rows of h not 16-byte aligned): test_expand_general_kernel.
 #   Every expand adds the MFMA chain of an element's rank blocks to y the same way, so all of them,
 #   and both forms of apply_linear, give the same bits.
-#   apply_linear: one launch, 1024-column chunks: decode-mid (rank 128, two slots' ranks
-#             outside [0, r_max]), decode-1k, fp32-mid; 2048-column chunks: decode-wide;
-#           shrink then expand: the others.
-ONE_LAUNCH = ("decode-mid", "decode-wide", "decode-1k", "fp32-mid")
+#   apply_linear: one launch (1024-column chunks): decode-mid (rank 128, two slots' ranks
+#             outside [0, r_max]), decode-1k, fp32-mid;
+#           shrink then expand: the others (decode-wide: a batch too wide for one launch).
+ONE_LAUNCH = ("decode-mid", "decode-1k", "fp32-mid")
 REQUESTS = {"prefill-like": 12, "fp32-prefill": 12, "prefill-long": 20, "prefill-many-slots": 16}
 
 
@@ -217,12 +219,15 @@ def _wide_stride_adapter(m, dtype):
     return store, a_dev
 
 
+@pytest.mark.parametrize("T", [203, 600, 2400])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_shrink_general_kernel(dtype):
+def test_shrink_general_kernel(dtype, T):
     """One slot's adapter rows spanning more than 2 GiB (a strided view): the
-    shrink without buffer descriptors, bit for bit on integer inputs."""
-    note(f"shrink general kernel {dtype}")
-    m = _case("ragged-ranks", 203, 64, (100, 28), 9, 40, (0, 3, 17, 40), 0.1, dtype, int_exact=True)
+    shrink without buffer descriptors, bit for bit on integer inputs, with
+    each of its tilings (203 tokens: 16-token tiles and one rank block; 600:
+    four rank blocks; 2400 over 9 slots: 64-token tiles)."""
+    note(f"shrink general kernel {dtype} T={T}")
+    m = _case("ragged-ranks", T, 64, (100, 28), 9, 40, (0, 3, 17, 40), 0.1, dtype, int_exact=True)
     addr, ranks = _addr(m)
     act, spec = _spec_mask(m)
     store, a_dev = _wide_stride_adapter(m, dtype)
@@ -340,12 +345,12 @@ def test_apply_linear(case):
     assert oracle.rel_frobenius(got[act] - m.y0[act], want[act] - m.y0[act]) <= tol(dtype)
 
 
-@pytest.mark.parametrize("name", list(ONE_LAUNCH) + ["decode-small", "prefill-like"])
+@pytest.mark.parametrize("name", list(ONE_LAUNCH) + ["decode-small", "decode-wide", "prefill-like"])
 def test_apply_linear_integer_exact(name):
     """lora_apply_linear bit for bit against the oracle on integer inputs:
-    the one-launch kernel (1024- and 2048-column chunks, ranks up to 128 and
-    clamped ones, bf16 and f32, fewer and more than 1024 tokens) and the
-    shrink-then-expand path; rows of inactive tokens untouched."""
+    the one-launch kernel (ranks up to 128 and clamped ones, bf16 and f32,
+    fewer and more than 1024 tokens) and the shrink-then-expand path; rows of
+    inactive tokens untouched."""
     case = next(c for c in CASES if c[0] == name)
     m = _case(*case, int_exact=True)
     dtype = case[-1]
