@@ -21,8 +21,8 @@
 //   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
 //                              descriptor loads and two register stages
 //   slot_shrink_rows_kernel    shrink for many tokens: a 128-token tile x up to
-//                              128 adapter rows per workgroup, x staged once in
-//                              LDS, waves split the rows
+//                              256 adapter rows per 8-wave workgroup, x staged
+//                              once in LDS, waves split the rows
 //   slot_expand_band_kernel    expand for 512 tokens or more: a token piece x
 //                              256-column band per workgroup, weights in
 //                              registers, h fragments shared through LDS,
@@ -778,11 +778,13 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
 }
 
 // Row-split shrink for bf16 inputs (x and one slot's a within 2 GiB
-// descriptors). A workgroup owns a tile of up to 128 grouped tokens of one
-// slot against up to 4*PPW (slice, 16-row rank block) pairs of its slices (a
-// slot with more pairs gets further row-group workgroups). Wave w takes pairs
-// w, w+4, ... of its row group over the whole feature axis, so no partial
-// sums are exchanged between waves.
+// descriptors). A workgroup of NW waves owns a tile of up to 128 grouped
+// tokens of one slot against up to NW*PPW (slice, 16-row rank block) pairs of
+// its slices (a slot with more pairs gets further row-group workgroups). Wave
+// w takes pairs w, w+NW, ... of its row group over the whole feature axis, so
+// no partial sums are exchanged between waves. One workgroup streams only so
+// fast (a lone 4-wave one about 28 GB/s), so 8 waves of two pairs each serve a
+// tile: 16 pairs per workgroup.
 // The tile's x rows are fetched once per stage of 32*U features by the whole
 // workgroup, row-linearly (each load instruction covers whole row segments),
 // into a double-buffered LDS tile with padded rows (every fragment read is
@@ -797,12 +799,12 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
 // so adapter and x rows are re-read from that XCD's L2.
 constexpr int kRowsGroup = 4;
 
-template <int TT, int U, int NP>
+template <int TT, int U, int NP, int NW>
 __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile& tl, int rho, rsrc_t rx, rsrc_t ra,
-                                                 const uint32_t (&xoff)[TT * U / 4], const bool (&bany)[TT],
+                                                 const uint32_t (&xoff)[TT * U / NW], const bool (&bany)[TT],
                                                  const int (&psl)[4], const int (&pj)[4],
                                                  const int* tok, char* lds, char* alds) {
-  constexpr int XV = TT * U / 4;     // x vectors per thread per stage
+  constexpr int XV = TT * U / NW;    // x vectors per thread per stage
   constexpr int NA = NP * U;         // adapter vectors per lane and stage (row-linear)
   constexpr int ARPI = 64 / (4 * U);  // adapter rows per load instruction
   constexpr int LPR = 4 * U;         // 16-byte pieces of a row per stage
@@ -820,14 +822,14 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[b][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // entry v = tid + 256*i of a stage: token row v / 4U, 16-byte piece v % 4U
+  // entry v = tid + 64*NW*i of a stage: token row v / 4U, 16-byte piece v % 4U
   // of the row's stage segment (features 32*u + 8*g with u = piece / 4,
   // g = piece % 4): each load instruction covers whole row segments; the
   // piece goes to LDS at row * PITCH + piece * 16
   auto load_x = [&](uint4 (&xs)[XV], int st) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
-      const int v = tid + 256 * i;
+      const int v = tid + 64 * NW * i;
       const int u = (v % LPR) >> 2;
       const int g = v & 3;
       const bool kok = st < nstage && (st * U + u) * 32 + g * 8 < K;
@@ -837,7 +839,7 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
   auto store_x = [&](const uint4 (&xs)[XV], int buf) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
-      const int v = tid + 256 * i;
+      const int v = tid + 64 * NW * i;
       *reinterpret_cast<uint4*>(lds + buf * BUFB + (v / LPR) * PITCH + (v % LPR) * 16) = xs[i];
     }
   };
@@ -933,14 +935,15 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile
   }
 }
 
-template <int TT, int U, int PPW>
-__global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
-  static_assert(TT * U >= 4 && (U & (U - 1)) == 0 && PPW >= 1 && PPW <= 4, "stage shape");
+template <int TT, int U, int PPW, int NW>
+__global__ __launch_bounds__(64 * NW) void slot_shrink_rows_kernel(ShrinkArgs p) {
+  static_assert((TT * U) % NW == 0 && (U & (U - 1)) == 0 && PPW >= 1 && PPW <= 4 && 64 * NW >= 16 * TT,
+                "stage shape");
   constexpr int TB = 16 * TT;
-  constexpr int XV = TT * U / 4;
-  constexpr int GP = 4 * PPW;  // (slice, rank block) pairs per workgroup
+  constexpr int XV = TT * U / NW;
+  constexpr int GP = NW * PPW;  // (slice, rank block) pairs per workgroup
   __shared__ __attribute__((aligned(16))) char lds[2 * 16 * TT * (64 * U + 16)];
-  __shared__ __attribute__((aligned(16))) char alds[4][16 * PPW * (64 * U + 16)];  // per wave: PPW pairs x 16 rows
+  __shared__ __attribute__((aligned(16))) char alds[NW][16 * PPW * (64 * U + 16)];  // per wave: PPW pairs x 16 rows
   __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
   const int tid = threadIdx.x;
@@ -967,10 +970,10 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   if (pbeg >= npairs) return;  // uniform over the workgroup
   if (tid < TB) sh_tok[tid] = (tid < tl.len) ? p.sorted[tl.start + tid] : 0;
   __syncthreads();
-  // this wave's pairs: pbeg + wave + 4i for i < npw (waves without pairs still
+  // this wave's pairs: pbeg + wave + NW*i for i < npw (waves without pairs still
   // load their share of x and take part in every barrier)
   const int avail = npairs - pbeg - wave;
-  const int npw = uniform_int(avail <= 0 ? 0 : (((avail + 3) >> 2) < PPW ? ((avail + 3) >> 2) : PPW));
+  const int npw = uniform_int(avail <= 0 ? 0 : (((avail + NW - 1) / NW) < PPW ? ((avail + NW - 1) / NW) : PPW));
 
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
   const rsrc_t ra = make_rsrc(static_cast<const uint16_t*>(p.a) + (int64_t)tl.slot * p.as0,
@@ -978,7 +981,7 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   uint32_t xoff[XV];
 #pragma unroll
   for (int i = 0; i < XV; ++i) {
-    const int v = tid + 256 * i;
+    const int v = tid + 64 * NW * i;
     const int row = v / (4 * U);
     const int u = (v % (4 * U)) >> 2;
     const int g = v & 3;
@@ -991,22 +994,22 @@ __global__ __launch_bounds__(256) void slot_shrink_rows_kernel(ShrinkArgs p) {
   int psl[4], pj[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int pg = pbeg + wave + 4 * i;
+    const int pg = pbeg + wave + NW * i;
     const int sl = pg / nq;
     psl[i] = sl;
     pj[i] = 16 * (pg - sl * nq);
   }
   switch (npw) {
-    case 0: shrink_rows_body<TT, U, 0>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
-    case 1: shrink_rows_body<TT, U, 1>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 0: shrink_rows_body<TT, U, 0, NW>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
+    case 1: shrink_rows_body<TT, U, 1, NW>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]); break;
     case 2:
-      if constexpr (PPW >= 2) shrink_rows_body<TT, U, 2>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
+      if constexpr (PPW >= 2) shrink_rows_body<TT, U, 2, NW>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
       break;
     case 3:
-      if constexpr (PPW >= 3) shrink_rows_body<TT, U, 3>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
+      if constexpr (PPW >= 3) shrink_rows_body<TT, U, 3, NW>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
       break;
     default:
-      if constexpr (PPW >= 4) shrink_rows_body<TT, U, 4>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
+      if constexpr (PPW >= 4) shrink_rows_body<TT, U, 4, NW>(p, tl, rho, rx, ra, xoff, bany, psl, pj, sh_tok, lds, alds[wave]);
       break;
   }
 }
@@ -1907,30 +1910,36 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   const int64_t tiles = ceil_div(T, 16 * bmb) + S;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Schedule, from the shapes: the row-split kernel for bf16 batches of 1024
-  // tokens or more whose grid fills the chip twice (at least 512 workgroups,
-  // counting every slot of the table as used); the pipelined kernel for the
-  // others; the general kernel (no buffer descriptors) where x or one slot's
-  // adapter spans more than a 2 GiB descriptor.
-  // Measured with bf16 inputs, K 4096, slices 4096 + 1024 + 1024, ranks up
-  // to 64, tokens spread evenly over the slots: 32 slots at 1024 / 2048 /
-  // 4096 / 8192 tokens take 17 / 27 / 27 / 48 us pipelined against 54 / 62 /
-  // 76 / 77 us row-split (grids of 128 to 192 workgroups); 128 slots at 8192
-  // tokens 53 against 66 us. The prefill batch (16731 tokens in 46 requests,
-  // K 8192, ranks up to 128, a grid of 864) takes 188 us row-split against
-  // 236 us pipelined.
+  // tokens or more whose grid (token tiles, counting every slot of the table
+  // as used, times groups of 16 (slice, rank block) pairs) fills the chip
+  // once, at least 256 workgroups; the pipelined kernel for the others; the
+  // general kernel (no buffer descriptors) where x or one slot's adapter
+  // spans more than a 2 GiB descriptor.
+  // Measured (us, row-split / pipelined): the prefill batch (16731 tokens in
+  // 46 requests over a 128-slot table, K 8192, slices 8192 + 1024 + 1024) at
+  // r_max 128 / 64 / 32 / 16: 193 / 238, 158 / 176, 122 / 164, 110 / 157.
+  // Tokens spread evenly over the slots (K 4096, slices 4096 + 1024 + 1024,
+  // r_max 64 / 32): 32 slots at 8192 tokens (grid 96) 83 / 49, 64 / 45; 64
+  // slots at 16384 (192) 85 / 70, 65 / 63; 128 slots at 12288 (224) 81 / 65,
+  // 61 / 61; at 16384 (256) 85 / 78, 66 / 63, the rule's miss: each slot's
+  // tokens spill a few rows into a second tile that streams the whole
+  // adapter; at 32768 (384) 88 / 131, 70 / 110.
   constexpr int tt = 8;    // row-split: 128-token tiles
+  constexpr int nw = 8;    // row-split: waves per workgroup
   constexpr int ppw = 2;   // row-split: (slice, rank block) pairs per wave
   const bool desc_ok = shrink_desc_ok(x, a, T, num_slices, r_max);
-  const int64_t row_groups = ceil_div((int64_t)num_slices * ceil_div(r_max, 16), 4 * ppw);
+  const int64_t row_groups = ceil_div((int64_t)num_slices * ceil_div(r_max, 16), nw * ppw);
   const int64_t rtiles = ceil_div(T, 16 * tt) + S;
-  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024 && rtiles * row_groups >= 512) {
-    // two (slice, rank block) pairs per wave, i.e. 8 per workgroup: the
-    // prefill batch has only 153 token tiles, and with 16 pairs per
-    // workgroup most of a tile's work sat on one CU (224 us); 8 pairs:
-    // 191 us, 4: 206 us; 64-token tiles 206-230 us; 128-feature stages 307 us
+  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024 && rtiles * row_groups >= 256) {
+    // 8 waves of two pairs each: the prefill batch at r_max 128 / 64 / 32
+    // 190 / 185 / 132 us with 4 waves of two pairs, 181 / 158 / 122 us with 8,
+    // 196 / 193 / 124 us with 8 of one pair, 252 / 159 / 117 us with 8 of
+    // three; 128-feature stages (8 waves of two pairs) 212 / 181 / 130 us.
+    // Earlier, with 4 waves: 4 pairs per wave 224 us, 1 pair 206 us,
+    // 64-token tiles 206-230 us (r_max 128).
     p.row_groups = static_cast<int>(row_groups);
     const dim3 grid(static_cast<unsigned>(round_up(rtiles, 8 * kRowsGroup) * p.row_groups));
-    launch((slot_shrink_rows_kernel<tt, 2, ppw>), grid, dim3(256), 0, st, p);
+    launch((slot_shrink_rows_kernel<tt, 2, ppw, nw>), grid, dim3(64 * nw), 0, st, p);
     return launch_status();
   }
   const bool pipe = desc_ok;

@@ -38,7 +38,7 @@ CASES = [
 #   grouping: one token per thread (<= 1024 tokens): decode-small, ragged-ranks, fp32, one-token,
 #             decode-mid, decode-wide, fp32-mid; one workgroup per 1024-token chunk: the others
 #             (and test_grouping_schedules_bitwise for every grouping kernel);
-#   shrink: row-split (bf16, >= 1024 tokens, a grid of >= 512 workgroups): prefill-many-slots;
+#   shrink: row-split (bf16, >= 1024 tokens, a grid of >= 256 workgroups): prefill-many-slots;
 #           pipelined, 64-token tiles, four rank blocks (>= 1024 tokens where the busiest CU streams
 #             fewer rows so): prefill-like, prefill-long;
 #           pipelined, 16-token tiles, four rank blocks (>= 512 tokens otherwise): fp32-prefill,
