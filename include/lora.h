@@ -55,7 +55,9 @@ typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
 enum {
   LORA_OK = 0,
   LORA_ERR_NULL = -1,      /* a required pointer is NULL */
-  LORA_ERR_SHAPE = -2,     /* operand shapes disagree, or a size is negative or unsupported */
+  LORA_ERR_SHAPE = -2,     /* operand shapes disagree, a size is negative or unsupported, or an
+                              operand (dims and strides) spans more than 2^47 bytes or has a
+                              negative stride */
   LORA_ERR_DTYPE = -3,     /* unsupported dtype or mixed input dtypes */
   LORA_ERR_STRIDE = -4,    /* unsupported stride or alignment of a streamed operand */
   LORA_ERR_RANK = -5,      /* rank outside [1, 128] (single adapter) or r_max outside [1, 128] */

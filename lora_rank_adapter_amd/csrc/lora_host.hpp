@@ -48,8 +48,43 @@ inline int check_colmajor_stream(const lora_mat* m) {
 
 inline bool float_dtype_ok(int32_t d) { return d == LORA_BF16 || d == LORA_F32; }
 
+// Every operand must fit in 2^47 bytes (128 TiB, more than any device holds):
+// dims and strides non-negative and at most 2^47 each, and its element count
+// and byte extent at most 2^47, computed without overflow. With that checked
+// first, every product the entry points form from the dims, strides and
+// element size of one operand fits an int64_t.
+constexpr int64_t kMaxOperand = int64_t(1) << 47;
+
+inline bool operand_fits(const int64_t* dims, const int64_t* strides, int n, int64_t es) {
+  bool empty = false;
+  for (int i = 0; i < n; ++i) {
+    if (dims[i] < 0 || dims[i] > kMaxOperand || strides[i] < 0 || strides[i] > kMaxOperand) return false;
+    empty = empty || dims[i] == 0;
+  }
+  if (empty) return true;
+  int64_t count = 1, last = 0;
+  for (int i = 0; i < n; ++i) {
+    int64_t step = 0;
+    if (__builtin_mul_overflow(count, dims[i], &count) || count > kMaxOperand) return false;
+    if (__builtin_mul_overflow(dims[i] - 1, strides[i], &step) || __builtin_add_overflow(last, step, &last) ||
+        last >= kMaxOperand)
+      return false;
+  }
+  return (last + 1) * es <= kMaxOperand && count * es <= kMaxOperand;
+}
+
 inline bool valid_dims(const lora_mat* m) {
-  return m->rows >= 0 && m->cols >= 0;
+  const int64_t dims[2] = {m->rows, m->cols};
+  const int64_t strides[2] = {m->stride_row, m->stride_col};
+  const int64_t es = static_cast<int64_t>(elem_size(m->dtype));
+  return operand_fits(dims, strides, 2, es > 0 ? es : 1);
+}
+
+inline bool valid_dims(const lora_t3* t) {
+  const int64_t dims[3] = {t->d0, t->d1, t->d2};
+  const int64_t strides[3] = {t->s0, t->s1, t->s2};
+  const int64_t es = static_cast<int64_t>(elem_size(t->dtype));
+  return operand_fits(dims, strides, 3, es > 0 ? es : 1);
 }
 
 // Carves 256-byte aligned sub-buffers out of a caller workspace.

@@ -1842,8 +1842,9 @@ static int shrink_checks(const lora_mat* x, const lora_t3* a, const lora_address
   if (rc != LORA_OK) return rc;
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
   if (num_slices < 1 || num_slices > kMaxSlices) return LORA_ERR_SHAPE;
+  if (!valid_dims(x) || !valid_dims(a) || !valid_dims(h)) return LORA_ERR_SHAPE;
   const int64_t T = addr->T, S = addr->S, K = x->cols;
-  if (x->rows != T || x->cols < 0) return LORA_ERR_SHAPE;
+  if (x->rows != T) return LORA_ERR_SHAPE;
   if (a->d0 != S || a->d1 != (int64_t)num_slices * r_max || a->d2 != K) return LORA_ERR_SHAPE;
   if (h->d0 != T || h->d1 != num_slices || h->d2 != r_max) return LORA_ERR_SHAPE;
   if (!float_dtype_ok(x->dtype) || a->dtype != x->dtype || h->dtype != LORA_F32) return LORA_ERR_DTYPE;
@@ -1960,10 +1961,11 @@ static int expand_checks(const lora_t3* h, const lora_t3* b, const lora_addressi
   if (rc != LORA_OK) return rc;
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
   if (num_slices < 1 || num_slices > kMaxSlices) return LORA_ERR_SHAPE;
+  if (!valid_dims(h) || !valid_dims(b) || !valid_dims(y)) return LORA_ERR_SHAPE;
   const int64_t T = addr->T, S = addr->S;
   int64_t O = 0;
   for (int i = 0; i < num_slices; ++i) {
-    if (out_slices[i] < 0 || out_slices[i] % 4 != 0) return LORA_ERR_SHAPE;
+    if (out_slices[i] < 0 || out_slices[i] > kMaxOperand || out_slices[i] % 4 != 0) return LORA_ERR_SHAPE;
     O += out_slices[i];
   }
   if (h->d0 != T || h->d1 != num_slices || h->d2 != r_max) return LORA_ERR_SHAPE;
@@ -2161,6 +2163,7 @@ extern "C" int lora_gather_shrink(const int32_t* ids, const lora_t3* a, const lo
   int rc = check_addressing(addr, ranks);
   if (rc != LORA_OK) return rc;
   if (r_max < 1 || r_max > 128) return LORA_ERR_RANK;
+  if (!valid_dims(a) || !valid_dims(h)) return LORA_ERR_SHAPE;
   const int64_t T = addr->T, S = addr->S, V = a->d2;
   if (a->d0 != S || a->d1 != r_max || V < 0) return LORA_ERR_SHAPE;
   if (h->d0 != T || h->d1 != 1 || h->d2 != r_max) return LORA_ERR_SHAPE;

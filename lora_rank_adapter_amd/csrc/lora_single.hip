@@ -1471,22 +1471,6 @@ struct BandTnRB {
   };
 };
 
-// The dX/dA call's kernels after the weights are in place: the fused
-// shrink-expand (writing the planes of s*dYB) and then the weight-gradient
-// partials; or, on the split schedule, the shrink and then dX's band expand
-// and dA's partials in one launch.
-template <class Tag, class OM, bool WT>
-static void run_dx_da(FusedArgs a, TnArgs t, const SinglePlan& pl, int rb, hipStream_t st) {
-  if (pl.fused) {
-    dispatch_dx_fused<FusedNW<Tag, OM, true, WT>::template L>(rb, pl.bmb, a, st);
-    launch_tn<Tag>(t, rb, 4, st);
-    return;
-  }
-  launch_shrink<Tag, true, true, WT>(a, rb, pl.bmb_shrink, st);
-  dispatch_dx_band<BandTnRB<Tag, OM, WT>::template L>(rb, a, t, st);
-}
-
-
 template <class Tag>
 static void launch_tn(TnArgs a, int rb, int nw, hipStream_t st) {
   tn_grid(a, 64 * nw);
@@ -1503,6 +1487,23 @@ static void launch_tn(TnArgs a, int rb, int nw, hipStream_t st) {
     default: launch((tn_kernel<Tag, 8, 8>), grid, block, 0, st, a); break;
   }
 }
+
+// The dX/dA call's kernels after the weights are in place: the fused
+// shrink-expand (writing the planes of s*dYB) and then the weight-gradient
+// partials; or, on the split schedule, the shrink and then dX's band expand
+// and dA's partials in one launch.
+template <class Tag, class OM, bool WT>
+static void run_dx_da(FusedArgs a, TnArgs t, const SinglePlan& pl, int rb, hipStream_t st) {
+  if (pl.fused) {
+    dispatch_dx_fused<FusedNW<Tag, OM, true, WT>::template L>(rb, pl.bmb, a, st);
+    launch_tn<Tag>(t, rb, 4, st);
+    return;
+  }
+  launch_shrink<Tag, true, true, WT>(a, rb, pl.bmb_shrink, st);
+  dispatch_dx_band<BandTnRB<Tag, OM, WT>::template L>(rb, a, t, st);
+}
+
+
 
 static PackJob pack_job(const void* src, int64_t s_i, int64_t s_j, int64_t rows, int64_t cols, void* dst,
                         int64_t dst_rows, int64_t dst_cols, int64_t ld) {
@@ -1719,6 +1720,12 @@ extern "C" const char* lora_status_string(int status) {
 extern "C" size_t lora_workspace_bytes(int op, int64_t M, int64_t K, int64_t L, int32_t r, int32_t dtype) {
   if (op < LORA_OP_FWD || op > LORA_OP_BWD_DB) return 0;
   if (M < 0 || K < 0 || L < 0 || r < 1 || r > 128 || !float_dtype_ok(dtype)) return 0;
+  // sizes whose x (M x K) or output (M x L) could not exist: every operand
+  // fits in kMaxOperand bytes
+  int64_t mk = 0, ml = 0;
+  if (K > kMaxOperand || L > kMaxOperand || M > kMaxOperand || __builtin_mul_overflow(M, K, &mk) ||
+      __builtin_mul_overflow(M, L, &ml) || mk > kMaxOperand || ml > kMaxOperand)
+    return 0;
   return layout_for(op, M, K, L, r, dtype).total();
 }
 

@@ -73,6 +73,16 @@ def test_workspace_bytes(lib):
     assert f(7, 8192, 4096, 4096, 16, 1) == 0       # unknown op
     assert f(1, 8192, 4096, 4096, 16, 5) == 0       # unknown dtype
     assert f(1, 16384, 4096, 14336, 64, 1) >= f(1, 8192, 4096, 4096, 16, 1)
+    # sizes no operand could have (x or the output beyond 2^47 elements) are
+    # invalid, and sizing them must not overflow
+    big = 1 << 47
+    assert f(1, 1 << 20, 1 << 27, 1 << 27, 64, 1) > 0             # M x K = 2^47 elements
+    assert f(1, 1 << 20, (1 << 27) + 8, 4096, 64, 1) == 0
+    for op in (0, 1, 2):
+        assert f(op, 1 << 40, 1 << 40, 1 << 40, 128, 1) == 0
+        assert f(op, 1 << 62, 4096, 4096, 64, 1) == 0
+        assert f(op, (1 << 63) - 1, (1 << 63) - 1, (1 << 63) - 1, 128, 0) == 0
+        assert f(op, 1, big + 8, 8, 16, 1) == 0
 
 
 def m(rows, cols, dtype=1, sr=None, sc=1, ptr=FAKE):
@@ -113,6 +123,12 @@ def test_fwd_validation(lib):
     assert fwd(lib, x, m(K, r), B, res, ctypes.c_void_p(FAKE + 128), 1 << 20) == -6   # not 256-byte aligned
     Kl = 8200
     assert fwd(lib, m(M, Kl), m(Kl, r, sr=1, sc=Kl), B, res) == -6          # split schedule
+    # operands that could not exist (beyond 2^47 bytes, or negative strides)
+    assert fwd(lib, m(1 << 62, K), A, B, m(1 << 62, L_, dtype=0)) == -2
+    assert fwd(lib, m(M, K, sr=1 << 50), A, B, res) == -2
+    assert fwd(lib, m(M, K, sr=-K), A, B, res) == -2
+    assert fwd(lib, x, m(K, r, sr=-1, sc=K), B, res) == -2
+    assert fwd(lib, m(1 << 40, 1 << 40, sr=1 << 40), m(1 << 40, r, sr=1, sc=1 << 40), B, res) == -2
     # empty problems launch nothing and succeed
     assert fwd(lib, m(0, K), A, B, m(0, L_, dtype=0)) == 0
     assert fwd(lib, m(M, 0), m(0, r, sr=1, sc=1), B, res) == 0
@@ -178,6 +194,10 @@ def test_multi_validation(lib):
     assert shrink(h_=LoraT3(FAKE, 1, 0, T, 2, r_max, 2 * r_max, r_max, 1)) == -3
     assert shrink(a_=LoraT3(FAKE, 1, 0, S, 2 * r_max, K, 2 * r_max * K, 1, K)) == -4
     assert shrink(addr_=LoraAddressing(FAKE, T, 2000, FAKE, FAKE, FAKE)) == -8
+    huge = 1 << 62
+    assert shrink(x_=m(T, huge), a_=LoraT3(FAKE, 1, 0, S, 2 * r_max, huge, 2 * r_max * K, K, 1)) == -2
+    assert shrink(a_=LoraT3(FAKE, 1, 0, S, 2 * r_max, K, huge, K, 1)) == -2
+    assert shrink(h_=LoraT3(FAKE, 0, 0, T, 2, r_max, -2 * r_max, r_max, 1)) == -2
     assert shrink(x_=m(0, K), addr_=LoraAddressing(FAKE, 0, S, FAKE, FAKE, FAKE),
                   h_=LoraT3(FAKE, 0, 0, 0, 2, r_max, 2 * r_max, r_max, 1)) == 0
 
@@ -196,6 +216,8 @@ def test_multi_validation(lib):
     assert expand(b_=b32, y_=m(T, 48, dtype=1)) == -3                 # bf16 y needs bf16 weights
     assert expand(y_=m(T, 48, dtype=7)) == -3
     assert expand(h_=LoraT3(FAKE, 0, 0, T, 2, r_max, 2 * r_max, 1, 2)) == -4      # rank index not contiguous
+    assert expand(slices=(ctypes.c_int64 * 2)(1 << 62, 48 - (1 << 62))) == -2       # widths beyond any operand
+    assert expand(b_=LoraT3(FAKE, 1, 0, S, 48, r_max, 1 << 60, r_max, 1)) == -2
 
     def apply(x_=x, y_=y, h_=h, slices=sl, n=2, b_=b):
         return lib.lora_apply_linear(ctypes.byref(x_), ctypes.byref(a), ctypes.byref(b_), ctypes.byref(addr),
