@@ -424,7 +424,7 @@ struct ShrinkArgs {
   const int32_t* ranks;
   int64_t K;
   int S, r_max, n_slices, row_chunks;
-  int row_groups;   // row-split kernel: workgroups per token tile (4 * PPW rank-block pairs each)
+  int row_groups;   // row-split kernel: workgroups per token tile (NW * PPW rank-block pairs each)
   int64_t x_bytes;  // bytes of x a descriptor may span (GEMM kernel)
   bool h_vec;  // h rows 16-byte aligned (strides multiples of 4)
 };
