@@ -966,13 +966,18 @@ __global__ __launch_bounds__(64 * NW) void slot_shrink_rows_kernel(ShrinkArgs p)
   const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
   const int nq = (rho + 15) >> 4;
   const int npairs = p.n_slices * nq;
-  const int pbeg = GP * rg;
-  if (pbeg >= npairs) return;  // uniform over the workgroup
+  // the slot's pairs split evenly over its row groups (a workgroup's time
+  // follows its bytes: 24 pairs as 12 + 12 rather than 16 + 8, prefill at
+  // r_max 128 187 -> 164 us, the same bits)
+  const int nu = (npairs + GP - 1) / GP;
+  if (rg >= nu) return;  // uniform over the workgroup
+  const int pbeg = rg * npairs / nu;
+  const int pend = (rg + 1) * npairs / nu;
   if (tid < TB) sh_tok[tid] = (tid < tl.len) ? p.sorted[tl.start + tid] : 0;
   __syncthreads();
   // this wave's pairs: pbeg + wave + NW*i for i < npw (waves without pairs still
   // load their share of x and take part in every barrier)
-  const int avail = npairs - pbeg - wave;
+  const int avail = pend - pbeg - wave;
   const int npw = uniform_int(avail <= 0 ? 0 : (((avail + NW - 1) / NW) < PPW ? ((avail + NW - 1) / NW) : PPW));
 
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
