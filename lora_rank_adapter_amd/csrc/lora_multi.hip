@@ -429,6 +429,58 @@ struct ShrinkArgs {
   bool h_vec;  // h rows 16-byte aligned (strides multiples of 4)
 };
 
+// Row-split units: a slot with c grouped tokens and clamped rank rho has
+// ceil(c / tb) token tiles of ceil(n_slices * ceil(rho / 16) / gp) row groups
+// each; units run in slot order, then tile, then row group.
+__device__ __forceinline__ int rows_units_of(int c, int rho, int tb, int gp, int n_slices) {
+  if (c <= 0 || rho <= 0) return 0;
+  return ((c + tb - 1) / tb) * ((n_slices * ((rho + 15) >> 4) + gp - 1) / gp);
+}
+
+struct RowsUnit {
+  int slot;  // -1: no such unit
+  int start, len, rg, nu;
+};
+
+// Wave-level: the unit count, and the u-th unit (u < 0: count only).
+__device__ RowsUnit find_rows_unit(int u, int tb, int gp, const ShrinkArgs& p, int* total) {
+  const int lane = threadIdx.x & 63;
+  int running = 0;
+  RowsUnit out{-1, 0, 0, 0, 0};
+  for (int s0 = 0; s0 < p.S; s0 += 64) {
+    const int s = s0 + lane;
+    const int c = (s < p.S) ? p.counts[s] : 0;
+    const int rho = (s < p.S) ? clamp_rank(p.ranks[s], p.r_max) : 0;
+    const int nu = (c > 0 && rho > 0) ? (p.n_slices * ((rho + 15) >> 4) + gp - 1) / gp : 0;
+    const int nt = rows_units_of(c, rho, tb, gp, p.n_slices);
+    int incl = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const int excl = running + incl - nt;
+    const bool mine = u >= excl && u < excl + nt;
+    const uint64_t who = __ballot(mine);
+    if (who) {
+      const int src = __ffsll(static_cast<long long>(who)) - 1;
+      const int local = u - __shfl(excl, src, 64);
+      const int nus = __shfl(nu, src, 64);
+      const int cs = __shfl(c, src, 64);
+      const int k = local / nus;
+      out.slot = s0 + src;
+      out.start = __shfl(s < p.S ? p.offsets[s] : 0, src, 64) + k * tb;
+      out.len = (cs - k * tb) < tb ? (cs - k * tb) : tb;
+      out.rg = local - k * nus;
+      out.nu = nus;
+    }
+    running += __shfl(incl, 63, 64);
+  }
+  *total = running;
+  return out;
+}
+
+
 template <class Tag, int BMB, int RB>
 __global__ __launch_bounds__(256) void slot_shrink_kernel(ShrinkArgs p) {
   using E = typename Tag::elem;
@@ -780,11 +832,12 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
 // Row-split shrink for bf16 inputs (x and one slot's a within 2 GiB
 // descriptors). A workgroup of NW waves owns a tile of up to 128 grouped
 // tokens of one slot against up to NW*PPW (slice, 16-row rank block) pairs of
-// its slices (a slot with more pairs gets further row-group workgroups). Wave
-// w takes pairs w, w+NW, ... of its row group over the whole feature axis, so
-// no partial sums are exchanged between waves. One workgroup streams only so
-// fast (a lone 4-wave one about 28 GB/s), so 8 waves of two pairs each serve a
-// tile: 16 pairs per workgroup.
+// its slices (a slot with more pairs gets further row-group workgroups, the
+// pairs split evenly over them). Wave w takes pairs w, w+NW, ... of its row
+// group over the whole feature axis, so no partial sums are exchanged between
+// waves. One workgroup streams only so fast (a lone 4-wave one about 28 GB/s)
+// and the time follows the workgroup that moves the most bytes, so 8 waves of
+// one pair each serve a tile: up to 8 pairs per workgroup.
 // The tile's x rows are fetched once per stage of 32*U features by the whole
 // workgroup, row-linearly (each load instruction covers whole row segments),
 // into a double-buffered LDS tile with padded rows (every fragment read is
@@ -794,10 +847,9 @@ __global__ __launch_bounds__(256) void slot_shrink_pipe_kernel(ShrinkArgs p) {
 // workgroup per (tile, slice, rank chunk), a tile's x rows reach the CU once
 // per row group instead of once per slice and rank chunk, and each adapter
 // row is shared by 128 tokens instead of 64.
-// Tiles go to the XCDs in groups of kRowsGroup consecutive tiles (mostly
-// tiles of one slot) with a tile's row-group workgroups next to each other,
-// so adapter and x rows are re-read from that XCD's L2.
-constexpr int kRowsGroup = 4;
+// Only live (tile, row group) units get a workgroup's work, dealt to the
+// XCDs in equal runs of consecutive units (see the kernel), so adapter and x
+// rows are re-read from one XCD's L2.
 
 template <int TT, int U, int NP, int NW>
 __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& p, const Tile& tl, int rho, rsrc_t rx, rsrc_t ra,
@@ -944,33 +996,37 @@ __global__ __launch_bounds__(64 * NW) void slot_shrink_rows_kernel(ShrinkArgs p)
   constexpr int GP = NW * PPW;  // (slice, rank block) pairs per workgroup
   __shared__ __attribute__((aligned(16))) char lds[2 * 16 * TT * (64 * U + 16)];
   __shared__ __attribute__((aligned(16))) char alds[NW][16 * PPW * (64 * U + 16)];  // per wave: PPW pairs x 16 rows
-  __shared__ Tile sh_tile;
   __shared__ int sh_tok[TB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
-  // workgroup -> (tile, row group): ids go round-robin over the 8 XCDs
-  const int rgs = p.row_groups;
-  const int kx = static_cast<int>(blockIdx.x >> 3);
-  const int gw = kRowsGroup * rgs;
-  const int r2 = kx % gw;
-  const int ti = ((kx / gw) * 8 + static_cast<int>(blockIdx.x & 7)) * kRowsGroup + r2 % kRowsGroup;
-  const int rg = r2 / kRowsGroup;
+  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The live units
+  // are cut into 8 runs of `per` consecutive units, run x on XCD x, so every
+  // XCD gets the same number and a tile's row groups and a slot's tiles
+  // share one L2; ids past the runs exit.
+  __shared__ RowsUnit sh_unit;
   if (wave == 0) {
-    const Tile tl = find_tile(ti, TB, p.counts, p.offsets, p.S);
-    if (lane == 0) sh_tile = tl;
+    int total = 0;
+    find_rows_unit(-1, TB, GP, p, &total);
+    const int per = (total + 7) >> 3;
+    const int k = static_cast<int>(blockIdx.x >> 3);
+    const int u = static_cast<int>(blockIdx.x & 7) * per + k;
+    RowsUnit un{-1, 0, 0, 0, 0};
+    if (k < per && u < total) un = find_rows_unit(u, TB, GP, p, &total);
+    if (lane == 0) sh_unit = un;
   }
   __syncthreads();
-  const Tile tl = sh_tile;
-  if (tl.slot < 0) return;
+  const RowsUnit un = sh_unit;
+  if (un.slot < 0) return;
+  const Tile tl{un.slot, un.start, un.len};
+  const int rg = un.rg;
   const int rho = clamp_rank(p.ranks[tl.slot], p.r_max);
   const int nq = (rho + 15) >> 4;
   const int npairs = p.n_slices * nq;
   // the slot's pairs split evenly over its row groups (a workgroup's time
   // follows its bytes: 24 pairs as 12 + 12 rather than 16 + 8, prefill at
   // r_max 128 187 -> 164 us, the same bits)
-  const int nu = (npairs + GP - 1) / GP;
-  if (rg >= nu) return;  // uniform over the workgroup
+  const int nu = un.nu;
   const int pbeg = rg * npairs / nu;
   const int pend = (rg + 1) * npairs / nu;
   if (tid < TB) sh_tok[tid] = (tid < tl.len) ? p.sorted[tl.start + tid] : 0;
@@ -1923,28 +1979,34 @@ extern "C" int lora_shrink(const lora_mat* x, const lora_t3* a, const lora_addre
   // spans more than a 2 GiB descriptor.
   // Measured (us, row-split / pipelined): the prefill batch (16731 tokens in
   // 46 requests over a 128-slot table, K 8192, slices 8192 + 1024 + 1024) at
-  // r_max 128 / 64 / 32 / 16: 193 / 238, 158 / 176, 122 / 164, 110 / 157.
+  // r_max 128 / 64 / 32 / 16: 143-151 / 236, 130 / 176, 127 / 164, 114 / 156.
   // Tokens spread evenly over the slots (K 4096, slices 4096 + 1024 + 1024,
-  // r_max 64 / 32): 32 slots at 8192 tokens (grid 96) 83 / 49, 64 / 45; 64
-  // slots at 16384 (192) 85 / 70, 65 / 63; 128 slots at 12288 (224) 81 / 65,
-  // 61 / 61; at 16384 (256) 85 / 78, 66 / 63, the rule's miss: each slot's
-  // tokens spill a few rows into a second tile that streams the whole
-  // adapter; at 32768 (384) 88 / 131, 70 / 110.
+  // r_max 64 / 32; grid as the rule counts it): 32 slots at 8192 tokens (96)
+  // 66 / 49, 66 / 44, at 16384 (160) 68 / 70, 66 / 64; 64 slots at 16384
+  // (192) 67 / 70, 66 / 63, at 32768 (320) 95 / 134, 71 / 111; 128 slots at
+  // 8192 (192) 55 / 50, 55 / 44, at 12288 (224) 64 / 64, 63 / 61, at 16384
+  // (256) 68 / 78, 67 / 64, at 24576 (320) 90 / 96, 68 / 84, at 32768 (384)
+  // 94 / 131, 71 / 109. A row-split workgroup streams its tile's x rows and
+  // up to 8 rank blocks over the whole feature axis (about 60 us at K 4096),
+  // so it pays once the pipelined kernel's re-reads take longer.
   constexpr int tt = 8;    // row-split: 128-token tiles
   constexpr int nw = 8;    // row-split: waves per workgroup
-  constexpr int ppw = 2;   // row-split: (slice, rank block) pairs per wave
+  constexpr int ppw = 1;   // row-split: (slice, rank block) pairs per wave
   const bool desc_ok = shrink_desc_ok(x, a, T, num_slices, r_max);
-  const int64_t row_groups = ceil_div((int64_t)num_slices * ceil_div(r_max, 16), nw * ppw);
+  const int64_t pairs = (int64_t)num_slices * ceil_div(r_max, 16);
   const int64_t rtiles = ceil_div(T, 16 * tt) + S;
-  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024 && rtiles * row_groups >= 256) {
-    // 8 waves of two pairs each: the prefill batch at r_max 128 / 64 / 32
-    // 190 / 185 / 132 us with 4 waves of two pairs, 181 / 158 / 122 us with 8,
-    // 196 / 193 / 124 us with 8 of one pair, 252 / 159 / 117 us with 8 of
-    // three; 128-feature stages (8 waves of two pairs) 212 / 181 / 130 us.
-    // Earlier, with 4 waves: 4 pairs per wave 224 us, 1 pair 206 us,
-    // 64-token tiles 206-230 us (r_max 128).
-    p.row_groups = static_cast<int>(row_groups);
-    const dim3 grid(static_cast<unsigned>(round_up(rtiles, 8 * kRowsGroup) * p.row_groups));
+  if (desc_ok && x->dtype == LORA_BF16 && T >= 1024 && rtiles * ceil_div(pairs, 16) >= 256) {
+    // 8 waves of one pair each, units dealt evenly to the XCDs: the prefill
+    // batch at r_max 128 / 64 / 32 143 / 130 / 128 us. Earlier forms (units
+    // by tile groups of four per XCD): 4 waves of two pairs 190 / 185 / 132
+    // us; 8 waves of two 181 / 158 / 122 (165 at 128 with a slot's pairs split
+    // evenly); 8 of one 196 / 193 / 124 (as many units as now, but up to 42 on
+    // one XCD's 32 CUs); 8 of three 252 / 159 / 117; 128-feature stages 212 /
+    // 181 / 130. With 4 waves: 4 pairs per wave 224 us, 64-token tiles 206-230
+    // us (r_max 128).
+    p.row_groups = static_cast<int>(ceil_div(pairs, nw * ppw));
+    // at most rtiles * row_groups units: 8 runs of at most that / 8 each
+    const dim3 grid(static_cast<unsigned>(8 * ceil_div(rtiles * p.row_groups, 8)));
     launch((slot_shrink_rows_kernel<tt, 2, ppw, nw>), grid, dim3(64 * nw), 0, st, p);
     return launch_status();
   }
