@@ -33,17 +33,19 @@ CASES = [
     ("decode-wide", 1000, 256, (3000, 500, 500), 16, 64, (0, 16, 40, 64), 0.1, "bf16"),
     ("decode-1k", 1100, 256, (1024, 256), 8, 32, (0, 8, 32), 0.1, "bf16"),
     ("fp32-mid", 600, 64, (32, 16), 8, 16, (0, 4, 16), 0.2, "f32"),
+    ("decode-many-slots", 400, 256, (128, 64), 1000, 32, (0, 8, 16, 32), 0.1, "bf16"),
 ]
 # Which kernel each case reaches (the library picks by shape):
 #   grouping: one token per thread (<= 1024 tokens): decode-small, ragged-ranks, fp32, one-token,
-#             decode-mid, decode-wide, fp32-mid; one workgroup per 1024-token chunk: the others
+#             decode-mid, decode-wide, fp32-mid, decode-many-slots; one workgroup per 1024-token chunk: the others
 #             (and test_grouping_schedules_bitwise for every grouping kernel);
 #   shrink: row-split (bf16, >= 1024 tokens, a grid of >= 256 workgroups): prefill-many-slots;
 #           pipelined, 64-token tiles, four rank blocks (>= 1024 tokens where the busiest CU streams
 #             fewer rows so): prefill-like, prefill-long;
 #           pipelined, 16-token tiles, four rank blocks (>= 512 tokens otherwise): fp32-prefill,
 #             decode-mid, decode-wide, decode-1k, fp32-mid;
-#           pipelined, 16-token tiles, one rank block (< 512 tokens): the others;
+#           pipelined, 16-token tiles, one rank block, live units counted on the device (< 512
+#             tokens): the others (decode-many-slots: a 1000-slot table, 16 chunks of the slot scan);
 #           general (no buffer descriptors): test_shrink_general_kernel.
 #   expand: column band (>= 512 tokens; 256-token pieces at r_max 128, 64 below): prefill-like,
 #             prefill-long, fp32-prefill, prefill-many-slots, decode-mid, decode-wide, decode-1k, fp32-mid;
@@ -183,7 +185,8 @@ def test_shrink(case):
     assert oracle.rel_frobenius(got[spec], want[spec]) <= tol(dtype)
 
 
-@pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-many-slots"])
+@pytest.mark.parametrize("name", ["decode-small", "prefill-like", "fp32", "fp32-prefill", "prefill-many-slots",
+                                  "decode-many-slots"])
 def test_shrink_integer_exact(name):
     """Each shrink kernel (pipelined with 16- and 64-token tiles, row-split,
     bf16 and f32) bit for bit on integer inputs; unspecified entries of h
