@@ -382,7 +382,7 @@ __device__ Tile find_tile(int ti, int tb, const int32_t* __restrict__ counts, co
   for (int s0 = 0; s0 < S; s0 += 64) {
     const int s = s0 + lane;
     const int c = (s < S) ? counts[s] : 0;
-    const int nt = (c + tb - 1) / tb;
+    const int nt = c > 0 ? (c - 1) / tb + 1 : 0;  // no overflow for counts near 2^31
     int incl = nt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -447,7 +447,7 @@ __device__ PipeUnit find_pipe_unit(int u, int tb, int rows, const ShrinkArgs& p,
     const int c = (s < p.S) ? p.counts[s] : 0;
     const int rho = (s < p.S) ? clamp_rank(p.ranks[s], p.r_max) : 0;
     const int nch = (rho + rows - 1) / rows;
-    const int nt = (c > 0 && rho > 0) ? ((c + tb - 1) / tb) * p.n_slices * nch : 0;
+    const int nt = (c > 0 && rho > 0) ? ((c - 1) / tb + 1) * p.n_slices * nch : 0;
     int incl = nt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -481,7 +481,7 @@ __device__ PipeUnit find_pipe_unit(int u, int tb, int rows, const ShrinkArgs& p,
 // each; units run in slot order, then tile, then row group.
 __device__ __forceinline__ int rows_units_of(int c, int rho, int tb, int gp, int n_slices) {
   if (c <= 0 || rho <= 0) return 0;
-  return ((c + tb - 1) / tb) * ((n_slices * ((rho + 15) >> 4) + gp - 1) / gp);
+  return ((c - 1) / tb + 1) * ((n_slices * ((rho + 15) >> 4) + gp - 1) / gp);
 }
 
 struct RowsUnit {
