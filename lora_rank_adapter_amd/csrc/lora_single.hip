@@ -1255,13 +1255,23 @@ static int bmb_shrink(int64_t M, int rb) {
   return 1;
 }
 
+// dX/dA's shrink of dY: at rank 16 or less, 32-token tiles (one workgroup per
+// CU at 8192 tokens) halve the weight rows each CU re-reads per dY row:
+// lora_bwd_dx_da at rank 16 57.0 -> 56.3 us at 8192 x 4096 x 4096, 104.5 ->
+// 101.0 at 16384 x 4096 x 4096, 166.8 -> 154.2 at 16384 x 4096 x 14336; the
+// X*A shrinks of the forward and of dB measured 0.6-1.1 us slower with them.
+static int bmb_shrink_dy(int64_t M, int rb) {
+  if (rb == 1) return ceil_div(M, 32) >= 256 ? 2 : 1;
+  return bmb_shrink(M, rb);
+}
+
 // forward (expand accumulates into its output) or dX (no output loads);
 // kin = contraction of the shrink, nout = width of the expand, oes = bytes
 // per output element.
 static SinglePlan plan_single(bool forward, int64_t M, int64_t kin, int64_t nout, int rb, int64_t oes) {
   SinglePlan p{};
   p.fused = kin <= kFusedMaxContraction && M * nout * oes < (forward ? kFusedMaxOutputBytes : kFusedMaxDxOutputBytes);
-  p.bmb_shrink = bmb_shrink(M, rb);
+  p.bmb_shrink = forward ? bmb_shrink(M, rb) : bmb_shrink_dy(M, rb);
   if (p.fused)
     p.bmb = forward ? bmb_expand(M, rb) : ((rb == 1 && ceil_div(M, 32) >= 256) ? 2 : 1);
   else
@@ -1417,10 +1427,11 @@ struct ExpandBandRB {
 
 template <class Tag, bool EMIT_G, bool EMIT_F, bool WT = false>
 static void launch_shrink(const FusedArgs& a, int rb, int bmb, hipStream_t st) {
-  // the pairs bmb_shrink() returns; 8 waves while the cross-wave partial-sum
+  // the pairs bmb_shrink() and bmb_shrink_dy() return; 8 waves while the cross-wave partial-sum
   // buffer (NW * rb * bmb KB) stays <= 32 KB, else 4
   switch (rb * 10 + bmb) {
     case 11: ShrinkLaunch<Tag, 8, 1, 1, EMIT_G, EMIT_F, WT>::run(a, st); break;
+    case 12: ShrinkLaunch<Tag, 8, 1, 2, EMIT_G, EMIT_F, WT>::run(a, st); break;
     case 21: ShrinkLaunch<Tag, 8, 2, 1, EMIT_G, EMIT_F, WT>::run(a, st); break;
     case 22: ShrinkLaunch<Tag, 8, 2, 2, EMIT_G, EMIT_F, WT>::run(a, st); break;
     case 24: ShrinkLaunch<Tag, 4, 2, 4, EMIT_G, EMIT_F, WT>::run(a, st); break;
