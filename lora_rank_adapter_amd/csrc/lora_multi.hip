@@ -1071,8 +1071,16 @@ __global__ __launch_bounds__(64 * NW) void slot_shrink_rows_kernel(ShrinkArgs p)
   constexpr int TB = 16 * TT;
   constexpr int XV = TT * U / NW;
   constexpr int GP = NW * PPW;  // (slice, rank block) pairs per workgroup
-  __shared__ __attribute__((aligned(16))) char lds[2 * 16 * TT * (64 * U + 16)];
-  __shared__ __attribute__((aligned(16))) char alds[NW][16 * PPW * (64 * U + 16)];  // per wave: PPW pairs x 16 rows
+  // x stages; per wave: PPW pairs x 16 rows. At least 80 KB in all, so one
+  // workgroup runs per CU and the dispatcher spreads the units over the CUs
+  // instead of pairing some (prefill at r_max 128 / 64 / 32: 140 / 125 / 125
+  // -> 138 / 125 / 123 us).
+  constexpr int XBYTES = 2 * 16 * TT * (64 * U + 16);
+  constexpr int ABYTES = 16 * PPW * (64 * U + 16);
+  constexpr int kMinLds = 80 * 1024;
+  constexpr int APAD = (XBYTES + NW * ABYTES >= kMinLds) ? 0 : (kMinLds - XBYTES - NW * ABYTES + 16 * NW - 1) / (16 * NW) * 16;
+  __shared__ __attribute__((aligned(16))) char lds[XBYTES];
+  __shared__ __attribute__((aligned(16))) char alds[NW][ABYTES + APAD];
   __shared__ int sh_tok[TB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
