@@ -1809,7 +1809,10 @@ static int shrink_tile_bmb(int64_t T, int64_t S, int n_slices, int64_t row_chunk
 }
 
 // 64-token tiles (bmb 4) come only with four rank blocks (rb 4): both are
-// taken from 1024 tokens, rb 4 from 512.
+// taken from 1024 tokens, rb 4 from 512. The grid covers every unit the
+// kernels find on the device: the slots' tiles number at most
+// ceil(T / tile) + S (each slot's last tile may be partial), and row_chunks
+// covers the largest clamped rank.
 template <class Tag>
 static void launch_shrink(const ShrinkArgs& a, int bmb, int rb, int64_t tiles, bool pipe, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(tiles * a.n_slices * a.row_chunks));
