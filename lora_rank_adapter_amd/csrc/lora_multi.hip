@@ -10,8 +10,10 @@
 //
 // Work decomposition: the active tokens of a slot, in grouped order, are cut
 // into tiles of TB tokens; tile k of the batch is found from counts[] with a
-// wave-level scan. Every tile touches one slot's adapter only, so its rows are
-// shared by all tokens of the tile.
+// wave-level scan (the row-split shrink and the pipelined shrink below 512
+// tokens scan counts[] and ranks[] for live units instead, and deal them to
+// the XCDs in equal runs). Every tile touches one slot's adapter only, so its
+// rows are shared by all tokens of the tile.
 //
 // Kernels:
 //   group_kernel               stable counting sort (one 1024-thread workgroup)
@@ -21,8 +23,8 @@
 //   slot_shrink_pipe_kernel    the same with contiguous per-wave feature ranges,
 //                              descriptor loads and two register stages
 //   slot_shrink_rows_kernel    shrink for many tokens: a 128-token tile x up to
-//                              256 adapter rows per 8-wave workgroup, x staged
-//                              once in LDS, waves split the rows
+//                              128 adapter rows per 8-wave workgroup, x staged
+//                              once in LDS, one 16-row rank block per wave
 //   slot_expand_band_kernel    expand for 512 tokens or more: a token piece x
 //                              256-column band per workgroup, weights in
 //                              registers, h fragments shared through LDS,
