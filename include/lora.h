@@ -312,7 +312,7 @@ int lora_expand_fused(const lora_t3* h, const lora_t3* b, const lora_addressing*
  *              call are unspecified.
  *   y[t, slice i] += scalings[slot(t)] * (x[t] @ a[s, slice i]^T) @ b[s, slice i]^T
  *   for active t on slot s (ranks as in the two calls). Batches of 512 tokens
- *   or more whose token tiles and 1024- or 2048-column chunks fit one round
+ *   or more whose token tiles and 1024-column chunks fit one round
  *   of the GPU's 256 CUs (tiles estimated as if the tokens spread evenly over
  *   the S slots), with x, a and b of one dtype, run as ONE launch that keeps
  *   the rank intermediate on chip and leaves h unwritten; the others run the
